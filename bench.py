@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Throughput of the WKV operator on one MI355X.
+
+Default workload: wkv_forward over B=16, T=4096, C=2048 with bf16 k/v/y and
+fp32 w/u/state (the configuration the bandwidth target is stated for).  A
+step is one wkv_forward call over that batch; inputs are synthetic (seeded,
+shaped like the pages' setting) and already resident in HBM.
+
+Prints one JSON line with tokens*channels/s, the dominant kernel's achieved
+HBM bandwidth against the 8 TB/s peak (algorithmic bytes over the kernel's
+average duration, timed with HIP events on the launch stream), and the fp64
+CPU oracle timed on the same workload on the host cores.
+
+Other workloads (--workload): tiny, small_lm, long_ctx (wkv_forward),
+decode (wkv_step over [32,256,4096] fp32), token_shift (bf16, B=16 T=4096
+C=2048).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "WKV forward tokens·channels/s and achieved HBM GB/s (% of peak) at 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_rnn_forward_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(workload)
+    if not entry or entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("traffic_bytes_per_launch")
+
+
+class ForwardBench:
+    def __init__(self, wl, dev):
+        import numpy as np
+        import torch
+
+        import synth
+        self.wl = wl
+        x = synth.make_forward_inputs(wl)
+        self.host = x
+        if wl.dtype == "bf16":
+            self.k = torch.from_numpy(x.k_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+            self.v = torch.from_numpy(x.v_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            self.k = torch.from_numpy(x.k).to(dev)
+            self.v = torch.from_numpy(x.v).to(dev)
+        self.w = torch.from_numpy(x.w).to(dev)
+        self.u = torch.from_numpy(x.u).to(dev)
+        self.y = torch.empty_like(self.k)
+        es = 2 if wl.dtype == "bf16" else 4
+        self.units = wl.B * wl.T * wl.C                       # tokens * channels per step
+        self.alg_bytes = 3 * es * self.units + 8 * wl.C       # k, v read; y written; w, u
+        self.dtype = "f32"                                    # arithmetic type
+        self.io = "bf16" if wl.dtype == "bf16" else "f32"
+        import linear_attention_rnn_forward_amd as wkv
+        self.wkv = wkv
+
+    def step(self):
+        self.wkv.forward(self.k, self.v, self.w, self.u, out=self.y)
+
+    def config(self):
+        return {"workload": self.wl.name, "B": self.wl.B, "T": self.wl.T, "C": self.wl.C,
+                "io_dtype": self.io, "state_dtype": "f32"}
+
+    def cpu_baseline(self):
+        import oracle
+        x = self.host
+        t0 = time.perf_counter()
+        oracle.forward(x.k, x.v, x.w, x.u)
+        dt = time.perf_counter() - t0
+        return {"value": self.units / dt, "unit": "tokens·channels/s", "cores": oracle.threads(),
+                "kind": "oracle",
+                "sample": f"the full workload ({self.units} tokens*channels), one pass, "
+                          f"{dt:.2f} s including fp64 conversion"}
+
+
+class DecodeBench:
+    """One wkv_step over [L,S,C] per step; k, v of 16 distinct tokens resident
+    in HBM and used in turn; the state starts from a 512-token prefill."""
+
+    def __init__(self, dev, ntok=16):
+        import torch
+
+        import linear_attention_rnn_forward_amd as wkv
+        import synth
+        import synth.device as sd
+        wl = synth.DECODE
+        self.wl = wl
+        self.wkv = wkv
+        w, u = synth.decode_params(wl)
+        self.w = torch.from_numpy(w).to(dev)
+        self.u = torch.from_numpy(u).to(dev)
+        Ln, S, C = wl.L, wl.S, wl.C
+        self.st = tuple(torch.empty((Ln, S, C), device=dev) for _ in range(3))
+        kp = torch.empty((S, wl.prefill_T, C), device=dev)
+        vp = torch.empty_like(kp)
+        for l in range(Ln):
+            sd.decode_prefill_kv(wl, l, kp, vp)
+            wkv.forward(kp, vp, self.w[l], self.u[l], state_out=(self.st[0][l], self.st[1][l], self.st[2][l]))
+        del kp, vp
+        self.kb = torch.empty((ntok, Ln, S, C), device=dev)
+        self.vb = torch.empty_like(self.kb)
+        sd.decode_step_kv(wl, 0, ntok, self.kb, self.vb)
+        self.y = torch.empty((Ln, S, C), device=dev)
+        self.i = 0
+        self.ntok = ntok
+        self.units = Ln * S * C
+        self.alg_bytes = 36 * self.units + 8 * Ln * C
+        self.dtype = "f32"
+
+    def step(self):
+        j = self.i % self.ntok
+        self.wkv.step(self.st, self.kb[j], self.vb[j], self.w, self.u, out=self.y, inplace=True)
+        self.i += 1
+
+    def config(self):
+        return {"workload": self.wl.name, "L": self.wl.L, "S": self.wl.S, "C": self.wl.C,
+                "io_dtype": "f32", "state_dtype": "f32"}
+
+    def cpu_baseline(self):
+        import numpy as np
+
+        import oracle
+        wl = self.wl
+        rng = np.random.default_rng(0)
+        Ls = 4   # a sample of 4 layers of the [32,256,4096] step, 10 steps
+        a = np.zeros((Ls, wl.S, wl.C))
+        b = np.ones((Ls, wl.S, wl.C))
+        p = rng.normal(0, 1, (Ls, wl.S, wl.C))
+        k = rng.normal(0, 1, (Ls, wl.S, wl.C))
+        v = rng.normal(0, 1, (Ls, wl.S, wl.C))
+        w = self.w[:Ls].cpu().numpy()
+        u = self.u[:Ls].cpu().numpy()
+        t0 = time.perf_counter()
+        st = (a, b, p)
+        for _ in range(10):
+            _, st = oracle.step(st, k, v, w, u)
+        dt = time.perf_counter() - t0
+        units = 10 * Ls * wl.S * wl.C
+        return {"value": units / dt, "unit": "tokens·channels/s", "cores": oracle.threads(),
+                "kind": "oracle", "sample": f"10 steps over 4 of the 32 layers ({units} states)"}
+
+
+class TokenShiftBench:
+    def __init__(self, dev):
+        import torch
+
+        import linear_attention_rnn_forward_amd as wkv
+        self.wkv = wkv
+        B, T, C = 16, 4096, 2048
+        g = torch.Generator(device="cpu").manual_seed(6)
+        self.x = torch.randn((B, T, C), generator=g).to(torch.bfloat16).to(dev)
+        self.mu = [torch.rand(C, generator=g).to(dev) for _ in range(3)]
+        self.units = B * T * C
+        self.alg_bytes = 4 * 2 * self.units + 12 * C
+        self.dtype = "f32"
+        self.shape = (B, T, C)
+
+    def step(self):
+        self.wkv.token_shift(self.x, *self.mu)
+
+    def config(self):
+        B, T, C = self.shape
+        return {"workload": "token shift B=16 T=4096 C=2048 bf16", "B": B, "T": T, "C": C,
+                "io_dtype": "bf16"}
+
+    def cpu_baseline(self):
+        import numpy as np
+
+        import oracle
+        x = self.x[:2].float().cpu().numpy()
+        mus = [m.cpu().numpy() for m in self.mu]
+        t0 = time.perf_counter()
+        oracle.token_shift(x, *mus)
+        dt = time.perf_counter() - t0
+        return {"value": x.size / dt, "unit": "tokens·channels/s", "cores": oracle.threads(),
+                "kind": "oracle", "sample": "2 of the 16 batch rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bf16_main",
+                    choices=["tiny", "small_lm", "bf16_main", "long_ctx", "decode", "token_shift"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU kernel only: run it with --gpus 1 "
+              "(the operator shards across GPUs without communication for batch x channels; "
+              "that path is not built here).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.workload in synth.FORWARD_WORKLOADS:
+        bench = ForwardBench(synth.FORWARD_WORKLOADS[args.workload], dev)
+    elif args.workload == "decode":
+        bench = DecodeBench(dev)
+    else:
+        bench = TokenShiftBench(dev)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        bench.step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        bench.step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernel_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
+    med_kernel_s = kernel_ms[len(kernel_ms) // 2] / 1e3
+
+    value = bench.units * args.steps / elapsed
+    achieved = bench.alg_bytes / avg_kernel_s / 1e9
+    traffic = measured_traffic(args.workload)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": traffic,
+                "alg_bytes_per_launch": bench.alg_bytes,
+                "avg_launch_us": round(avg_kernel_s * 1e6, 2),
+                "median_launch_us": round(med_kernel_s * 1e6, 2)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = bench.cpu_baseline()
+        cpu["value"] = float(f"{cpu['value']:.4g}")
+    line = {"metric": METRIC, "value": float(f"{value:.6g}"), "unit": "tokens·channels/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": bench.dtype, "data": "synthetic",
+            "config": bench.config(), "roofline": roofline, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+/*
+ * wkv.h -- C ABI of libwkv: the RWKV-4 WKV operator on AMD MI355X (gfx950).
+ *
+ * Sources for what the operator computes (cited by page and section):
+ *   [aiwiki]    aiwiki.thehackersbrain.dev/entries/rwkv -- "RWKV", the wkv_step
+ *               listing and the note under it
+ *   [tm-math]   aicassindra.com/blogs/transformer_math/tm_rwkv_math.html --
+ *               "The WKV operator: attention with a fixed decay", "Why it
+ *               collapses into a recurrence", "Numerical stability: carry the
+ *               exponent", "Token shift: a two-tap causal convolution"
+ *   [vanos]     vanos001.github.io/placement_prep/llm/architectures/rwkv.html --
+ *               "The WKV Operator: Attention and RNN at Once"
+ *   [multigrid] multigrid.ai/learn/rwkv -- "Prefill, decode, and where each
+ *               form is used", "The state, in bytes"
+ *
+ * Definition ([tm-math] "The WKV operator"), per batch row b and channel c,
+ * tokens counted from 0:
+ *
+ *   y_t = ( sum_{i<t} e^{-(t-1-i) w + k_i} v_i + e^{u + k_t} v_t )
+ *       / ( sum_{i<t} e^{-(t-1-i) w + k_i}     + e^{u + k_t}     )
+ *
+ * with w > 0 the per-channel decay rate and u the current-token bonus.  It is
+ * evaluated by the max-stabilised recurrence on a state (a, b, p) whose true
+ * accumulators are e^p a and e^p b ([tm-math] "Numerical stability"; [aiwiki]
+ * wkv_step).  The empty history is a = b = 0, p = -inf.
+ *
+ * Conventions shared by every call:
+ *   - All array pointers are DEVICE pointers, owned by the caller.  The
+ *     library never allocates, frees or keeps a pointer after returning.
+ *   - Arrays are dense and row-major ("C-contiguous"); shapes are given in
+ *     each call's comment.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls validate their
+ *     arguments on the host, enqueue work on `stream` and return without
+ *     synchronising.  A nonzero return means nothing was enqueued, except
+ *     WKV_ERR_HIP, which reports a launch failure.
+ *   - Errors are negative wkv_status codes; wkv_last_error() gives a message
+ *     for the last failing call on the calling thread.
+ *   - Floating-point results are fp32 arithmetic; bf16 outputs are rounded
+ *     to nearest-even.  p arguments are in natural-log units.  On input any
+ *     p <= -1e30 (including -inf) means "empty"; an empty state is returned
+ *     as p = -inf.
+ *   - Non-finite inputs are outside the contract.
+ *   - w <= 0 is outside the contract ([tm-math] states w = exp(omega) > 0);
+ *     it is not checked.
+ */
+#ifndef WKV_H
+#define WKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of k, v, y (and of x, xr, xk, xv in wkv_token_shift).
+ * w, u and the state are always fp32. */
+typedef enum {
+    WKV_F32 = 0,
+    WKV_BF16 = 1
+} wkv_dtype;
+
+typedef enum {
+    WKV_OK = 0,
+    WKV_ERR_NULL = -1,        /* a required pointer is NULL                       */
+    WKV_ERR_SHAPE = -2,       /* a size is negative / zero where not allowed,     */
+                              /* or a product overflows int64                     */
+    WKV_ERR_DTYPE = -3,       /* unknown wkv_dtype                                */
+    WKV_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than the size query    */
+    WKV_ERR_ALIAS = -5,       /* an output overlaps an input it may not overlap   */
+    WKV_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed       */
+    WKV_ERR_UNSUPPORTED = -7, /* an option this build does not provide            */
+    WKV_ERR_ARG = -8          /* an argument out of its documented range          */
+} wkv_status;
+
+/* Execution path for wkv_forward_path(). */
+typedef enum {
+    WKV_PATH_AUTO = 0,        /* chosen from B*C, T and the device's CU count     */
+    WKV_PATH_SERIAL = 1,      /* one lane per (b, channel group), scan along T    */
+    WKV_PATH_CHUNKED = 2,     /* time-parallel tiles on separate workgroups; partial   */
+                              /* states passed through the workspace                   */
+    WKV_PATH_CHAINED = 3      /* one workgroup per channel group; its waves take       */
+                              /* consecutive sub-chunks and pass the carry through LDS */
+} wkv_path;
+
+/* Bytes of device workspace wkv_forward needs for these sizes on the current
+ * device (0 when the chosen path needs none).  Returns 0 for invalid sizes.
+ * Only the chunked path (WKV_PATH_CHUNKED, chosen when B*C is too small to
+ * occupy the device otherwise) uses one: per-tile partial states, flags and a
+ * tile counter.  Its contents on entry do not matter.  Calls that share a
+ * workspace must be ordered on one stream. */
+size_t wkv_forward_workspace_size(int64_t B, int64_t T, int64_t C, int dtype);
+
+/* Same, for an explicitly chosen path. */
+size_t wkv_forward_workspace_size_path(int64_t B, int64_t T, int64_t C, int dtype, int path);
+
+/*
+ * Training / prefill form: y for every position, and optionally the state
+ * after the last token ([tm-math] "Why it collapses into a recurrence": one
+ * scan over time, parallel across batch and channels; [vanos] "The WKV
+ * Operator", training mode; [multigrid] "Prefill, decode, ...": prefill
+ * yields the state after the last prompt token).
+ *
+ *   B >= 1, T >= 0, C >= 1
+ *   w, u        [C] fp32            decay rate (> 0) and bonus
+ *   k, v        [B,T,C] dtype       keys, values
+ *   y           [B,T,C] dtype       output; must not overlap k, v, w, u or the state
+ *   a_in, b_in, p_in   [B,C] fp32   prior state; all NULL = empty history
+ *   a_out, b_out, p_out [B,C] fp32  state after token T-1; all NULL = not wanted.
+ *                                   May be the same arrays as *_in.
+ *   workspace   device buffer of at least wkv_forward_workspace_size() bytes
+ *               (may be NULL when that size is 0)
+ * T = 0 writes no y and copies the prior state (or the empty state) to *_out.
+ */
+int wkv_forward(int64_t B, int64_t T, int64_t C, int dtype,
+                const float *w, const float *u,
+                const void *k, const void *v, void *y,
+                const float *a_in, const float *b_in, const float *p_in,
+                float *a_out, float *b_out, float *p_out,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/* wkv_forward with the execution path forced (testing and tuning).  The
+ * workspace must be sized with wkv_forward_workspace_size_path() for the same
+ * path. */
+int wkv_forward_path(int64_t B, int64_t T, int64_t C, int dtype, int path,
+                     const float *w, const float *u,
+                     const void *k, const void *v, void *y,
+                     const float *a_in, const float *b_in, const float *p_in,
+                     float *a_out, float *b_out, float *p_out,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Decode: one token for every (layer l, sequence s, channel c) of [L,S,C]
+ * ([aiwiki] wkv_step: state in, (y, state') out; [vanos] "The WKV Operator",
+ * inference mode; [multigrid] "Prefill, decode, ...").
+ *
+ *   L, S, C >= 1
+ *   w, u        [L,C] fp32          per-layer decay rate and bonus
+ *   k, v        [L,S,C] dtype
+ *   y           [L,S,C] dtype       must not overlap any input
+ *   a_in, b_in, p_in    [L,S,C] fp32  required (use p = -inf for an empty history)
+ *   a_out, b_out, p_out [L,S,C] fp32  required; each may equal its *_in (in place),
+ *                                     but must not partially overlap any array
+ * The state is rounded to fp32 after every step (its exponent p once per
+ * token), so a chain of steps follows wkv_forward's outputs to within that
+ * rounding (about 1e-6 relative for keys of unit scale).
+ */
+int wkv_step(int64_t L, int64_t S, int64_t C, int dtype,
+             const float *w, const float *u,
+             const void *k, const void *v, void *y,
+             const float *a_in, const float *b_in, const float *p_in,
+             float *a_out, float *b_out, float *p_out,
+             void *stream);
+
+/*
+ * Token shift ([tm-math] "Token shift: a two-tap causal convolution";
+ * [multigrid] "Token shift and channel mixing"): for each of the three
+ * blends mu_r, mu_k, mu_v
+ *
+ *   xbar_t = mu * x_t + (1 - mu) * x_{t-1}
+ *
+ * over x [B,T,C].  x_{-1} is x_prev [B,C] when given, else 0.
+ *
+ *   x           [B,T,C] dtype
+ *   x_prev      [B,C] dtype or NULL
+ *   mu_r, mu_k, mu_v  [C] fp32
+ *   xr, xk, xv  [B,T,C] dtype       must not overlap x or each other
+ *   x_last      [B,C] dtype or NULL receives x_{T-1} (x_prev or 0 when T = 0)
+ * Evaluated as x_{t-1} + mu * (x_t - x_{t-1}) in fp32.
+ */
+int wkv_token_shift(int64_t B, int64_t T, int64_t C, int dtype,
+                    const void *x, const void *x_prev,
+                    const float *mu_r, const float *mu_k, const float *mu_v,
+                    void *xr, void *xk, void *xv, void *x_last, void *stream);
+
+/* Static description of a status code. */
+const char *wkv_status_string(int status);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char *wkv_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int wkv_abi_version(void);
+
+#define WKV_ABI_VERSION 100
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WKV_H */

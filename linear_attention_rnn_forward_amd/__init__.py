@@ -1,0 +1,266 @@
+"""RWKV-4 WKV operator for AMD MI355X (gfx950): Python binding of libwkv.
+
+This module only marshals arguments: it checks tensors, takes their device
+pointers and the current HIP stream, and calls the C ABI declared in
+``include/wkv.h``.  Every step of the computation runs in the HIP kernels of
+``libwkv.so``; there is no fallback.  PyTorch provides device memory and
+streams.
+
+Operator (aicassindra.com tm_rwkv_math, "The WKV operator: attention with a
+fixed decay"), per batch row and channel::
+
+    y_t = (sum_{i<t} e^{-(t-1-i) w + k_i} v_i + e^{u + k_t} v_t)
+        / (sum_{i<t} e^{-(t-1-i) w + k_i}     + e^{u + k_t})
+
+with decay rate ``w > 0`` and bonus ``u``; the state (a, b, p) carries the
+history with true accumulators e^p a, e^p b (same page, "Numerical
+stability: carry the exponent").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwkv.so")
+
+F32 = 0
+BF16 = 1
+PATH_AUTO = 0
+PATH_SERIAL = 1
+PATH_CHUNKED = 2
+PATH_CHAINED = 3
+_PATHS = {"auto": PATH_AUTO, "serial": PATH_SERIAL, "chunked": PATH_CHUNKED,
+          "chained": PATH_CHAINED}
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+class WkvError(RuntimeError):
+    """A libwkv call returned a nonzero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libwkv status {status}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libwkv.so with its argument types declared.
+
+    Raises RuntimeError when the library has not been built: there is no
+    other implementation to fall back to.
+    """
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(hipcc, gfx950) before using linear_attention_rnn_forward_amd")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        L.wkv_forward_workspace_size.restype = sz
+        L.wkv_forward_workspace_size.argtypes = [i64, i64, i64, i32]
+        L.wkv_forward_workspace_size_path.restype = sz
+        L.wkv_forward_workspace_size_path.argtypes = [i64, i64, i64, i32, i32]
+        L.wkv_forward.restype = i32
+        L.wkv_forward.argtypes = [i64, i64, i64, i32] + [vp] * 11 + [vp, sz, vp]
+        L.wkv_forward_path.restype = i32
+        L.wkv_forward_path.argtypes = [i64, i64, i64, i32, i32] + [vp] * 11 + [vp, sz, vp]
+        L.wkv_step.restype = i32
+        L.wkv_step.argtypes = [i64, i64, i64, i32] + [vp] * 11 + [vp]
+        L.wkv_token_shift.restype = i32
+        L.wkv_token_shift.argtypes = [i64, i64, i64, i32] + [vp] * 9 + [vp]
+        L.wkv_status_string.restype = ctypes.c_char_p
+        L.wkv_status_string.argtypes = [i32]
+        L.wkv_last_error.restype = ctypes.c_char_p
+        L.wkv_last_error.argtypes = []
+        L.wkv_abi_version.restype = i32
+        L.wkv_abi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def check(status: int) -> None:
+    """Raise WkvError for a nonzero libwkv status."""
+    if status != 0:
+        L = lib()
+        msg = L.wkv_last_error().decode() or L.wkv_status_string(status).decode()
+        raise WkvError(status, msg)
+
+
+# ---------------------------------------------------------------------------
+# tensor helpers (torch is imported lazily: the C ABI itself never sees it)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"k, v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _need(t, name, shape=None, dtype=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+
+
+_workspaces: dict = {}
+
+
+def _workspace(device, nbytes: int):
+    """A cached device workspace of at least nbytes for `device` (contents are
+    irrelevant to the library).  Reused across calls on the same stream."""
+    if nbytes == 0:
+        return None
+    torch = _torch()
+    key = (device.type, device.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def workspace_size(B: int, T: int, C: int, dtype: int = F32, path: str = "auto") -> int:
+    """Bytes of workspace wkv_forward needs for these sizes on the current device."""
+    return int(lib().wkv_forward_workspace_size_path(B, T, C, dtype, _PATHS[path]))
+
+
+# ---------------------------------------------------------------------------
+# public calls
+# ---------------------------------------------------------------------------
+
+def forward(k, v, w, u, state=None, return_state=False, path="auto", out=None, state_out=None,
+            workspace=None):
+    """Training / prefill form over all positions.
+
+    k, v: [B,T,C] float32 or bfloat16 (same dtype); w, u: [C] float32.
+    state: None (empty history) or (a, b, p), each [B,C] float32.
+    Returns y [B,T,C] (dtype of k), or (y, (a, b, p)) with return_state.
+    path: "auto", or "serial", "chained", "chunked" to force an execution path.
+    """
+    torch = _torch()
+    _need(k, "k")
+    if k.dim() != 3:
+        raise ValueError("k must be [B,T,C]")
+    B, T, C = k.shape
+    dev = k.device
+    dt = _dtype_code(k)
+    _need(v, "v", k.shape, k.dtype, dev)
+    _need(w, "w", (C,), torch.float32, dev)
+    _need(u, "u", (C,), torch.float32, dev)
+    a_in = b_in = p_in = None
+    if state is not None:
+        a_in, b_in, p_in = (_need(x, n, (B, C), torch.float32, dev)
+                            for x, n in zip(state, ("a_in", "b_in", "p_in")))
+    y = out if out is not None else torch.empty_like(k)
+    _need(y, "out", k.shape, k.dtype, dev)
+    a_out = b_out = p_out = None
+    if return_state or state_out is not None:
+        if state_out is None:
+            state_out = tuple(torch.empty((B, C), dtype=torch.float32, device=dev) for _ in range(3))
+        a_out, b_out, p_out = (_need(x, n, (B, C), torch.float32, dev)
+                               for x, n in zip(state_out, ("a_out", "b_out", "p_out")))
+    code = _PATHS[path]
+    need = int(lib().wkv_forward_workspace_size_path(B, T, C, dt, code))
+    ws = workspace if workspace is not None else _workspace(dev, need)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    with torch.cuda.device(dev):
+        check(lib().wkv_forward_path(B, T, C, dt, code, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                     _ptr(a_in), _ptr(b_in), _ptr(p_in), _ptr(a_out), _ptr(b_out),
+                                     _ptr(p_out), _ptr(ws), ws_bytes, _stream(dev)))
+    if return_state or state_out is not None:
+        return y, (a_out, b_out, p_out)
+    return y
+
+
+def step(state, k, v, w, u, out=None, state_out=None, inplace=False):
+    """One decode token for every (layer, sequence, channel).
+
+    state: (a, b, p), each [L,S,C] float32 (p = -inf for an empty history).
+    k, v: [L,S,C] float32 or bfloat16; w, u: [L,C] float32.
+    Returns (y, (a', b', p')).  inplace=True writes the new state into `state`.
+    """
+    torch = _torch()
+    _need(k, "k")
+    if k.dim() != 3:
+        raise ValueError("k must be [L,S,C]")
+    Ln, S, C = k.shape
+    dev = k.device
+    dt = _dtype_code(k)
+    _need(v, "v", k.shape, k.dtype, dev)
+    _need(w, "w", (Ln, C), torch.float32, dev)
+    _need(u, "u", (Ln, C), torch.float32, dev)
+    a_in, b_in, p_in = (_need(x, n, (Ln, S, C), torch.float32, dev)
+                        for x, n in zip(state, ("a", "b", "p")))
+    if inplace:
+        state_out = (a_in, b_in, p_in)
+    elif state_out is None:
+        state_out = tuple(torch.empty_like(a_in) for _ in range(3))
+    a_out, b_out, p_out = (_need(x, n, (Ln, S, C), torch.float32, dev)
+                           for x, n in zip(state_out, ("a_out", "b_out", "p_out")))
+    y = out if out is not None else torch.empty_like(k)
+    _need(y, "out", k.shape, k.dtype, dev)
+    with torch.cuda.device(dev):
+        check(lib().wkv_step(Ln, S, C, dt, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y), _ptr(a_in),
+                             _ptr(b_in), _ptr(p_in), _ptr(a_out), _ptr(b_out), _ptr(p_out),
+                             _stream(dev)))
+    return y, (a_out, b_out, p_out)
+
+
+def token_shift(x, mu_r, mu_k, mu_v, x_prev=None, return_last=False):
+    """Two-tap causal lerp for the three blends; x [B,T,C] float32/bfloat16,
+    mu_* [C] float32, x_prev [B,C] (dtype of x) or None (zeros).
+    Returns (xr, xk, xv) or (xr, xk, xv, x_last)."""
+    torch = _torch()
+    _need(x, "x")
+    if x.dim() != 3:
+        raise ValueError("x must be [B,T,C]")
+    B, T, C = x.shape
+    dev = x.device
+    dt = _dtype_code(x)
+    for m, n in ((mu_r, "mu_r"), (mu_k, "mu_k"), (mu_v, "mu_v")):
+        _need(m, n, (C,), torch.float32, dev)
+    if x_prev is not None:
+        _need(x_prev, "x_prev", (B, C), x.dtype, dev)
+    xr, xk, xv = (torch.empty_like(x) for _ in range(3))
+    x_last = torch.empty((B, C), dtype=x.dtype, device=dev) if return_last else None
+    with torch.cuda.device(dev):
+        check(lib().wkv_token_shift(B, T, C, dt, _ptr(x), _ptr(x_prev), _ptr(mu_r), _ptr(mu_k),
+                                    _ptr(mu_v), _ptr(xr), _ptr(xk), _ptr(xv), _ptr(x_last),
+                                    _stream(dev)))
+    if return_last:
+        return xr, xk, xv, x_last
+    return xr, xk, xv

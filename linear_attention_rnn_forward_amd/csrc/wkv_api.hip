@@ -1,0 +1,363 @@
+// C ABI of libwkv (declared in include/wkv.h): argument validation, path
+// selection and launch.  No call allocates memory or synchronises.
+#include "wkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "wkv_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return WKV_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(WKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// a*b*c without int64 overflow (all >= 0)
+bool mul3(int64_t a, int64_t b, int64_t c, int64_t* out) {
+    __int128 r = (__int128)a * b;
+    if (r > INT64_MAX) return false;
+    r *= c;
+    if (r > INT64_MAX) return false;
+    *out = (int64_t)r;
+    return true;
+}
+
+struct Range {
+    const char* name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range rng(const char* name, const void* p, int64_t bytes) {
+    Range r;
+    r.name = name;
+    r.lo = reinterpret_cast<uintptr_t>(p);
+    r.hi = r.lo + (p ? uintptr_t(bytes) : 0);
+    return r;
+}
+
+bool overlap(const Range& a, const Range& b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t esize(int dtype) { return dtype == WKV_BF16 ? 2 : 4; }
+
+// outputs may coincide exactly with the input of the same role (in place) but
+// must not overlap any other array
+int check_state_aliasing(const Range* outs, int nouts, const Range* ins, int nins, bool same_role_ok) {
+    for (int i = 0; i < nouts; i++) {
+        for (int j = 0; j < nins; j++) {
+            if (!overlap(outs[i], ins[j])) continue;
+            const bool exact = outs[i].lo == ins[j].lo && outs[i].hi == ins[j].hi;
+            if (same_role_ok && exact && i == j) continue;
+            return fail(WKV_ERR_ALIAS, "%s overlaps %s", outs[i].name, ins[j].name);
+        }
+        for (int j = 0; j < i; j++)
+            if (overlap(outs[i], outs[j]))
+                return fail(WKV_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+    }
+    return WKV_OK;
+}
+
+int forward_impl(int64_t B, int64_t T, int64_t C, int dtype, int path, const float* w,
+                 const float* u, const void* k, const void* v, void* y, const float* a_in,
+                 const float* b_in, const float* p_in, float* a_out, float* b_out, float* p_out,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != WKV_F32 && dtype != WKV_BF16) return fail(WKV_ERR_DTYPE, "unknown dtype %d", dtype);
+    if (path != WKV_PATH_AUTO && path != WKV_PATH_SERIAL && path != WKV_PATH_CHUNKED &&
+        path != WKV_PATH_CHAINED)
+        return fail(WKV_ERR_ARG, "unknown path %d", path);
+    if (B < 1 || C < 1 || T < 0)
+        return fail(WKV_ERR_SHAPE, "need B >= 1, T >= 0, C >= 1 (got B=%lld T=%lld C=%lld)",
+                    (long long)B, (long long)T, (long long)C);
+    int64_t n = 0;
+    if (!mul3(B, T, C, &n) || !mul3(n, 4, 1, &n) || !mul3(B, C, 12, &n))
+        return fail(WKV_ERR_SHAPE, "B*T*C too large");
+    const bool has_in = a_in || b_in || p_in;
+    const bool has_out = a_out || b_out || p_out;
+    if (has_in && !(a_in && b_in && p_in)) return fail(WKV_ERR_NULL, "a_in, b_in, p_in: all or none");
+    if (has_out && !(a_out && b_out && p_out))
+        return fail(WKV_ERR_NULL, "a_out, b_out, p_out: all or none");
+    if (!w || !u) return fail(WKV_ERR_NULL, "w and u are required");
+    if (T > 0 && (!k || !v || !y)) return fail(WKV_ERR_NULL, "k, v and y are required when T > 0");
+
+    const int64_t io_bytes = B * T * C * int64_t(esize(dtype));
+    const int64_t st_bytes = B * C * 4;
+    const Range r_in[] = {rng("a_in", a_in, st_bytes), rng("b_in", b_in, st_bytes),
+                          rng("p_in", p_in, st_bytes), rng("k", k, io_bytes),
+                          rng("v", v, io_bytes), rng("w", w, C * 4), rng("u", u, C * 4)};
+    const Range r_y = rng("y", y, io_bytes);
+    for (const Range& r : r_in)
+        if (overlap(r_y, r)) return fail(WKV_ERR_ALIAS, "y overlaps %s", r.name);
+    const Range r_out[] = {rng("a_out", a_out, st_bytes), rng("b_out", b_out, st_bytes),
+                           rng("p_out", p_out, st_bytes)};
+    if (int rc = check_state_aliasing(r_out, 3, r_in, 7, true)) return rc;
+    for (const Range& r : r_out)
+        if (overlap(r, r_y)) return fail(WKV_ERR_ALIAS, "%s overlaps y", r.name);
+
+    wkv::ForwardProblem pr;
+    pr.B = B;
+    pr.T = T;
+    pr.C = C;
+    pr.dtype = dtype;
+    pr.vec = wkv::pick_forward_vec(C, dtype, aligned(k, 4) && aligned(v, 4) && aligned(y, 4));
+    pr.w = w;
+    pr.u = u;
+    pr.k = k;
+    pr.v = v;
+    pr.y = y;
+    pr.a_in = a_in;
+    pr.b_in = b_in;
+    pr.p_in = p_in;
+    pr.a_out = a_out;
+    pr.b_out = b_out;
+    pr.p_out = p_out;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if (T == 0) {
+        if (!has_out) return ok();
+        hipError_t e = wkv::launch_state_passthrough(pr, s);
+        return e == hipSuccess ? ok() : hip_fail(e, "state copy launch");
+    }
+    if (path == WKV_PATH_AUTO) path = wkv::choose_forward_path(pr, wkv::device_cu_count());
+    if (path == WKV_PATH_CHUNKED) {
+        const wkv::ChunkPlan pl = wkv::plan_chunked(B, T, C, pr.vec);
+        if (double(pl.ngroups) * double(pl.tiles_per_group) > 2147483647.0)
+            return fail(WKV_ERR_SHAPE, "too many tiles for one launch");
+        const size_t need = wkv::forward_workspace_bytes(B, T, C, dtype, WKV_PATH_CHUNKED);
+        if (workspace == nullptr || workspace_bytes < need)
+            return fail(WKV_ERR_WORKSPACE, "chunked path needs %zu workspace bytes, got %zu", need,
+                        workspace ? workspace_bytes : size_t(0));
+        if (!aligned(workspace, 256)) return fail(WKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        const Range r_ws = rng("workspace", workspace, int64_t(need));
+        for (const Range& r : r_in)
+            if (overlap(r_ws, r)) return fail(WKV_ERR_ALIAS, "workspace overlaps %s", r.name);
+        for (const Range& r : r_out)
+            if (overlap(r_ws, r)) return fail(WKV_ERR_ALIAS, "workspace overlaps %s", r.name);
+        if (overlap(r_ws, r_y)) return fail(WKV_ERR_ALIAS, "workspace overlaps y");
+        hipError_t e = wkv::launch_forward_chunked(pr, workspace, s);
+        return e == hipSuccess ? ok() : hip_fail(e, "chunked forward launch");
+    }
+    const int64_t cg = 64 * pr.vec;
+    if (double(B) * double((C + cg - 1) / cg) > 2147483647.0)
+        return fail(WKV_ERR_SHAPE, "too many column groups for one launch");
+    if (path == WKV_PATH_CHAINED) {
+        hipError_t e = wkv::launch_forward_chained(pr, s);
+        return e == hipSuccess ? ok() : hip_fail(e, "chained forward launch");
+    }
+    hipError_t e = wkv::launch_forward_serial(pr, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "serial forward launch");
+}
+
+std::atomic<int> g_cus[64];
+
+}  // namespace
+
+namespace wkv {
+int device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = g_cus[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    g_cus[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+}  // namespace wkv
+
+extern "C" {
+
+int wkv_abi_version(void) { return WKV_ABI_VERSION; }
+
+const char* wkv_status_string(int status) {
+    switch (status) {
+        case WKV_OK: return "ok";
+        case WKV_ERR_NULL: return "a required pointer is NULL";
+        case WKV_ERR_SHAPE: return "invalid or too large shape";
+        case WKV_ERR_DTYPE: return "unknown dtype";
+        case WKV_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+        case WKV_ERR_ALIAS: return "an output overlaps an input it may not overlap";
+        case WKV_ERR_HIP: return "HIP runtime error";
+        case WKV_ERR_UNSUPPORTED: return "unsupported option";
+        case WKV_ERR_ARG: return "argument out of range";
+        default: return "unknown status";
+    }
+}
+
+const char* wkv_last_error(void) { return g_last_error.c_str(); }
+
+size_t wkv_forward_workspace_size_path(int64_t B, int64_t T, int64_t C, int dtype, int path) {
+    if (B < 1 || C < 1 || T < 0) return 0;
+    if (dtype != WKV_F32 && dtype != WKV_BF16) return 0;
+    int64_t n = 0;
+    if (!mul3(B, T, C, &n)) return 0;
+    if (path == WKV_PATH_AUTO) {
+        wkv::ForwardProblem pr{};
+        pr.B = B;
+        pr.T = T;
+        pr.C = C;
+        pr.dtype = dtype;
+        pr.vec = wkv::pick_forward_vec(C, dtype, true);
+        path = wkv::choose_forward_path(pr, wkv::device_cu_count());
+        // the chosen vec can be 1 for misaligned pointers: cover both
+        if (path != WKV_PATH_CHUNKED) {
+            pr.vec = 1;
+            path = wkv::choose_forward_path(pr, wkv::device_cu_count());
+        }
+    }
+    return wkv::forward_workspace_bytes(B, T, C, dtype, path);
+}
+
+size_t wkv_forward_workspace_size(int64_t B, int64_t T, int64_t C, int dtype) {
+    return wkv_forward_workspace_size_path(B, T, C, dtype, WKV_PATH_AUTO);
+}
+
+int wkv_forward(int64_t B, int64_t T, int64_t C, int dtype, const float* w, const float* u,
+                const void* k, const void* v, void* y, const float* a_in, const float* b_in,
+                const float* p_in, float* a_out, float* b_out, float* p_out, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    return forward_impl(B, T, C, dtype, WKV_PATH_AUTO, w, u, k, v, y, a_in, b_in, p_in, a_out,
+                        b_out, p_out, workspace, workspace_bytes, stream);
+}
+
+int wkv_forward_path(int64_t B, int64_t T, int64_t C, int dtype, int path, const float* w,
+                     const float* u, const void* k, const void* v, void* y, const float* a_in,
+                     const float* b_in, const float* p_in, float* a_out, float* b_out,
+                     float* p_out, void* workspace, size_t workspace_bytes, void* stream) {
+    return forward_impl(B, T, C, dtype, path, w, u, k, v, y, a_in, b_in, p_in, a_out, b_out, p_out,
+                        workspace, workspace_bytes, stream);
+}
+
+int wkv_step(int64_t L, int64_t S, int64_t C, int dtype, const float* w, const float* u,
+             const void* k, const void* v, void* y, const float* a_in, const float* b_in,
+             const float* p_in, float* a_out, float* b_out, float* p_out, void* stream) {
+    if (dtype != WKV_F32 && dtype != WKV_BF16) return fail(WKV_ERR_DTYPE, "unknown dtype %d", dtype);
+    if (L < 1 || S < 1 || C < 1)
+        return fail(WKV_ERR_SHAPE, "need L, S, C >= 1 (got L=%lld S=%lld C=%lld)", (long long)L,
+                    (long long)S, (long long)C);
+    int64_t n = 0;
+    if (!mul3(L, S, C, &n) || !mul3(n, 4, 1, &n)) return fail(WKV_ERR_SHAPE, "L*S*C too large");
+    n = L * S * C;
+    if (!w || !u || !k || !v || !y || !a_in || !b_in || !p_in || !a_out || !b_out || !p_out)
+        return fail(WKV_ERR_NULL, "every wkv_step array is required");
+    const int64_t io = n * int64_t(esize(dtype));
+    const Range r_in[] = {rng("a_in", a_in, n * 4), rng("b_in", b_in, n * 4), rng("p_in", p_in, n * 4),
+                          rng("k", k, io), rng("v", v, io), rng("w", w, L * C * 4),
+                          rng("u", u, L * C * 4)};
+    const Range r_y = rng("y", y, io);
+    for (const Range& r : r_in)
+        if (overlap(r_y, r)) return fail(WKV_ERR_ALIAS, "y overlaps %s", r.name);
+    const Range r_out[] = {rng("a_out", a_out, n * 4), rng("b_out", b_out, n * 4),
+                           rng("p_out", p_out, n * 4)};
+    if (int rc = check_state_aliasing(r_out, 3, r_in, 7, true)) return rc;
+    for (const Range& r : r_out)
+        if (overlap(r, r_y)) return fail(WKV_ERR_ALIAS, "%s overlaps y", r.name);
+    if (double(n) / 256.0 > 2147483647.0) return fail(WKV_ERR_SHAPE, "too many elements for one launch");
+
+    wkv::StepProblem pr;
+    pr.L = L;
+    pr.S = S;
+    pr.C = C;
+    pr.dtype = dtype;
+    const uintptr_t io_align = dtype == WKV_BF16 ? 8 : 16;
+    const bool al = aligned(k, io_align) && aligned(v, io_align) && aligned(y, io_align) &&
+                    aligned(a_in, 16) && aligned(b_in, 16) && aligned(p_in, 16) &&
+                    aligned(a_out, 16) && aligned(b_out, 16) && aligned(p_out, 16);
+    pr.vec = (C % 4 == 0 && al) ? 4 : 1;
+    pr.w = w;
+    pr.u = u;
+    pr.k = k;
+    pr.v = v;
+    pr.y = y;
+    pr.a_in = a_in;
+    pr.b_in = b_in;
+    pr.p_in = p_in;
+    pr.a_out = a_out;
+    pr.b_out = b_out;
+    pr.p_out = p_out;
+    hipError_t e = wkv::launch_step(pr, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "step launch");
+}
+
+int wkv_token_shift(int64_t B, int64_t T, int64_t C, int dtype, const void* x, const void* x_prev,
+                    const float* mu_r, const float* mu_k, const float* mu_v, void* xr, void* xk,
+                    void* xv, void* x_last, void* stream) {
+    if (dtype != WKV_F32 && dtype != WKV_BF16) return fail(WKV_ERR_DTYPE, "unknown dtype %d", dtype);
+    if (B < 1 || C < 1 || T < 0)
+        return fail(WKV_ERR_SHAPE, "need B >= 1, T >= 0, C >= 1 (got B=%lld T=%lld C=%lld)",
+                    (long long)B, (long long)T, (long long)C);
+    int64_t n = 0;
+    if (!mul3(B, T, C, &n) || !mul3(n, 4, 1, &n)) return fail(WKV_ERR_SHAPE, "B*T*C too large");
+    n = B * T * C;
+    if (!mu_r || !mu_k || !mu_v) return fail(WKV_ERR_NULL, "mu_r, mu_k, mu_v are required");
+    if (T > 0 && (!x || !xr || !xk || !xv)) return fail(WKV_ERR_NULL, "x, xr, xk, xv are required");
+    const int64_t es = int64_t(esize(dtype));
+    const Range r_in[] = {rng("x", x, n * es), rng("x_prev", x_prev, B * C * es),
+                          rng("mu_r", mu_r, C * 4), rng("mu_k", mu_k, C * 4), rng("mu_v", mu_v, C * 4)};
+    const Range r_out[] = {rng("xr", xr, n * es), rng("xk", xk, n * es), rng("xv", xv, n * es),
+                           rng("x_last", x_last, B * C * es)};
+    for (int i = 0; i < 4; i++) {
+        for (const Range& r : r_in)
+            if (overlap(r_out[i], r)) return fail(WKV_ERR_ALIAS, "%s overlaps %s", r_out[i].name, r.name);
+        for (int j = 0; j < i; j++)
+            if (overlap(r_out[i], r_out[j]))
+                return fail(WKV_ERR_ALIAS, "%s overlaps %s", r_out[i].name, r_out[j].name);
+    }
+    int vec = 1;
+    for (int cand : {4, 2}) {
+        const uintptr_t a = uintptr_t(cand) * uintptr_t(es);
+        if (C % cand == 0 && aligned(x, a) && aligned(xr, a) && aligned(xk, a) && aligned(xv, a) &&
+            aligned(x_prev, a) && aligned(x_last, a)) {
+            vec = cand;
+            break;
+        }
+    }
+    if (double(B) * double((T + 31) / 32) * double(C / vec) / 256.0 > 2147483647.0)
+        return fail(WKV_ERR_SHAPE, "too many elements for one launch");
+    wkv::ShiftProblem pr;
+    pr.B = B;
+    pr.T = T;
+    pr.C = C;
+    pr.dtype = dtype;
+    pr.vec = vec;
+    pr.x = x;
+    pr.x_prev = x_prev;
+    pr.mu_r = mu_r;
+    pr.mu_k = mu_k;
+    pr.mu_v = mu_v;
+    pr.xr = xr;
+    pr.xk = xk;
+    pr.xv = xv;
+    pr.x_last = x_last;
+    hipError_t e = wkv::launch_token_shift(pr, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "token shift launch");
+}
+
+}  // extern "C"

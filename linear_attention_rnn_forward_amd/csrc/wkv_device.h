@@ -1,0 +1,376 @@
+// Device-side building blocks of the WKV kernels (gfx950, wave64).
+//
+// The operator ([tm-math] = aicassindra.com tm_rwkv_math, "The WKV operator:
+// attention with a fixed decay"; "Numerical stability: carry the exponent"):
+// per channel, state (a, b, p) with true accumulators e^p a, e^p b; per token
+//
+//   read-out  y  = (e^{p} a + e^{u+k} v) / (e^{p} b + e^{u+k})    (history + bonus)
+//   fold-in   p' = max(p - w, k)
+//             a' = e^{p-w-p'} a + e^{k-p'} v,   b' = e^{p-w-p'} b + e^{k-p'}
+//
+// How it is evaluated here (fp32 throughout; every exp argument is <= 0):
+//
+// 1. Exponents stay in natural-log units; a weight e^{x} is v_exp_f32 of
+//    x log2 e, and the multiply by log2 e is applied to differences of
+//    exponents (small where it matters), never to the exponents themselves.
+//
+// 2. One exponential per token.  With d the exponent of the decayed history
+//    minus that of the new token, exactly one of the two weights is e^0 = 1
+//    and the other is e = e^{-|d|}:
+//      d >= 0:  alpha = 1, beta = e   (the history keeps the maximum)
+//      d <  0:  alpha = e, beta = 1   (the new token becomes the maximum)
+//
+// 3. The read-out reuses the fold-in weights.  Multiplying numerator and
+//    denominator of the read-out by e^{-w-p'} gives
+//      y = (alpha a + beta c v) / (alpha b + beta c),   c = e^{u-w}
+//    -- the same ratio with one per-channel constant and no second
+//    exponential.  It is used when |u - w| <= 44 (c within [2^-64, 2^64]);
+//    other channels take the read-out as written, with its own single
+//    exponential.
+//
+// 4. No rounding accumulates in the running maximum.  Subtracting w from p at
+//    every token would round at every token, and over many tokens the error
+//    in p (which sets the weight of the whole history against each new token)
+//    grows linearly.  Instead, inside a block of tokens the maximum is held
+//    as an anchor `kas` in the frame of the block start: before token i of
+//    the block p = kas - i w, and the new key enters the frame as
+//    r = k + (i+1) w (one fma).  Then d = kas - r and the new anchor is
+//    max(kas, r); nothing is subtracted token by token.  Between blocks the
+//    state carries the anchor A and an exact token count m (p = A - m w),
+//    so each exponent is formed with a couple of roundings however long the
+//    sequence is.
+//
+// 5. exp is v_exp_f32 (2^x); the division is v_rcp_f32 and a multiply.  Both
+//    are within about 1 ulp.
+//
+// 6. The empty history has exponent kEmptyP (a large finite negative), so
+//    differences of two empty exponents are 0 rather than NaN.
+//
+// 7. Chunks.  Over a span of n tokens a state X becomes e^{-n w} X + G
+//    ([tm-math] "Why it collapses into a recurrence": every older term gains
+//    one factor e^{-w} per token), where G is the span's own state started
+//    from the empty history.  In (a, b, A, m) form that is combine() below.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wkv {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kEmptyP = -1.0e38f;      // the empty history's exponent
+constexpr float kEmptyIn = -1.0e30f;     // state inputs at or below this are empty
+constexpr float kFusedMaxAbsUW = 44.0f;  // |u - w| bound for the fused read-out
+
+enum : int { kF32 = 0, kBF16 = 1 };
+
+// e^{-|d|}
+__device__ __forceinline__ float exp_neg_abs(float d) {
+    return __builtin_amdgcn_exp2f(-__builtin_fabsf(d * kLog2e));
+}
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Per-channel constants of the forward kernels.
+struct Chan {
+    float w;     // decay rate
+    float wmu;   // w - u
+    float c;     // e^{u-w}
+    bool fused;  // fused read-out allowed
+};
+
+__device__ __forceinline__ Chan make_chan(float w, float u) {
+    Chan ch;
+    ch.w = w;
+    ch.wmu = w - u;
+    ch.fused = __builtin_fabsf(ch.wmu) <= kFusedMaxAbsUW;
+    ch.c = __builtin_amdgcn_exp2f(ch.fused ? -ch.wmu * kLog2e : 0.0f);
+    return ch;
+}
+
+// One token inside a frame (see 4.).  ip1 = i + 1 for token i of the frame.
+// Updates a, b and the anchor kas; returns y.  `keep` is false when the new
+// token became the maximum.
+template <bool FUSED_ONLY>
+__device__ __forceinline__ float frame_token(float& a, float& b, float& kas, float k, float v,
+                                             const Chan& ch, float ip1, bool& keep_out) {
+    const float r = __builtin_fmaf(ip1, ch.w, k);  // new key in the block frame
+    const float d = kas - r;                       // decayed history minus new token
+    const float e = exp_neg_abs(d);
+    const bool keep = d >= 0.0f;
+    const float alpha = keep ? 1.0f : e;
+    const float beta = keep ? e : 1.0f;
+    const float t1 = alpha * a;
+    float y;
+    if (FUSED_ONLY || ch.fused) {
+        const float delta = beta * ch.c;
+        y = __builtin_fmaf(delta, v, t1) * fast_rcp(__builtin_fmaf(alpha, b, delta));
+    } else {
+        // read-out as written: history exponent p = kas - i w against u + k
+        const float dr = d + ch.wmu;
+        const float er = exp_neg_abs(dr);
+        const bool kr = dr >= 0.0f;
+        const float ar = kr ? 1.0f : er;
+        const float br = kr ? er : 1.0f;
+        y = __builtin_fmaf(br, v, ar * a) * fast_rcp(__builtin_fmaf(ar, b, br));
+    }
+    a = __builtin_fmaf(beta, v, t1);
+    b = __builtin_fmaf(alpha, b, beta);
+    kas = __builtin_fmaxf(kas, r);
+    keep_out = keep;
+    return y;
+}
+
+// X <- X (+) G: G is the state of the n tokens that follow X, started from
+// the empty history; both in anchor form (exponent = A - m w).
+__device__ __forceinline__ void combine(float& xa, float& xb, float& xA, float& xm, float ga,
+                                        float gb, float gA, float gm, float n, float w) {
+    const float xm2 = xm + n;
+    const float px = __builtin_fmaf(-xm2, w, xA);
+    const float pg = __builtin_fmaf(-gm, w, gA);
+    const float d = px - pg;
+    const float e = exp_neg_abs(d);
+    const bool keep = d >= 0.0f;
+    const float alpha = keep ? 1.0f : e;
+    const float beta = keep ? e : 1.0f;
+    xa = __builtin_fmaf(beta, ga, alpha * xa);
+    xb = __builtin_fmaf(beta, gb, alpha * xb);
+    xA = keep ? xA : gA;
+    xm = keep ? xm2 : gm;
+}
+
+// Decode step: the state is stored after every token, so its exponent is
+// rounded once per token (p' = fl(p - w) when the history keeps the maximum).
+__device__ __forceinline__ float decode_token(float& a, float& b, float& p, float k, float v,
+                                              float w, float u) {
+    const float pw = p - w;
+    const float d = pw - k;
+    const float e = exp_neg_abs(d);
+    const bool keep = d >= 0.0f;
+    const float alpha = keep ? 1.0f : e;
+    const float beta = keep ? e : 1.0f;
+    const float t1 = alpha * a;
+    const float wmu = w - u;
+    float y;
+    if (__builtin_fabsf(wmu) <= kFusedMaxAbsUW) {
+        const float delta = beta * __builtin_amdgcn_exp2f(-wmu * kLog2e);
+        y = __builtin_fmaf(delta, v, t1) * fast_rcp(__builtin_fmaf(alpha, b, delta));
+    } else {
+        const float dr = d + wmu;
+        const float er = exp_neg_abs(dr);
+        const bool kr = dr >= 0.0f;
+        const float ar = kr ? 1.0f : er;
+        const float br = kr ? er : 1.0f;
+        y = __builtin_fmaf(br, v, ar * a) * fast_rcp(__builtin_fmaf(ar, b, br));
+    }
+    a = __builtin_fmaf(beta, v, t1);
+    b = __builtin_fmaf(alpha, b, beta);
+    p = keep ? pw : k;
+    return y;
+}
+
+__device__ __forceinline__ float clamp_empty(float p) { return p <= kEmptyIn ? kEmptyP : p; }
+__device__ __forceinline__ float export_p(float p) { return p <= kEmptyIn ? -__builtin_inff() : p; }
+
+// ---------------------------------------------------------------------------
+// Storage of k, v, y: VEC consecutive channels per lane in one "raw" word.
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    // v_cvt_pk_bf16_f32: round to nearest even
+    f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+// Widening is recomputed at every use (the asm is opaque to common
+// subexpression elimination): keeping the widened values of a whole chunk live
+// between passes would double the registers the chunk occupies.
+__device__ __forceinline__ float bf16_lo(uint32_t r) {
+    uint32_t x;
+    asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(x) : "v"(r));
+    return __uint_as_float(x);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t r) {
+    uint32_t x;
+    asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(x) : "v"(r));
+    return __uint_as_float(x);
+}
+
+template <int DT, int VEC>
+struct Io;
+
+template <>
+struct Io<kF32, 1> {
+    using Raw = float;
+    static __device__ __forceinline__ void unpack(Raw r, float (&x)[1]) { x[0] = r; }
+    static __device__ __forceinline__ Raw pack(const float (&x)[1]) { return x[0]; }
+    static __device__ __forceinline__ Raw zero() { return 0.0f; }
+};
+
+template <>
+struct Io<kF32, 2> {
+    using Raw = float2;
+    static __device__ __forceinline__ void unpack(Raw r, float (&x)[2]) { x[0] = r.x; x[1] = r.y; }
+    static __device__ __forceinline__ Raw pack(const float (&x)[2]) { return make_float2(x[0], x[1]); }
+    static __device__ __forceinline__ Raw zero() { return make_float2(0.0f, 0.0f); }
+};
+
+template <>
+struct Io<kF32, 4> {
+    using Raw = float4;
+    static __device__ __forceinline__ void unpack(Raw r, float (&x)[4]) {
+        x[0] = r.x; x[1] = r.y; x[2] = r.z; x[3] = r.w;
+    }
+    static __device__ __forceinline__ Raw pack(const float (&x)[4]) {
+        return make_float4(x[0], x[1], x[2], x[3]);
+    }
+    static __device__ __forceinline__ Raw zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+};
+
+template <>
+struct Io<kBF16, 1> {
+    using Raw = uint16_t;
+    static __device__ __forceinline__ void unpack(Raw r, float (&x)[1]) {
+        x[0] = __uint_as_float(uint32_t(r) << 16);
+    }
+    static __device__ __forceinline__ Raw pack(const float (&x)[1]) {
+        return uint16_t(pack_bf16x2(x[0], 0.0f) & 0xffffu);
+    }
+    static __device__ __forceinline__ Raw zero() { return 0; }
+};
+
+template <>
+struct Io<kBF16, 2> {
+    using Raw = uint32_t;
+    static __device__ __forceinline__ void unpack(Raw r, float (&x)[2]) {
+        x[0] = bf16_lo(r);
+        x[1] = bf16_hi(r);
+    }
+    static __device__ __forceinline__ Raw pack(const float (&x)[2]) { return pack_bf16x2(x[0], x[1]); }
+    static __device__ __forceinline__ Raw zero() { return 0u; }
+};
+
+template <>
+struct Io<kBF16, 4> {
+    using Raw = uint2;
+    static __device__ __forceinline__ void unpack(Raw r, float (&x)[4]) {
+        x[0] = bf16_lo(r.x); x[1] = bf16_hi(r.x); x[2] = bf16_lo(r.y); x[3] = bf16_hi(r.y);
+    }
+    static __device__ __forceinline__ Raw pack(const float (&x)[4]) {
+        return make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+    }
+    static __device__ __forceinline__ Raw zero() { return make_uint2(0u, 0u); }
+};
+
+// ---------------------------------------------------------------------------
+// Buffer addressing: a wave-uniform base in a buffer resource (SGPRs), a
+// per-lane byte offset (VGPR, fixed for the kernel) and a per-token byte
+// offset (SGPR).  Address arithmetic then costs no vector instructions.
+// ---------------------------------------------------------------------------
+
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer (stride 0) covering 4 GiB from `base`; dword 3 selects 32-bit
+// data format, as required by untyped buffer instructions on gfx9.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+
+template <typename Raw>
+struct Buf;
+
+template <>
+struct Buf<float> {
+    static __device__ __forceinline__ float load(rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    }
+    static __device__ __forceinline__ void store(float x, rsrc_t r, uint32_t voff, uint32_t soff) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff, soff, 0);
+    }
+};
+template <>
+struct Buf<uint32_t> {
+    static __device__ __forceinline__ uint32_t load(rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    }
+    static __device__ __forceinline__ void store(uint32_t x, rsrc_t r, uint32_t voff, uint32_t soff) {
+        __builtin_amdgcn_raw_buffer_store_b32(x, r, voff, soff, 0);
+    }
+};
+template <>
+struct Buf<uint16_t> {
+    static __device__ __forceinline__ uint16_t load(rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    }
+    static __device__ __forceinline__ void store(uint16_t x, rsrc_t r, uint32_t voff, uint32_t soff) {
+        __builtin_amdgcn_raw_buffer_store_b16(x, r, voff, soff, 0);
+    }
+};
+template <>
+struct Buf<float2> {
+    static __device__ __forceinline__ float2 load(rsrc_t r, uint32_t voff, uint32_t soff) {
+        const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        return make_float2(__uint_as_float(x.x), __uint_as_float(x.y));
+    }
+    static __device__ __forceinline__ void store(float2 x, rsrc_t r, uint32_t voff, uint32_t soff) {
+        const u32x2_t v = {__float_as_uint(x.x), __float_as_uint(x.y)};
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
+    }
+};
+template <>
+struct Buf<uint2> {
+    static __device__ __forceinline__ uint2 load(rsrc_t r, uint32_t voff, uint32_t soff) {
+        const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        return make_uint2(x.x, x.y);
+    }
+    static __device__ __forceinline__ void store(uint2 x, rsrc_t r, uint32_t voff, uint32_t soff) {
+        const u32x2_t v = {x.x, x.y};
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
+    }
+};
+template <>
+struct Buf<float4> {
+    static __device__ __forceinline__ float4 load(rsrc_t r, uint32_t voff, uint32_t soff) {
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+        return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                           __uint_as_float(x.w));
+    }
+    static __device__ __forceinline__ void store(float4 x, rsrc_t r, uint32_t voff, uint32_t soff) {
+        const u32x4_t v = {__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z),
+                           __float_as_uint(x.w)};
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup publication of partial states.
+//
+// Data words are written with agent-scope relaxed atomic stores and read with
+// agent-scope relaxed atomic loads: those are coherent across the chip's
+// XCDs without flushing or invalidating the L2.  A publisher orders its data
+// before its flag by waiting for all of its outstanding memory operations
+// (s_waitcnt vmcnt(0)) before the flag store; a reader issues its data loads
+// only after its flag load has returned the expected value.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void st_agent(float* p, float x) {
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_flag(uint64_t* p, uint64_t x) {
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_flag(const uint64_t* p) {
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave has issued has completed.
+__device__ __forceinline__ void wait_all_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Keep the compiler from moving memory operations across this point.
+__device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
+}  // namespace wkv

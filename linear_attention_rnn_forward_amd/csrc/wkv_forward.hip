@@ -1,0 +1,841 @@
+// wkv_forward kernels: the training/prefill form over [B,T,C].
+//
+// Two execution paths compute the same recurrence ([tm-math] = aicassindra.com
+// tm_rwkv_math, "Why it collapses into a recurrence": a scan over time that
+// parallelises across batch and channels; [vanos] = vanos001.github.io rwkv,
+// "The WKV Operator": a serial per-position scan or a chunked parallel form):
+//
+// serial   One wave per column group (64 lanes x VEC adjacent channels of one
+//          batch row); each lane scans its channels along T with the state in
+//          registers.  Used when B*C alone fills the chip.
+//
+// chunked  One workgroup per tile = (column group, NW*L consecutive tokens);
+//          wave w of the tile owns L tokens.  Each wave loads its k, v once
+//          into registers, folds them into a partial state from the empty
+//          history, and the partial states are combined
+//            - across the waves of the tile in LDS, and
+//            - across tiles of the same column group through global memory
+//              with a single-pass decoupled look-back (each tile publishes
+//              its own aggregate, then its inclusive prefix; a successor
+//              combines aggregates backwards until it meets an inclusive
+//              prefix).
+//          With its carried-in state each wave then re-runs its tokens from
+//          registers and writes y.  k and v are read from HBM once.
+//          Tiles are handed out in (chunk, group) order by an atomic ticket,
+//          so a tile only ever waits for tiles that already started.
+#include "wkv_device.h"
+#include "wkv_internal.h"
+
+#include <atomic>
+
+namespace wkv {
+namespace {
+
+// Launch geometry (the macros exist so that tuning builds can override them).
+#ifndef WKV_SERIAL_TOKENS
+#define WKV_SERIAL_TOKENS 16
+#endif
+#ifndef WKV_CHUNK_TOKENS
+#define WKV_CHUNK_TOKENS 32
+#endif
+#ifndef WKV_CHUNK_WAVES
+#define WKV_CHUNK_WAVES 8
+#endif
+#ifndef WKV_FRAME_TOKENS
+#define WKV_FRAME_TOKENS 8
+#endif
+constexpr int kSerialWaves = 4;                  // waves per workgroup on the serial path
+constexpr int kSerialTokens = WKV_SERIAL_TOKENS; // tokens loaded per batch on the serial path
+constexpr int kChunkTokens = WKV_CHUNK_TOKENS;   // L: tokens per wave on the chunked path
+constexpr int kChunkWaves = WKV_CHUNK_WAVES;     // NW: waves per tile
+constexpr int kFrameTokens = WKV_FRAME_TOKENS;   // tokens per frame of the running maximum
+constexpr uint64_t kSpinTicks = 20000000;  // 200 ms at 100 MHz
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Per-lane state of VEC channels: accumulators a, b and the exponent of the
+// running maximum in anchor form, p = A - m * w (m a token count).
+template <int VEC>
+struct Lane {
+    Chan ch[VEC];
+    float a[VEC], b[VEC], A[VEC], m[VEC];
+};
+
+template <int VEC>
+__device__ __forceinline__ void load_params(Lane<VEC>& s, const ForwardProblem& pr, int64_t c,
+                                            bool active) {
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        const float w = active ? pr.w[c + q] : 1.0f;
+        const float u = active ? pr.u[c + q] : 0.0f;
+        s.ch[q] = make_chan(w, u);
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_state(float (&a)[VEC], float (&b)[VEC], float (&A)[VEC],
+                                           float (&m)[VEC], const ForwardProblem& pr, int64_t col,
+                                           bool active) {
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        m[q] = 0.0f;
+        if (active && pr.a_in != nullptr) {
+            a[q] = pr.a_in[col + q];
+            b[q] = pr.b_in[col + q];
+            A[q] = clamp_empty(pr.p_in[col + q]);
+        } else {
+            a[q] = 0.0f;
+            b[q] = 0.0f;
+            A[q] = kEmptyP;
+        }
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void store_state(const Lane<VEC>& s, const ForwardProblem& pr, int64_t col) {
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        pr.a_out[col + q] = s.a[q];
+        pr.b_out[col + q] = s.b[q];
+        pr.p_out[col + q] = export_p(__builtin_fmaf(-s.m[q], s.ch[q].w, s.A[q]));
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ bool wave_all_fused(const Lane<VEC>& s) {
+    bool f = true;
+#pragma unroll
+    for (int q = 0; q < VEC; q++) f = f && s.ch[q].fused;
+    return __builtin_amdgcn_ballot_w64(!f) == 0;
+}
+
+// Run n tokens (n == NTOK when FULL) from the state in s, writing y.  The
+// tokens are the first n of kr/vr.  The frame of the running maximum (see
+// wkv_device.h, 4.) moves forward every kFrameTokens tokens, so a key enters
+// its frame shifted by at most kFrameTokens * w and its rounding stays at the
+// scale of the key itself.  Moving the frame rounds once; an exact anchor
+// and token count are kept across blocks.
+template <int DT, int VEC, int NTOK, bool FUSED_ONLY, bool FULL>
+__device__ __forceinline__ void run_block(Lane<VEC>& s, const typename Io<DT, VEC>::Raw (&kr)[NTOK],
+                                          const typename Io<DT, VEC>::Raw (&vr)[NTOK], rsrc_t yr_,
+                                          uint32_t voff, uint32_t row_bytes, int n, bool active) {
+    using IO = Io<DT, VEC>;
+    using Raw = typename IO::Raw;
+    constexpr int F = kFrameTokens;
+    static_assert(NTOK % F == 0, "blocks are whole frames");
+    float kas[VEC];
+    bool all_keep[VEC];
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        kas[q] = __builtin_fmaf(-s.m[q], s.ch[q].w, s.A[q]);
+        all_keep[q] = true;
+    }
+#pragma unroll
+    for (int i = 0; i < NTOK; i++) {
+        if (FULL || i < n) {
+            if (i % F == 0 && i > 0) {
+#pragma unroll
+                for (int q = 0; q < VEC; q++) kas[q] = __builtin_fmaf(-float(F), s.ch[q].w, kas[q]);
+            }
+            float kf[VEC], vf[VEC], yf[VEC];
+            IO::unpack(kr[i], kf);
+            IO::unpack(vr[i], vf);
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                bool keep;
+                yf[q] = frame_token<FUSED_ONLY>(s.a[q], s.b[q], kas[q], kf[q], vf[q], s.ch[q],
+                                                float(i % F + 1), keep);
+                all_keep[q] = all_keep[q] && keep;
+            }
+            if (active) Buf<Raw>::store(IO::pack(yf), yr_, voff, uint32_t(i) * row_bytes);
+        }
+    }
+    // the last frame starts at token f0 of the block
+    const int last = (FULL ? NTOK : n) - 1;
+    const float since = float(last - (last / F) * F + 1);  // tokens since the last frame start
+    const float nf = FULL ? float(NTOK) : float(n);
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        // a new maximum inside the block becomes the anchor, in the last frame
+        s.A[q] = all_keep[q] ? s.A[q] : kas[q];
+        s.m[q] = all_keep[q] ? s.m[q] + nf : since;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// serial path
+// ---------------------------------------------------------------------------
+
+template <int DT, int VEC, bool FUSED_ONLY>
+__device__ __forceinline__ void serial_scan(Lane<VEC>& s, const ForwardProblem& pr, const char* kbase,
+                                            const char* vbase, char* ybase, uint32_t voff,
+                                            uint32_t row_bytes, bool active) {
+    using IO = Io<DT, VEC>;
+    using Raw = typename IO::Raw;
+    constexpr int U = kSerialTokens;
+    const int64_t T = pr.T;
+    for (int64_t t0 = 0; t0 < T; t0 += U) {
+        const int n = (T - t0) < U ? int(T - t0) : U;
+        const int64_t off = t0 * int64_t(row_bytes);
+        const rsrc_t kr_ = make_rsrc(kbase + off);
+        const rsrc_t vr_ = make_rsrc(vbase + off);
+        const rsrc_t yr_ = make_rsrc(ybase + off);
+        Raw kr[U], vr[U];
+        if (n == U) {
+#pragma unroll
+            for (int i = 0; i < U; i++) {
+                kr[i] = Buf<Raw>::load(kr_, voff, uint32_t(i) * row_bytes);
+                vr[i] = Buf<Raw>::load(vr_, voff, uint32_t(i) * row_bytes);
+            }
+            run_block<DT, VEC, U, FUSED_ONLY, true>(s, kr, vr, yr_, voff, row_bytes, n, active);
+        } else {
+#pragma unroll
+            for (int i = 0; i < U; i++) {
+                kr[i] = IO::zero();
+                vr[i] = IO::zero();
+                if (i < n) {
+                    kr[i] = Buf<Raw>::load(kr_, voff, uint32_t(i) * row_bytes);
+                    vr[i] = Buf<Raw>::load(vr_, voff, uint32_t(i) * row_bytes);
+                }
+            }
+            run_block<DT, VEC, U, FUSED_ONLY, false>(s, kr, vr, yr_, voff, row_bytes, n, active);
+        }
+    }
+}
+
+template <int DT, int VEC>
+__global__ __launch_bounds__(kSerialWaves * 64) void forward_serial_kernel(ForwardProblem pr,
+                                                                           int64_t ngroups,
+                                                                           int64_t gpr) {
+    using IO = Io<DT, VEC>;
+    using Raw = typename IO::Raw;
+    const int64_t g = int64_t(blockIdx.x) * kSerialWaves + wave_id();
+    if (g >= ngroups) return;
+    const int lane = lane_id();
+    const int64_t bb = g / gpr;
+    const int64_t c0 = (g - bb * gpr) * (64 * VEC);
+    const int64_t c = c0 + int64_t(lane) * VEC;
+    const bool active = c < pr.C;
+    constexpr int64_t es = sizeof(Raw) / VEC;
+    const uint32_t row_bytes = uint32_t(pr.C * es);
+    // lanes past C read lane 0's words (in bounds) and never store
+    const uint32_t voff = active ? uint32_t(lane) * uint32_t(sizeof(Raw)) : 0u;
+    const int64_t base = (bb * pr.T * pr.C + c0) * es;
+
+    Lane<VEC> s;
+    load_params(s, pr, c, active);
+    load_state(s.a, s.b, s.A, s.m, pr, bb * pr.C + c, active);
+
+    const char* kbase = static_cast<const char*>(pr.k) + base;
+    const char* vbase = static_cast<const char*>(pr.v) + base;
+    char* ybase = static_cast<char*>(pr.y) + base;
+    if (wave_all_fused(s))
+        serial_scan<DT, VEC, true>(s, pr, kbase, vbase, ybase, voff, row_bytes, active);
+    else
+        serial_scan<DT, VEC, false>(s, pr, kbase, vbase, ybase, voff, row_bytes, active);
+    if (active && pr.a_out != nullptr) store_state(s, pr, bb * pr.C + c);
+}
+
+// ---------------------------------------------------------------------------
+// chunked path
+// ---------------------------------------------------------------------------
+
+struct ChunkArgs {
+    int64_t ngroups;          // column groups
+    int64_t gpr;              // column groups per batch row
+    int64_t tiles_per_group;  // tiles along T
+    uint32_t* ticket;         // tile dispenser (zeroed before the launch)
+    uint32_t* error;          // set to 1 if a look-back wait gave up
+    uint64_t* flags;          // [ngroups * tiles_per_group]: (epoch << 2) | status
+    float* desc;              // [ngroups * tiles_per_group][2][4][64 * VEC]
+    uint64_t epoch;           // distinguishes this launch's flags from stale ones
+};
+
+enum : uint64_t { kAggregate = 1, kInclusive = 2 };
+
+// a partial state in anchor form, VEC channels
+template <int VEC>
+struct Part {
+    float a[VEC], b[VEC], A[VEC], m[VEC];
+    __device__ __forceinline__ void set_empty() {
+#pragma unroll
+        for (int q = 0; q < VEC; q++) { a[q] = 0.0f; b[q] = 0.0f; A[q] = kEmptyP; m[q] = 0.0f; }
+    }
+    // this <- this (+) g, g spanning n tokens
+    __device__ __forceinline__ void absorb(const Part& g, float n, const Lane<VEC>& s) {
+#pragma unroll
+        for (int q = 0; q < VEC; q++)
+            combine(a[q], b[q], A[q], m[q], g.a[q], g.b[q], g.A[q], g.m[q], n, s.ch[q].w);
+    }
+};
+
+template <int VEC>
+__device__ __forceinline__ float* desc_ptr(const ChunkArgs& ca, int64_t g, int64_t j, int kind) {
+    return ca.desc + ((g * ca.tiles_per_group + j) * 2 + kind) * (4 * 64 * VEC);
+}
+
+template <int VEC>
+__device__ __forceinline__ void publish(const ChunkArgs& ca, int64_t g, int64_t j, int kind,
+                                        const Part<VEC>& x, int lane) {
+    float* d = desc_ptr<VEC>(ca, g, j, kind);
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        st_agent(d + 0 * 64 * VEC + lane * VEC + q, x.a[q]);
+        st_agent(d + 1 * 64 * VEC + lane * VEC + q, x.b[q]);
+        st_agent(d + 2 * 64 * VEC + lane * VEC + q, x.A[q]);
+        st_agent(d + 3 * 64 * VEC + lane * VEC + q, x.m[q]);
+    }
+    wait_all_memory();
+    if (lane == 0)
+        st_flag(ca.flags + g * ca.tiles_per_group + j,
+                (ca.epoch << 2) | (kind == 0 ? kAggregate : kInclusive));
+}
+
+template <int VEC>
+__device__ __forceinline__ void read_desc(const ChunkArgs& ca, int64_t g, int64_t j, int kind,
+                                          Part<VEC>& x, int lane) {
+    const float* d = desc_ptr<VEC>(ca, g, j, kind);
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        x.a[q] = ld_agent(d + 0 * 64 * VEC + lane * VEC + q);
+        x.b[q] = ld_agent(d + 1 * 64 * VEC + lane * VEC + q);
+        x.A[q] = ld_agent(d + 2 * 64 * VEC + lane * VEC + q);
+        x.m[q] = ld_agent(d + 3 * 64 * VEC + lane * VEC + q);
+    }
+}
+
+// Exclusive prefix of tile j of group g: combine published aggregates of
+// tiles j-1, j-2, ... (newest first) until an inclusive prefix is found.
+template <int VEC>
+__device__ void look_back(const ChunkArgs& ca, int64_t g, int64_t j, int tile_tokens,
+                          const Lane<VEC>& s, Part<VEC>& x, int lane) {
+    Part<VEC> sfx;  // combined aggregates of tiles jj+1 .. j-1
+    sfx.set_empty();
+    float span = 0.0f;
+    for (int64_t jj = j - 1;; jj--) {
+        const uint64_t* fp = ca.flags + g * ca.tiles_per_group + jj;
+        uint64_t f = 0;
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        for (;;) {
+            const uint64_t raw = ld_flag(fp);
+            const uint64_t seen = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(raw)))) |
+                                  (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(raw >> 32)))) << 32);
+            if ((seen >> 2) == ca.epoch && (seen & 3) != 0) { f = seen; break; }
+            // bounded wait: give up after kSpinTicks of the 100 MHz real-time
+            // counter, or at once when another tile already gave up
+            if (__builtin_amdgcn_readfirstlane(
+                    __hip_atomic_load(ca.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
+                break;
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        compiler_fence();
+        if (f == 0) {
+            // never expected: record it and continue with what we have, so the
+            // kernel still terminates
+            if (lane == 0) atomicOr(ca.error, 1u);
+            x = sfx;
+            return;
+        }
+        const int kind = (f & 3) == kInclusive ? 1 : 0;
+        Part<VEC> d;
+        read_desc<VEC>(ca, g, jj, kind, d, lane);
+        d.absorb(sfx, span, s);
+        if (kind == 1) {
+            x = d;
+            return;
+        }
+        sfx = d;
+        span += float(tile_tokens);
+    }
+}
+
+// Load this wave's n tokens of k, v (n == L when FULL).
+template <int DT, int VEC, bool FULL>
+__device__ __forceinline__ void chunk_load(typename Io<DT, VEC>::Raw (&kr)[kChunkTokens],
+                                           typename Io<DT, VEC>::Raw (&vr)[kChunkTokens], rsrc_t kr_,
+                                           rsrc_t vr_, uint32_t voff, uint32_t row_bytes, int n) {
+    using IO = Io<DT, VEC>;
+    using Raw = typename IO::Raw;
+#pragma unroll
+    for (int i = 0; i < kChunkTokens; i++) {
+        if (FULL || i < n) {
+            kr[i] = Buf<Raw>::load(kr_, voff, uint32_t(i) * row_bytes);
+            vr[i] = Buf<Raw>::load(vr_, voff, uint32_t(i) * row_bytes);
+        } else {
+            kr[i] = IO::zero();
+            vr[i] = IO::zero();
+        }
+    }
+}
+
+// State of this wave's n tokens started from the empty history, by two
+// passes: the largest decayed key x_i = k_i - (n-1-i) w, then the sums of
+// e^{x_i - max} and e^{x_i - max} v_i.  This is the closed form of the
+// recurrence over the tokens (the state's exponent is the running maximum),
+// without a serial chain of maxima.
+template <int DT, int VEC, bool FULL>
+__device__ __forceinline__ void chunk_aggregate(const Lane<VEC>& s,
+                                                const typename Io<DT, VEC>::Raw (&kr)[kChunkTokens],
+                                                const typename Io<DT, VEC>::Raw (&vr)[kChunkTokens],
+                                                int n, Part<VEC>& g) {
+    using IO = Io<DT, VEC>;
+    constexpr int L = kChunkTokens;
+    float mx[VEC];
+#pragma unroll
+    for (int q = 0; q < VEC; q++) mx[q] = kEmptyP;
+#pragma unroll
+    for (int i = 0; i < L; i++) {
+        if (FULL || i < n) {
+            const float ci = FULL ? float(i - (L - 1)) : float(i - (n - 1));
+            float kf[VEC];
+            IO::unpack(kr[i], kf);
+#pragma unroll
+            for (int q = 0; q < VEC; q++) mx[q] = __builtin_fmaxf(mx[q], __builtin_fmaf(ci, s.ch[q].w, kf[q]));
+        }
+    }
+    float mxl[VEC];
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        g.a[q] = 0.0f;
+        g.b[q] = 0.0f;
+        g.A[q] = mx[q];
+        g.m[q] = 0.0f;
+        mxl[q] = mx[q] * kLog2e;
+    }
+#pragma unroll
+    for (int i = 0; i < L; i++) {
+        if (FULL || i < n) {
+            const float ci = FULL ? float(i - (L - 1)) : float(i - (n - 1));
+            float kf[VEC], vf[VEC];
+            IO::unpack(kr[i], kf);
+            IO::unpack(vr[i], vf);
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                const float x = __builtin_fmaf(ci, s.ch[q].w, kf[q]);
+                // e^{x - max}; a rounding of max * log2e scales every term alike
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -mxl[q]));
+                g.b[q] += e;
+                g.a[q] = __builtin_fmaf(e, vf[q], g.a[q]);
+            }
+        }
+    }
+}
+
+template <int DT, int VEC>
+__global__ __launch_bounds__(kChunkWaves * 64) void forward_chunked_kernel(ForwardProblem pr,
+                                                                           ChunkArgs ca) {
+    using IO = Io<DT, VEC>;
+    using Raw = typename IO::Raw;
+    constexpr int L = kChunkTokens;
+    constexpr int NW = kChunkWaves;
+    constexpr int CG = 64 * VEC;
+    constexpr int TILE = NW * L;
+    // per-wave partial states, then their exclusive prefixes; [NW] = tile carry
+    __shared__ float s_part[NW + 1][4][CG];
+    __shared__ uint32_t s_ticket;
+
+    const int wave = wave_id();
+    const int lane = lane_id();
+    if (threadIdx.x == 0) s_ticket = atomicAdd(ca.ticket, 1u);
+    __syncthreads();
+    const int64_t tile = __builtin_amdgcn_readfirstlane(s_ticket);
+    const int64_t j = tile / ca.ngroups;
+    const int64_t g = tile - j * ca.ngroups;
+    const int64_t bb = g / ca.gpr;
+    const int64_t c0 = (g - bb * ca.gpr) * CG;
+    const int64_t c = c0 + int64_t(lane) * VEC;
+    const bool active = c < pr.C;
+    const int64_t T = pr.T;
+    const int64_t t_begin = j * TILE + int64_t(wave) * L;
+    const int n = T - t_begin >= L ? L : (T - t_begin > 0 ? int(T - t_begin) : 0);
+
+    Lane<VEC> s;
+    load_params(s, pr, c, active);
+
+    // k, v of this wave's tokens, kept in registers until y is written
+    constexpr int64_t es = sizeof(Raw) / VEC;
+    const uint32_t row_bytes = uint32_t(pr.C * es);
+    // lanes past C read lane 0's words (in bounds) and never store
+    const uint32_t voff = active ? uint32_t(lane) * uint32_t(sizeof(Raw)) : 0u;
+    const int64_t base = ((bb * T + t_begin) * pr.C + c0) * es;
+    Raw kr[L], vr[L];
+    {
+        const rsrc_t kr_ = make_rsrc(static_cast<const char*>(pr.k) + base);
+        const rsrc_t vr_ = make_rsrc(static_cast<const char*>(pr.v) + base);
+        if (n == L)
+            chunk_load<DT, VEC, true>(kr, vr, kr_, vr_, voff, row_bytes, n);
+        else
+            chunk_load<DT, VEC, false>(kr, vr, kr_, vr_, voff, row_bytes, n);
+    }
+
+    // phase 1: this wave's partial state from the empty history
+    {
+        Part<VEC> gw;
+        if (n == L)
+            chunk_aggregate<DT, VEC, true>(s, kr, vr, n, gw);
+        else
+            chunk_aggregate<DT, VEC, false>(s, kr, vr, n, gw);
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            s_part[wave][0][lane * VEC + q] = gw.a[q];
+            s_part[wave][1][lane * VEC + q] = gw.b[q];
+            s_part[wave][2][lane * VEC + q] = gw.A[q];
+            s_part[wave][3][lane * VEC + q] = gw.m[q];
+        }
+    }
+    __syncthreads();
+
+    // wave 0: prefixes inside the tile, the tile's carry, publication
+    if (wave == 0) {
+        Part<VEC> pre;
+        pre.set_empty();
+        for (int w2 = 0; w2 < NW; w2++) {
+            const int64_t tb = j * TILE + int64_t(w2) * L;
+            const int n2 = T - tb >= L ? L : (T - tb > 0 ? int(T - tb) : 0);
+            Part<VEC> gw;
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                gw.a[q] = s_part[w2][0][lane * VEC + q];
+                gw.b[q] = s_part[w2][1][lane * VEC + q];
+                gw.A[q] = s_part[w2][2][lane * VEC + q];
+                gw.m[q] = s_part[w2][3][lane * VEC + q];
+                s_part[w2][0][lane * VEC + q] = pre.a[q];
+                s_part[w2][1][lane * VEC + q] = pre.b[q];
+                s_part[w2][2][lane * VEC + q] = pre.A[q];
+                s_part[w2][3][lane * VEC + q] = pre.m[q];
+            }
+            pre.absorb(gw, float(n2), s);
+        }
+        const int64_t tile_tokens = (T - j * TILE) < TILE ? (T - j * TILE) : TILE;
+        const bool last_tile = j == ca.tiles_per_group - 1;
+        Part<VEC> x;
+        if (j == 0) {
+            load_state(x.a, x.b, x.A, x.m, pr, bb * pr.C + c, active);
+        } else {
+            if (!last_tile) publish<VEC>(ca, g, j, 0, pre, lane);
+            look_back<VEC>(ca, g, j, TILE, s, x, lane);
+        }
+        if (!last_tile) {
+            Part<VEC> inc = x;
+            inc.absorb(pre, float(tile_tokens), s);
+            publish<VEC>(ca, g, j, 1, inc, lane);
+        }
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            s_part[NW][0][lane * VEC + q] = x.a[q];
+            s_part[NW][1][lane * VEC + q] = x.b[q];
+            s_part[NW][2][lane * VEC + q] = x.A[q];
+            s_part[NW][3][lane * VEC + q] = x.m[q];
+        }
+    }
+    __syncthreads();
+    if (n == 0) return;
+
+    // phase 3: carry-in of this wave, then the tokens again with outputs
+    {
+        Part<VEC> x;
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            x.a[q] = s_part[NW][0][lane * VEC + q];
+            x.b[q] = s_part[NW][1][lane * VEC + q];
+            x.A[q] = s_part[NW][2][lane * VEC + q];
+            x.m[q] = s_part[NW][3][lane * VEC + q];
+        }
+        if (wave > 0) {
+            Part<VEC> pw;
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                pw.a[q] = s_part[wave][0][lane * VEC + q];
+                pw.b[q] = s_part[wave][1][lane * VEC + q];
+                pw.A[q] = s_part[wave][2][lane * VEC + q];
+                pw.m[q] = s_part[wave][3][lane * VEC + q];
+            }
+            x.absorb(pw, float(wave * L), s);
+        }
+#pragma unroll
+        for (int q = 0; q < VEC; q++) { s.a[q] = x.a[q]; s.b[q] = x.b[q]; s.A[q] = x.A[q]; s.m[q] = x.m[q]; }
+    }
+    const rsrc_t yr_ = make_rsrc(static_cast<char*>(pr.y) + base);
+    const bool fused = wave_all_fused(s);
+    if (n == L) {
+        if (fused)
+            run_block<DT, VEC, L, true, true>(s, kr, vr, yr_, voff, row_bytes, n, active);
+        else
+            run_block<DT, VEC, L, false, true>(s, kr, vr, yr_, voff, row_bytes, n, active);
+    } else {
+        if (fused)
+            run_block<DT, VEC, L, true, false>(s, kr, vr, yr_, voff, row_bytes, n, active);
+        else
+            run_block<DT, VEC, L, false, false>(s, kr, vr, yr_, voff, row_bytes, n, active);
+    }
+    if (t_begin + n == T && active && pr.a_out != nullptr) store_state(s, pr, bb * pr.C + c);
+}
+
+// ---------------------------------------------------------------------------
+// chained path
+//
+// One workgroup of NWV waves owns a whole column group.  The group's tokens
+// are cut into sub-chunks of L tokens handed to the waves round-robin
+// (sub-chunk c goes to wave c % NWV).  For each of its sub-chunks a wave
+// loads k, v into registers, folds them into a partial state from the empty
+// history, then waits for the carry (the state before the sub-chunk) in LDS,
+// passes on carry (+) partial to the next sub-chunk's wave, and re-runs its
+// tokens from the carry to write y.  The carry chain costs one combine per
+// sub-chunk; the loads and both passes of different waves overlap freely.
+// No global memory besides k, v, y and the state is touched, and the result
+// does not depend on timing.
+// ---------------------------------------------------------------------------
+
+template <int DT, int VEC, int NWV>
+__global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProblem pr, int64_t gpr,
+                                                                   int64_t nsub) {
+    using IO = Io<DT, VEC>;
+    using Raw = typename IO::Raw;
+    constexpr int L = kChunkTokens;
+    constexpr int CG = 64 * VEC;
+    __shared__ float s_carry[4][CG];  // a, b, A, m of the state before sub-chunk s_seq
+    __shared__ int s_seq;
+
+    const int wave = wave_id();
+    const int lane = lane_id();
+    const int64_t g = blockIdx.x;
+    const int64_t bb = g / gpr;
+    const int64_t c0 = (g - bb * gpr) * CG;
+    const int64_t c = c0 + int64_t(lane) * VEC;
+    const bool active = c < pr.C;
+    const int64_t T = pr.T;
+
+    Lane<VEC> s;
+    load_params(s, pr, c, active);
+    if (wave == 0) {
+        float a[VEC], b[VEC], A[VEC], m[VEC];
+        load_state(a, b, A, m, pr, bb * pr.C + c, active);
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            s_carry[0][lane * VEC + q] = a[q];
+            s_carry[1][lane * VEC + q] = b[q];
+            s_carry[2][lane * VEC + q] = A[q];
+            s_carry[3][lane * VEC + q] = m[q];
+        }
+        if (lane == 0) s_seq = 0;
+    }
+    __syncthreads();
+
+    constexpr int64_t es = sizeof(Raw) / VEC;
+    const uint32_t row_bytes = uint32_t(pr.C * es);
+    const uint32_t voff = active ? uint32_t(lane) * uint32_t(sizeof(Raw)) : 0u;
+    const int64_t gbase = (bb * T * pr.C + c0) * es;
+    const bool fused = wave_all_fused(s);
+
+    for (int64_t sc = wave; sc < nsub; sc += NWV) {
+        const int64_t t0 = sc * L;
+        const int n = T - t0 >= L ? L : int(T - t0);
+        const int64_t base = gbase + t0 * int64_t(row_bytes);
+        Raw kr[L], vr[L];
+        Part<VEC> gw;
+        {
+            const rsrc_t kr_ = make_rsrc(static_cast<const char*>(pr.k) + base);
+            const rsrc_t vr_ = make_rsrc(static_cast<const char*>(pr.v) + base);
+            if (n == L) {
+                chunk_load<DT, VEC, true>(kr, vr, kr_, vr_, voff, row_bytes, n);
+                chunk_aggregate<DT, VEC, true>(s, kr, vr, n, gw);
+            } else {
+                chunk_load<DT, VEC, false>(kr, vr, kr_, vr_, voff, row_bytes, n);
+                chunk_aggregate<DT, VEC, false>(s, kr, vr, n, gw);
+            }
+        }
+        // the carry of this sub-chunk, then the next one's
+        while (__hip_atomic_load(&s_seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != int(sc))
+            __builtin_amdgcn_s_sleep(1);
+        Part<VEC> x;
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            x.a[q] = s_carry[0][lane * VEC + q];
+            x.b[q] = s_carry[1][lane * VEC + q];
+            x.A[q] = s_carry[2][lane * VEC + q];
+            x.m[q] = s_carry[3][lane * VEC + q];
+        }
+        if (sc + 1 < nsub) {
+            Part<VEC> nx = x;
+            nx.absorb(gw, float(n), s);
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                s_carry[0][lane * VEC + q] = nx.a[q];
+                s_carry[1][lane * VEC + q] = nx.b[q];
+                s_carry[2][lane * VEC + q] = nx.A[q];
+                s_carry[3][lane * VEC + q] = nx.m[q];
+            }
+            if (lane == 0)
+                __hip_atomic_store(&s_seq, int(sc + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+#pragma unroll
+        for (int q = 0; q < VEC; q++) { s.a[q] = x.a[q]; s.b[q] = x.b[q]; s.A[q] = x.A[q]; s.m[q] = x.m[q]; }
+        const rsrc_t yr_ = make_rsrc(static_cast<char*>(pr.y) + base);
+        if (n == L) {
+            if (fused)
+                run_block<DT, VEC, L, true, true>(s, kr, vr, yr_, voff, row_bytes, n, active);
+            else
+                run_block<DT, VEC, L, false, true>(s, kr, vr, yr_, voff, row_bytes, n, active);
+        } else {
+            if (fused)
+                run_block<DT, VEC, L, true, false>(s, kr, vr, yr_, voff, row_bytes, n, active);
+            else
+                run_block<DT, VEC, L, false, false>(s, kr, vr, yr_, voff, row_bytes, n, active);
+        }
+        if (sc == nsub - 1 && active && pr.a_out != nullptr) store_state(s, pr, bb * pr.C + c);
+    }
+}
+
+__global__ void reset_chunk_counters(uint32_t* ticket) {
+    if (threadIdx.x == 0) {
+        ticket[0] = 0u;  // tile dispenser
+        ticket[1] = 0u;  // look-back error flag
+    }
+}
+
+__global__ void state_passthrough_kernel(int64_t n, const float* a_in, const float* b_in,
+                                         const float* p_in, float* a_out, float* b_out,
+                                         float* p_out) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    if (a_in != nullptr) {
+        const float a = a_in[i], b = b_in[i], p = p_in[i];
+        a_out[i] = a;
+        b_out[i] = b;
+        p_out[i] = export_p(clamp_empty(p));  // empty inputs come back as -inf
+    } else {
+        a_out[i] = 0.0f;
+        b_out[i] = 0.0f;
+        p_out[i] = -__builtin_inff();
+    }
+}
+
+std::atomic<uint64_t> g_epoch{1};
+
+}  // namespace
+
+int pick_forward_vec(int64_t C, int dtype, bool aligned) {
+    if (dtype == kBF16 && C % 2 == 0 && aligned) return 2;
+    return 1;
+}
+
+ChunkPlan plan_chunked(int64_t B, int64_t T, int64_t C, int vec) {
+    ChunkPlan pl;
+    pl.vec = vec;
+    const int64_t cg = 64 * pl.vec;
+    const int64_t gpr = (C + cg - 1) / cg;
+    pl.ngroups = B * gpr;
+    pl.tile_tokens = kChunkTokens * kChunkWaves;
+    pl.tiles_per_group = (T + pl.tile_tokens - 1) / pl.tile_tokens;
+    const size_t ntiles = size_t(pl.ngroups) * size_t(pl.tiles_per_group);
+    const size_t flags = (ntiles * sizeof(uint64_t) + 255) & ~size_t(255);
+    const size_t desc = ntiles * 2 * 4 * size_t(cg) * sizeof(float);
+    pl.workspace_bytes = ntiles == 0 ? 0 : 256 + flags + desc;
+    return pl;
+}
+
+size_t forward_workspace_bytes(int64_t B, int64_t T, int64_t C, int dtype, int path) {
+    if (path != 2 || T == 0) return 0;
+    // the size query does not see the pointers: cover both lane widths
+    const size_t w1 = plan_chunked(B, T, C, 1).workspace_bytes;
+    const size_t w2 = plan_chunked(B, T, C, pick_forward_vec(C, dtype, true)).workspace_bytes;
+    return w1 > w2 ? w1 : w2;
+}
+
+int choose_forward_path(const ForwardProblem& pr, int device_cus) {
+    const int64_t cg = 64 * pr.vec;
+    const int64_t ngroups = pr.B * ((pr.C + cg - 1) / cg);
+    if (pr.T <= kChunkTokens) return 1;                       // a single block
+    if (ngroups >= int64_t(device_cus) * 16) return 1;        // 4 waves per SIMD without splitting T
+    if (4 * ngroups >= 3 * int64_t(device_cus)) return 3;     // a workgroup per column group fills the chip
+    return 2;                                                 // split T across workgroups
+}
+
+int chained_waves(int64_t ngroups, int device_cus) {
+    // enough waves per workgroup for 16 per CU, a power of two in [2, 16]
+    int nw = 16;
+    while (nw > 2 && int64_t(nw) * ngroups > int64_t(device_cus) * 16) nw /= 2;
+    return nw;
+}
+
+hipError_t launch_forward_chained(const ForwardProblem& pr, hipStream_t stream) {
+    const int vec = pr.vec;
+    const int64_t cg = 64 * vec;
+    const int64_t gpr = (pr.C + cg - 1) / cg;
+    const int64_t ngroups = pr.B * gpr;
+    const int64_t nsub = (pr.T + kChunkTokens - 1) / kChunkTokens;
+    const int nw = chained_waves(ngroups, device_cu_count());
+    const dim3 grid(static_cast<unsigned>(ngroups)), block(nw * 64);
+#define WKV_LAUNCH_CHAINED(DT, V, NW) \
+    hipLaunchKernelGGL((forward_chained_kernel<DT, V, NW>), grid, block, 0, stream, pr, gpr, nsub)
+#define WKV_CHAINED_NW(DT, V)                                   \
+    switch (nw) {                                              \
+        case 16: WKV_LAUNCH_CHAINED(DT, V, 16); break;         \
+        case 8: WKV_LAUNCH_CHAINED(DT, V, 8); break;           \
+        case 4: WKV_LAUNCH_CHAINED(DT, V, 4); break;           \
+        default: WKV_LAUNCH_CHAINED(DT, V, 2); break;          \
+    }
+    if (pr.dtype == kBF16 && vec == 2) {
+        WKV_CHAINED_NW(kBF16, 2)
+    } else if (pr.dtype == kBF16) {
+        WKV_CHAINED_NW(kBF16, 1)
+    } else {
+        WKV_CHAINED_NW(kF32, 1)
+    }
+#undef WKV_CHAINED_NW
+#undef WKV_LAUNCH_CHAINED
+    return hipGetLastError();
+}
+
+hipError_t launch_forward_serial(const ForwardProblem& pr, hipStream_t stream) {
+    const int vec = pr.vec;
+    const int64_t cg = 64 * vec;
+    const int64_t gpr = (pr.C + cg - 1) / cg;
+    const int64_t ngroups = pr.B * gpr;
+    const int64_t blocks = (ngroups + kSerialWaves - 1) / kSerialWaves;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kSerialWaves * 64);
+    if (pr.dtype == kBF16 && vec == 2)
+        hipLaunchKernelGGL((forward_serial_kernel<kBF16, 2>), grid, block, 0, stream, pr, ngroups, gpr);
+    else if (pr.dtype == kBF16)
+        hipLaunchKernelGGL((forward_serial_kernel<kBF16, 1>), grid, block, 0, stream, pr, ngroups, gpr);
+    else
+        hipLaunchKernelGGL((forward_serial_kernel<kF32, 1>), grid, block, 0, stream, pr, ngroups, gpr);
+    return hipGetLastError();
+}
+
+hipError_t launch_forward_chunked(const ForwardProblem& pr, void* workspace, hipStream_t stream) {
+    const ChunkPlan pl = plan_chunked(pr.B, pr.T, pr.C, pr.vec);
+    ChunkArgs ca;
+    ca.ngroups = pl.ngroups;
+    ca.gpr = pl.ngroups / pr.B;
+    ca.tiles_per_group = pl.tiles_per_group;
+    char* ws = static_cast<char*>(workspace);
+    ca.ticket = reinterpret_cast<uint32_t*>(ws);
+    ca.error = ca.ticket + 1;
+    const size_t ntiles = size_t(pl.ngroups) * size_t(pl.tiles_per_group);
+    const size_t flags = (ntiles * sizeof(uint64_t) + 255) & ~size_t(255);
+    ca.flags = reinterpret_cast<uint64_t*>(ws + 256);
+    ca.desc = reinterpret_cast<float*>(ws + 256 + flags);
+    ca.epoch = g_epoch.fetch_add(1);
+    hipLaunchKernelGGL(reset_chunk_counters, dim3(1), dim3(64), 0, stream, ca.ticket);
+    const dim3 grid(static_cast<unsigned>(ntiles)), block(kChunkWaves * 64);
+    if (pr.dtype == kBF16 && pl.vec == 2)
+        hipLaunchKernelGGL((forward_chunked_kernel<kBF16, 2>), grid, block, 0, stream, pr, ca);
+    else if (pr.dtype == kBF16)
+        hipLaunchKernelGGL((forward_chunked_kernel<kBF16, 1>), grid, block, 0, stream, pr, ca);
+    else
+        hipLaunchKernelGGL((forward_chunked_kernel<kF32, 1>), grid, block, 0, stream, pr, ca);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_passthrough(const ForwardProblem& pr, hipStream_t stream) {
+    const int64_t n = pr.B * pr.C;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(state_passthrough_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, n,
+                       pr.a_in, pr.b_in, pr.p_in, pr.a_out, pr.b_out, pr.p_out);
+    return hipGetLastError();
+}
+
+}  // namespace wkv

@@ -1,0 +1,69 @@
+// Host-side interface between the C ABI layer (wkv_api.hip) and the kernel
+// launchers.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wkv {
+
+struct ForwardProblem {
+    int64_t B, T, C;
+    int dtype;
+    int vec;                          // channels per lane (from pick_forward_vec)
+    const float *w, *u;
+    const void *k, *v;
+    void *y;
+    const float *a_in, *b_in, *p_in;  // all null or all set
+    float *a_out, *b_out, *p_out;     // all null or all set
+};
+
+// Geometry of the chunked path for one problem.
+struct ChunkPlan {
+    int vec;                 // channels per lane
+    int64_t ngroups;         // column groups: B * ceil(C / (64 * vec))
+    int64_t tiles_per_group; // ceil(T / tile_tokens)
+    int tile_tokens;         // tokens per workgroup tile
+    size_t workspace_bytes;
+};
+
+// Which path wkv_forward takes for a problem (never returns WKV_PATH_AUTO).
+int choose_forward_path(const ForwardProblem& pr, int device_cus);
+ChunkPlan plan_chunked(int64_t B, int64_t T, int64_t C, int vec);
+// Channels per lane for wkv_forward: 2 for bf16 when C is even and k, v, y
+// are 4-byte aligned, else 1.
+int pick_forward_vec(int64_t C, int dtype, bool aligned);
+size_t forward_workspace_bytes(int64_t B, int64_t T, int64_t C, int dtype, int path);
+
+hipError_t launch_forward_serial(const ForwardProblem& pr, hipStream_t stream);
+hipError_t launch_forward_chunked(const ForwardProblem& pr, void* workspace, hipStream_t stream);
+hipError_t launch_forward_chained(const ForwardProblem& pr, hipStream_t stream);
+// T == 0: state_out = state_in (or the empty state).
+hipError_t launch_state_passthrough(const ForwardProblem& pr, hipStream_t stream);
+
+struct StepProblem {
+    int64_t L, S, C;
+    int dtype;
+    int vec;  // 4 when C % 4 == 0 and every array is 16-byte aligned, else 1
+    const float *w, *u;
+    const void *k, *v;
+    void *y;
+    const float *a_in, *b_in, *p_in;
+    float *a_out, *b_out, *p_out;
+};
+hipError_t launch_step(const StepProblem& pr, hipStream_t stream);
+
+struct ShiftProblem {
+    int64_t B, T, C;
+    int dtype;
+    int vec;  // 4, 2 or 1 channels per lane, dividing C, arrays aligned for it
+    const void *x, *x_prev;
+    const float *mu_r, *mu_k, *mu_v;
+    void *xr, *xk, *xv, *x_last;
+};
+hipError_t launch_token_shift(const ShiftProblem& pr, hipStream_t stream);
+
+int device_cu_count();  // CUs of the current device (cached per device)
+
+}  // namespace wkv

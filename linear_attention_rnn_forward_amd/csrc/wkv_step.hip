@@ -1,0 +1,83 @@
+// wkv_step: one decode token for every (layer, sequence, channel) of [L,S,C]
+// ([aiwiki] = aiwiki.thehackersbrain.dev rwkv, the wkv_step listing: state
+// (a, b, p) in, output and new state out; [multigrid] = multigrid.ai rwkv,
+// "Prefill, decode, and where each form is used").
+//
+// Purely elementwise: every element reads k, v, a, b, p and writes y, a', b',
+// p'.  VEC adjacent channels per lane with vector loads.  The per-element
+// arithmetic is decode_token() from wkv_device.h: natural-log exponents and
+// one rounding of p per token (the state is stored between tokens).
+#include "wkv_device.h"
+#include "wkv_internal.h"
+
+namespace wkv {
+namespace {
+
+template <int VEC>
+struct F32v;
+template <>
+struct F32v<1> {
+    using T = float;
+    static __device__ __forceinline__ void get(T r, float (&x)[1]) { x[0] = r; }
+    static __device__ __forceinline__ T put(const float (&x)[1]) { return x[0]; }
+};
+template <>
+struct F32v<4> {
+    using T = float4;
+    static __device__ __forceinline__ void get(T r, float (&x)[4]) {
+        x[0] = r.x; x[1] = r.y; x[2] = r.z; x[3] = r.w;
+    }
+    static __device__ __forceinline__ T put(const float (&x)[4]) { return make_float4(x[0], x[1], x[2], x[3]); }
+};
+
+template <int DT, int VEC>
+__global__ __launch_bounds__(256) void step_kernel(StepProblem pr, int64_t nvec) {
+    using IO = Io<DT, VEC>;
+    using Raw = typename IO::Raw;
+    using FV = F32v<VEC>;
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= nvec) return;
+    const int64_t e0 = i * VEC;                 // first element
+    const int64_t l = e0 / (pr.S * pr.C);
+    const int64_t c = e0 % pr.C;
+    const float* wp = pr.w + l * pr.C + c;
+    const float* up = pr.u + l * pr.C + c;
+
+    float kf[VEC], vf[VEC], a[VEC], b[VEC], p[VEC], y[VEC];
+    IO::unpack(reinterpret_cast<const Raw*>(pr.k)[i], kf);
+    IO::unpack(reinterpret_cast<const Raw*>(pr.v)[i], vf);
+    FV::get(reinterpret_cast<const typename FV::T*>(pr.a_in)[i], a);
+    FV::get(reinterpret_cast<const typename FV::T*>(pr.b_in)[i], b);
+    FV::get(reinterpret_cast<const typename FV::T*>(pr.p_in)[i], p);
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        p[q] = clamp_empty(p[q]);
+        y[q] = decode_token(a[q], b[q], p[q], kf[q], vf[q], wp[q], up[q]);
+        p[q] = export_p(p[q]);
+    }
+    reinterpret_cast<Raw*>(pr.y)[i] = IO::pack(y);
+    reinterpret_cast<typename FV::T*>(pr.a_out)[i] = FV::put(a);
+    reinterpret_cast<typename FV::T*>(pr.b_out)[i] = FV::put(b);
+    reinterpret_cast<typename FV::T*>(pr.p_out)[i] = FV::put(p);
+}
+
+}  // namespace
+
+hipError_t launch_step(const StepProblem& pr, hipStream_t stream) {
+    const int64_t n = pr.L * pr.S * pr.C;
+    const int vec = pr.vec;
+    const int64_t nvec = n / vec;
+    const int64_t blocks = (nvec + 255) / 256;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+    if (pr.dtype == kBF16 && vec == 4)
+        hipLaunchKernelGGL((step_kernel<kBF16, 4>), grid, block, 0, stream, pr, nvec);
+    else if (pr.dtype == kBF16)
+        hipLaunchKernelGGL((step_kernel<kBF16, 1>), grid, block, 0, stream, pr, nvec);
+    else if (vec == 4)
+        hipLaunchKernelGGL((step_kernel<kF32, 4>), grid, block, 0, stream, pr, nvec);
+    else
+        hipLaunchKernelGGL((step_kernel<kF32, 1>), grid, block, 0, stream, pr, nvec);
+    return hipGetLastError();
+}
+
+}  // namespace wkv

@@ -1,6 +1,8 @@
 import os
 import sys
 
+import pytest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -8,3 +10,21 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) and the built HIP library")
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    # name the case before any GPU work, so a run that dies names its test
+    if request.node.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu case] {request.node.nodeid}", flush=True)
+    yield
+
+
+@pytest.fixture(scope="session")
+def device():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import linear_attention_rnn_forward_amd as wkv
+    wkv.lib()  # fails loudly when the library was not built
+    return torch.device("cuda:0")

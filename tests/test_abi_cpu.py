@@ -1,0 +1,110 @@
+"""The C-ABI libraries load and export what include/*.h declares; host-side
+argument validation.  CPU only: no call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_rnn_forward_amd as wkv
+import synth.device
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DECL = re.compile(r"^\s*(?:const\s+)?(?:int|size_t|char|void)\s*\*?\s*(\w+)\s*\(", re.M)
+
+
+def _declared(header):
+    with open(os.path.join(ROOT, "include", header)) as f:
+        return sorted(set(DECL.findall(f.read())))
+
+
+@pytest.mark.parametrize("header,libpath", [("wkv.h", wkv.LIB_PATH),
+                                            ("wkv_synth.h", synth.device.LIB_PATH)])
+def test_every_declared_symbol_is_exported(header, libpath):
+    names = _declared(header)
+    assert names, header
+    lib = ctypes.CDLL(libpath)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, f"{os.path.basename(libpath)} lacks {missing}"
+
+
+def test_header_lists_the_boundary_calls():
+    names = _declared("wkv.h")
+    for n in ("wkv_forward", "wkv_step", "wkv_token_shift", "wkv_forward_workspace_size",
+              "wkv_status_string", "wkv_last_error"):
+        assert n in names
+
+
+def test_abi_version_and_status_strings():
+    L = wkv.lib()
+    assert L.wkv_abi_version() == 100
+    for code in range(0, -9, -1):
+        assert L.wkv_status_string(code).decode()
+    assert L.wkv_status_string(-100).decode() == "unknown status"
+
+
+P = ctypes.c_void_p
+
+
+G = 1 << 30   # fake device addresses, far enough apart not to overlap
+
+
+def _fwd(path=0, B=1, T=8, C=64, dtype=0, w=1 * G, u=2 * G, k=3 * G, v=4 * G, y=5 * G, a_in=None, b_in=None, p_in=None, a_out=None, b_out=None, p_out=None,
+         ws=None, ws_bytes=0):
+    L = wkv.lib()
+    return L.wkv_forward_path(B, T, C, dtype, path, P(w), P(u), P(k), P(v), P(y), P(a_in),
+                              P(b_in), P(p_in), P(a_out), P(b_out), P(p_out), P(ws), ws_bytes,
+                              None)
+
+
+def test_forward_rejects_bad_arguments():
+    L = wkv.lib()
+    assert _fwd(dtype=7) == -3
+    assert _fwd(B=0) == -2 and _fwd(C=0) == -2 and _fwd(T=-1) == -2
+    assert _fwd(B=1 << 40, T=1 << 40) == -2
+    assert _fwd(path=9) == -8
+    assert _fwd(k=None) == -1 and _fwd(w=None) == -1
+    assert _fwd(a_in=6 * G) == -1          # state in: all or none
+    assert _fwd(a_out=6 * G, b_out=7 * G) == -1
+    # y overlapping k
+    assert _fwd(y=3 * G + 16) == -5
+    assert b"y overlaps k" in L.wkv_last_error()
+    # state out overlapping a different state input
+    st = dict(a_in=8 * G, b_in=9 * G, p_in=10 * G)
+    assert _fwd(**st, a_out=9 * G, b_out=11 * G, p_out=12 * G) == -5
+    assert _fwd(**st, a_out=8 * G + 4, b_out=11 * G, p_out=12 * G) == -5   # partial overlap
+    # chunked path without workspace
+    assert _fwd(path=2, T=1024) == -4
+    need = L.wkv_forward_workspace_size_path(1, 1024, 64, 0, 2)
+    assert need > 0
+    assert _fwd(path=2, T=1024, ws=13 * G, ws_bytes=need - 1) == -4
+    assert _fwd(path=2, T=1024, ws=13 * G + 8, ws_bytes=need) == -4   # misaligned
+
+
+def test_step_and_shift_reject_bad_arguments():
+    L = wkv.lib()
+    args = [P(G * (i + 1)) for i in range(11)]
+    assert L.wkv_step(0, 1, 1, 0, *args, None) == -2
+    assert L.wkv_step(1, 1, 4, 5, *args, None) == -3
+    nul = list(args)
+    nul[3] = P(None)
+    assert L.wkv_step(1, 1, 4, 0, *nul, None) == -1
+    # y (index 4) equal to k (index 2)
+    al = list(args)
+    al[4] = al[2]
+    assert L.wkv_step(1, 1, 4, 0, *al, None) == -5
+    sa = [P(G * (i + 1)) for i in range(9)]
+    assert L.wkv_token_shift(0, 4, 4, 0, *sa, None) == -2
+    bad = list(sa)
+    bad[5] = sa[0]   # xr == x
+    assert L.wkv_token_shift(1, 4, 4, 0, *bad, None) == -5
+
+
+def test_workspace_sizes():
+    L = wkv.lib()
+    # serial path and T = 0 need none; the chunked path needs flags + partial states
+    assert L.wkv_forward_workspace_size_path(4, 100, 64, 0, 1) == 0
+    assert L.wkv_forward_workspace_size_path(4, 0, 64, 0, 2) == 0
+    n = L.wkv_forward_workspace_size_path(1, 65536, 4096, 0, 2)
+    assert 256 < n < 128 << 20
+    assert L.wkv_forward_workspace_size_path(0, 10, 10, 0, 2) == 0
