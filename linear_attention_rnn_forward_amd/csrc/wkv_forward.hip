@@ -1,28 +1,32 @@
 // wkv_forward kernels: the training/prefill form over [B,T,C].
 //
-// Two execution paths compute the same recurrence ([tm-math] = aicassindra.com
+// Three execution paths compute the same recurrence ([tm-math] = aicassindra.com
 // tm_rwkv_math, "Why it collapses into a recurrence": a scan over time that
 // parallelises across batch and channels; [vanos] = vanos001.github.io rwkv,
-// "The WKV Operator": a serial per-position scan or a chunked parallel form):
+// "The WKV Operator": a serial per-position scan or a chunked parallel form).
+// A column group is 64 lanes x VEC adjacent channels of one batch row.
 //
-// serial   One wave per column group (64 lanes x VEC adjacent channels of one
-//          batch row); each lane scans its channels along T with the state in
-//          registers.  Used when B*C alone fills the chip.
+// serial   One wave per column group scans all of T with the state in
+//          registers.  Used when the column groups alone give every SIMD
+//          several waves.
+//
+// chained  One workgroup of up to 16 waves per column group.  Its tokens are
+//          cut into sub-chunks that the waves take round-robin; each wave
+//          loads a sub-chunk into registers, folds it into a partial state,
+//          receives the carry from the previous sub-chunk's wave through LDS,
+//          hands carry (+) partial to the next one and re-runs its tokens to
+//          write y.  k, v are read once, no workspace, timing-independent
+//          results.  Used when there are about as many column groups as CUs.
 //
 // chunked  One workgroup per tile = (column group, NW*L consecutive tokens);
-//          wave w of the tile owns L tokens.  Each wave loads its k, v once
-//          into registers, folds them into a partial state from the empty
-//          history, and the partial states are combined
-//            - across the waves of the tile in LDS, and
-//            - across tiles of the same column group through global memory
-//              with a single-pass decoupled look-back (each tile publishes
-//              its own aggregate, then its inclusive prefix; a successor
-//              combines aggregates backwards until it meets an inclusive
-//              prefix).
-//          With its carried-in state each wave then re-runs its tokens from
-//          registers and writes y.  k and v are read from HBM once.
-//          Tiles are handed out in (chunk, group) order by an atomic ticket,
-//          so a tile only ever waits for tiles that already started.
+//          wave w of the tile owns L tokens.  Partial states are combined
+//          across the waves of the tile in LDS and across tiles of a column
+//          group through global memory with a single-pass decoupled
+//          look-back (each tile publishes its aggregate, then its inclusive
+//          prefix; a successor combines aggregates backwards until it meets
+//          an inclusive prefix).  k, v are read once.  Tiles are handed out in
+//          (chunk, group) order by an atomic ticket, so a tile only waits for
+//          tiles that already started.  Used when B*C is small.
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
@@ -41,6 +45,9 @@ namespace {
 #ifndef WKV_CHUNK_WAVES
 #define WKV_CHUNK_WAVES 8
 #endif
+#ifndef WKV_CHAIN_TOKENS
+#define WKV_CHAIN_TOKENS 16
+#endif
 #ifndef WKV_FRAME_TOKENS
 #define WKV_FRAME_TOKENS 8
 #endif
@@ -48,6 +55,7 @@ constexpr int kSerialWaves = 4;                  // waves per workgroup on the s
 constexpr int kSerialTokens = WKV_SERIAL_TOKENS; // tokens loaded per batch on the serial path
 constexpr int kChunkTokens = WKV_CHUNK_TOKENS;   // L: tokens per wave on the chunked path
 constexpr int kChunkWaves = WKV_CHUNK_WAVES;     // NW: waves per tile
+constexpr int kChainTokens = WKV_CHAIN_TOKENS;   // tokens per sub-chunk on the chained path
 constexpr int kFrameTokens = WKV_FRAME_TOKENS;   // tokens per frame of the running maximum
 constexpr uint64_t kSpinTicks = 20000000;  // 200 ms at 100 MHz
 
@@ -352,14 +360,14 @@ __device__ void look_back(const ChunkArgs& ca, int64_t g, int64_t j, int tile_to
 }
 
 // Load this wave's n tokens of k, v (n == L when FULL).
-template <int DT, int VEC, bool FULL>
-__device__ __forceinline__ void chunk_load(typename Io<DT, VEC>::Raw (&kr)[kChunkTokens],
-                                           typename Io<DT, VEC>::Raw (&vr)[kChunkTokens], rsrc_t kr_,
+template <int DT, int VEC, int L, bool FULL>
+__device__ __forceinline__ void chunk_load(typename Io<DT, VEC>::Raw (&kr)[L],
+                                           typename Io<DT, VEC>::Raw (&vr)[L], rsrc_t kr_,
                                            rsrc_t vr_, uint32_t voff, uint32_t row_bytes, int n) {
     using IO = Io<DT, VEC>;
     using Raw = typename IO::Raw;
 #pragma unroll
-    for (int i = 0; i < kChunkTokens; i++) {
+    for (int i = 0; i < L; i++) {
         if (FULL || i < n) {
             kr[i] = Buf<Raw>::load(kr_, voff, uint32_t(i) * row_bytes);
             vr[i] = Buf<Raw>::load(vr_, voff, uint32_t(i) * row_bytes);
@@ -375,13 +383,12 @@ __device__ __forceinline__ void chunk_load(typename Io<DT, VEC>::Raw (&kr)[kChun
 // e^{x_i - max} and e^{x_i - max} v_i.  This is the closed form of the
 // recurrence over the tokens (the state's exponent is the running maximum),
 // without a serial chain of maxima.
-template <int DT, int VEC, bool FULL>
+template <int DT, int VEC, int L, bool FULL>
 __device__ __forceinline__ void chunk_aggregate(const Lane<VEC>& s,
-                                                const typename Io<DT, VEC>::Raw (&kr)[kChunkTokens],
-                                                const typename Io<DT, VEC>::Raw (&vr)[kChunkTokens],
+                                                const typename Io<DT, VEC>::Raw (&kr)[L],
+                                                const typename Io<DT, VEC>::Raw (&vr)[L],
                                                 int n, Part<VEC>& g) {
     using IO = Io<DT, VEC>;
-    constexpr int L = kChunkTokens;
     float mx[VEC];
 #pragma unroll
     for (int q = 0; q < VEC; q++) mx[q] = kEmptyP;
@@ -465,18 +472,18 @@ __global__ __launch_bounds__(kChunkWaves * 64) void forward_chunked_kernel(Forwa
         const rsrc_t kr_ = make_rsrc(static_cast<const char*>(pr.k) + base);
         const rsrc_t vr_ = make_rsrc(static_cast<const char*>(pr.v) + base);
         if (n == L)
-            chunk_load<DT, VEC, true>(kr, vr, kr_, vr_, voff, row_bytes, n);
+            chunk_load<DT, VEC, L, true>(kr, vr, kr_, vr_, voff, row_bytes, n);
         else
-            chunk_load<DT, VEC, false>(kr, vr, kr_, vr_, voff, row_bytes, n);
+            chunk_load<DT, VEC, L, false>(kr, vr, kr_, vr_, voff, row_bytes, n);
     }
 
     // phase 1: this wave's partial state from the empty history
     {
         Part<VEC> gw;
         if (n == L)
-            chunk_aggregate<DT, VEC, true>(s, kr, vr, n, gw);
+            chunk_aggregate<DT, VEC, L, true>(s, kr, vr, n, gw);
         else
-            chunk_aggregate<DT, VEC, false>(s, kr, vr, n, gw);
+            chunk_aggregate<DT, VEC, L, false>(s, kr, vr, n, gw);
 #pragma unroll
         for (int q = 0; q < VEC; q++) {
             s_part[wave][0][lane * VEC + q] = gw.a[q];
@@ -577,8 +584,8 @@ __global__ __launch_bounds__(kChunkWaves * 64) void forward_chunked_kernel(Forwa
 // chained path
 //
 // One workgroup of NWV waves owns a whole column group.  The group's tokens
-// are cut into sub-chunks of L tokens handed to the waves round-robin
-// (sub-chunk c goes to wave c % NWV).  For each of its sub-chunks a wave
+// are cut into sub-chunks of kChainTokens tokens handed to the waves round-robin
+// (sub-chunk c goes to wave c % NWV), kChainTokens tokens each.  For each of its sub-chunks a wave
 // loads k, v into registers, folds them into a partial state from the empty
 // history, then waits for the carry (the state before the sub-chunk) in LDS,
 // passes on carry (+) partial to the next sub-chunk's wave, and re-runs its
@@ -593,7 +600,7 @@ __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProble
                                                                    int64_t nsub) {
     using IO = Io<DT, VEC>;
     using Raw = typename IO::Raw;
-    constexpr int L = kChunkTokens;
+    constexpr int L = kChainTokens;
     constexpr int CG = 64 * VEC;
     __shared__ float s_carry[4][CG];  // a, b, A, m of the state before sub-chunk s_seq
     __shared__ int s_seq;
@@ -639,11 +646,11 @@ __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProble
             const rsrc_t kr_ = make_rsrc(static_cast<const char*>(pr.k) + base);
             const rsrc_t vr_ = make_rsrc(static_cast<const char*>(pr.v) + base);
             if (n == L) {
-                chunk_load<DT, VEC, true>(kr, vr, kr_, vr_, voff, row_bytes, n);
-                chunk_aggregate<DT, VEC, true>(s, kr, vr, n, gw);
+                chunk_load<DT, VEC, L, true>(kr, vr, kr_, vr_, voff, row_bytes, n);
+                chunk_aggregate<DT, VEC, L, true>(s, kr, vr, n, gw);
             } else {
-                chunk_load<DT, VEC, false>(kr, vr, kr_, vr_, voff, row_bytes, n);
-                chunk_aggregate<DT, VEC, false>(s, kr, vr, n, gw);
+                chunk_load<DT, VEC, L, false>(kr, vr, kr_, vr_, voff, row_bytes, n);
+                chunk_aggregate<DT, VEC, L, false>(s, kr, vr, n, gw);
             }
         }
         // the carry of this sub-chunk, then the next one's
@@ -765,7 +772,7 @@ hipError_t launch_forward_chained(const ForwardProblem& pr, hipStream_t stream) 
     const int64_t cg = 64 * vec;
     const int64_t gpr = (pr.C + cg - 1) / cg;
     const int64_t ngroups = pr.B * gpr;
-    const int64_t nsub = (pr.T + kChunkTokens - 1) / kChunkTokens;
+    const int64_t nsub = (pr.T + kChainTokens - 1) / kChainTokens;
     const int nw = chained_waves(ngroups, device_cu_count());
     const dim3 grid(static_cast<unsigned>(ngroups)), block(nw * 64);
 #define WKV_LAUNCH_CHAINED(DT, V, NW) \
