@@ -83,6 +83,20 @@ class ForwardBench:
     def step(self):
         self.wkv.forward(self.k, self.v, self.w, self.u, out=self.y)
 
+    def check_replay(self):
+        """The graph's last output matches an eager launch's: bit for bit, or
+        within the parity tolerance on the chunked path, whose look-back groups
+        its combines by timing."""
+        import torch
+        y = self.y.clone().float()
+        self.step()
+        torch.cuda.synchronize()
+        ref = self.y.float()
+        scale = torch.clamp(ref.abs(), min=float(ref.square().mean().sqrt()))
+        err = float(((y - ref).abs() / scale).max())
+        if err > (2e-2 if self.io == "bf16" else 1e-4):
+            raise RuntimeError(f"graph replay output differs from the eager launch ({err:.3e})")
+
     def config(self):
         return {"workload": self.wl.name, "B": self.wl.B, "T": self.wl.T, "C": self.wl.C,
                 "io_dtype": self.io, "state_dtype": "f32"}
@@ -138,6 +152,26 @@ class DecodeBench:
         self.wkv.step(self.st, self.kb[j], self.vb[j], self.w, self.u, out=self.y, inplace=True)
         self.i += 1
 
+    def begin_capture(self):
+        self.i_capture = self.i
+
+    def snapshot(self):
+        self.st_before = tuple(s.clone() for s in self.st)
+
+    def check_replay(self):
+        """The replayed steps, re-run eagerly from the saved state, give the
+        same state and output, bit for bit."""
+        import torch
+        st = self.st_before
+        steps = self.i - self.i_capture
+        for n in range(steps):
+            j = (self.i_capture + n) % self.ntok
+            y, st = self.wkv.step(st, self.kb[j], self.vb[j], self.w, self.u, inplace=True)
+        torch.cuda.synchronize()
+        if not (torch.equal(y, self.y) and all(torch.equal(a, b) for a, b in zip(st, self.st))):
+            raise RuntimeError("graph replay of the decode steps differs from eager launches")
+        self.st_before = None
+
     def config(self):
         return {"workload": self.wl.name, "L": self.wl.L, "S": self.wl.S, "C": self.wl.C,
                 "io_dtype": "f32", "state_dtype": "f32"}
@@ -181,6 +215,11 @@ class CopyBench:
     def step(self):
         self.y.copy_(self.x)
 
+    def check_replay(self):
+        import torch
+        if not torch.equal(self.x, self.y):
+            raise RuntimeError("graph replay of the copy is wrong")
+
     def config(self):
         return {"workload": "device copy of 256 MiB (counter calibration)", "bytes": self.alg_bytes}
 
@@ -204,7 +243,15 @@ class TokenShiftBench:
         self.shape = (B, T, C)
 
     def step(self):
-        self.wkv.token_shift(self.x, *self.mu)
+        self.out = self.wkv.token_shift(self.x, *self.mu)
+
+    def check_replay(self):
+        import torch
+        got = [t.clone() for t in self.out]
+        ref = self.wkv.token_shift(self.x, *self.mu)
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(got, ref)):
+            raise RuntimeError("graph replay of the token shift differs from the eager launch")
 
     def config(self):
         B, T, C = self.shape
@@ -233,6 +280,8 @@ def main():
                     choices=["tiny", "small_lm", "bf16_main", "long_ctx", "decode", "token_shift",
                              "hbm_copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch each step from Python instead of replaying a HIP graph of the steps")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -259,17 +308,42 @@ def main():
     for _ in range(args.warmup):
         bench.step()
     torch.cuda.synchronize()
+    graph = None
+    if not args.eager:
+        # the K steps as one HIP graph: the same kernels, launched without the
+        # per-step Python and launch-queue gaps
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            bench.step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        getattr(bench, "begin_capture", lambda: None)()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                bench.step()
+        torch.cuda.synchronize()
+        graph.replay()   # untimed first replay
+        torch.cuda.synchronize()
+        getattr(bench, "snapshot", lambda: None)()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        bench.step()
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(args.steps):
+            bench.step()
     ev1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    if graph is not None:
+        bench.check_replay()
     # average duration of one launch on the launch stream: HIP events around the
     # timed region, divided by the launch count
     avg_kernel_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
@@ -291,7 +365,9 @@ def main():
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": bench.dtype, "data": "synthetic",
-            "config": bench.config(), "roofline": roofline, "cpu_baseline": cpu}
+            "config": dict(bench.config(), launch="hip graph of the timed steps" if graph is not None
+                           else "one launch per step"),
+            "roofline": roofline, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 
 

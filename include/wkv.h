@@ -87,8 +87,10 @@ typedef enum {
  * device (0 when the chosen path needs none).  Returns 0 for invalid sizes.
  * Only the chunked path (WKV_PATH_CHUNKED, chosen when B*C is too small to
  * occupy the device otherwise) uses one: per-tile partial states, flags and a
- * tile counter.  Its contents on entry do not matter.  Calls that share a
- * workspace must be ordered on one stream. */
+ * tile counter.  Its contents on entry do not matter: each call clears what it
+ * uses with a kernel of its own (no memset node), so calls may be recorded in
+ * a HIP graph and replayed.  Calls that share a workspace must be ordered on
+ * one stream. */
 size_t wkv_forward_workspace_size(int64_t B, int64_t T, int64_t C, int dtype);
 
 /* Same, for an explicitly chosen path. */

@@ -30,7 +30,7 @@
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
-#include <atomic>
+#include <algorithm>
 
 namespace wkv {
 namespace {
@@ -255,12 +255,14 @@ struct ChunkArgs {
     int64_t tiles_per_group;  // tiles along T
     uint32_t* ticket;         // tile dispenser (zeroed before the launch)
     uint32_t* error;          // set to 1 if a look-back wait gave up
-    uint64_t* flags;          // [ngroups * tiles_per_group]: (epoch << 2) | status
+    uint64_t* flags;          // [ngroups * tiles_per_group]: status, zeroed before the launch
     float* desc;              // [ngroups * tiles_per_group][2][4][64 * VEC]
-    uint64_t epoch;           // distinguishes this launch's flags from stale ones
 };
 
-enum : uint64_t { kAggregate = 1, kInclusive = 2 };
+// Tile status.  Every flag is cleared by a kernel launched just before the
+// tiles, so a launch never sees another launch's flags, also when the pair
+// of launches is recorded once in a HIP graph and replayed.
+enum : uint64_t { kEmpty = 0, kAggregate = 1, kInclusive = 2 };
 
 // a partial state in anchor form, VEC channels
 template <int VEC>
@@ -296,8 +298,7 @@ __device__ __forceinline__ void publish(const ChunkArgs& ca, int64_t g, int64_t 
     }
     wait_all_memory();
     if (lane == 0)
-        st_flag(ca.flags + g * ca.tiles_per_group + j,
-                (ca.epoch << 2) | (kind == 0 ? kAggregate : kInclusive));
+        st_flag(ca.flags + g * ca.tiles_per_group + j, kind == 0 ? kAggregate : kInclusive);
 }
 
 template <int VEC>
@@ -329,7 +330,7 @@ __device__ void look_back(const ChunkArgs& ca, int64_t g, int64_t j, int tile_to
             const uint64_t raw = ld_flag(fp);
             const uint64_t seen = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(raw)))) |
                                   (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(raw >> 32)))) << 32);
-            if ((seen >> 2) == ca.epoch && (seen & 3) != 0) { f = seen; break; }
+            if (seen != kEmpty) { f = seen; break; }
             // bounded wait: give up after kSpinTicks of the 100 MHz real-time
             // counter, or at once when another tile already gave up
             if (__builtin_amdgcn_readfirstlane(
@@ -346,7 +347,7 @@ __device__ void look_back(const ChunkArgs& ca, int64_t g, int64_t j, int tile_to
             x = sfx;
             return;
         }
-        const int kind = (f & 3) == kInclusive ? 1 : 0;
+        const int kind = f == kInclusive ? 1 : 0;
         Part<VEC> d;
         read_desc<VEC>(ca, g, jj, kind, d, lane);
         d.absorb(sfx, span, s);
@@ -695,11 +696,14 @@ __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProble
     }
 }
 
-__global__ void reset_chunk_counters(uint32_t* ticket) {
-    if (threadIdx.x == 0) {
+// Clears the tile dispenser, the error flag and the n tile flags.
+__global__ void reset_chunk_counters(uint32_t* ticket, uint64_t* flags, int64_t n) {
+    const int64_t i0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i0 == 0) {
         ticket[0] = 0u;  // tile dispenser
         ticket[1] = 0u;  // look-back error flag
     }
+    for (int64_t i = i0; i < n; i += int64_t(gridDim.x) * blockDim.x) flags[i] = kEmpty;
 }
 
 __global__ void state_passthrough_kernel(int64_t n, const float* a_in, const float* b_in,
@@ -718,8 +722,6 @@ __global__ void state_passthrough_kernel(int64_t n, const float* a_in, const flo
         p_out[i] = -__builtin_inff();
     }
 }
-
-std::atomic<uint64_t> g_epoch{1};
 
 }  // namespace
 
@@ -825,8 +827,9 @@ hipError_t launch_forward_chunked(const ForwardProblem& pr, void* workspace, hip
     const size_t flags = (ntiles * sizeof(uint64_t) + 255) & ~size_t(255);
     ca.flags = reinterpret_cast<uint64_t*>(ws + 256);
     ca.desc = reinterpret_cast<float*>(ws + 256 + flags);
-    ca.epoch = g_epoch.fetch_add(1);
-    hipLaunchKernelGGL(reset_chunk_counters, dim3(1), dim3(64), 0, stream, ca.ticket);
+    const int64_t reset_blocks = std::min<int64_t>((int64_t(ntiles) + 255) / 256, 1024);
+    hipLaunchKernelGGL(reset_chunk_counters, dim3(static_cast<unsigned>(reset_blocks)), dim3(256), 0,
+                       stream, ca.ticket, ca.flags, int64_t(ntiles));
     const dim3 grid(static_cast<unsigned>(ntiles)), block(kChunkWaves * 64);
     if (pr.dtype == kBF16 && pl.vec == 2)
         hipLaunchKernelGGL((forward_chunked_kernel<kBF16, 2>), grid, block, 0, stream, pr, ca);
