@@ -390,6 +390,9 @@ __device__ __forceinline__ void chunk_aggregate(const Lane<VEC>& s,
                                                 const typename Io<DT, VEC>::Raw (&vr)[L],
                                                 int n, Part<VEC>& g) {
     using IO = Io<DT, VEC>;
+    // short blocks keep the decayed keys of the first pass for the second
+    constexpr bool kKeepX = L <= 16;
+    float xs[kKeepX ? L : 1][VEC];
     float mx[VEC];
 #pragma unroll
     for (int q = 0; q < VEC; q++) mx[q] = kEmptyP;
@@ -400,7 +403,11 @@ __device__ __forceinline__ void chunk_aggregate(const Lane<VEC>& s,
             float kf[VEC];
             IO::unpack(kr[i], kf);
 #pragma unroll
-            for (int q = 0; q < VEC; q++) mx[q] = __builtin_fmaxf(mx[q], __builtin_fmaf(ci, s.ch[q].w, kf[q]));
+            for (int q = 0; q < VEC; q++) {
+                const float x = __builtin_fmaf(ci, s.ch[q].w, kf[q]);
+                if constexpr (kKeepX) xs[i][q] = x;
+                mx[q] = __builtin_fmaxf(mx[q], x);
+            }
         }
     }
     float mxl[VEC];
@@ -415,13 +422,18 @@ __device__ __forceinline__ void chunk_aggregate(const Lane<VEC>& s,
 #pragma unroll
     for (int i = 0; i < L; i++) {
         if (FULL || i < n) {
-            const float ci = FULL ? float(i - (L - 1)) : float(i - (n - 1));
             float kf[VEC], vf[VEC];
-            IO::unpack(kr[i], kf);
+            if constexpr (!kKeepX) IO::unpack(kr[i], kf);
             IO::unpack(vr[i], vf);
 #pragma unroll
             for (int q = 0; q < VEC; q++) {
-                const float x = __builtin_fmaf(ci, s.ch[q].w, kf[q]);
+                float x;
+                if constexpr (kKeepX) {
+                    x = xs[i][q];
+                } else {
+                    const float ci = FULL ? float(i - (L - 1)) : float(i - (n - 1));
+                    x = __builtin_fmaf(ci, s.ch[q].w, kf[q]);
+                }
                 // e^{x - max}; a rounding of max * log2e scales every term alike
                 const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -mxl[q]));
                 g.b[q] += e;
