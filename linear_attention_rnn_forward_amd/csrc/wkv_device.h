@@ -288,13 +288,48 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
 }
 
+// Cache policies of the k, v loads: non-temporal (each word is read once),
+// which streams the strip-per-workgroup pattern of the serial and chained
+// token loops at a markedly higher rate on MI355X, and the default one,
+// which the chunked path's tiles measure faster with.
+constexpr int kStreamLoad = 2;
+constexpr int kDefaultLoad = 0;
+
+// A non-temporal load through a plain pointer (2, 4, 8 or 16 bytes), for
+// the elementwise kernels' once-read inputs.
+template <typename T>
+__device__ __forceinline__ T load_stream(const T* p) {
+    if constexpr (sizeof(T) == 2)
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p)));
+    else if constexpr (sizeof(T) == 4)
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)));
+    else if constexpr (sizeof(T) == 8)
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p)));
+    else
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
+
+// A non-temporal store through a plain pointer (2, 4, 8 or 16 bytes).
+template <typename T>
+__device__ __forceinline__ void store_stream(T* p, T x) {
+    if constexpr (sizeof(T) == 2)
+        __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, x), reinterpret_cast<uint16_t*>(p));
+    else if constexpr (sizeof(T) == 4)
+        __builtin_nontemporal_store(__builtin_bit_cast(uint32_t, x), reinterpret_cast<uint32_t*>(p));
+    else if constexpr (sizeof(T) == 8)
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x2_t, x), reinterpret_cast<u32x2_t*>(p));
+    else
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, x), reinterpret_cast<u32x4_t*>(p));
+}
+
 template <typename Raw>
 struct Buf;
 
 template <>
 struct Buf<float> {
+    template <int AUX = kStreamLoad>
     static __device__ __forceinline__ float load(rsrc_t r, uint32_t voff, uint32_t soff) {
-        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX));
     }
     static __device__ __forceinline__ void store(float x, rsrc_t r, uint32_t voff, uint32_t soff) {
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff, soff, 0);
@@ -302,8 +337,9 @@ struct Buf<float> {
 };
 template <>
 struct Buf<uint32_t> {
+    template <int AUX = kStreamLoad>
     static __device__ __forceinline__ uint32_t load(rsrc_t r, uint32_t voff, uint32_t soff) {
-        return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+        return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX);
     }
     static __device__ __forceinline__ void store(uint32_t x, rsrc_t r, uint32_t voff, uint32_t soff) {
         __builtin_amdgcn_raw_buffer_store_b32(x, r, voff, soff, 0);
@@ -311,8 +347,9 @@ struct Buf<uint32_t> {
 };
 template <>
 struct Buf<uint16_t> {
+    template <int AUX = kStreamLoad>
     static __device__ __forceinline__ uint16_t load(rsrc_t r, uint32_t voff, uint32_t soff) {
-        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, AUX);
     }
     static __device__ __forceinline__ void store(uint16_t x, rsrc_t r, uint32_t voff, uint32_t soff) {
         __builtin_amdgcn_raw_buffer_store_b16(x, r, voff, soff, 0);
@@ -320,8 +357,9 @@ struct Buf<uint16_t> {
 };
 template <>
 struct Buf<float2> {
+    template <int AUX = kStreamLoad>
     static __device__ __forceinline__ float2 load(rsrc_t r, uint32_t voff, uint32_t soff) {
-        const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX);
         return make_float2(__uint_as_float(x.x), __uint_as_float(x.y));
     }
     static __device__ __forceinline__ void store(float2 x, rsrc_t r, uint32_t voff, uint32_t soff) {
@@ -331,8 +369,9 @@ struct Buf<float2> {
 };
 template <>
 struct Buf<uint2> {
+    template <int AUX = kStreamLoad>
     static __device__ __forceinline__ uint2 load(rsrc_t r, uint32_t voff, uint32_t soff) {
-        const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX);
         return make_uint2(x.x, x.y);
     }
     static __device__ __forceinline__ void store(uint2 x, rsrc_t r, uint32_t voff, uint32_t soff) {
@@ -342,8 +381,9 @@ struct Buf<uint2> {
 };
 template <>
 struct Buf<float4> {
+    template <int AUX = kStreamLoad>
     static __device__ __forceinline__ float4 load(rsrc_t r, uint32_t voff, uint32_t soff) {
-        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX);
         return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
                            __uint_as_float(x.w));
     }

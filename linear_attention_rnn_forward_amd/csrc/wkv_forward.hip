@@ -360,8 +360,8 @@ __device__ void look_back(const ChunkArgs& ca, int64_t g, int64_t j, int tile_to
     }
 }
 
-// Load this wave's n tokens of k, v (n == L when FULL).
-template <int DT, int VEC, int L, bool FULL>
+// Load this wave's n tokens of k, v (n == L when FULL) with cache policy AUX.
+template <int DT, int VEC, int L, bool FULL, int AUX>
 __device__ __forceinline__ void chunk_load(typename Io<DT, VEC>::Raw (&kr)[L],
                                            typename Io<DT, VEC>::Raw (&vr)[L], rsrc_t kr_,
                                            rsrc_t vr_, uint32_t voff, uint32_t row_bytes, int n) {
@@ -370,8 +370,8 @@ __device__ __forceinline__ void chunk_load(typename Io<DT, VEC>::Raw (&kr)[L],
 #pragma unroll
     for (int i = 0; i < L; i++) {
         if (FULL || i < n) {
-            kr[i] = Buf<Raw>::load(kr_, voff, uint32_t(i) * row_bytes);
-            vr[i] = Buf<Raw>::load(vr_, voff, uint32_t(i) * row_bytes);
+            kr[i] = Buf<Raw>::template load<AUX>(kr_, voff, uint32_t(i) * row_bytes);
+            vr[i] = Buf<Raw>::template load<AUX>(vr_, voff, uint32_t(i) * row_bytes);
         } else {
             kr[i] = IO::zero();
             vr[i] = IO::zero();
@@ -485,9 +485,9 @@ __global__ __launch_bounds__(kChunkWaves * 64) void forward_chunked_kernel(Forwa
         const rsrc_t kr_ = make_rsrc(static_cast<const char*>(pr.k) + base);
         const rsrc_t vr_ = make_rsrc(static_cast<const char*>(pr.v) + base);
         if (n == L)
-            chunk_load<DT, VEC, L, true>(kr, vr, kr_, vr_, voff, row_bytes, n);
+            chunk_load<DT, VEC, L, true, kDefaultLoad>(kr, vr, kr_, vr_, voff, row_bytes, n);
         else
-            chunk_load<DT, VEC, L, false>(kr, vr, kr_, vr_, voff, row_bytes, n);
+            chunk_load<DT, VEC, L, false, kDefaultLoad>(kr, vr, kr_, vr_, voff, row_bytes, n);
     }
 
     // phase 1: this wave's partial state from the empty history
@@ -659,10 +659,10 @@ __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProble
             const rsrc_t kr_ = make_rsrc(static_cast<const char*>(pr.k) + base);
             const rsrc_t vr_ = make_rsrc(static_cast<const char*>(pr.v) + base);
             if (n == L) {
-                chunk_load<DT, VEC, L, true>(kr, vr, kr_, vr_, voff, row_bytes, n);
+                chunk_load<DT, VEC, L, true, kStreamLoad>(kr, vr, kr_, vr_, voff, row_bytes, n);
                 chunk_aggregate<DT, VEC, L, true>(s, kr, vr, n, gw);
             } else {
-                chunk_load<DT, VEC, L, false>(kr, vr, kr_, vr_, voff, row_bytes, n);
+                chunk_load<DT, VEC, L, false, kStreamLoad>(kr, vr, kr_, vr_, voff, row_bytes, n);
                 chunk_aggregate<DT, VEC, L, false>(s, kr, vr, n, gw);
             }
         }

@@ -44,11 +44,11 @@ __global__ __launch_bounds__(256) void step_kernel(StepProblem pr, int64_t nvec)
     const float* up = pr.u + l * pr.C + c;
 
     float kf[VEC], vf[VEC], a[VEC], b[VEC], p[VEC], y[VEC];
-    IO::unpack(reinterpret_cast<const Raw*>(pr.k)[i], kf);
-    IO::unpack(reinterpret_cast<const Raw*>(pr.v)[i], vf);
-    FV::get(reinterpret_cast<const typename FV::T*>(pr.a_in)[i], a);
-    FV::get(reinterpret_cast<const typename FV::T*>(pr.b_in)[i], b);
-    FV::get(reinterpret_cast<const typename FV::T*>(pr.p_in)[i], p);
+    IO::unpack(load_stream(reinterpret_cast<const Raw*>(pr.k) + i), kf);
+    IO::unpack(load_stream(reinterpret_cast<const Raw*>(pr.v) + i), vf);
+    FV::get(load_stream(reinterpret_cast<const typename FV::T*>(pr.a_in) + i), a);
+    FV::get(load_stream(reinterpret_cast<const typename FV::T*>(pr.b_in) + i), b);
+    FV::get(load_stream(reinterpret_cast<const typename FV::T*>(pr.p_in) + i), p);
 #pragma unroll
     for (int q = 0; q < VEC; q++) {
         p[q] = clamp_empty(p[q]);

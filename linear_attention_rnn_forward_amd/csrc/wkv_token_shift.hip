@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void token_shift_kernel(ShiftProblem pr, int64
     for (int64_t t = t0; t < t1; t++) {
         const int64_t idx = (bb * pr.T + t) * lanes_per_row + cl;
         float cur[VEC], orr[VEC], ok[VEC], ov[VEC];
-        IO::unpack(x[idx], cur);
+        IO::unpack(load_stream(x + idx), cur);
 #pragma unroll
         for (int q = 0; q < VEC; q++) {
             const float d = cur[q] - prev[q];
@@ -64,9 +64,10 @@ __global__ __launch_bounds__(256) void token_shift_kernel(ShiftProblem pr, int64
             ov[q] = __builtin_fmaf(mv[q], d, prev[q]);
             prev[q] = cur[q];
         }
-        xr[idx] = IO::pack(orr);
-        xk[idx] = IO::pack(ok);
-        xv[idx] = IO::pack(ov);
+        // written once and not read back here: non-temporal stores
+        store_stream(xr + idx, IO::pack(orr));
+        store_stream(xk + idx, IO::pack(ok));
+        store_stream(xv + idx, IO::pack(ov));
     }
     if (t1 == pr.T && pr.x_last != nullptr)
         reinterpret_cast<Raw*>(pr.x_last)[bb * lanes_per_row + cl] = IO::pack(prev);
