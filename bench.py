@@ -237,18 +237,19 @@ class TokenShiftBench:
         g = torch.Generator(device="cpu").manual_seed(6)
         self.x = torch.randn((B, T, C), generator=g).to(torch.bfloat16).to(dev)
         self.mu = [torch.rand(C, generator=g).to(dev) for _ in range(3)]
+        self.out = tuple(torch.empty_like(self.x) for _ in range(3))
         self.units = B * T * C
         self.alg_bytes = 4 * 2 * self.units + 12 * C
         self.dtype = "f32"
         self.shape = (B, T, C)
 
     def step(self):
-        self.out = self.wkv.token_shift(self.x, *self.mu)
+        self.wkv.token_shift(self.x, *self.mu, out=self.out)
 
     def check_replay(self):
         import torch
         got = [t.clone() for t in self.out]
-        ref = self.wkv.token_shift(self.x, *self.mu)
+        ref = self.wkv.token_shift(self.x, *self.mu)   # fresh outputs
         torch.cuda.synchronize()
         if not all(torch.equal(a, b) for a, b in zip(got, ref)):
             raise RuntimeError("graph replay of the token shift differs from the eager launch")
@@ -274,8 +275,8 @@ class TokenShiftBench:
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="bf16_main",
                     choices=["tiny", "small_lm", "bf16_main", "long_ctx", "decode", "token_shift",
                              "hbm_copy"])

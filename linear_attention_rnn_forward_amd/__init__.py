@@ -240,9 +240,10 @@ def step(state, k, v, w, u, out=None, state_out=None, inplace=False):
     return y, (a_out, b_out, p_out)
 
 
-def token_shift(x, mu_r, mu_k, mu_v, x_prev=None, return_last=False):
+def token_shift(x, mu_r, mu_k, mu_v, x_prev=None, return_last=False, out=None):
     """Two-tap causal lerp for the three blends; x [B,T,C] float32/bfloat16,
     mu_* [C] float32, x_prev [B,C] (dtype of x) or None (zeros).
+    out: None, or (xr, xk, xv) preallocated like x.
     Returns (xr, xk, xv) or (xr, xk, xv, x_last)."""
     torch = _torch()
     _need(x, "x")
@@ -255,7 +256,10 @@ def token_shift(x, mu_r, mu_k, mu_v, x_prev=None, return_last=False):
         _need(m, n, (C,), torch.float32, dev)
     if x_prev is not None:
         _need(x_prev, "x_prev", (B, C), x.dtype, dev)
-    xr, xk, xv = (torch.empty_like(x) for _ in range(3))
+    if out is None:
+        xr, xk, xv = (torch.empty_like(x) for _ in range(3))
+    else:
+        xr, xk, xv = (_need(t, n, x.shape, x.dtype, dev) for t, n in zip(out, ("xr", "xk", "xv")))
     x_last = torch.empty((B, C), dtype=x.dtype, device=dev) if return_last else None
     with torch.cuda.device(dev):
         check(lib().wkv_token_shift(B, T, C, dt, _ptr(x), _ptr(x_prev), _ptr(mu_r), _ptr(mu_k),
