@@ -156,7 +156,7 @@ __device__ __forceinline__ void run_block(Lane<VEC>& s, const typename Io<DT, VE
                                                 float(i % F + 1), keep);
                 all_keep[q] = all_keep[q] && keep;
             }
-            if (active) Buf<Raw>::store(IO::pack(yf), yr_, voff, uint32_t(i) * row_bytes);
+            if (active) Buf<Raw>::store(IO::pack(yf), yr_, voff + uint32_t(i) * row_bytes, 0u);
         }
     }
     // the last frame starts at token f0 of the block
@@ -370,8 +370,8 @@ __device__ __forceinline__ void chunk_load(typename Io<DT, VEC>::Raw (&kr)[L],
 #pragma unroll
     for (int i = 0; i < L; i++) {
         if (FULL || i < n) {
-            kr[i] = Buf<Raw>::template load<AUX>(kr_, voff, uint32_t(i) * row_bytes);
-            vr[i] = Buf<Raw>::template load<AUX>(vr_, voff, uint32_t(i) * row_bytes);
+            kr[i] = Buf<Raw>::template load<AUX>(kr_, voff + uint32_t(i) * row_bytes, 0u);
+            vr[i] = Buf<Raw>::template load<AUX>(vr_, voff + uint32_t(i) * row_bytes, 0u);
         } else {
             kr[i] = IO::zero();
             vr[i] = IO::zero();
