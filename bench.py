@@ -12,8 +12,9 @@ average duration, timed with HIP events on the launch stream), and the fp64
 CPU oracle timed on the same workload on the host cores.
 
 Other workloads (--workload): tiny, small_lm, long_ctx (wkv_forward),
-decode (wkv_step over [32,256,4096] fp32), token_shift (bf16, B=16 T=4096
-C=2048).
+bf16_main_gated (the default workload through wkv_forward_gated, the
+receptance gate fused), decode (wkv_step over [32,256,4096] fp32),
+token_shift (bf16, B=16 T=4096 C=2048).
 """
 import argparse
 import hashlib
@@ -55,33 +56,42 @@ def measured_traffic(workload: str):
 
 
 class ForwardBench:
-    def __init__(self, wl, dev):
+    def __init__(self, wl, dev, gated=False):
         import numpy as np
         import torch
 
         import synth
         self.wl = wl
+        self.gated = gated
         x = synth.make_forward_inputs(wl)
         self.host = x
+        self.r = self.r_host = None
+        if gated:
+            self.r_host, r_bits = synth.make_receptance(wl)
         if wl.dtype == "bf16":
             self.k = torch.from_numpy(x.k_bits.view(np.int16)).to(dev).view(torch.bfloat16)
             self.v = torch.from_numpy(x.v_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+            if gated:
+                self.r = torch.from_numpy(r_bits.view(np.int16)).to(dev).view(torch.bfloat16)
         else:
             self.k = torch.from_numpy(x.k).to(dev)
             self.v = torch.from_numpy(x.v).to(dev)
+            if gated:
+                self.r = torch.from_numpy(self.r_host).to(dev)
         self.w = torch.from_numpy(x.w).to(dev)
         self.u = torch.from_numpy(x.u).to(dev)
         self.y = torch.empty_like(self.k)
         es = 2 if wl.dtype == "bf16" else 4
         self.units = wl.B * wl.T * wl.C                       # tokens * channels per step
-        self.alg_bytes = 3 * es * self.units + 8 * wl.C       # k, v read; y written; w, u
+        # k, v (and r) read; y written; w, u
+        self.alg_bytes = (4 if gated else 3) * es * self.units + 8 * wl.C
         self.dtype = "f32"                                    # arithmetic type
         self.io = "bf16" if wl.dtype == "bf16" else "f32"
         import linear_attention_rnn_forward_amd as wkv
         self.wkv = wkv
 
     def step(self):
-        self.wkv.forward(self.k, self.v, self.w, self.u, out=self.y)
+        self.wkv.forward(self.k, self.v, self.w, self.u, out=self.y, r=self.r)
 
     def check_replay(self):
         """The graph's last output matches an eager launch's: bit for bit, or
@@ -98,14 +108,18 @@ class ForwardBench:
             raise RuntimeError(f"graph replay output differs from the eager launch ({err:.3e})")
 
     def config(self):
-        return {"workload": self.wl.name, "B": self.wl.B, "T": self.wl.T, "C": self.wl.C,
+        name = self.wl.name + (", receptance gate fused (o = sigmoid(r) * wkv)" if self.gated else "")
+        return {"workload": name, "B": self.wl.B, "T": self.wl.T, "C": self.wl.C,
                 "io_dtype": self.io, "state_dtype": "f32"}
 
     def cpu_baseline(self):
         import oracle
         x = self.host
         t0 = time.perf_counter()
-        oracle.forward(x.k, x.v, x.w, x.u)
+        if self.gated:
+            oracle.forward_gated(x.k, x.v, self.r_host, x.w, x.u)
+        else:
+            oracle.forward(x.k, x.v, x.w, x.u)
         dt = time.perf_counter() - t0
         return {"value": self.units / dt, "unit": "tokens·channels/s", "cores": oracle.threads(),
                 "kind": "oracle",
@@ -278,8 +292,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="bf16_main",
-                    choices=["tiny", "small_lm", "bf16_main", "long_ctx", "decode", "token_shift",
-                             "hbm_copy"])
+                    choices=["tiny", "small_lm", "bf16_main", "bf16_main_gated", "long_ctx", "decode",
+                             "token_shift", "hbm_copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch each step from Python instead of replaying a HIP graph of the steps")
@@ -298,6 +312,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload in synth.FORWARD_WORKLOADS:
         bench = ForwardBench(synth.FORWARD_WORKLOADS[args.workload], dev)
+    elif args.workload == "bf16_main_gated":
+        bench = ForwardBench(synth.BF16_MAIN, dev, gated=True)
     elif args.workload == "decode":
         bench = DecodeBench(dev)
     elif args.workload == "hbm_copy":

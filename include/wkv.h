@@ -132,6 +132,30 @@ int wkv_forward_path(int64_t B, int64_t T, int64_t C, int dtype, int path,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Training / prefill form with the receptance gate fused on the way out
+ * ([tm-math] "Receptance: the gate on the way out"): for every position
+ *
+ *   o = sigmoid(r) * wkv,   sigmoid(r) = 1 / (1 + e^{-r}),  elementwise,
+ *
+ * where wkv is what wkv_forward writes to y.  Reading r in the same pass
+ * saves writing wkv and reading it back.  The projection W_o that follows on
+ * the pages is not part of the call.
+ *
+ *   path        a wkv_path (WKV_PATH_AUTO to let the library choose)
+ *   r           [B,T,C] dtype       receptance; required when T > 0
+ *   o           [B,T,C] dtype       output; must not overlap k, v, r, w, u or the state
+ * All other arguments, the state outputs (the plain recurrence's state: the
+ * gate does not enter it), the workspace (wkv_forward_workspace_size_path of
+ * the same path) and the error behaviour are as in wkv_forward_path.
+ */
+int wkv_forward_gated(int64_t B, int64_t T, int64_t C, int dtype, int path,
+                      const float *w, const float *u,
+                      const void *k, const void *v, const void *r, void *o,
+                      const float *a_in, const float *b_in, const float *p_in,
+                      float *a_out, float *b_out, float *p_out,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Decode: one token for every (layer l, sequence s, channel c) of [L,S,C]
  * ([aiwiki] wkv_step: state in, (y, state') out; [vanos] "The WKV Operator",
  * inference mode; [multigrid] "Prefill, decode, ...").
@@ -153,6 +177,19 @@ int wkv_step(int64_t L, int64_t S, int64_t C, int dtype,
              const float *a_in, const float *b_in, const float *p_in,
              float *a_out, float *b_out, float *p_out,
              void *stream);
+
+/*
+ * wkv_step with the receptance gate ([tm-math] "Receptance: the gate on the
+ * way out"): y = sigmoid(r) * wkv for the one token.
+ *   r           [L,S,C] dtype       receptance, required; y must not overlap it
+ * Everything else as in wkv_step; the state is the plain recurrence's.
+ */
+int wkv_step_gated(int64_t L, int64_t S, int64_t C, int dtype,
+                   const float *w, const float *u,
+                   const void *k, const void *v, const void *r, void *y,
+                   const float *a_in, const float *b_in, const float *p_in,
+                   float *a_out, float *b_out, float *p_out,
+                   void *stream);
 
 /*
  * Token shift ([tm-math] "Token shift: a two-tap causal convolution";
@@ -184,7 +221,7 @@ const char *wkv_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int wkv_abi_version(void);
 
-#define WKV_ABI_VERSION 100
+#define WKV_ABI_VERSION 101
 
 #ifdef __cplusplus
 }

@@ -71,8 +71,12 @@ def lib() -> ctypes.CDLL:
         L.wkv_forward.argtypes = [i64, i64, i64, i32] + [vp] * 11 + [vp, sz, vp]
         L.wkv_forward_path.restype = i32
         L.wkv_forward_path.argtypes = [i64, i64, i64, i32, i32] + [vp] * 11 + [vp, sz, vp]
+        L.wkv_forward_gated.restype = i32
+        L.wkv_forward_gated.argtypes = [i64, i64, i64, i32, i32] + [vp] * 12 + [vp, sz, vp]
         L.wkv_step.restype = i32
         L.wkv_step.argtypes = [i64, i64, i64, i32] + [vp] * 11 + [vp]
+        L.wkv_step_gated.restype = i32
+        L.wkv_step_gated.argtypes = [i64, i64, i64, i32] + [vp] * 12 + [vp]
         L.wkv_token_shift.restype = i32
         L.wkv_token_shift.argtypes = [i64, i64, i64, i32] + [vp] * 9 + [vp]
         L.wkv_status_string.restype = ctypes.c_char_p
@@ -163,11 +167,13 @@ def workspace_size(B: int, T: int, C: int, dtype: int = F32, path: str = "auto")
 # ---------------------------------------------------------------------------
 
 def forward(k, v, w, u, state=None, return_state=False, path="auto", out=None, state_out=None,
-            workspace=None):
+            workspace=None, r=None):
     """Training / prefill form over all positions.
 
     k, v: [B,T,C] float32 or bfloat16 (same dtype); w, u: [C] float32.
     state: None (empty history) or (a, b, p), each [B,C] float32.
+    r: None, or the receptance [B,T,C] (dtype of k): the output is then
+    sigmoid(r) * wkv (the gate fused into the same pass).
     Returns y [B,T,C] (dtype of k), or (y, (a, b, p)) with return_state.
     path: "auto", or "serial", "chained", "chunked" to force an execution path.
     """
@@ -193,24 +199,33 @@ def forward(k, v, w, u, state=None, return_state=False, path="auto", out=None, s
             state_out = tuple(torch.empty((B, C), dtype=torch.float32, device=dev) for _ in range(3))
         a_out, b_out, p_out = (_need(x, n, (B, C), torch.float32, dev)
                                for x, n in zip(state_out, ("a_out", "b_out", "p_out")))
+    if r is not None:
+        _need(r, "r", k.shape, k.dtype, dev)
     code = _PATHS[path]
     need = int(lib().wkv_forward_workspace_size_path(B, T, C, dt, code))
     ws = workspace if workspace is not None else _workspace(dev, need)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     with torch.cuda.device(dev):
-        check(lib().wkv_forward_path(B, T, C, dt, code, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
-                                     _ptr(a_in), _ptr(b_in), _ptr(p_in), _ptr(a_out), _ptr(b_out),
-                                     _ptr(p_out), _ptr(ws), ws_bytes, _stream(dev)))
+        if r is None:
+            check(lib().wkv_forward_path(B, T, C, dt, code, _ptr(w), _ptr(u), _ptr(k), _ptr(v),
+                                         _ptr(y), _ptr(a_in), _ptr(b_in), _ptr(p_in), _ptr(a_out),
+                                         _ptr(b_out), _ptr(p_out), _ptr(ws), ws_bytes, _stream(dev)))
+        else:
+            check(lib().wkv_forward_gated(B, T, C, dt, code, _ptr(w), _ptr(u), _ptr(k), _ptr(v),
+                                          _ptr(r), _ptr(y), _ptr(a_in), _ptr(b_in), _ptr(p_in),
+                                          _ptr(a_out), _ptr(b_out), _ptr(p_out), _ptr(ws), ws_bytes,
+                                          _stream(dev)))
     if return_state or state_out is not None:
         return y, (a_out, b_out, p_out)
     return y
 
 
-def step(state, k, v, w, u, out=None, state_out=None, inplace=False):
+def step(state, k, v, w, u, out=None, state_out=None, inplace=False, r=None):
     """One decode token for every (layer, sequence, channel).
 
     state: (a, b, p), each [L,S,C] float32 (p = -inf for an empty history).
     k, v: [L,S,C] float32 or bfloat16; w, u: [L,C] float32.
+    r: None, or the receptance [L,S,C] (dtype of k): y = sigmoid(r) * wkv.
     Returns (y, (a', b', p')).  inplace=True writes the new state into `state`.
     """
     torch = _torch()
@@ -233,10 +248,17 @@ def step(state, k, v, w, u, out=None, state_out=None, inplace=False):
                            for x, n in zip(state_out, ("a_out", "b_out", "p_out")))
     y = out if out is not None else torch.empty_like(k)
     _need(y, "out", k.shape, k.dtype, dev)
+    if r is not None:
+        _need(r, "r", k.shape, k.dtype, dev)
     with torch.cuda.device(dev):
-        check(lib().wkv_step(Ln, S, C, dt, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y), _ptr(a_in),
-                             _ptr(b_in), _ptr(p_in), _ptr(a_out), _ptr(b_out), _ptr(p_out),
-                             _stream(dev)))
+        if r is None:
+            check(lib().wkv_step(Ln, S, C, dt, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                 _ptr(a_in), _ptr(b_in), _ptr(p_in), _ptr(a_out), _ptr(b_out),
+                                 _ptr(p_out), _stream(dev)))
+        else:
+            check(lib().wkv_step_gated(Ln, S, C, dt, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
+                                       _ptr(y), _ptr(a_in), _ptr(b_in), _ptr(p_in), _ptr(a_out),
+                                       _ptr(b_out), _ptr(p_out), _stream(dev)))
     return y, (a_out, b_out, p_out)
 
 

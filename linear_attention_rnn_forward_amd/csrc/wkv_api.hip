@@ -84,10 +84,12 @@ int check_state_aliasing(const Range* outs, int nouts, const Range* ins, int nin
     return WKV_OK;
 }
 
+// r == nullptr: plain forward; else the gated form (y = sigmoid(r) * wkv).
 int forward_impl(int64_t B, int64_t T, int64_t C, int dtype, int path, const float* w,
-                 const float* u, const void* k, const void* v, void* y, const float* a_in,
-                 const float* b_in, const float* p_in, float* a_out, float* b_out, float* p_out,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+                 const float* u, const void* k, const void* v, const void* r, void* y,
+                 const float* a_in, const float* b_in, const float* p_in, float* a_out,
+                 float* b_out, float* p_out, void* workspace, size_t workspace_bytes, void* stream,
+                 bool gated) {
     if (dtype != WKV_F32 && dtype != WKV_BF16) return fail(WKV_ERR_DTYPE, "unknown dtype %d", dtype);
     if (path != WKV_PATH_AUTO && path != WKV_PATH_SERIAL && path != WKV_PATH_CHUNKED &&
         path != WKV_PATH_CHAINED)
@@ -105,27 +107,30 @@ int forward_impl(int64_t B, int64_t T, int64_t C, int dtype, int path, const flo
         return fail(WKV_ERR_NULL, "a_out, b_out, p_out: all or none");
     if (!w || !u) return fail(WKV_ERR_NULL, "w and u are required");
     if (T > 0 && (!k || !v || !y)) return fail(WKV_ERR_NULL, "k, v and y are required when T > 0");
+    if (gated && T > 0 && !r) return fail(WKV_ERR_NULL, "r is required when T > 0");
 
     const int64_t io_bytes = B * T * C * int64_t(esize(dtype));
     const int64_t st_bytes = B * C * 4;
     const Range r_in[] = {rng("a_in", a_in, st_bytes), rng("b_in", b_in, st_bytes),
                           rng("p_in", p_in, st_bytes), rng("k", k, io_bytes),
-                          rng("v", v, io_bytes), rng("w", w, C * 4), rng("u", u, C * 4)};
+                          rng("v", v, io_bytes), rng("w", w, C * 4), rng("u", u, C * 4),
+                          rng("r", gated ? r : nullptr, io_bytes)};
     const Range r_y = rng("y", y, io_bytes);
-    for (const Range& r : r_in)
-        if (overlap(r_y, r)) return fail(WKV_ERR_ALIAS, "y overlaps %s", r.name);
+    for (const Range& ri : r_in)
+        if (overlap(r_y, ri)) return fail(WKV_ERR_ALIAS, "y overlaps %s", ri.name);
     const Range r_out[] = {rng("a_out", a_out, st_bytes), rng("b_out", b_out, st_bytes),
                            rng("p_out", p_out, st_bytes)};
-    if (int rc = check_state_aliasing(r_out, 3, r_in, 7, true)) return rc;
-    for (const Range& r : r_out)
-        if (overlap(r, r_y)) return fail(WKV_ERR_ALIAS, "%s overlaps y", r.name);
+    if (int rc = check_state_aliasing(r_out, 3, r_in, 8, true)) return rc;
+    for (const Range& ro : r_out)
+        if (overlap(ro, r_y)) return fail(WKV_ERR_ALIAS, "%s overlaps y", ro.name);
 
     wkv::ForwardProblem pr;
     pr.B = B;
     pr.T = T;
     pr.C = C;
     pr.dtype = dtype;
-    pr.vec = wkv::pick_forward_vec(C, dtype, aligned(k, 4) && aligned(v, 4) && aligned(y, 4));
+    pr.vec = wkv::pick_forward_vec(C, dtype, aligned(k, 4) && aligned(v, 4) && aligned(y, 4) &&
+                                                  (!gated || aligned(r, 4)));
     pr.w = w;
     pr.u = u;
     pr.k = k;
@@ -137,6 +142,7 @@ int forward_impl(int64_t B, int64_t T, int64_t C, int dtype, int path, const flo
     pr.a_out = a_out;
     pr.b_out = b_out;
     pr.p_out = p_out;
+    pr.r = gated ? r : nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     if (T == 0) {
@@ -155,10 +161,10 @@ int forward_impl(int64_t B, int64_t T, int64_t C, int dtype, int path, const flo
                         workspace ? workspace_bytes : size_t(0));
         if (!aligned(workspace, 256)) return fail(WKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
         const Range r_ws = rng("workspace", workspace, int64_t(need));
-        for (const Range& r : r_in)
-            if (overlap(r_ws, r)) return fail(WKV_ERR_ALIAS, "workspace overlaps %s", r.name);
-        for (const Range& r : r_out)
-            if (overlap(r_ws, r)) return fail(WKV_ERR_ALIAS, "workspace overlaps %s", r.name);
+        for (const Range& ri : r_in)
+            if (overlap(r_ws, ri)) return fail(WKV_ERR_ALIAS, "workspace overlaps %s", ri.name);
+        for (const Range& ro : r_out)
+            if (overlap(r_ws, ro)) return fail(WKV_ERR_ALIAS, "workspace overlaps %s", ro.name);
         if (overlap(r_ws, r_y)) return fail(WKV_ERR_ALIAS, "workspace overlaps y");
         hipError_t e = wkv::launch_forward_chunked(pr, workspace, s);
         return e == hipSuccess ? ok() : hip_fail(e, "chunked forward launch");
@@ -243,21 +249,35 @@ int wkv_forward(int64_t B, int64_t T, int64_t C, int dtype, const float* w, cons
                 const void* k, const void* v, void* y, const float* a_in, const float* b_in,
                 const float* p_in, float* a_out, float* b_out, float* p_out, void* workspace,
                 size_t workspace_bytes, void* stream) {
-    return forward_impl(B, T, C, dtype, WKV_PATH_AUTO, w, u, k, v, y, a_in, b_in, p_in, a_out,
-                        b_out, p_out, workspace, workspace_bytes, stream);
+    return forward_impl(B, T, C, dtype, WKV_PATH_AUTO, w, u, k, v, nullptr, y, a_in, b_in, p_in,
+                        a_out, b_out, p_out, workspace, workspace_bytes, stream, false);
 }
 
 int wkv_forward_path(int64_t B, int64_t T, int64_t C, int dtype, int path, const float* w,
                      const float* u, const void* k, const void* v, void* y, const float* a_in,
                      const float* b_in, const float* p_in, float* a_out, float* b_out,
                      float* p_out, void* workspace, size_t workspace_bytes, void* stream) {
-    return forward_impl(B, T, C, dtype, path, w, u, k, v, y, a_in, b_in, p_in, a_out, b_out, p_out,
-                        workspace, workspace_bytes, stream);
+    return forward_impl(B, T, C, dtype, path, w, u, k, v, nullptr, y, a_in, b_in, p_in, a_out, b_out,
+                        p_out, workspace, workspace_bytes, stream, false);
 }
 
-int wkv_step(int64_t L, int64_t S, int64_t C, int dtype, const float* w, const float* u,
-             const void* k, const void* v, void* y, const float* a_in, const float* b_in,
-             const float* p_in, float* a_out, float* b_out, float* p_out, void* stream) {
+int wkv_forward_gated(int64_t B, int64_t T, int64_t C, int dtype, int path, const float* w,
+                      const float* u, const void* k, const void* v, const void* r, void* o,
+                      const float* a_in, const float* b_in, const float* p_in, float* a_out,
+                      float* b_out, float* p_out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    return forward_impl(B, T, C, dtype, path, w, u, k, v, r, o, a_in, b_in, p_in, a_out, b_out,
+                        p_out, workspace, workspace_bytes, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+// r == nullptr and !gated: plain step; gated: y = sigmoid(r) * wkv.
+int step_impl(int64_t L, int64_t S, int64_t C, int dtype, const float* w, const float* u,
+              const void* k, const void* v, const void* r, void* y, const float* a_in,
+              const float* b_in, const float* p_in, float* a_out, float* b_out, float* p_out,
+              void* stream, bool gated) {
     if (dtype != WKV_F32 && dtype != WKV_BF16) return fail(WKV_ERR_DTYPE, "unknown dtype %d", dtype);
     if (L < 1 || S < 1 || C < 1)
         return fail(WKV_ERR_SHAPE, "need L, S, C >= 1 (got L=%lld S=%lld C=%lld)", (long long)L,
@@ -267,18 +287,19 @@ int wkv_step(int64_t L, int64_t S, int64_t C, int dtype, const float* w, const f
     n = L * S * C;
     if (!w || !u || !k || !v || !y || !a_in || !b_in || !p_in || !a_out || !b_out || !p_out)
         return fail(WKV_ERR_NULL, "every wkv_step array is required");
+    if (gated && !r) return fail(WKV_ERR_NULL, "r is required");
     const int64_t io = n * int64_t(esize(dtype));
     const Range r_in[] = {rng("a_in", a_in, n * 4), rng("b_in", b_in, n * 4), rng("p_in", p_in, n * 4),
                           rng("k", k, io), rng("v", v, io), rng("w", w, L * C * 4),
-                          rng("u", u, L * C * 4)};
+                          rng("u", u, L * C * 4), rng("r", gated ? r : nullptr, io)};
     const Range r_y = rng("y", y, io);
-    for (const Range& r : r_in)
-        if (overlap(r_y, r)) return fail(WKV_ERR_ALIAS, "y overlaps %s", r.name);
+    for (const Range& ri : r_in)
+        if (overlap(r_y, ri)) return fail(WKV_ERR_ALIAS, "y overlaps %s", ri.name);
     const Range r_out[] = {rng("a_out", a_out, n * 4), rng("b_out", b_out, n * 4),
                            rng("p_out", p_out, n * 4)};
-    if (int rc = check_state_aliasing(r_out, 3, r_in, 7, true)) return rc;
-    for (const Range& r : r_out)
-        if (overlap(r, r_y)) return fail(WKV_ERR_ALIAS, "%s overlaps y", r.name);
+    if (int rc = check_state_aliasing(r_out, 3, r_in, 8, true)) return rc;
+    for (const Range& ro : r_out)
+        if (overlap(ro, r_y)) return fail(WKV_ERR_ALIAS, "%s overlaps y", ro.name);
     if (double(n) / 256.0 > 2147483647.0) return fail(WKV_ERR_SHAPE, "too many elements for one launch");
 
     wkv::StepProblem pr;
@@ -288,6 +309,7 @@ int wkv_step(int64_t L, int64_t S, int64_t C, int dtype, const float* w, const f
     pr.dtype = dtype;
     const uintptr_t io_align = dtype == WKV_BF16 ? 8 : 16;
     const bool al = aligned(k, io_align) && aligned(v, io_align) && aligned(y, io_align) &&
+                    (!gated || aligned(r, io_align)) &&
                     aligned(a_in, 16) && aligned(b_in, 16) && aligned(p_in, 16) &&
                     aligned(a_out, 16) && aligned(b_out, 16) && aligned(p_out, 16);
     pr.vec = (C % 4 == 0 && al) ? 4 : 1;
@@ -302,8 +324,27 @@ int wkv_step(int64_t L, int64_t S, int64_t C, int dtype, const float* w, const f
     pr.a_out = a_out;
     pr.b_out = b_out;
     pr.p_out = p_out;
+    pr.r = gated ? r : nullptr;
     hipError_t e = wkv::launch_step(pr, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ok() : hip_fail(e, "step launch");
+}
+}  // namespace
+
+extern "C" {
+
+int wkv_step(int64_t L, int64_t S, int64_t C, int dtype, const float* w, const float* u,
+             const void* k, const void* v, void* y, const float* a_in, const float* b_in,
+             const float* p_in, float* a_out, float* b_out, float* p_out, void* stream) {
+    return step_impl(L, S, C, dtype, w, u, k, v, nullptr, y, a_in, b_in, p_in, a_out, b_out, p_out,
+                     stream, false);
+}
+
+int wkv_step_gated(int64_t L, int64_t S, int64_t C, int dtype, const float* w, const float* u,
+                   const void* k, const void* v, const void* r, void* y, const float* a_in,
+                   const float* b_in, const float* p_in, float* a_out, float* b_out, float* p_out,
+                   void* stream) {
+    return step_impl(L, S, C, dtype, w, u, k, v, r, y, a_in, b_in, p_in, a_out, b_out, p_out,
+                     stream, true);
 }
 
 int wkv_token_shift(int64_t B, int64_t T, int64_t C, int dtype, const void* x, const void* x_prev,

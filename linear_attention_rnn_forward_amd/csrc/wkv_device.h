@@ -70,6 +70,10 @@ __device__ __forceinline__ float exp_neg_abs(float d) {
 }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// 1 + e^{-r}: the receptance gate sigmoid(r) = 1 / (1 + e^{-r}) is applied as
+// a factor of the read-out's denominator.
+__device__ __forceinline__ float gate_den(float r) { return 1.0f + __builtin_amdgcn_exp2f(-r * kLog2e); }
+
 // max(a, b) of two numbers that are never NaN, as one v_max_f32: the
 // compiler's fmaxf first quiets every operand it cannot prove canonical,
 // which costs two more instructions per call in the token loop.
@@ -99,9 +103,15 @@ __device__ __forceinline__ Chan make_chan(float w, float u) {
 // One token inside a frame (see 4.).  ip1 = i + 1 for token i of the frame.
 // Updates a, b and the anchor kas; returns y.  `keep` is false when the new
 // token became the maximum.
-template <bool FUSED_ONLY>
+//
+// GATED: the output is sigmoid(r) * y (the receptance gate, [tm-math]
+// "Receptance: the gate on the way out"), passed in as gd = 1 + e^{-r}: the
+// read-out's denominator is multiplied by gd, so the gate costs no second
+// reciprocal.  gd = inf (r very negative) gives 0, the gate's limit.
+template <bool FUSED_ONLY, bool GATED = false>
 __device__ __forceinline__ float frame_token(float& a, float& b, float& kas, float k, float v,
-                                             const Chan& ch, float ip1, bool& keep_out) {
+                                             const Chan& ch, float ip1, bool& keep_out,
+                                             float gd = 1.0f) {
     const float r = __builtin_fmaf(ip1, ch.w, k);  // new key in the block frame
     const float d = kas - r;                       // decayed history minus new token
     const float e = exp_neg_abs(d);
@@ -112,7 +122,8 @@ __device__ __forceinline__ float frame_token(float& a, float& b, float& kas, flo
     float y;
     if (FUSED_ONLY || ch.fused) {
         const float delta = beta * ch.c;
-        y = __builtin_fmaf(delta, v, t1) * fast_rcp(__builtin_fmaf(alpha, b, delta));
+        const float den = __builtin_fmaf(alpha, b, delta);
+        y = __builtin_fmaf(delta, v, t1) * fast_rcp(GATED ? den * gd : den);
     } else {
         // read-out as written: history exponent p = kas - i w against u + k
         const float dr = d + ch.wmu;
@@ -120,7 +131,8 @@ __device__ __forceinline__ float frame_token(float& a, float& b, float& kas, flo
         const bool kr = dr >= 0.0f;
         const float ar = kr ? 1.0f : er;
         const float br = kr ? er : 1.0f;
-        y = __builtin_fmaf(br, v, ar * a) * fast_rcp(__builtin_fmaf(ar, b, br));
+        const float den = __builtin_fmaf(ar, b, br);
+        y = __builtin_fmaf(br, v, ar * a) * fast_rcp(GATED ? den * gd : den);
     }
     a = __builtin_fmaf(beta, v, t1);
     b = __builtin_fmaf(alpha, b, beta);
@@ -149,8 +161,10 @@ __device__ __forceinline__ void combine(float& xa, float& xb, float& xA, float& 
 
 // Decode step: the state is stored after every token, so its exponent is
 // rounded once per token (p' = fl(p - w) when the history keeps the maximum).
+// GATED as in frame_token: gd = 1 + e^{-r}.
+template <bool GATED = false>
 __device__ __forceinline__ float decode_token(float& a, float& b, float& p, float k, float v,
-                                              float w, float u) {
+                                              float w, float u, float gd = 1.0f) {
     const float pw = p - w;
     const float d = pw - k;
     const float e = exp_neg_abs(d);
@@ -162,14 +176,16 @@ __device__ __forceinline__ float decode_token(float& a, float& b, float& p, floa
     float y;
     if (__builtin_fabsf(wmu) <= kFusedMaxAbsUW) {
         const float delta = beta * __builtin_amdgcn_exp2f(-wmu * kLog2e);
-        y = __builtin_fmaf(delta, v, t1) * fast_rcp(__builtin_fmaf(alpha, b, delta));
+        const float den = __builtin_fmaf(alpha, b, delta);
+        y = __builtin_fmaf(delta, v, t1) * fast_rcp(GATED ? den * gd : den);
     } else {
         const float dr = d + wmu;
         const float er = exp_neg_abs(dr);
         const bool kr = dr >= 0.0f;
         const float ar = kr ? 1.0f : er;
         const float br = kr ? er : 1.0f;
-        y = __builtin_fmaf(br, v, ar * a) * fast_rcp(__builtin_fmaf(ar, b, br));
+        const float den = __builtin_fmaf(ar, b, br);
+        y = __builtin_fmaf(br, v, ar * a) * fast_rcp(GATED ? den * gd : den);
     }
     a = __builtin_fmaf(beta, v, t1);
     b = __builtin_fmaf(alpha, b, beta);

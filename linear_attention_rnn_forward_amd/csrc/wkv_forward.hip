@@ -124,9 +124,12 @@ __device__ __forceinline__ bool wave_all_fused(const Lane<VEC>& s) {
 // its frame shifted by at most kFrameTokens * w and its rounding stays at the
 // scale of the key itself.  Moving the frame rounds once; an exact anchor
 // and token count are kept across blocks.
-template <int DT, int VEC, int NTOK, bool FUSED_ONLY, bool FULL>
+// GATED: rr holds the receptance of the same tokens and the block writes
+// sigmoid(r) * y.
+template <int DT, int VEC, int NTOK, bool FUSED_ONLY, bool FULL, bool GATED>
 __device__ __forceinline__ void run_block(Lane<VEC>& s, const typename Io<DT, VEC>::Raw (&kr)[NTOK],
-                                          const typename Io<DT, VEC>::Raw (&vr)[NTOK], rsrc_t yr_,
+                                          const typename Io<DT, VEC>::Raw (&vr)[NTOK],
+                                          const typename Io<DT, VEC>::Raw (&rr)[NTOK], rsrc_t yr_,
                                           uint32_t voff, uint32_t row_bytes, int n, bool active) {
     using IO = Io<DT, VEC>;
     using Raw = typename IO::Raw;
@@ -146,14 +149,20 @@ __device__ __forceinline__ void run_block(Lane<VEC>& s, const typename Io<DT, VE
 #pragma unroll
                 for (int q = 0; q < VEC; q++) kas[q] = __builtin_fmaf(-float(F), s.ch[q].w, kas[q]);
             }
-            float kf[VEC], vf[VEC], yf[VEC];
+            float kf[VEC], vf[VEC], yf[VEC], gd[VEC];
             IO::unpack(kr[i], kf);
             IO::unpack(vr[i], vf);
+            if constexpr (GATED) {
+                float rf[VEC];
+                IO::unpack(rr[i], rf);
+#pragma unroll
+                for (int q = 0; q < VEC; q++) gd[q] = gate_den(rf[q]);
+            }
 #pragma unroll
             for (int q = 0; q < VEC; q++) {
                 bool keep;
-                yf[q] = frame_token<FUSED_ONLY>(s.a[q], s.b[q], kas[q], kf[q], vf[q], s.ch[q],
-                                                float(i % F + 1), keep);
+                yf[q] = frame_token<FUSED_ONLY, GATED>(s.a[q], s.b[q], kas[q], kf[q], vf[q], s.ch[q],
+                                                       float(i % F + 1), keep, GATED ? gd[q] : 1.0f);
                 all_keep[q] = all_keep[q] && keep;
             }
             if (active) Buf<Raw>::store(IO::pack(yf), yr_, voff + uint32_t(i) * row_bytes, 0u);
@@ -171,14 +180,24 @@ __device__ __forceinline__ void run_block(Lane<VEC>& s, const typename Io<DT, VE
     }
 }
 
+// The receptance array run_block reads: rr when GATED, else any array of the
+// right length (never read).
+template <bool GATED, typename Raw, int N, int M>
+__device__ __forceinline__ const Raw (&gated_rr(const Raw (&rr)[M], const Raw (&kr)[N]))[N] {
+    if constexpr (GATED)
+        return rr;
+    else
+        return kr;
+}
+
 // ---------------------------------------------------------------------------
 // serial path
 // ---------------------------------------------------------------------------
 
-template <int DT, int VEC, bool FUSED_ONLY>
+template <int DT, int VEC, bool FUSED_ONLY, bool GATED>
 __device__ __forceinline__ void serial_scan(Lane<VEC>& s, const ForwardProblem& pr, const char* kbase,
-                                            const char* vbase, char* ybase, uint32_t voff,
-                                            uint32_t row_bytes, bool active) {
+                                            const char* vbase, const char* rbase, char* ybase,
+                                            uint32_t voff, uint32_t row_bytes, bool active) {
     using IO = Io<DT, VEC>;
     using Raw = typename IO::Raw;
     constexpr int U = kSerialTokens;
@@ -188,31 +207,37 @@ __device__ __forceinline__ void serial_scan(Lane<VEC>& s, const ForwardProblem& 
         const int64_t off = t0 * int64_t(row_bytes);
         const rsrc_t kr_ = make_rsrc(kbase + off);
         const rsrc_t vr_ = make_rsrc(vbase + off);
+        const rsrc_t rr_ = make_rsrc((GATED ? rbase : kbase) + off);
         const rsrc_t yr_ = make_rsrc(ybase + off);
-        Raw kr[U], vr[U];
+        Raw kr[U], vr[U], rr[GATED ? U : 1];
         if (n == U) {
 #pragma unroll
             for (int i = 0; i < U; i++) {
                 kr[i] = Buf<Raw>::load(kr_, voff, uint32_t(i) * row_bytes);
                 vr[i] = Buf<Raw>::load(vr_, voff, uint32_t(i) * row_bytes);
+                if constexpr (GATED) rr[i] = Buf<Raw>::load(rr_, voff, uint32_t(i) * row_bytes);
             }
-            run_block<DT, VEC, U, FUSED_ONLY, true>(s, kr, vr, yr_, voff, row_bytes, n, active);
+            run_block<DT, VEC, U, FUSED_ONLY, true, GATED>(s, kr, vr, gated_rr<GATED>(rr, kr), yr_,
+                                                           voff, row_bytes, n, active);
         } else {
 #pragma unroll
             for (int i = 0; i < U; i++) {
                 kr[i] = IO::zero();
                 vr[i] = IO::zero();
+                if constexpr (GATED) rr[i] = IO::zero();
                 if (i < n) {
                     kr[i] = Buf<Raw>::load(kr_, voff, uint32_t(i) * row_bytes);
                     vr[i] = Buf<Raw>::load(vr_, voff, uint32_t(i) * row_bytes);
+                    if constexpr (GATED) rr[i] = Buf<Raw>::load(rr_, voff, uint32_t(i) * row_bytes);
                 }
             }
-            run_block<DT, VEC, U, FUSED_ONLY, false>(s, kr, vr, yr_, voff, row_bytes, n, active);
+            run_block<DT, VEC, U, FUSED_ONLY, false, GATED>(s, kr, vr, gated_rr<GATED>(rr, kr), yr_,
+                                                            voff, row_bytes, n, active);
         }
     }
 }
 
-template <int DT, int VEC>
+template <int DT, int VEC, bool GATED>
 __global__ __launch_bounds__(kSerialWaves * 64) void forward_serial_kernel(ForwardProblem pr,
                                                                            int64_t ngroups,
                                                                            int64_t gpr) {
@@ -237,11 +262,12 @@ __global__ __launch_bounds__(kSerialWaves * 64) void forward_serial_kernel(Forwa
 
     const char* kbase = static_cast<const char*>(pr.k) + base;
     const char* vbase = static_cast<const char*>(pr.v) + base;
+    const char* rbase = GATED ? static_cast<const char*>(pr.r) + base : nullptr;
     char* ybase = static_cast<char*>(pr.y) + base;
     if (wave_all_fused(s))
-        serial_scan<DT, VEC, true>(s, pr, kbase, vbase, ybase, voff, row_bytes, active);
+        serial_scan<DT, VEC, true, GATED>(s, pr, kbase, vbase, rbase, ybase, voff, row_bytes, active);
     else
-        serial_scan<DT, VEC, false>(s, pr, kbase, vbase, ybase, voff, row_bytes, active);
+        serial_scan<DT, VEC, false, GATED>(s, pr, kbase, vbase, rbase, ybase, voff, row_bytes, active);
     if (active && pr.a_out != nullptr) store_state(s, pr, bb * pr.C + c);
 }
 
@@ -379,19 +405,35 @@ __device__ __forceinline__ void chunk_load(typename Io<DT, VEC>::Raw (&kr)[L],
     }
 }
 
+// Load this wave's n tokens of one array (the receptance) like chunk_load.
+template <int DT, int VEC, int L, bool FULL, int AUX>
+__device__ __forceinline__ void chunk_load_one(typename Io<DT, VEC>::Raw (&xr)[L], rsrc_t x_,
+                                               uint32_t voff, uint32_t row_bytes, int n) {
+    using IO = Io<DT, VEC>;
+    using Raw = typename IO::Raw;
+#pragma unroll
+    for (int i = 0; i < L; i++) {
+        if (FULL || i < n)
+            xr[i] = Buf<Raw>::template load<AUX>(x_, voff + uint32_t(i) * row_bytes, 0u);
+        else
+            xr[i] = IO::zero();
+    }
+}
+
 // State of this wave's n tokens started from the empty history, by two
 // passes: the largest decayed key x_i = k_i - (n-1-i) w, then the sums of
 // e^{x_i - max} and e^{x_i - max} v_i.  This is the closed form of the
 // recurrence over the tokens (the state's exponent is the running maximum),
 // without a serial chain of maxima.
-template <int DT, int VEC, int L, bool FULL>
+template <int DT, int VEC, int L, bool FULL, bool KEEP = true>
 __device__ __forceinline__ void chunk_aggregate(const Lane<VEC>& s,
                                                 const typename Io<DT, VEC>::Raw (&kr)[L],
                                                 const typename Io<DT, VEC>::Raw (&vr)[L],
                                                 int n, Part<VEC>& g) {
     using IO = Io<DT, VEC>;
     // short blocks keep the decayed keys of the first pass for the second
-    constexpr bool kKeepX = L <= 16;
+    // (unless the caller needs the registers: KEEP)
+    constexpr bool kKeepX = KEEP && L <= 16;
     float xs[kKeepX ? L : 1][VEC];
     float mx[VEC];
 #pragma unroll
@@ -443,7 +485,7 @@ __device__ __forceinline__ void chunk_aggregate(const Lane<VEC>& s,
     }
 }
 
-template <int DT, int VEC>
+template <int DT, int VEC, bool GATED>
 __global__ __launch_bounds__(kChunkWaves * 64) void forward_chunked_kernel(ForwardProblem pr,
                                                                            ChunkArgs ca) {
     using IO = Io<DT, VEC>;
@@ -480,7 +522,7 @@ __global__ __launch_bounds__(kChunkWaves * 64) void forward_chunked_kernel(Forwa
     // lanes past C read lane 0's words (in bounds) and never store
     const uint32_t voff = active ? uint32_t(lane) * uint32_t(sizeof(Raw)) : 0u;
     const int64_t base = ((bb * T + t_begin) * pr.C + c0) * es;
-    Raw kr[L], vr[L];
+    Raw kr[L], vr[L], rr[GATED ? L : 1];
     {
         const rsrc_t kr_ = make_rsrc(static_cast<const char*>(pr.k) + base);
         const rsrc_t vr_ = make_rsrc(static_cast<const char*>(pr.v) + base);
@@ -488,6 +530,13 @@ __global__ __launch_bounds__(kChunkWaves * 64) void forward_chunked_kernel(Forwa
             chunk_load<DT, VEC, L, true, kDefaultLoad>(kr, vr, kr_, vr_, voff, row_bytes, n);
         else
             chunk_load<DT, VEC, L, false, kDefaultLoad>(kr, vr, kr_, vr_, voff, row_bytes, n);
+        if constexpr (GATED) {
+            const rsrc_t rr_ = make_rsrc(static_cast<const char*>(pr.r) + base);
+            if (n == L)
+                chunk_load_one<DT, VEC, L, true, kDefaultLoad>(rr, rr_, voff, row_bytes, n);
+            else
+                chunk_load_one<DT, VEC, L, false, kDefaultLoad>(rr, rr_, voff, row_bytes, n);
+        }
     }
 
     // phase 1: this wave's partial state from the empty history
@@ -579,16 +628,17 @@ __global__ __launch_bounds__(kChunkWaves * 64) void forward_chunked_kernel(Forwa
     }
     const rsrc_t yr_ = make_rsrc(static_cast<char*>(pr.y) + base);
     const bool fused = wave_all_fused(s);
+    const Raw (&rg)[L] = gated_rr<GATED>(rr, kr);
     if (n == L) {
         if (fused)
-            run_block<DT, VEC, L, true, true>(s, kr, vr, yr_, voff, row_bytes, n, active);
+            run_block<DT, VEC, L, true, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
         else
-            run_block<DT, VEC, L, false, true>(s, kr, vr, yr_, voff, row_bytes, n, active);
+            run_block<DT, VEC, L, false, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
     } else {
         if (fused)
-            run_block<DT, VEC, L, true, false>(s, kr, vr, yr_, voff, row_bytes, n, active);
+            run_block<DT, VEC, L, true, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
         else
-            run_block<DT, VEC, L, false, false>(s, kr, vr, yr_, voff, row_bytes, n, active);
+            run_block<DT, VEC, L, false, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
     }
     if (t_begin + n == T && active && pr.a_out != nullptr) store_state(s, pr, bb * pr.C + c);
 }
@@ -608,7 +658,7 @@ __global__ __launch_bounds__(kChunkWaves * 64) void forward_chunked_kernel(Forwa
 // does not depend on timing.
 // ---------------------------------------------------------------------------
 
-template <int DT, int VEC, int NWV>
+template <int DT, int VEC, int NWV, bool GATED>
 __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProblem pr, int64_t gpr,
                                                                    int64_t nsub) {
     using IO = Io<DT, VEC>;
@@ -653,17 +703,25 @@ __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProble
         const int64_t t0 = sc * L;
         const int n = T - t0 >= L ? L : int(T - t0);
         const int64_t base = gbase + t0 * int64_t(row_bytes);
-        Raw kr[L], vr[L];
+        Raw kr[L], vr[L], rr[GATED ? L : 1];
         Part<VEC> gw;
         {
             const rsrc_t kr_ = make_rsrc(static_cast<const char*>(pr.k) + base);
             const rsrc_t vr_ = make_rsrc(static_cast<const char*>(pr.v) + base);
+            // the receptance is needed only after the carry: its loads are
+            // issued after the aggregate, to overlap the wait for the carry
             if (n == L) {
                 chunk_load<DT, VEC, L, true, kStreamLoad>(kr, vr, kr_, vr_, voff, row_bytes, n);
-                chunk_aggregate<DT, VEC, L, true>(s, kr, vr, n, gw);
+                chunk_aggregate<DT, VEC, L, true, !GATED>(s, kr, vr, n, gw);
+                if constexpr (GATED)
+                    chunk_load_one<DT, VEC, L, true, kStreamLoad>(
+                        rr, make_rsrc(static_cast<const char*>(pr.r) + base), voff, row_bytes, n);
             } else {
                 chunk_load<DT, VEC, L, false, kStreamLoad>(kr, vr, kr_, vr_, voff, row_bytes, n);
-                chunk_aggregate<DT, VEC, L, false>(s, kr, vr, n, gw);
+                chunk_aggregate<DT, VEC, L, false, !GATED>(s, kr, vr, n, gw);
+                if constexpr (GATED)
+                    chunk_load_one<DT, VEC, L, false, kStreamLoad>(
+                        rr, make_rsrc(static_cast<const char*>(pr.r) + base), voff, row_bytes, n);
             }
         }
         // the carry of this sub-chunk, then the next one's
@@ -693,16 +751,17 @@ __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProble
 #pragma unroll
         for (int q = 0; q < VEC; q++) { s.a[q] = x.a[q]; s.b[q] = x.b[q]; s.A[q] = x.A[q]; s.m[q] = x.m[q]; }
         const rsrc_t yr_ = make_rsrc(static_cast<char*>(pr.y) + base);
+        const Raw (&rg)[L] = gated_rr<GATED>(rr, kr);
         if (n == L) {
             if (fused)
-                run_block<DT, VEC, L, true, true>(s, kr, vr, yr_, voff, row_bytes, n, active);
+                run_block<DT, VEC, L, true, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
             else
-                run_block<DT, VEC, L, false, true>(s, kr, vr, yr_, voff, row_bytes, n, active);
+                run_block<DT, VEC, L, false, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
         } else {
             if (fused)
-                run_block<DT, VEC, L, true, false>(s, kr, vr, yr_, voff, row_bytes, n, active);
+                run_block<DT, VEC, L, true, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
             else
-                run_block<DT, VEC, L, false, false>(s, kr, vr, yr_, voff, row_bytes, n, active);
+                run_block<DT, VEC, L, false, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
         }
         if (sc == nsub - 1 && active && pr.a_out != nullptr) store_state(s, pr, bb * pr.C + c);
     }
@@ -781,16 +840,14 @@ int chained_waves(int64_t ngroups, int device_cus) {
     return nw;
 }
 
-hipError_t launch_forward_chained(const ForwardProblem& pr, hipStream_t stream) {
-    const int vec = pr.vec;
-    const int64_t cg = 64 * vec;
-    const int64_t gpr = (pr.C + cg - 1) / cg;
-    const int64_t ngroups = pr.B * gpr;
-    const int64_t nsub = (pr.T + kChainTokens - 1) / kChainTokens;
-    const int nw = chained_waves(ngroups, device_cu_count());
-    const dim3 grid(static_cast<unsigned>(ngroups)), block(nw * 64);
-#define WKV_LAUNCH_CHAINED(DT, V, NW) \
-    hipLaunchKernelGGL((forward_chained_kernel<DT, V, NW>), grid, block, 0, stream, pr, gpr, nsub)
+namespace {
+template <bool GATED>
+void launch_chained_t(const ForwardProblem& pr, int nw, dim3 grid, int64_t gpr, int64_t nsub,
+                      hipStream_t stream) {
+    const dim3 block(nw * 64);
+#define WKV_LAUNCH_CHAINED(DT, V, NW)                                                             \
+    hipLaunchKernelGGL((forward_chained_kernel<DT, V, NW, GATED>), grid, block, 0, stream, pr, gpr, \
+                       nsub)
 #define WKV_CHAINED_NW(DT, V)                                   \
     switch (nw) {                                              \
         case 16: WKV_LAUNCH_CHAINED(DT, V, 16); break;         \
@@ -798,7 +855,7 @@ hipError_t launch_forward_chained(const ForwardProblem& pr, hipStream_t stream) 
         case 4: WKV_LAUNCH_CHAINED(DT, V, 4); break;           \
         default: WKV_LAUNCH_CHAINED(DT, V, 2); break;          \
     }
-    if (pr.dtype == kBF16 && vec == 2) {
+    if (pr.dtype == kBF16 && pr.vec == 2) {
         WKV_CHAINED_NW(kBF16, 2)
     } else if (pr.dtype == kBF16) {
         WKV_CHAINED_NW(kBF16, 1)
@@ -807,24 +864,63 @@ hipError_t launch_forward_chained(const ForwardProblem& pr, hipStream_t stream) 
     }
 #undef WKV_CHAINED_NW
 #undef WKV_LAUNCH_CHAINED
+}
+}  // namespace
+
+hipError_t launch_forward_chained(const ForwardProblem& pr, hipStream_t stream) {
+    const int64_t cg = 64 * pr.vec;
+    const int64_t gpr = (pr.C + cg - 1) / cg;
+    const int64_t ngroups = pr.B * gpr;
+    const int64_t nsub = (pr.T + kChainTokens - 1) / kChainTokens;
+    const int nw = chained_waves(ngroups, device_cu_count());
+    const dim3 grid(static_cast<unsigned>(ngroups));
+    if (pr.r != nullptr)
+        launch_chained_t<true>(pr, nw, grid, gpr, nsub, stream);
+    else
+        launch_chained_t<false>(pr, nw, grid, gpr, nsub, stream);
     return hipGetLastError();
 }
 
+namespace {
+template <bool GATED>
+void launch_serial_t(const ForwardProblem& pr, dim3 grid, int64_t ngroups, int64_t gpr,
+                     hipStream_t stream) {
+    const dim3 block(kSerialWaves * 64);
+    if (pr.dtype == kBF16 && pr.vec == 2)
+        hipLaunchKernelGGL((forward_serial_kernel<kBF16, 2, GATED>), grid, block, 0, stream, pr, ngroups, gpr);
+    else if (pr.dtype == kBF16)
+        hipLaunchKernelGGL((forward_serial_kernel<kBF16, 1, GATED>), grid, block, 0, stream, pr, ngroups, gpr);
+    else
+        hipLaunchKernelGGL((forward_serial_kernel<kF32, 1, GATED>), grid, block, 0, stream, pr, ngroups, gpr);
+}
+}  // namespace
+
 hipError_t launch_forward_serial(const ForwardProblem& pr, hipStream_t stream) {
-    const int vec = pr.vec;
-    const int64_t cg = 64 * vec;
+    const int64_t cg = 64 * pr.vec;
     const int64_t gpr = (pr.C + cg - 1) / cg;
     const int64_t ngroups = pr.B * gpr;
     const int64_t blocks = (ngroups + kSerialWaves - 1) / kSerialWaves;
-    const dim3 grid(static_cast<unsigned>(blocks)), block(kSerialWaves * 64);
-    if (pr.dtype == kBF16 && vec == 2)
-        hipLaunchKernelGGL((forward_serial_kernel<kBF16, 2>), grid, block, 0, stream, pr, ngroups, gpr);
-    else if (pr.dtype == kBF16)
-        hipLaunchKernelGGL((forward_serial_kernel<kBF16, 1>), grid, block, 0, stream, pr, ngroups, gpr);
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (pr.r != nullptr)
+        launch_serial_t<true>(pr, grid, ngroups, gpr, stream);
     else
-        hipLaunchKernelGGL((forward_serial_kernel<kF32, 1>), grid, block, 0, stream, pr, ngroups, gpr);
+        launch_serial_t<false>(pr, grid, ngroups, gpr, stream);
     return hipGetLastError();
 }
+
+namespace {
+template <bool GATED>
+void launch_chunked_t(const ForwardProblem& pr, const ChunkArgs& ca, int vec, dim3 grid,
+                      hipStream_t stream) {
+    const dim3 block(kChunkWaves * 64);
+    if (pr.dtype == kBF16 && vec == 2)
+        hipLaunchKernelGGL((forward_chunked_kernel<kBF16, 2, GATED>), grid, block, 0, stream, pr, ca);
+    else if (pr.dtype == kBF16)
+        hipLaunchKernelGGL((forward_chunked_kernel<kBF16, 1, GATED>), grid, block, 0, stream, pr, ca);
+    else
+        hipLaunchKernelGGL((forward_chunked_kernel<kF32, 1, GATED>), grid, block, 0, stream, pr, ca);
+}
+}  // namespace
 
 hipError_t launch_forward_chunked(const ForwardProblem& pr, void* workspace, hipStream_t stream) {
     const ChunkPlan pl = plan_chunked(pr.B, pr.T, pr.C, pr.vec);
@@ -842,13 +938,11 @@ hipError_t launch_forward_chunked(const ForwardProblem& pr, void* workspace, hip
     const int64_t reset_blocks = std::min<int64_t>((int64_t(ntiles) + 255) / 256, 1024);
     hipLaunchKernelGGL(reset_chunk_counters, dim3(static_cast<unsigned>(reset_blocks)), dim3(256), 0,
                        stream, ca.ticket, ca.flags, int64_t(ntiles));
-    const dim3 grid(static_cast<unsigned>(ntiles)), block(kChunkWaves * 64);
-    if (pr.dtype == kBF16 && pl.vec == 2)
-        hipLaunchKernelGGL((forward_chunked_kernel<kBF16, 2>), grid, block, 0, stream, pr, ca);
-    else if (pr.dtype == kBF16)
-        hipLaunchKernelGGL((forward_chunked_kernel<kBF16, 1>), grid, block, 0, stream, pr, ca);
+    const dim3 grid(static_cast<unsigned>(ntiles));
+    if (pr.r != nullptr)
+        launch_chunked_t<true>(pr, ca, pl.vec, grid, stream);
     else
-        hipLaunchKernelGGL((forward_chunked_kernel<kF32, 1>), grid, block, 0, stream, pr, ca);
+        launch_chunked_t<false>(pr, ca, pl.vec, grid, stream);
     return hipGetLastError();
 }
 

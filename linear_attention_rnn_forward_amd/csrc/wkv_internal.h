@@ -17,6 +17,7 @@ struct ForwardProblem {
     void *y;
     const float *a_in, *b_in, *p_in;  // all null or all set
     float *a_out, *b_out, *p_out;     // all null or all set
+    const void* r = nullptr;          // receptance [B,T,C]: y = sigmoid(r) * wkv when set
 };
 
 // Geometry of the chunked path for one problem.
@@ -51,6 +52,7 @@ struct StepProblem {
     void *y;
     const float *a_in, *b_in, *p_in;
     float *a_out, *b_out, *p_out;
+    const void* r = nullptr;  // receptance [L,S,C]: y = sigmoid(r) * wkv when set
 };
 hipError_t launch_step(const StepProblem& pr, hipStream_t stream);
 

@@ -30,7 +30,9 @@ struct F32v<4> {
     static __device__ __forceinline__ T put(const float (&x)[4]) { return make_float4(x[0], x[1], x[2], x[3]); }
 };
 
-template <int DT, int VEC>
+// GATED: y = sigmoid(r) * wkv (the receptance gate, [tm-math] "Receptance:
+// the gate on the way out").
+template <int DT, int VEC, bool GATED>
 __global__ __launch_bounds__(256) void step_kernel(StepProblem pr, int64_t nvec) {
     using IO = Io<DT, VEC>;
     using Raw = typename IO::Raw;
@@ -43,16 +45,18 @@ __global__ __launch_bounds__(256) void step_kernel(StepProblem pr, int64_t nvec)
     const float* wp = pr.w + l * pr.C + c;
     const float* up = pr.u + l * pr.C + c;
 
-    float kf[VEC], vf[VEC], a[VEC], b[VEC], p[VEC], y[VEC];
+    float kf[VEC], vf[VEC], a[VEC], b[VEC], p[VEC], y[VEC], rf[VEC];
     IO::unpack(load_stream(reinterpret_cast<const Raw*>(pr.k) + i), kf);
     IO::unpack(load_stream(reinterpret_cast<const Raw*>(pr.v) + i), vf);
     FV::get(load_stream(reinterpret_cast<const typename FV::T*>(pr.a_in) + i), a);
     FV::get(load_stream(reinterpret_cast<const typename FV::T*>(pr.b_in) + i), b);
     FV::get(load_stream(reinterpret_cast<const typename FV::T*>(pr.p_in) + i), p);
+    if constexpr (GATED) IO::unpack(load_stream(reinterpret_cast<const Raw*>(pr.r) + i), rf);
 #pragma unroll
     for (int q = 0; q < VEC; q++) {
         p[q] = clamp_empty(p[q]);
-        y[q] = decode_token(a[q], b[q], p[q], kf[q], vf[q], wp[q], up[q]);
+        y[q] = decode_token<GATED>(a[q], b[q], p[q], kf[q], vf[q], wp[q], up[q],
+                                   GATED ? gate_den(rf[q]) : 1.0f);
         p[q] = export_p(p[q]);
     }
     reinterpret_cast<Raw*>(pr.y)[i] = IO::pack(y);
@@ -63,20 +67,28 @@ __global__ __launch_bounds__(256) void step_kernel(StepProblem pr, int64_t nvec)
 
 }  // namespace
 
-hipError_t launch_step(const StepProblem& pr, hipStream_t stream) {
-    const int64_t n = pr.L * pr.S * pr.C;
-    const int vec = pr.vec;
-    const int64_t nvec = n / vec;
+namespace {
+template <bool GATED>
+void launch_step_t(const StepProblem& pr, int64_t nvec, hipStream_t stream) {
     const int64_t blocks = (nvec + 255) / 256;
     const dim3 grid(static_cast<unsigned>(blocks)), block(256);
-    if (pr.dtype == kBF16 && vec == 4)
-        hipLaunchKernelGGL((step_kernel<kBF16, 4>), grid, block, 0, stream, pr, nvec);
+    if (pr.dtype == kBF16 && pr.vec == 4)
+        hipLaunchKernelGGL((step_kernel<kBF16, 4, GATED>), grid, block, 0, stream, pr, nvec);
     else if (pr.dtype == kBF16)
-        hipLaunchKernelGGL((step_kernel<kBF16, 1>), grid, block, 0, stream, pr, nvec);
-    else if (vec == 4)
-        hipLaunchKernelGGL((step_kernel<kF32, 4>), grid, block, 0, stream, pr, nvec);
+        hipLaunchKernelGGL((step_kernel<kBF16, 1, GATED>), grid, block, 0, stream, pr, nvec);
+    else if (pr.vec == 4)
+        hipLaunchKernelGGL((step_kernel<kF32, 4, GATED>), grid, block, 0, stream, pr, nvec);
     else
-        hipLaunchKernelGGL((step_kernel<kF32, 1>), grid, block, 0, stream, pr, nvec);
+        hipLaunchKernelGGL((step_kernel<kF32, 1, GATED>), grid, block, 0, stream, pr, nvec);
+}
+}  // namespace
+
+hipError_t launch_step(const StepProblem& pr, hipStream_t stream) {
+    const int64_t nvec = pr.L * pr.S * pr.C / pr.vec;
+    if (pr.r != nullptr)
+        launch_step_t<true>(pr, nvec, stream);
+    else
+        launch_step_t<false>(pr, nvec, stream);
     return hipGetLastError();
 }
 

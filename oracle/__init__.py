@@ -21,6 +21,10 @@ What each routine follows (pages cited by address and section):
   type; used only to show the overflow the stabilised form avoids.
 * ``token_shift`` — the two-tap causal lerp (tm_rwkv_math, "Token shift: a
   two-tap causal convolution"), in C, fp64.
+* ``sigmoid`` / ``gate`` / ``forward_gated`` / ``step_gated`` — the
+  receptance gate o = sigmoid(r) * wkv applied elementwise to the output of
+  ``forward`` / ``step`` (tm_rwkv_math, "Receptance: the gate on the way
+  out"), NumPy fp64.  The state is the plain recurrence's.
 
 Pins (what ties these to the pages rather than to themselves) live in
 ``tests/test_oracle_pins.py``.  Inputs are promoted exactly to fp64 from
@@ -248,3 +252,29 @@ def naive(k, v, w, u, dtype=np.float64):
             a_hist[:, t, :] = a
             b_hist[:, t, :] = b
     return y, a_hist, b_hist
+
+
+def sigmoid(r):
+    """The logistic function 1 / (1 + e^{-r}) in fp64 (tm_rwkv_math,
+    "Receptance: the gate on the way out"), written in the form that does not
+    overflow: e^{r} / (1 + e^{r}) for r < 0."""
+    r = _f64(r)
+    e = np.exp(-np.abs(r))
+    return np.where(r >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def gate(y, r):
+    """o = sigmoid(r) * y, elementwise (the receptance gate)."""
+    return sigmoid(r) * _f64(y)
+
+
+def forward_gated(k, v, r, w, u, state=None):
+    """``forward`` followed by the receptance gate: (o, state)."""
+    y, st = forward(k, v, w, u, state=state)
+    return gate(y, r), st
+
+
+def step_gated(state, k, v, r, w, u):
+    """``step`` followed by the receptance gate: (o, state')."""
+    y, st = step(state, k, v, w, u)
+    return gate(y, r), st

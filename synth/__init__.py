@@ -149,6 +149,25 @@ def make_forward_inputs(wl: ForwardWorkload) -> ForwardInputs:
     return ForwardInputs(w, u, k, v, k_bits, v_bits)
 
 
+# The receptance r of the gated form: r ~ N(0, RECEPTANCE_STD) from its own
+# generator (seed offset below), so the k, v, w, u of a workload are the same
+# with or without the gate.
+RECEPTANCE_STD = 2.0
+RECEPTANCE_SEED_OFFSET = 1000
+
+
+def make_receptance(wl: ForwardWorkload):
+    """r [B,T,C] for `wl`: fp32 values as stored, and the uint16 bits when the
+    storage type is bf16 (else None)."""
+    rng = np.random.default_rng(wl.seed + RECEPTANCE_SEED_OFFSET)
+    r = rng.standard_normal(size=(wl.B, wl.T, wl.C), dtype=np.float32)
+    r *= np.float32(RECEPTANCE_STD)
+    if wl.dtype == "bf16":
+        bits = f32_to_bf16_bits(r)
+        return bf16_bits_to_f32(bits), bits
+    return r, None
+
+
 def decode_params(wl: DecodeWorkload):
     """Per-layer decay and bonus [L,C] for the decode workload."""
     rng = np.random.default_rng(wl.seed)

@@ -31,13 +31,13 @@ def test_every_declared_symbol_is_exported(header, libpath):
 def test_header_lists_the_boundary_calls():
     names = _declared("wkv.h")
     for n in ("wkv_forward", "wkv_step", "wkv_token_shift", "wkv_forward_workspace_size",
-              "wkv_status_string", "wkv_last_error"):
+              "wkv_forward_gated", "wkv_step_gated", "wkv_status_string", "wkv_last_error"):
         assert n in names
 
 
 def test_abi_version_and_status_strings():
     L = wkv.lib()
-    assert L.wkv_abi_version() == 100
+    assert L.wkv_abi_version() == 101
     for code in range(0, -9, -1):
         assert L.wkv_status_string(code).decode()
     assert L.wkv_status_string(-100).decode() == "unknown status"
@@ -108,3 +108,42 @@ def test_workspace_sizes():
     n = L.wkv_forward_workspace_size_path(1, 65536, 4096, 0, 2)
     assert 256 < n < 128 << 20
     assert L.wkv_forward_workspace_size_path(0, 10, 10, 0, 2) == 0
+
+
+def _fwd_gated(path=0, B=1, T=8, C=64, dtype=0, w=1 * G, u=2 * G, k=3 * G, v=4 * G, r=6 * G, o=5 * G,
+               a_in=None, b_in=None, p_in=None, a_out=None, b_out=None, p_out=None):
+    L = wkv.lib()
+    return L.wkv_forward_gated(B, T, C, dtype, path, P(w), P(u), P(k), P(v), P(r), P(o), P(a_in),
+                               P(b_in), P(p_in), P(a_out), P(b_out), P(p_out), None, 0, None)
+
+
+def test_forward_gated_rejects_bad_arguments():
+    """r is required (T > 0) and the output may not overlap it; the plain
+    checks apply unchanged."""
+    assert _fwd_gated(r=None) == -1            # WKV_ERR_NULL
+    assert _fwd_gated(r=5 * G) == -5           # o overlaps r
+    assert _fwd_gated(r=5 * G + 64) == -5      # partial overlap
+    assert _fwd_gated(dtype=7) == -3
+    assert _fwd_gated(B=0) == -2
+    assert _fwd_gated(path=9) == -8
+    assert _fwd_gated(a_out=7 * G, b_out=8 * G, p_out=6 * G) == -5   # state output overlaps r
+    # T = 0 needs no r
+    L = wkv.lib()
+    assert L.wkv_forward_gated(1, 0, 64, 0, 0, P(G), P(2 * G), None, None, None, None, None, None,
+                               None, None, None, None, None, 0, None) == 0
+
+
+def test_step_gated_rejects_bad_arguments():
+    L = wkv.lib()
+    n = [P(i * G) for i in range(1, 13)]   # w u k v r y a_in b_in p_in a_out b_out p_out
+
+    def call(**over):
+        args = dict(zip("w u k v r y ai bi pi ao bo po".split(), n))
+        args.update({k2: P(v2) if v2 is not None else None for k2, v2 in over.items()})
+        return L.wkv_step_gated(2, 3, 64, 0, args["w"], args["u"], args["k"], args["v"], args["r"],
+                                args["y"], args["ai"], args["bi"], args["pi"], args["ao"], args["bo"],
+                                args["po"], None)
+
+    assert call(r=None) == -1
+    assert call(r=6 * G) == -5        # y (6 G) overlaps r
+    assert call(ao=5 * G) == -5       # a_out overlaps r

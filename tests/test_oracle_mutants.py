@@ -93,3 +93,45 @@ def test_mutant_is_caught(tmp_path, name):
     with oracle.library(lib):
         failed = _checks_fail()
     assert failed, f"mutant {name} passed every pin"
+
+
+# ---------------------------------------------------------------------------
+# the receptance gate's logistic function (NumPy side of the oracle)
+# ---------------------------------------------------------------------------
+
+SIGMOID_MUTANTS = {
+    "negated_argument": lambda r: 1.0 / (1.0 + np.exp(r)),
+    "tanh": np.tanh,
+    "missing_one": lambda r: np.exp(r),
+    "half_slope": lambda r: 1.0 / (1.0 + np.exp(-r / 2)),
+    "shifted": lambda r: 1.0 / (1.0 + np.exp(-(r + 0.1))),
+}
+
+
+def _sigmoid_checks_fail(sig):
+    """The closed-form pins of test_oracle_pins.py, applied to `sig`."""
+    failed = []
+    if sig(np.float64(0.0)) != 0.5:
+        failed.append("half_at_zero")
+    if abs(sig(np.log(3.0)) - 0.75) > 1e-15:
+        failed.append("three_quarters_at_ln3")
+    r = np.linspace(-30.0, 30.0, 601)
+    if np.max(np.abs(sig(r) + sig(-r) - 1.0)) > 4.5e-16:
+        failed.append("symmetry")
+    h = 1e-5
+    rr = np.linspace(-8.0, 8.0, 65)
+    d = (sig(rr + h) - sig(rr - h)) / (2 * h)
+    s = sig(rr)
+    if not np.allclose(d, s * (1 - s), rtol=1e-6, atol=1e-10):
+        failed.append("derivative")
+    return failed
+
+
+def test_real_sigmoid_passes_its_pins():
+    assert _sigmoid_checks_fail(oracle.sigmoid) == []
+
+
+@pytest.mark.parametrize("name", sorted(SIGMOID_MUTANTS))
+def test_sigmoid_mutant_is_caught(name):
+    with np.errstate(over="ignore", invalid="ignore"):
+        assert _sigmoid_checks_fail(SIGMOID_MUTANTS[name]), name

@@ -389,3 +389,75 @@ def test_empty_sequence_passes_state_through():
     assert y.shape == (2, 0, 3)
     for s, s_ref in zip(st_out, st):
         np.testing.assert_array_equal(s, s_ref)
+
+
+# ---------------------------------------------------------------------------
+# receptance gate (aicassindra.com tm_rwkv_math, "Receptance: the gate on the
+# way out"): o = sigmoid(r) * wkv, sigmoid the logistic function
+# ---------------------------------------------------------------------------
+
+def test_sigmoid_closed_forms():
+    """Values fixed by the logistic function's definition, which a swapped
+    sign, a tanh or a missing 1 would each break."""
+    assert oracle.sigmoid(0.0) == 0.5
+    # 1 / (1 + e^{-ln 3}) = 1 / (1 + 1/3) = 3/4 and its mirror 1/4
+    assert abs(oracle.sigmoid(np.log(3.0)) - 0.75) < 1e-15
+    assert abs(oracle.sigmoid(-np.log(3.0)) - 0.25) < 1e-15
+    r = np.linspace(-60.0, 60.0, 2401)
+    s = oracle.sigmoid(r)
+    np.testing.assert_allclose(s + oracle.sigmoid(-r), 1.0, rtol=0, atol=4.5e-16)   # symmetry
+    assert np.all(np.diff(s) >= 0) and np.all(s > 0) and np.all(s <= 1)
+    # no overflow far out; the limits
+    with np.errstate(over="raise", invalid="raise"):
+        big = oracle.sigmoid(np.array([-1000.0, 1000.0]))
+    assert big[0] == 0.0 and big[1] == 1.0
+
+
+def test_sigmoid_derivative_identity():
+    """sigma' = sigma (1 - sigma), checked by central differences."""
+    r = np.linspace(-8.0, 8.0, 65)
+    h = 1e-5
+    d = (oracle.sigmoid(r + h) - oracle.sigmoid(r - h)) / (2 * h)
+    s = oracle.sigmoid(r)
+    np.testing.assert_allclose(d, s * (1 - s), rtol=1e-6, atol=1e-10)
+
+
+def test_gated_forward_special_cases():
+    """r = 0 halves the output, r -> +inf passes it, r -> -inf mutes it; the
+    state is the plain recurrence's."""
+    rng = np.random.default_rng(77)
+    B, T, C = 2, 40, 5
+    k = rng.normal(0, 2, (B, T, C))
+    v = rng.normal(0, 1, (B, T, C))
+    w = np.exp(rng.uniform(-3, 1, C))
+    u = rng.normal(0, 0.5, C)
+    y, st = oracle.forward(k, v, w, u)
+    o0, st0 = oracle.forward_gated(k, v, np.zeros_like(k), w, u)
+    np.testing.assert_array_equal(o0, y / 2)
+    for a, b in zip(st0, st):
+        np.testing.assert_array_equal(a, b)
+    op, _ = oracle.forward_gated(k, v, np.full_like(k, 50.0), w, u)
+    np.testing.assert_allclose(op, y, rtol=1e-20, atol=1e-20 + 2e-22 * np.abs(y).max())
+    om, _ = oracle.forward_gated(k, v, np.full_like(k, -800.0), w, u)
+    assert np.all(om == 0.0)
+    # a gate is applied per element: mixing r between two positions mixes only them
+    r = rng.normal(0, 2, (B, T, C))
+    o, _ = oracle.forward_gated(k, v, r, w, u)
+    np.testing.assert_allclose(o, y / (1 + np.exp(-r)), rtol=1e-15, atol=0)
+
+
+def test_gated_step_chain_equals_gated_forward():
+    rng = np.random.default_rng(78)
+    B, T, C = 3, 25, 4
+    k = rng.normal(0, 2, (B, T, C))
+    v = rng.normal(0, 1, (B, T, C))
+    r = rng.normal(0, 2, (B, T, C))
+    w = np.exp(rng.uniform(-3, 1, C))
+    u = rng.normal(0, 0.5, C)
+    o_f, st_f = oracle.forward_gated(k, v, r, w, u)
+    st = (np.zeros((1, B, C)), np.zeros((1, B, C)), np.full((1, B, C), -np.inf))
+    outs = []
+    for t in range(T):
+        o_t, st = oracle.step_gated(st, k[None, :, t], v[None, :, t], r[None, :, t], w[None], u[None])
+        outs.append(o_t[0])
+    np.testing.assert_allclose(np.stack(outs, axis=1), o_f, rtol=1e-12, atol=1e-14)
