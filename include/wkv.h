@@ -212,6 +212,43 @@ int wkv_token_shift(int64_t B, int64_t T, int64_t C, int dtype,
                     const float *mu_r, const float *mu_k, const float *mu_v,
                     void *xr, void *xk, void *xv, void *x_last, void *stream);
 
+/*
+ * Session state save and resume ([multigrid] "The state, in bytes" and its
+ * closing note: a session's state is small and constant in length, so it can
+ * be serialised, stored and resumed elsewhere at full fidelity).  The state
+ * of ONE sequence `seq` of a decode batch -- a, b, p of every layer plus
+ * n_shift shifted-token arrays (the previous step's token of each sub-block
+ * that token-shifts) -- is copied to or from a host blob:
+ *
+ *   header (64 bytes: magic "WKVS", format version 1, L, C, dtype, n_shift),
+ *   a, b, p [L][C] fp32 each, then n_shift arrays [L][C] in dtype.
+ *
+ *   L, S, C           decode-batch shape; seq in [0, S)
+ *   a, b, p           [L,S,C] fp32 device arrays (the wkv_step state)
+ *   shift             host array of n_shift device pointers, each [L,S,C]
+ *                     in dtype (may be NULL when n_shift == 0);
+ *                     0 <= n_shift <= WKV_SESSION_MAX_SHIFT
+ *   blob              host memory of at least wkv_session_bytes() bytes
+ *                     (pinned memory makes the copies asynchronous)
+ *
+ * Both calls enqueue row copies (hipMemcpy2DAsync) on `stream` and return:
+ * a saved blob is complete, and a loaded state usable, once the stream
+ * reaches them.  wkv_session_save writes the header at once.
+ * wkv_session_load checks the header (magic, version, L, C, dtype, n_shift)
+ * and the blob size first and enqueues nothing on a mismatch.  The other
+ * sequences of the batch are not touched.
+ */
+#define WKV_SESSION_MAX_SHIFT 8
+size_t wkv_session_bytes(int64_t L, int64_t C, int dtype, int n_shift);
+int wkv_session_save(int64_t L, int64_t S, int64_t C, int dtype, int64_t seq,
+                     const float *a, const float *b, const float *p,
+                     const void *const *shift, int n_shift,
+                     void *blob, size_t blob_bytes, void *stream);
+int wkv_session_load(int64_t L, int64_t S, int64_t C, int dtype, int64_t seq,
+                     const void *blob, size_t blob_bytes,
+                     float *a, float *b, float *p, void *const *shift, int n_shift,
+                     void *stream);
+
 /* Static description of a status code. */
 const char *wkv_status_string(int status);
 
@@ -221,7 +258,7 @@ const char *wkv_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int wkv_abi_version(void);
 
-#define WKV_ABI_VERSION 101
+#define WKV_ABI_VERSION 102
 
 #ifdef __cplusplus
 }

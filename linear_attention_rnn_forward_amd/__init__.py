@@ -77,6 +77,12 @@ def lib() -> ctypes.CDLL:
         L.wkv_step.argtypes = [i64, i64, i64, i32] + [vp] * 11 + [vp]
         L.wkv_step_gated.restype = i32
         L.wkv_step_gated.argtypes = [i64, i64, i64, i32] + [vp] * 12 + [vp]
+        L.wkv_session_bytes.restype = sz
+        L.wkv_session_bytes.argtypes = [i64, i64, i32, i32]
+        L.wkv_session_save.restype = i32
+        L.wkv_session_save.argtypes = [i64, i64, i64, i32, i64, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.wkv_session_load.restype = i32
+        L.wkv_session_load.argtypes = [i64, i64, i64, i32, i64, vp, sz, vp, vp, vp, vp, i32, vp]
         L.wkv_token_shift.restype = i32
         L.wkv_token_shift.argtypes = [i64, i64, i64, i32] + [vp] * 9 + [vp]
         L.wkv_status_string.restype = ctypes.c_char_p
@@ -290,3 +296,65 @@ def token_shift(x, mu_r, mu_k, mu_v, x_prev=None, return_last=False, out=None):
     if return_last:
         return xr, xk, xv, x_last
     return xr, xk, xv
+
+
+# ---------------------------------------------------------------------------
+# session save / resume
+# ---------------------------------------------------------------------------
+
+def _ptr_array(ts):
+    arr = (ctypes.c_void_p * max(len(ts), 1))(*[t.data_ptr() for t in ts])
+    return arr if ts else None
+
+
+def session_bytes(L: int, C: int, dtype: int = F32, n_shift: int = 0) -> int:
+    """Bytes of one sequence's session blob (header, a, b, p, shifted tokens)."""
+    return int(lib().wkv_session_bytes(L, C, dtype, n_shift))
+
+
+def save_session(state, seq, shifts=()):
+    """The state of sequence `seq` of a decode batch as bytes.
+
+    state: (a, b, p), each [L,S,C] float32 on the GPU; shifts: shifted-token
+    arrays [L,S,C] (float32 or bfloat16, all one dtype).  Copies into pinned
+    host memory on the current stream and waits for them."""
+    torch = _torch()
+    a, b, p = state
+    _need(a, "a")
+    Ln, S, C = a.shape
+    dev = a.device
+    for x, n in zip(state, ("a", "b", "p")):
+        _need(x, n, (Ln, S, C), torch.float32, dev)
+    dt = _dtype_code(shifts[0]) if shifts else F32
+    for i, x in enumerate(shifts):
+        _need(x, f"shifts[{i}]", (Ln, S, C), shifts[0].dtype, dev)
+    n = session_bytes(Ln, C, dt, len(shifts))
+    if n == 0:
+        raise ValueError("invalid session shape")
+    blob = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    with torch.cuda.device(dev):
+        check(lib().wkv_session_save(Ln, S, C, dt, seq, _ptr(a), _ptr(b), _ptr(p),
+                                     _ptr_array(list(shifts)), len(shifts), _ptr(blob), n,
+                                     _stream(dev)))
+        torch.cuda.current_stream(dev).synchronize()
+    return bytes(blob.numpy())
+
+
+def load_session(blob, state, seq, shifts=()):
+    """Write a blob from save_session into sequence `seq` of `state` (and of
+    `shifts`), on the current stream; waits for the copies."""
+    torch = _torch()
+    a, b, p = state
+    _need(a, "a")
+    Ln, S, C = a.shape
+    dev = a.device
+    for x, n in zip(state, ("a", "b", "p")):
+        _need(x, n, (Ln, S, C), torch.float32, dev)
+    dt = _dtype_code(shifts[0]) if shifts else F32
+    for i, x in enumerate(shifts):
+        _need(x, f"shifts[{i}]", (Ln, S, C), shifts[0].dtype, dev)
+    host = torch.frombuffer(bytearray(blob), dtype=torch.uint8).pin_memory()
+    with torch.cuda.device(dev):
+        check(lib().wkv_session_load(Ln, S, C, dt, seq, _ptr(host), host.numel(), _ptr(a), _ptr(b),
+                                     _ptr(p), _ptr_array(list(shifts)), len(shifts), _stream(dev)))
+        torch.cuda.current_stream(dev).synchronize()

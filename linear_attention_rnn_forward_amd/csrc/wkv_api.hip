@@ -184,6 +184,12 @@ std::atomic<int> g_cus[64];
 
 }  // namespace
 
+namespace wkv_detail {
+// Error reporting for the other host files of the library.
+int fail_status(int status, const char* msg) { return fail(status, "%s", msg); }
+int ok_status() { return ok(); }
+}  // namespace wkv_detail
+
 namespace wkv {
 int device_cu_count() {
     int dev = 0;

@@ -37,7 +37,7 @@ def test_header_lists_the_boundary_calls():
 
 def test_abi_version_and_status_strings():
     L = wkv.lib()
-    assert L.wkv_abi_version() == 101
+    assert L.wkv_abi_version() == 102
     for code in range(0, -9, -1):
         assert L.wkv_status_string(code).decode()
     assert L.wkv_status_string(-100).decode() == "unknown status"
@@ -147,3 +147,57 @@ def test_step_gated_rejects_bad_arguments():
     assert call(r=None) == -1
     assert call(r=6 * G) == -5        # y (6 G) overlaps r
     assert call(ao=5 * G) == -5       # a_out overlaps r
+
+
+def test_session_blob_size():
+    """Header plus a, b, p (fp32) and the shifted tokens: for the pages' 7B
+    configuration (32 layers, 4096 channels, two token-shifting sub-blocks,
+    bf16 shifts) that is 64 + 32*4096*(12 + 2*2) bytes."""
+    L = wkv.lib()
+    assert L.wkv_session_bytes(32, 4096, 1, 2) == 64 + 32 * 4096 * 16
+    assert L.wkv_session_bytes(2, 3, 0, 0) == 64 + 2 * 3 * 12
+    assert L.wkv_session_bytes(0, 8, 0, 0) == 0
+    assert L.wkv_session_bytes(2, 8, 5, 0) == 0
+    assert L.wkv_session_bytes(2, 8, 0, 9) == 0
+
+
+def test_session_load_checks_the_header_first():
+    """A wrong magic, version, shape or a short blob is refused before any
+    copy is enqueued (the device pointers here are never touched)."""
+    import struct
+    L = wkv.lib()
+    Ln, S, C, dt, ns = 2, 3, 8, 0, 1
+    n = L.wkv_session_bytes(Ln, C, dt, ns)
+    good = struct.pack("<IIqqii", 0x53564B57, 1, Ln, C, dt, ns).ljust(64, b"\0") + bytes(n - 64)
+    fake = [P(i * G) for i in range(1, 5)]
+    shifts = (ctypes.c_void_p * 1)(4 * G)
+
+    def load(blob, **kw):
+        args = dict(L=Ln, S=S, C=C, dt=dt, seq=1, ns=ns)
+        args.update(kw)
+        buf = ctypes.create_string_buffer(blob, len(blob))
+        return L.wkv_session_load(args["L"], args["S"], args["C"], args["dt"], args["seq"], buf,
+                                  len(blob), fake[0], fake[1], fake[2], shifts, args["ns"], None)
+
+    bad_magic = b"XXXX" + good[4:]
+    bad_version = good[:4] + struct.pack("<I", 7) + good[8:]
+    assert load(bad_magic) == -8
+    assert load(bad_version) == -7
+    assert load(good, C=16) == -8          # saved with another C
+    assert load(good, ns=0) == -8          # saved with another n_shift
+    assert load(good[:100]) == -8          # truncated
+    assert load(good[:10]) == -8           # shorter than the header
+    assert load(good, seq=3) == -8         # seq out of range
+    assert load(good, S=0) == -2
+    load(bad_magic)
+    assert b"magic" in L.wkv_last_error()
+
+
+def test_session_save_checks_arguments():
+    L = wkv.lib()
+    buf = ctypes.create_string_buffer(10)
+    # blob too small: refused before any copy
+    assert L.wkv_session_save(2, 3, 8, 0, 0, P(G), P(2 * G), P(3 * G), None, 0, buf, 10, None) == -8
+    assert L.wkv_session_save(2, 3, 8, 0, 0, None, P(2 * G), P(3 * G), None, 0, buf, 10, None) == -1
+    assert L.wkv_session_save(2, 3, 8, 0, 5, P(G), P(2 * G), P(3 * G), None, 0, buf, 10, None) == -8
+    assert L.wkv_session_save(2, 3, 8, 0, 0, P(G), P(2 * G), P(3 * G), None, 1, buf, 10, None) == -1
