@@ -21,6 +21,11 @@ What each routine follows (pages cited by address and section):
   type; used only to show the overflow the stabilised form avoids.
 * ``token_shift`` — the two-tap causal lerp (tm_rwkv_math, "Token shift: a
   two-tap causal convolution"), in C, fp64.
+* ``backward`` — the gradients of the summed definition of wkv_t (empty
+  history) with respect to k, v, w and u, written out in NumPy fp64 from
+  the softmax form of "The WKV operator" (tm_rwkv_math): every output is a
+  weighted mean of values, so d wkv_t / d(term exponent) = weight * (v_i -
+  wkv_t).  O(T^2) per column.
 * ``sigmoid`` / ``gate`` / ``forward_gated`` / ``step_gated`` — the
   receptance gate o = sigmoid(r) * wkv applied elementwise to the output of
   ``forward`` / ``step`` (tm_rwkv_math, "Receptance: the gate on the way
@@ -278,3 +283,48 @@ def step_gated(state, k, v, r, w, u):
     """``step`` followed by the receptance gate: (o, state')."""
     y, st = step(state, k, v, w, u)
     return gate(y, r), st
+
+
+def backward(k, v, w, u, gy):
+    """Gradients of L = sum(gy * wkv) for wkv over [B,T,C] from the empty
+    history: returns (gk, gv [B,T,C], gw, gu [C]) in fp64.
+
+    For one column, wkv_t = sum_i alpha[t,i] v_i with alpha row t the softmax
+    of the exponents X[t,i] = -(t-1-i) w + k_i (i < t) and u + k_t (i = t)
+    (tm_rwkv_math, "The WKV operator: attention with a fixed decay").  Then
+    d wkv_t / d v_i = alpha[t,i] and d wkv_t / d X[t,i] = alpha[t,i] (v_i -
+    wkv_t); X[t,i] moves one for one with k_i, with u on the diagonal, and by
+    -(t-1-i) with w.  Only for small T (materialises T x T per column).
+    """
+    k = _f64(k)
+    v = _f64(v)
+    g = _f64(gy)
+    B, T, C = k.shape
+    w = _f64(w).reshape(C)
+    u = _f64(u).reshape(C)
+    t_idx = np.arange(T)[:, None]
+    i_idx = np.arange(T)[None, :]
+    dist = (t_idx - 1 - i_idx).astype(np.float64)
+    past = i_idx < t_idx
+    now = i_idx == t_idx
+    gk = np.zeros_like(k)
+    gv = np.zeros_like(k)
+    gw = np.zeros(C)
+    gu = np.zeros(C)
+    for bb in range(B):
+        for c in range(C):
+            kc, vc, gc = k[bb, :, c], v[bb, :, c], g[bb, :, c]
+            X = np.full((T, T), -np.inf)
+            X[past] = (-dist * w[c] + kc[None, :])[past]
+            X[now] = u[c] + kc
+            X = X - X.max(axis=1, keepdims=True)
+            E = np.exp(X)
+            alpha = E / E.sum(axis=1, keepdims=True)
+            y = alpha @ vc
+            ga = gc[:, None] * alpha                       # d L / d v_i, per (t, i)
+            G = ga * (vc[None, :] - y[:, None])           # d L / d X[t,i]
+            gv[bb, :, c] = ga.sum(axis=0)
+            gk[bb, :, c] = G.sum(axis=0)
+            gu[c] += np.trace(G)
+            gw[c] -= (dist * G)[past].sum()
+    return gk, gv, gw, gu

@@ -461,3 +461,71 @@ def test_gated_step_chain_equals_gated_forward():
         o_t, st = oracle.step_gated(st, k[None, :, t], v[None, :, t], r[None, :, t], w[None], u[None])
         outs.append(o_t[0])
     np.testing.assert_allclose(np.stack(outs, axis=1), o_f, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# backward: the gradients of the summed definition, pinned by central finite
+# differences of the stabilised forward (the C recurrence, a separate code
+# path) and by closed forms
+# ---------------------------------------------------------------------------
+
+def _loss(k, v, w, u, g):
+    y, _ = oracle.forward(k, v, w, u)
+    return float((y * g).sum())
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_backward_matches_finite_differences(seed):
+    rng = np.random.default_rng(300 + seed)
+    B, T, C = 2, 9, 3
+    k = rng.normal(0, 2, (B, T, C))
+    v = rng.normal(0, 1, (B, T, C))
+    w = np.exp(rng.uniform(-2, 1, C))
+    u = rng.normal(0, 0.7, C)
+    g = rng.normal(0, 1, (B, T, C))
+    gk, gv, gw, gu = oracle.backward(k, v, w, u, g)
+    h = 1e-6
+    for arr, grad in ((k, gk), (v, gv)):
+        for idx in [(0, 0, 0), (1, 4, 2), (0, 8, 1), (1, 3, 0), (0, 5, 2)]:
+            ap, am = arr.copy(), arr.copy()
+            ap[idx] += h
+            am[idx] -= h
+            args_p = (ap, v, w, u, g) if arr is k else (k, ap, w, u, g)
+            args_m = (am, v, w, u, g) if arr is k else (k, am, w, u, g)
+            fd = (_loss(*args_p) - _loss(*args_m)) / (2 * h)
+            assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd)), (idx, fd, grad[idx])
+    for c in range(C):
+        for arr, grad in ((w, gw), (u, gu)):
+            ap, am = arr.copy(), arr.copy()
+            ap[c] += h
+            am[c] -= h
+            args_p = (k, v, ap, u, g) if arr is w else (k, v, w, ap, g)
+            args_m = (k, v, am, u, g) if arr is w else (k, v, w, am, g)
+            fd = (_loss(*args_p) - _loss(*args_m)) / (2 * h)
+            assert abs(fd - grad[c]) <= 1e-7 * max(1.0, abs(fd)), (c, fd, grad[c])
+
+
+def test_backward_closed_forms():
+    """One token: wkv_0 = v_0 whatever k, u, w are.  Constant values: wkv is
+    that constant, so nothing but v has a gradient, and gv sums to sum(g)
+    (each output's weights sum to one)."""
+    rng = np.random.default_rng(310)
+    k = rng.normal(0, 2, (3, 1, 4))
+    v = rng.normal(0, 1, (3, 1, 4))
+    g = rng.normal(0, 1, (3, 1, 4))
+    w = np.exp(rng.uniform(-2, 1, 4))
+    u = rng.normal(0, 0.5, 4)
+    gk, gv, gw, gu = oracle.backward(k, v, w, u, g)
+    np.testing.assert_array_equal(gk, 0.0)
+    np.testing.assert_allclose(gv, g, rtol=1e-15)
+    np.testing.assert_array_equal(gw, 0.0)
+    np.testing.assert_array_equal(gu, 0.0)
+    B, T, C = 2, 12, 3
+    k = rng.normal(0, 2, (B, T, C))
+    v = np.full((B, T, C), 0.625)
+    g = rng.normal(0, 1, (B, T, C))
+    gk, gv, gw, gu = oracle.backward(k, v, w[:C], u[:C], g)
+    np.testing.assert_allclose(gk, 0.0, atol=1e-14)
+    np.testing.assert_allclose(gw, 0.0, atol=1e-13)
+    np.testing.assert_allclose(gu, 0.0, atol=1e-13)
+    np.testing.assert_allclose(gv.sum(axis=1), g.sum(axis=1), rtol=1e-12)
