@@ -13,7 +13,8 @@ CPU oracle timed on the same workload on the host cores.
 
 Other workloads (--workload): tiny, small_lm, long_ctx (wkv_forward),
 bf16_main_gated (the default workload through wkv_forward_gated, the
-receptance gate fused), decode (wkv_step over [32,256,4096] fp32),
+receptance gate fused), bf16_main_backward (wkv_backward over the default
+workload's shape; a step is its three launches), decode (wkv_step over [32,256,4096] fp32),
 token_shift (bf16, B=16 T=4096 C=2048).
 """
 import argparse
@@ -125,6 +126,76 @@ class ForwardBench:
                 "kind": "oracle",
                 "sample": f"the full workload ({self.units} tokens*channels), one pass, "
                           f"{dt:.2f} s including fp64 conversion"}
+
+
+class BackwardBench:
+    """wkv_backward over the forward workload's shape: k, v and the output
+    gradient gy read, gk, gv written (plus gw, gu [C])."""
+
+    def __init__(self, wl, dev):
+        import numpy as np
+        import torch
+
+        import synth
+        self.wl = wl
+        x = synth.make_forward_inputs(wl)
+        g, g_bits = synth.make_output_grad(wl)
+        self.host = (x, g)
+        if wl.dtype == "bf16":
+            def put(bits):
+                return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+            self.k, self.v, self.g = put(x.k_bits), put(x.v_bits), put(g_bits)
+        else:
+            self.k, self.v, self.g = (torch.from_numpy(a).to(dev) for a in (x.k, x.v, g))
+        self.w = torch.from_numpy(x.w).to(dev)
+        self.u = torch.from_numpy(x.u).to(dev)
+        self.out = (torch.empty_like(self.k), torch.empty_like(self.k),
+                    torch.empty(wl.C, device=dev), torch.empty(wl.C, device=dev))
+        import linear_attention_rnn_forward_amd as wkv
+        self.wkv = wkv
+        self.ws = torch.empty(wkv.backward_workspace_size(wl.B, wl.T, wl.C), dtype=torch.uint8,
+                              device=dev)
+        es = 2 if wl.dtype == "bf16" else 4
+        self.units = wl.B * wl.T * wl.C
+        # k, v, gy read and gk, gv written once; w, u read, gw, gu written
+        self.alg_bytes = 5 * es * self.units + 16 * wl.C
+        self.launches = 3          # forward-in-time pass, reverse pass, batch reduction
+        self.dtype = "f32"
+        self.io = "bf16" if wl.dtype == "bf16" else "f32"
+
+    def step(self):
+        self.wkv.backward(self.k, self.v, self.w, self.u, self.g, out=self.out, workspace=self.ws)
+
+    def check_replay(self):
+        """The graph's last outputs equal an eager launch's bit for bit (the
+        backward has no timing-dependent order)."""
+        import torch
+        saved = [t.clone() for t in self.out]
+        self.step()
+        torch.cuda.synchronize()
+        for a, b in zip(saved, self.out):
+            if not torch.equal(a, b):
+                raise RuntimeError("graph replay gradients differ from the eager launch")
+
+    def config(self):
+        return {"workload": "wkv_backward (gradients of k, v, w, u) over " + self.wl.name,
+                "B": self.wl.B, "T": self.wl.T, "C": self.wl.C, "io_dtype": self.io,
+                "state_dtype": "f32"}
+
+    def cpu_baseline(self):
+        import oracle
+        x, g = self.host
+        c0 = 1234 % self.wl.C
+        sl = (slice(None), slice(None), slice(c0, c0 + 1))
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):      # the NumPy oracle on one core, as reported
+            t0 = time.perf_counter()
+            oracle.backward(x.k[sl], x.v[sl], x.w[c0:c0 + 1], x.u[c0:c0 + 1], g[sl])
+            dt = time.perf_counter() - t0
+        n = self.wl.B * self.wl.T
+        return {"value": n / dt, "unit": "tokens·channels/s", "cores": 1, "kind": "oracle",
+                "sample": f"channel {c0} of every batch row ({n} tokens*channels; the oracle is "
+                          f"O(T^2) per column), {dt:.2f} s"}
 
 
 class DecodeBench:
@@ -292,8 +363,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="bf16_main",
-                    choices=["tiny", "small_lm", "bf16_main", "bf16_main_gated", "long_ctx", "decode",
-                             "token_shift", "hbm_copy"])
+                    choices=["tiny", "small_lm", "bf16_main", "bf16_main_gated", "bf16_main_backward",
+                             "long_ctx", "decode", "token_shift", "hbm_copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch each step from Python instead of replaying a HIP graph of the steps")
@@ -314,6 +385,8 @@ def main():
         bench = ForwardBench(synth.FORWARD_WORKLOADS[args.workload], dev)
     elif args.workload == "bf16_main_gated":
         bench = ForwardBench(synth.BF16_MAIN, dev, gated=True)
+    elif args.workload == "bf16_main_backward":
+        bench = BackwardBench(synth.BF16_MAIN, dev)
     elif args.workload == "decode":
         bench = DecodeBench(dev)
     elif args.workload == "hbm_copy":
@@ -372,6 +445,7 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": traffic,
                 "alg_bytes_per_launch": bench.alg_bytes,
+                "launches_per_step": getattr(bench, "launches", 1),
                 "avg_launch_us": round(avg_kernel_s * 1e6, 2)}
     cpu = None
     if not args.no_cpu_baseline:

@@ -249,6 +249,35 @@ int wkv_session_load(int64_t L, int64_t S, int64_t C, int dtype, int64_t seq,
                      float *a, float *b, float *p, void *const *shift, int n_shift,
                      void *stream);
 
+/*
+ * Gradients of wkv_forward from the empty history (training):
+ * with L = sum over b, t, c of gy * y, where y is wkv_forward's output for
+ * (k, v, w, u) and no initial state, returns dL/dk, dL/dv [B,T,C] and
+ * dL/dw, dL/du [C] (summed over the batch and the tokens).  Each y_t is a
+ * weighted mean of the values ([tm-math] "The WKV operator"), so its partial
+ * derivatives are those of a softmax-weighted mean whose exponents move one
+ * for one with k_i, with u on the current token, and by -(t-1-i) with w.
+ *
+ *   B, C >= 1, T >= 0
+ *   w, u        [C] fp32
+ *   k, v, gy    [B,T,C] dtype       inputs and the gradient of L wrt y
+ *   gk, gv      [B,T,C] dtype       outputs (rounded to dtype)
+ *   gw, gu      [C] fp32            outputs; zero when T = 0
+ *   workspace   device memory of wkv_backward_workspace_size(B, T, C) bytes,
+ *               256-byte aligned (NULL allowed when T = 0); it holds the
+ *               forward pass's per-token log-normaliser and output (fp32)
+ *               and per-column partial sums, and is overwritten
+ * No output may overlap any input, another output or the workspace.
+ * Arithmetic is fp32 with every exponential of a non-positive argument;
+ * gw, gu are reduced over the batch in a fixed order (deterministic).
+ */
+size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C);
+int wkv_backward(int64_t B, int64_t T, int64_t C, int dtype,
+                 const float *w, const float *u,
+                 const void *k, const void *v, const void *gy,
+                 void *gk, void *gv, float *gw, float *gu,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *wkv_status_string(int status);
 
@@ -258,7 +287,7 @@ const char *wkv_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int wkv_abi_version(void);
 
-#define WKV_ABI_VERSION 102
+#define WKV_ABI_VERSION 103
 
 #ifdef __cplusplus
 }

@@ -83,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.wkv_session_save.argtypes = [i64, i64, i64, i32, i64, vp, vp, vp, vp, i32, vp, sz, vp]
         L.wkv_session_load.restype = i32
         L.wkv_session_load.argtypes = [i64, i64, i64, i32, i64, vp, sz, vp, vp, vp, vp, i32, vp]
+        L.wkv_backward_workspace_size.restype = sz
+        L.wkv_backward_workspace_size.argtypes = [i64, i64, i64]
+        L.wkv_backward.restype = i32
+        L.wkv_backward.argtypes = [i64, i64, i64, i32] + [vp] * 9 + [vp, sz, vp]
         L.wkv_token_shift.restype = i32
         L.wkv_token_shift.argtypes = [i64, i64, i64, i32] + [vp] * 9 + [vp]
         L.wkv_status_string.restype = ctypes.c_char_p
@@ -224,6 +228,49 @@ def forward(k, v, w, u, state=None, return_state=False, path="auto", out=None, s
     if return_state or state_out is not None:
         return y, (a_out, b_out, p_out)
     return y
+
+
+def backward_workspace_size(B: int, T: int, C: int) -> int:
+    """Bytes of workspace wkv_backward needs for these sizes."""
+    return int(lib().wkv_backward_workspace_size(B, T, C))
+
+
+def backward(k, v, w, u, gy, out=None, workspace=None):
+    """Gradients of sum(gy * forward(k, v, w, u)) from the empty history.
+
+    k, v, gy: [B,T,C] float32 or bfloat16 (same dtype); w, u: [C] float32.
+    Returns (gk, gv, gw, gu): gk, gv [B,T,C] in the dtype of k, gw, gu [C]
+    float32 (summed over batch and tokens).  out: optional preallocated
+    (gk, gv, gw, gu).
+    """
+    torch = _torch()
+    _need(k, "k")
+    if k.dim() != 3:
+        raise ValueError("k must be [B,T,C]")
+    B, T, C = k.shape
+    dev = k.device
+    dt = _dtype_code(k)
+    _need(v, "v", k.shape, k.dtype, dev)
+    _need(gy, "gy", k.shape, k.dtype, dev)
+    _need(w, "w", (C,), torch.float32, dev)
+    _need(u, "u", (C,), torch.float32, dev)
+    if out is None:
+        out = (torch.empty_like(k), torch.empty_like(k),
+               torch.empty(C, dtype=torch.float32, device=dev),
+               torch.empty(C, dtype=torch.float32, device=dev))
+    gk, gv, gw, gu = out
+    _need(gk, "gk", k.shape, k.dtype, dev)
+    _need(gv, "gv", k.shape, k.dtype, dev)
+    _need(gw, "gw", (C,), torch.float32, dev)
+    _need(gu, "gu", (C,), torch.float32, dev)
+    need = int(lib().wkv_backward_workspace_size(B, T, C))
+    ws = workspace if workspace is not None else _workspace(dev, need)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    with torch.cuda.device(dev):
+        check(lib().wkv_backward(B, T, C, dt, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy),
+                                 _ptr(gk), _ptr(gv), _ptr(gw), _ptr(gu), _ptr(ws), ws_bytes,
+                                 _stream(dev)))
+    return gk, gv, gw, gu
 
 
 def step(state, k, v, w, u, out=None, state_out=None, inplace=False, r=None):

@@ -353,6 +353,66 @@ int wkv_step_gated(int64_t L, int64_t S, int64_t C, int dtype, const float* w, c
                      stream, true);
 }
 
+size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C) {
+    if (B < 1 || C < 1 || T < 0) return 0;
+    int64_t n = 0;
+    if (!mul3(B, T, C, &n) || !mul3(n, 8, 1, &n)) return 0;
+    return wkv::backward_workspace_bytes(B, T, C);
+}
+
+int wkv_backward(int64_t B, int64_t T, int64_t C, int dtype, const float* w, const float* u,
+                 const void* k, const void* v, const void* gy, void* gk, void* gv, float* gw,
+                 float* gu, void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != WKV_F32 && dtype != WKV_BF16) return fail(WKV_ERR_DTYPE, "unknown dtype %d", dtype);
+    if (B < 1 || C < 1 || T < 0)
+        return fail(WKV_ERR_SHAPE, "need B >= 1, T >= 0, C >= 1 (got B=%lld T=%lld C=%lld)",
+                    (long long)B, (long long)T, (long long)C);
+    int64_t n = 0;
+    if (!mul3(B, T, C, &n) || !mul3(n, 8, 1, &n) || !mul3(B, C, 8, &n))
+        return fail(WKV_ERR_SHAPE, "B*T*C too large");
+    n = B * T * C;
+    if (!w || !u || !gw || !gu) return fail(WKV_ERR_NULL, "w, u, gw and gu are required");
+    if (T > 0 && (!k || !v || !gy || !gk || !gv))
+        return fail(WKV_ERR_NULL, "k, v, gy, gk and gv are required when T > 0");
+    if (double(B) * double(C) / 256.0 > 2147483647.0)
+        return fail(WKV_ERR_SHAPE, "too many columns for one launch");
+    const int64_t io = n * int64_t(esize(dtype));
+    const Range r_in[] = {rng("k", k, io), rng("v", v, io), rng("gy", gy, io), rng("w", w, C * 4),
+                          rng("u", u, C * 4)};
+    const size_t need = T > 0 ? wkv::backward_workspace_bytes(B, T, C) : 0;
+    const Range r_out[] = {rng("gk", gk, io), rng("gv", gv, io), rng("gw", gw, C * 4),
+                           rng("gu", gu, C * 4), rng("workspace", T > 0 ? workspace : nullptr, int64_t(need))};
+    for (int i = 0; i < 5; i++) {
+        for (const Range& r : r_in)
+            if (overlap(r_out[i], r)) return fail(WKV_ERR_ALIAS, "%s overlaps %s", r_out[i].name, r.name);
+        for (int j = 0; j < i; j++)
+            if (overlap(r_out[i], r_out[j]))
+                return fail(WKV_ERR_ALIAS, "%s overlaps %s", r_out[i].name, r_out[j].name);
+    }
+    if (T > 0) {
+        if (workspace == nullptr || workspace_bytes < need)
+            return fail(WKV_ERR_WORKSPACE, "backward needs %zu workspace bytes, got %zu", need,
+                        workspace ? workspace_bytes : size_t(0));
+        if (!aligned(workspace, 256)) return fail(WKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    }
+    wkv::BackwardProblem pr;
+    pr.B = B;
+    pr.T = T;
+    pr.C = C;
+    pr.dtype = dtype;
+    pr.w = w;
+    pr.u = u;
+    pr.k = k;
+    pr.v = v;
+    pr.gy = gy;
+    pr.gk = gk;
+    pr.gv = gv;
+    pr.gw = gw;
+    pr.gu = gu;
+    hipError_t e = wkv::launch_backward(pr, workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "backward launch");
+}
+
 int wkv_token_shift(int64_t B, int64_t T, int64_t C, int dtype, const void* x, const void* x_prev,
                     const float* mu_r, const float* mu_k, const float* mu_v, void* xr, void* xk,
                     void* xv, void* x_last, void* stream) {

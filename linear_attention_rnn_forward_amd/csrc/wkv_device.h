@@ -83,6 +83,12 @@ __device__ __forceinline__ float max_num(float a, float b) {
     return r;
 }
 
+__device__ __forceinline__ float min_num(float a, float b) {
+    float r;
+    asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // Per-channel constants of the forward kernels.
 struct Chan {
     float w;     // decay rate

@@ -56,6 +56,23 @@ struct StepProblem {
 };
 hipError_t launch_step(const StepProblem& pr, hipStream_t stream);
 
+// Gradients of sum(gy * wkv) for wkv_forward from the empty history.
+struct BackwardProblem {
+    int64_t B, T, C;
+    int dtype;
+    const float *w, *u;
+    const void *k, *v, *gy;        // [B,T,C] dtype
+    void *gk, *gv;                 // [B,T,C] dtype
+    float *gw, *gu;                // [C]
+    // workspace sections (set by launch_backward)
+    float* z = nullptr;            // [B,T,C] log of each output's weight sum
+    float* ys = nullptr;           // [B,T,C] the outputs, fp32
+    float* part_w = nullptr;       // [B,C] per-column gw
+    float* part_u = nullptr;       // [B,C] per-column gu
+};
+size_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C);
+hipError_t launch_backward(BackwardProblem pr, void* workspace, hipStream_t stream);
+
 struct ShiftProblem {
     int64_t B, T, C;
     int dtype;

@@ -285,9 +285,14 @@ def step_gated(state, k, v, r, w, u):
     return gate(y, r), st
 
 
-def backward(k, v, w, u, gy):
+def backward(k, v, w, u, gy, magnitude=False):
     """Gradients of L = sum(gy * wkv) for wkv over [B,T,C] from the empty
     history: returns (gk, gv [B,T,C], gw, gu [C]) in fp64.
+
+    magnitude=True returns instead the same sums with every term made
+    non-negative -- gy_t alpha[t,i] by its absolute value and (v_i - wkv_t)
+    by |v_i| + |wkv_t| -- the scale against which the rounding error of any
+    evaluation order of those sums is measured.
 
     For one column, wkv_t = sum_i alpha[t,i] v_i with alpha row t the softmax
     of the exponents X[t,i] = -(t-1-i) w + k_i (i < t) and u + k_t (i = t)
@@ -322,9 +327,13 @@ def backward(k, v, w, u, gy):
             alpha = E / E.sum(axis=1, keepdims=True)
             y = alpha @ vc
             ga = gc[:, None] * alpha                       # d L / d v_i, per (t, i)
-            G = ga * (vc[None, :] - y[:, None])           # d L / d X[t,i]
+            if magnitude:
+                ga = np.abs(ga)
+                G = ga * (np.abs(vc)[None, :] + np.abs(y)[:, None])
+            else:
+                G = ga * (vc[None, :] - y[:, None])       # d L / d X[t,i]
             gv[bb, :, c] = ga.sum(axis=0)
             gk[bb, :, c] = G.sum(axis=0)
             gu[c] += np.trace(G)
-            gw[c] -= (dist * G)[past].sum()
+            gw[c] += (1.0 if magnitude else -1.0) * (dist * G)[past].sum()
     return gk, gv, gw, gu

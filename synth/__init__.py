@@ -168,6 +168,22 @@ def make_receptance(wl: ForwardWorkload):
     return r, None
 
 
+# The output gradient gy of a backward workload: gy ~ N(0, 1) from its own
+# generator, so k, v, w, u are those of the forward workload of the same name.
+OUTPUT_GRAD_SEED_OFFSET = 2000
+
+
+def make_output_grad(wl: ForwardWorkload):
+    """gy [B,T,C] for `wl`: fp32 values as stored, and the uint16 bits when
+    the storage type is bf16 (else None)."""
+    rng = np.random.default_rng(wl.seed + OUTPUT_GRAD_SEED_OFFSET)
+    g = rng.standard_normal(size=(wl.B, wl.T, wl.C), dtype=np.float32)
+    if wl.dtype == "bf16":
+        bits = f32_to_bf16_bits(g)
+        return bf16_bits_to_f32(bits), bits
+    return g, None
+
+
 def decode_params(wl: DecodeWorkload):
     """Per-layer decay and bonus [L,C] for the decode workload."""
     rng = np.random.default_rng(wl.seed)

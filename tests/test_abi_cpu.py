@@ -31,13 +31,14 @@ def test_every_declared_symbol_is_exported(header, libpath):
 def test_header_lists_the_boundary_calls():
     names = _declared("wkv.h")
     for n in ("wkv_forward", "wkv_step", "wkv_token_shift", "wkv_forward_workspace_size",
-              "wkv_forward_gated", "wkv_step_gated", "wkv_status_string", "wkv_last_error"):
+              "wkv_forward_gated", "wkv_step_gated", "wkv_backward", "wkv_backward_workspace_size",
+              "wkv_status_string", "wkv_last_error"):
         assert n in names
 
 
 def test_abi_version_and_status_strings():
     L = wkv.lib()
-    assert L.wkv_abi_version() == 102
+    assert L.wkv_abi_version() == 103
     for code in range(0, -9, -1):
         assert L.wkv_status_string(code).decode()
     assert L.wkv_status_string(-100).decode() == "unknown status"
@@ -201,3 +202,42 @@ def test_session_save_checks_arguments():
     assert L.wkv_session_save(2, 3, 8, 0, 0, None, P(2 * G), P(3 * G), None, 0, buf, 10, None) == -1
     assert L.wkv_session_save(2, 3, 8, 0, 5, P(G), P(2 * G), P(3 * G), None, 0, buf, 10, None) == -8
     assert L.wkv_session_save(2, 3, 8, 0, 0, P(G), P(2 * G), P(3 * G), None, 1, buf, 10, None) == -1
+
+
+def test_backward_workspace_size():
+    """Per-token log-normaliser and output (fp32, 8 bytes a token-channel)
+    plus per-column gw, gu partials (8 bytes a column), each section rounded
+    up to 256 bytes."""
+    L = wkv.lib()
+    assert L.wkv_backward_workspace_size(2, 3, 64) == 2 * 1536 + 2 * 512
+    assert L.wkv_backward_workspace_size(16, 4096, 2048) == 8 * 16 * 4096 * 2048 + 8 * 16 * 2048
+    assert L.wkv_backward_workspace_size(1, 1, 1) == 4 * 256
+    assert L.wkv_backward_workspace_size(0, 8, 8) == 0
+    assert L.wkv_backward_workspace_size(1 << 40, 1 << 40, 8) == 0
+
+
+def test_backward_rejects_bad_arguments():
+    L = wkv.lib()
+    B, T, C = 2, 3, 64
+    need = L.wkv_backward_workspace_size(B, T, C)
+
+    def call(dtype=0, B=B, T=T, C=C, ws=20 * G, ws_bytes=need, **over):
+        a = dict(w=1, u=2, k=3, v=4, gy=5, gk=6, gv=7, gw=8, gu=9)
+        a.update(over)
+        ptr = {n: (P(int(x * G)) if x is not None else None) for n, x in a.items()}
+        return L.wkv_backward(B, T, C, dtype, ptr["w"], ptr["u"], ptr["k"], ptr["v"], ptr["gy"],
+                              ptr["gk"], ptr["gv"], ptr["gw"], ptr["gu"], P(ws) if ws else None,
+                              ws_bytes, None)
+
+    assert call(dtype=5) == -3
+    assert call(B=0) == -2 and call(C=0) == -2 and call(T=-1) == -2
+    assert call(B=1 << 40, T=1 << 40) == -2
+    assert call(gw=None) == -1 and call(u=None) == -1
+    assert call(gy=None) == -1 and call(gk=None) == -1
+    assert call(gk=4) == -5                        # gk on v
+    assert b"gk overlaps v" in L.wkv_last_error()
+    assert call(gu=8) == -5                        # gu on gw
+    assert call(ws=None) == -4
+    assert call(ws_bytes=need - 1) == -4
+    assert call(ws=20 * G + 16) == -4              # misaligned
+    assert call(ws=6 * G) == -5                    # workspace on gk

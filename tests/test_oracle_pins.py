@@ -529,3 +529,34 @@ def test_backward_closed_forms():
     np.testing.assert_allclose(gw, 0.0, atol=1e-13)
     np.testing.assert_allclose(gu, 0.0, atol=1e-13)
     np.testing.assert_allclose(gv.sum(axis=1), g.sum(axis=1), rtol=1e-12)
+
+
+def test_backward_magnitude_bounds_and_closed_forms():
+    """The term-magnitude sums bound the signed gradients; with gy >= 0 the
+    value magnitudes are the signed gv; with constant positive values c
+    (wkv = c everywhere) the key magnitude is 2 c gv; one token: gy_0 * 2|v_0|."""
+    rng = np.random.default_rng(320)
+    B, T, C = 2, 11, 3
+    k = rng.normal(0, 2, (B, T, C))
+    v = rng.normal(0, 1, (B, T, C))
+    w = np.exp(rng.uniform(-2, 1, C))
+    u = rng.normal(0, 0.7, C)
+    g = rng.normal(0, 1, (B, T, C))
+    signed = oracle.backward(k, v, w, u, g)
+    mag = oracle.backward(k, v, w, u, g, magnitude=True)
+    for s_, m_ in zip(signed, mag):
+        assert np.all(m_ >= np.abs(s_) - 1e-13)
+    assert np.all(mag[2] > 0) and np.all(mag[3] > 0)
+    gpos = np.abs(g)
+    np.testing.assert_allclose(oracle.backward(k, v, w, u, gpos, magnitude=True)[1],
+                               oracle.backward(k, v, w, u, gpos)[1], rtol=1e-13)
+    vc = np.full((B, T, C), 0.625)
+    gv_c = oracle.backward(k, vc, w, u, gpos)[1]
+    np.testing.assert_allclose(oracle.backward(k, vc, w, u, gpos, magnitude=True)[0],
+                               2 * 0.625 * gv_c, rtol=1e-13)
+    k1, v1, g1 = k[:, :1], v[:, :1], g[:, :1]
+    mk, mv, mw, mu = oracle.backward(k1, v1, w, u, g1, magnitude=True)
+    np.testing.assert_allclose(mk, np.abs(g1) * 2 * np.abs(v1), rtol=1e-15)
+    np.testing.assert_allclose(mv, np.abs(g1), rtol=1e-15)
+    np.testing.assert_array_equal(mw, 0.0)
+    np.testing.assert_allclose(mu, (np.abs(g1) * 2 * np.abs(v1)).sum(axis=(0, 1)), rtol=1e-14)
