@@ -258,15 +258,16 @@ int wkv_session_load(int64_t L, int64_t S, int64_t C, int dtype, int64_t seq,
  * derivatives are those of a softmax-weighted mean whose exponents move one
  * for one with k_i, with u on the current token, and by -(t-1-i) with w.
  *
- *   B, C >= 1, T >= 0
+ *   B, C >= 1, T >= 0, C * 68 < 2^32
  *   w, u        [C] fp32
  *   k, v, gy    [B,T,C] dtype       inputs and the gradient of L wrt y
  *   gk, gv      [B,T,C] dtype       outputs (rounded to dtype)
  *   gw, gu      [C] fp32            outputs; zero when T = 0
  *   workspace   device memory of wkv_backward_workspace_size(B, T, C) bytes,
  *               256-byte aligned (NULL allowed when T = 0); it holds the
- *               forward pass's per-token log-normaliser and output (fp32)
- *               and per-column partial sums, and is overwritten
+ *               forward state before every 16-token sub-chunk (6 fp32 per
+ *               channel, 1.5 bytes per token-channel) and per-column partial
+ *               sums, and is overwritten
  * No output may overlap any input, another output or the workspace.
  * Arithmetic is fp32 with every exponential of a non-positive argument;
  * gw, gu are reduced over the batch in a fixed order (deterministic).

@@ -374,8 +374,10 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, int dtype, const float* w, con
     if (!w || !u || !gw || !gu) return fail(WKV_ERR_NULL, "w, u, gw and gu are required");
     if (T > 0 && (!k || !v || !gy || !gk || !gv))
         return fail(WKV_ERR_NULL, "k, v, gy, gk and gv are required when T > 0");
-    if (double(B) * double(C) / 256.0 > 2147483647.0)
-        return fail(WKV_ERR_SHAPE, "too many columns for one launch");
+    if (double(B) * double((C + 63) / 64) > 2147483647.0)
+        return fail(WKV_ERR_SHAPE, "too many column groups for one launch");
+    if (double(C) * 4.0 * 17.0 > 4294967295.0)
+        return fail(WKV_ERR_SHAPE, "C too large for 32-bit offsets within a sub-chunk");
     const int64_t io = n * int64_t(esize(dtype));
     const Range r_in[] = {rng("k", k, io), rng("v", v, io), rng("gy", gy, io), rng("w", w, C * 4),
                           rng("u", u, C * 4)};
@@ -409,6 +411,8 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, int dtype, const float* w, con
     pr.gv = gv;
     pr.gw = gw;
     pr.gu = gu;
+    pr.vec = wkv::backward_vec(C, dtype, aligned(k, 4) && aligned(v, 4) && aligned(gy, 4) &&
+                                             aligned(gk, 4) && aligned(gv, 4));
     hipError_t e = wkv::launch_backward(pr, workspace, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ok() : hip_fail(e, "backward launch");
 }

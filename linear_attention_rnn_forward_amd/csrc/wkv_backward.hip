@@ -10,174 +10,433 @@
 //   gw   = -sum_t gy_t (A'_t - y_t B'_t) / D_t
 //
 // where P_i = sum_{t>i} e^{-(t-1-i)w} gy_t / D_t and Q_i the same with
-// gy_t y_t (a scan backwards in time: P_{i-1} = gy_i / D_i + e^{-w} P_i), and
-// A'_t, B'_t the history sums weighted by their age t-1-i (a scan forwards:
-// A'_{t+1} = e^{-w} (A'_t + A_t)).  gw and gu are summed over B and T.
+// gy_t y_t (a scan backwards in time: P_{i-1} = gy_i / D_i + e^{-w} P_i),
+// A_t, B_t the history sums of the forward recurrence and A'_t, B'_t the
+// same weighted by age t-1-i (a scan forwards: A'_{t+1} = e^{-w} (A'_t +
+// A_t)).  gw and gu are summed over B and T.
 //
-// Two passes per column (b, c), one lane per column:
-//   1. forward in t: the stabilised state (a, b, a', b') with exponent p,
-//      kept as an anchor and a token count (p = A - m w, one rounding per
-//      token, none accumulated); writes z_t = log D_t and y_t (fp32) to the
-//      workspace and accumulates the column's gw, gu terms;
-//   2. backward in t: (P, Q) scaled by e^{pi}, pi kept the same way as an
-//      anchor and a count; writes gk, gv.
-// Every exponential has a non-positive argument: p <= z_t, k_i + pi <= 0
-// (D_t contains token i's own weight), u + k_t <= z_t.
-// A final kernel sums the per-column gw, gu over the batch in a fixed order.
+// Execution (one workgroup of NWV waves per column group = 64 lanes x VEC
+// channels of one batch row; the tokens cut into sub-chunks of kBwdTokens,
+// handed to the waves round-robin as on the forward's chained path):
+//
+//   phase F  forward in time.  Each wave loads k, v of its sub-chunk and
+//            folds them into a partial state (a, b, a', b') from the empty
+//            history; the carry (the state before the sub-chunk) arrives
+//            through LDS, carry (+) partial goes on to the next sub-chunk, and
+//            the carry is stored to the workspace as that sub-chunk's
+//            checkpoint.
+//   phase R  backward in time, sub-chunks from the last.  Each wave loads
+//            k, v, gy and its checkpoint, re-runs the forward recurrence over
+//            the sub-chunk (outputs y_t, 1/D_t, the gu and gw terms) and
+//            folds the sub-chunk's (P, Q) contribution into a partial; the
+//            (P, Q) carry from the later sub-chunk arrives through LDS,
+//            carry (+) partial goes on to the earlier one, and the tokens are
+//            walked backwards from the carry to write gk, gv.
+//
+// Stabilisation: every scale is an exponent in anchor form, anchor - count w,
+// and every weight an exponential of a non-positive difference formed
+// anchor-relative: (anchor - key) is exact when the two are close, and the
+// count w term is added by one fma at the difference's own magnitude, so no
+// rounding at the keys' magnitude accumulates through the rescalings.  The
+// (P, Q) scan is held against e^{-q_t}, q_t the larger of the two read-out
+// exponents (the history's and u + k_t), with the bounded factor 1/delta_t
+// (delta_t = D_t e^{-q_t} in [1, tokens]) folded into its terms.
+//
+// gw, gu are reduced per column over the waves in LDS (fixed order), stored
+// per (b, c), and summed over the batch by a last kernel in batch order: the
+// result does not depend on timing.
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
 namespace wkv {
 namespace {
 
-constexpr int kBwdTokens = 16;  // tokens loaded ahead per lane
+constexpr int kBwdTokens = 16;  // tokens per sub-chunk
+constexpr int kCkptFields = 6;  // a, b, a', b', anchor, count
 
-__device__ __forceinline__ float expf_(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
-__device__ __forceinline__ float logf_(float x) { return __builtin_amdgcn_logf(x) * 0.69314718055994531f; }
+__device__ __forceinline__ int bwd_wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int bwd_lane_id() { return threadIdx.x & 63; }
 
-template <int DT>
-__global__ __launch_bounds__(256) void backward_forward_pass(BackwardProblem pr) {
-    using IO = Io<DT, 1>;
+// Forward state in anchor form: exponent p = A - m w; a, b the history sums
+// and ap, bp the age-weighted ones, all scaled by e^{-p}.
+struct FState {
+    float a, b, ap, bp, A, m;
+    __device__ __forceinline__ void set_empty() {
+        a = b = ap = bp = 0.0f;
+        A = kEmptyP;
+        m = 0.0f;
+    }
+};
+
+// Fold token (k, v) into s: the history decays by e^{-w}, the age-weighted
+// sums gain the history, the new key enters with weight e^{k}.
+__device__ __forceinline__ void fold_forward(FState& s, float k, float v, float w) {
+    const float e = __builtin_fmaf(-(s.m + 1.0f), w, s.A - k);  // (p - w) - k
+    const float x = exp_neg_abs(e);
+    const bool reset = e < 0.0f;                                  // the new key is the maximum
+    const float al = reset ? x : 1.0f;
+    const float be = reset ? 1.0f : x;
+    s.ap = al * (s.ap + s.a);
+    s.bp = al * (s.bp + s.b);
+    s.a = __builtin_fmaf(al, s.a, be * v);
+    s.b = __builtin_fmaf(al, s.b, be);
+    s.A = reset ? k : s.A;
+    s.m = reset ? 0.0f : s.m + 1.0f;
+}
+
+// X <- X (+) G, G the state of the n tokens after X from the empty history.
+// Over n tokens X's terms gain n in age: a' -> e^{-n w} (a' + n a).
+__device__ __forceinline__ void combine_forward(FState& x, const FState& g, float n, float w) {
+    const float d = __builtin_fmaf(-(x.m + n - g.m), w, x.A - g.A);  // X's exponent - G's
+    const float e = exp_neg_abs(d);
+    const bool keep = d >= 0.0f;
+    const float ax = keep ? 1.0f : e;
+    const float ag = keep ? e : 1.0f;
+    const float apx = __builtin_fmaf(n, x.a, x.ap);
+    const float bpx = __builtin_fmaf(n, x.b, x.bp);
+    x.a = __builtin_fmaf(ax, x.a, ag * g.a);
+    x.b = __builtin_fmaf(ax, x.b, ag * g.b);
+    x.ap = __builtin_fmaf(ax, apx, ag * g.ap);
+    x.bp = __builtin_fmaf(ax, bpx, ag * g.bp);
+    x.A = keep ? x.A : g.A;
+    x.m = keep ? x.m + n : g.m;
+}
+
+// Reverse accumulator (P, Q) in anchor form: exponent Pi - n w.
+struct RState {
+    float P, Q, Pi, n;
+    __device__ __forceinline__ void set_empty() {
+        P = Q = 0.0f;
+        Pi = kEmptyP;
+        n = 0.0f;
+    }
+};
+
+// X <- X (+) G for the reverse scan: X holds the tokens after a span of n
+// tokens (its exponent gains -n w at the span's start), G the span's own.
+__device__ __forceinline__ void combine_reverse(RState& x, const RState& g, float n, float w) {
+    const float d = __builtin_fmaf(-(x.n + n - g.n), w, x.Pi - g.Pi);
+    const float e = exp_neg_abs(d);
+    const bool keep = d >= 0.0f;
+    const float ax = keep ? 1.0f : e;
+    const float ag = keep ? e : 1.0f;
+    x.P = __builtin_fmaf(ax, x.P, ag * g.P);
+    x.Q = __builtin_fmaf(ax, x.Q, ag * g.Q);
+    x.Pi = keep ? x.Pi : g.Pi;
+    x.n = keep ? x.n + n : g.n;
+}
+
+// Per-token values the backward walk needs, per channel.
+struct TokenOut {
+    float y;   // the output wkv_t
+    float q;   // the read-out's larger exponent
+    float gr;  // gy_t / delta_t  (gy_t / D_t = gr e^{-q})
+    float ed;  // gy_t e^{u+k_t} / D_t
+};
+
+// The forward read-out of one token from state s, its gw, gu terms, its
+// term of the sub-chunk's (P, Q) partial (token index i in the sub-chunk,
+// exponent -q - i w at the sub-chunk start), then the fold-in.
+__device__ __forceinline__ TokenOut forward_detail(FState& s, RState& rg, float k, float v, float g,
+                                                   float w, float u, float fi, float& gw, float& gu) {
+    TokenOut o;
+    const float ak = s.A - k;
+    const float d = __builtin_fmaf(-s.m, w, ak - u);  // p - (u + k)
+    const float x = exp_neg_abs(d);
+    const bool keep = d >= 0.0f;
+    const float al = keep ? 1.0f : x;  // e^{p - q}
+    const float be = keep ? x : 1.0f;  // e^{u + k - q}
+    const float del = __builtin_fmaf(al, s.b, be);
+    const float rd = fast_rcp(del);
+    o.y = __builtin_fmaf(al, s.a, be * v) * rd;
+    o.gr = g * rd;
+    o.ed = o.gr * be;
+    // u + k is rounded as in d's reference point, so q + log(delta) = log D
+    o.q = keep ? __builtin_fmaf(-s.m, w, s.A) : u + k;
+    gu = __builtin_fmaf(o.ed, v - o.y, gu);
+    gw = __builtin_fmaf(-(o.gr * al), __builtin_fmaf(-o.y, s.bp, s.ap), gw);
+    // (P, Q) partial of the sub-chunk, in forward order
+    {
+        const float dr = __builtin_fmaf(-(fi - rg.n), w, -(o.q + rg.Pi));  // new term - running
+        const float xr = exp_neg_abs(dr);
+        const bool nm = dr > 0.0f;
+        const float ar = nm ? xr : 1.0f;
+        const float br = nm ? 1.0f : xr;
+        const float t = br * o.gr;
+        rg.P = __builtin_fmaf(ar, rg.P, t);
+        rg.Q = __builtin_fmaf(ar, rg.Q, t * o.y);
+        rg.Pi = nm ? -o.q : rg.Pi;
+        rg.n = nm ? fi : rg.n;
+    }
+    fold_forward(s, k, v, w);
+    return o;
+}
+
+// One token of the backward walk: gk, gv from the running (P, Q) of the
+// later tokens, then fold this token's term in (skipped for a sub-chunk's
+// first token, whose successor is the next sub-chunk's carry).
+__device__ __forceinline__ void reverse_detail(RState& r, const TokenOut& o, float k, float v, float w,
+                                               bool fold, float& gk, float& gv) {
+    const float eh = __builtin_amdgcn_exp2f(__builtin_fmaf(-r.n, w, k + r.Pi) * kLog2e);
+    gv = __builtin_fmaf(eh, r.P, o.ed);
+    gk = __builtin_fmaf(eh, __builtin_fmaf(v, r.P, -r.Q), o.ed * (v - o.y));
+    if (fold) {
+        const float e = __builtin_fmaf(-(r.n + 1.0f), w, r.Pi + o.q);  // (pi - w) - (-q)
+        const float x = exp_neg_abs(e);
+        const bool reset = e < 0.0f;
+        const float al = reset ? x : 1.0f;
+        const float be = reset ? 1.0f : x;
+        const float t = be * o.gr;
+        r.P = __builtin_fmaf(al, r.P, t);
+        r.Q = __builtin_fmaf(al, r.Q, t * o.y);
+        r.Pi = reset ? -o.q : r.Pi;
+        r.n = reset ? 0.0f : r.n + 1.0f;
+    }
+}
+
+template <int DT, int VEC, int NWV>
+__global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProblem pr, int64_t gpr,
+                                                                    int64_t nsub) {
+    using IO = Io<DT, VEC>;
     using Raw = typename IO::Raw;
-    const int64_t col = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (col >= pr.B * pr.C) return;
-    const int64_t bb = col / pr.C;
-    const int64_t c = col - bb * pr.C;
-    const int64_t T = pr.T, C = pr.C;
-    const float w = pr.w[c], u = pr.u[c];
-    const Raw* kp = static_cast<const Raw*>(pr.k) + bb * T * C + c;
-    const Raw* vp = static_cast<const Raw*>(pr.v) + bb * T * C + c;
-    const Raw* gp = static_cast<const Raw*>(pr.gy) + bb * T * C + c;
-    float* zp = pr.z + bb * T * C + c;
-    float* yp = pr.ys + bb * T * C + c;
+    constexpr int L = kBwdTokens;
+    constexpr int CG = 64 * VEC;
+    __shared__ float s_fc[kCkptFields][CG];  // forward carry before sub-chunk s_fseq
+    __shared__ float s_rc[4][CG];            // reverse carry after sub-chunk nsub-1-s_rseq
+    __shared__ float s_red[2][NWV][CG];      // per-wave gw, gu
+    __shared__ int s_fseq, s_rseq;
 
-    float A = kEmptyP, m = 0.0f;              // history exponent p = A - m w
-    float a = 0.0f, b = 0.0f, ap = 0.0f, bp = 0.0f;
-    float gw = 0.0f, gu = 0.0f;
-    for (int64_t t0 = 0; t0 < T; t0 += kBwdTokens) {
-        const int n = T - t0 < kBwdTokens ? int(T - t0) : kBwdTokens;
-        float kf[kBwdTokens], vf[kBwdTokens], gf[kBwdTokens];
+    const int wave = bwd_wave_id();
+    const int lane = bwd_lane_id();
+    const int64_t grp = blockIdx.x;
+    const int64_t bb = grp / gpr;
+    const int64_t c0 = (grp - bb * gpr) * CG;
+    const int64_t c = c0 + int64_t(lane) * VEC;
+    const bool active = c < pr.C;
+    const int64_t T = pr.T, C = pr.C;
+
+    float w[VEC], u[VEC];
 #pragma unroll
-        for (int i = 0; i < kBwdTokens; i++) {
+    for (int q = 0; q < VEC; q++) {
+        w[q] = active ? pr.w[c + q] : 1.0f;
+        u[q] = active ? pr.u[c + q] : 0.0f;
+    }
+    if (wave == 0) {
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            FState e;
+            e.set_empty();
+            s_fc[0][lane * VEC + q] = e.a;
+            s_fc[1][lane * VEC + q] = e.b;
+            s_fc[2][lane * VEC + q] = e.ap;
+            s_fc[3][lane * VEC + q] = e.bp;
+            s_fc[4][lane * VEC + q] = e.A;
+            s_fc[5][lane * VEC + q] = e.m;
+            RState r;
+            r.set_empty();
+            s_rc[0][lane * VEC + q] = r.P;
+            s_rc[1][lane * VEC + q] = r.Q;
+            s_rc[2][lane * VEC + q] = r.Pi;
+            s_rc[3][lane * VEC + q] = r.n;
+        }
+        if (lane == 0) {
+            s_fseq = 0;
+            s_rseq = 0;
+        }
+    }
+    __syncthreads();
+
+    constexpr int64_t es = sizeof(Raw) / VEC;
+    const uint32_t row_bytes = uint32_t(C * es);
+    const uint32_t voff = active ? uint32_t(lane) * uint32_t(sizeof(Raw)) : 0u;
+    uint32_t toff[L];
+#pragma unroll
+    for (int i = 0; i < L; i++) toff[i] = voff + uint32_t(i) * row_bytes;
+    const int64_t gbase = (bb * T * C + c0) * es;
+    // checkpoints: [B][nsub][field][C] fp32
+    float* ckpt = pr.ckpt + bb * nsub * kCkptFields * C + c;
+
+    // ---------------- phase F: forward carries and checkpoints ----------------
+    for (int64_t sc = wave; sc < nsub; sc += NWV) {
+        const int64_t t0 = sc * L;
+        const int n = T - t0 >= L ? L : int(T - t0);
+        const int64_t base = gbase + t0 * int64_t(row_bytes);
+        const rsrc_t kr_ = make_rsrc(static_cast<const char*>(pr.k) + base);
+        const rsrc_t vr_ = make_rsrc(static_cast<const char*>(pr.v) + base);
+        Raw kr[L], vr[L];
+#pragma unroll
+        for (int i = 0; i < L; i++) {
             if (i < n) {
-                float x[1];
-                IO::unpack(load_stream(kp + (t0 + i) * C), x); kf[i] = x[0];
-                IO::unpack(load_stream(vp + (t0 + i) * C), x); vf[i] = x[0];
-                IO::unpack(load_stream(gp + (t0 + i) * C), x); gf[i] = x[0];
+                kr[i] = Buf<Raw>::template load<kStreamLoad>(kr_, toff[i], 0);
+                vr[i] = Buf<Raw>::template load<kStreamLoad>(vr_, toff[i], 0);
             }
         }
+        FState g[VEC];
 #pragma unroll
-        for (int i = 0; i < kBwdTokens; i++) {
+        for (int q = 0; q < VEC; q++) g[q].set_empty();
+#pragma unroll
+        for (int i = 0; i < L; i++) {
             if (i < n) {
-                const float k = kf[i], v = vf[i], g = gf[i];
-                // exponent differences are formed anchor-relative: A - k is
-                // exact when the two are close (Sterbenz) and the m w term is
-                // added by one fma at the difference's own magnitude, so the
-                // per-token rescalings carry no rounding of |k| ~ 100
-                const float ak = A - k;
-                const float d = __builtin_fmaf(-m, w, ak - u);       // p - (u + k)
-                const float al = expf_(min_num(d, 0.0f));             // e^{p - q}
-                const float be = expf_(min_num(-d, 0.0f));            // e^{u + k - q}
-                const float del = __builtin_fmaf(al, b, be);
-                const float y = __builtin_fmaf(al, a, be * v) * fast_rcp(del);
-                const float ld = logf_(del);
-                const float q = d >= 0.0f ? __builtin_fmaf(-m, w, A) : u + k;
-                zp[(t0 + i) * C] = q + ld;
-                yp[(t0 + i) * C] = y;
-                // this token's terms of gu and gw (1/D_t = e^{-z_t})
-                gu = __builtin_fmaf(g * expf_(min_num(-d, 0.0f) - ld), v - y, gu);
-                gw = __builtin_fmaf(-g * expf_(min_num(d, 0.0f) - ld), __builtin_fmaf(-y, bp, ap), gw);
-                // fold token t in: the history decays by e^{-w}, the age-weighted
-                // sums gain the history, the new key enters with weight e^{k};
-                // e = (p - w) - k
-                const float e = __builtin_fmaf(-(m + 1.0f), w, ak);
-                if (e < 0.0f) {
-                    const float s = expf_(e);
-                    ap = s * (ap + a);
-                    bp = s * (bp + b);
-                    a = __builtin_fmaf(s, a, v);
-                    b = __builtin_fmaf(s, b, 1.0f);
-                    A = k;
-                    m = 0.0f;
-                } else {
-                    const float s = expf_(-e);
-                    ap += a;
-                    bp += b;
-                    a = __builtin_fmaf(s, v, a);
-                    b += s;
-                    m += 1.0f;
+                float kf[VEC], vf[VEC];
+                IO::unpack(kr[i], kf);
+                IO::unpack(vr[i], vf);
+#pragma unroll
+                for (int q = 0; q < VEC; q++) fold_forward(g[q], kf[q], vf[q], w[q]);
+            }
+        }
+        while (__hip_atomic_load(&s_fseq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != int(sc))
+            __builtin_amdgcn_s_sleep(1);
+        FState x[VEC];
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            x[q].a = s_fc[0][lane * VEC + q];
+            x[q].b = s_fc[1][lane * VEC + q];
+            x[q].ap = s_fc[2][lane * VEC + q];
+            x[q].bp = s_fc[3][lane * VEC + q];
+            x[q].A = s_fc[4][lane * VEC + q];
+            x[q].m = s_fc[5][lane * VEC + q];
+        }
+        if (sc + 1 < nsub) {
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                FState nx = x[q];
+                combine_forward(nx, g[q], float(n), w[q]);
+                s_fc[0][lane * VEC + q] = nx.a;
+                s_fc[1][lane * VEC + q] = nx.b;
+                s_fc[2][lane * VEC + q] = nx.ap;
+                s_fc[3][lane * VEC + q] = nx.bp;
+                s_fc[4][lane * VEC + q] = nx.A;
+                s_fc[5][lane * VEC + q] = nx.m;
+            }
+            if (lane == 0)
+                __hip_atomic_store(&s_fseq, int(sc + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        if (active) {
+            float* ck = ckpt + sc * kCkptFields * C;
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                ck[0 * C + q] = x[q].a;
+                ck[1 * C + q] = x[q].b;
+                ck[2 * C + q] = x[q].ap;
+                ck[3 * C + q] = x[q].bp;
+                ck[4 * C + q] = x[q].A;
+                ck[5 * C + q] = x[q].m;
+            }
+        }
+    }
+    // every checkpoint is written (and visible to the workgroup) past here
+    __syncthreads();
+
+    // ---------------- phase R: the backward walk ----------------
+    float gw[VEC], gu[VEC];
+#pragma unroll
+    for (int q = 0; q < VEC; q++) gw[q] = gu[q] = 0.0f;
+    for (int64_t j = wave; j < nsub; j += NWV) {
+        const int64_t sc = nsub - 1 - j;
+        const int64_t t0 = sc * L;
+        const int n = T - t0 >= L ? L : int(T - t0);
+        const int64_t base = gbase + t0 * int64_t(row_bytes);
+        const rsrc_t kr_ = make_rsrc(static_cast<const char*>(pr.k) + base);
+        const rsrc_t vr_ = make_rsrc(static_cast<const char*>(pr.v) + base);
+        const rsrc_t gr_ = make_rsrc(static_cast<const char*>(pr.gy) + base);
+        Raw kr[L], vr[L], gyr[L];
+#pragma unroll
+        for (int i = 0; i < L; i++) {
+            if (i < n) {
+                kr[i] = Buf<Raw>::template load<kStreamLoad>(kr_, toff[i], 0);
+                vr[i] = Buf<Raw>::template load<kStreamLoad>(vr_, toff[i], 0);
+                gyr[i] = Buf<Raw>::template load<kStreamLoad>(gr_, toff[i], 0);
+            }
+        }
+        FState s[VEC];
+        {
+            const float* ck = ckpt + sc * kCkptFields * C;
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                s[q].a = ck[0 * C + q];
+                s[q].b = ck[1 * C + q];
+                s[q].ap = ck[2 * C + q];
+                s[q].bp = ck[3 * C + q];
+                s[q].A = ck[4 * C + q];
+                s[q].m = ck[5 * C + q];
+            }
+        }
+        RState rg[VEC];
+#pragma unroll
+        for (int q = 0; q < VEC; q++) rg[q].set_empty();
+        TokenOut to[L][VEC];
+#pragma unroll
+        for (int i = 0; i < L; i++) {
+            if (i < n) {
+                float kf[VEC], vf[VEC], gf[VEC];
+                IO::unpack(kr[i], kf);
+                IO::unpack(vr[i], vf);
+                IO::unpack(gyr[i], gf);
+#pragma unroll
+                for (int q = 0; q < VEC; q++)
+                    to[i][q] = forward_detail(s[q], rg[q], kf[q], vf[q], gf[q], w[q], u[q], float(i),
+                                              gw[q], gu[q]);
+            }
+        }
+        while (__hip_atomic_load(&s_rseq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != int(j))
+            __builtin_amdgcn_s_sleep(1);
+        RState r[VEC];
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            r[q].P = s_rc[0][lane * VEC + q];
+            r[q].Q = s_rc[1][lane * VEC + q];
+            r[q].Pi = s_rc[2][lane * VEC + q];
+            r[q].n = s_rc[3][lane * VEC + q];
+        }
+        if (sc > 0) {
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                RState nr = r[q];
+                combine_reverse(nr, rg[q], float(n), w[q]);
+                s_rc[0][lane * VEC + q] = nr.P;
+                s_rc[1][lane * VEC + q] = nr.Q;
+                s_rc[2][lane * VEC + q] = nr.Pi;
+                s_rc[3][lane * VEC + q] = nr.n;
+            }
+            if (lane == 0)
+                __hip_atomic_store(&s_rseq, int(j + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        const rsrc_t gkr_ = make_rsrc(static_cast<char*>(pr.gk) + base);
+        const rsrc_t gvr_ = make_rsrc(static_cast<char*>(pr.gv) + base);
+#pragma unroll
+        for (int i = L - 1; i >= 0; i--) {
+            if (i < n) {
+                float kf[VEC], vf[VEC], gkf[VEC], gvf[VEC];
+                IO::unpack(kr[i], kf);
+                IO::unpack(vr[i], vf);
+#pragma unroll
+                for (int q = 0; q < VEC; q++)
+                    reverse_detail(r[q], to[i][q], kf[q], vf[q], w[q], i > 0, gkf[q], gvf[q]);
+                if (active) {
+                    Buf<Raw>::store(IO::pack(gkf), gkr_, toff[i], 0);
+                    Buf<Raw>::store(IO::pack(gvf), gvr_, toff[i], 0);
                 }
             }
         }
     }
-    pr.part_w[col] = gw;
-    pr.part_u[col] = gu;
-}
 
-template <int DT>
-__global__ __launch_bounds__(256) void backward_reverse_pass(BackwardProblem pr) {
-    using IO = Io<DT, 1>;
-    using Raw = typename IO::Raw;
-    const int64_t col = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (col >= pr.B * pr.C) return;
-    const int64_t bb = col / pr.C;
-    const int64_t c = col - bb * pr.C;
-    const int64_t T = pr.T, C = pr.C;
-    const float w = pr.w[c], u = pr.u[c];
-    const Raw* kp = static_cast<const Raw*>(pr.k) + bb * T * C + c;
-    const Raw* vp = static_cast<const Raw*>(pr.v) + bb * T * C + c;
-    const Raw* gp = static_cast<const Raw*>(pr.gy) + bb * T * C + c;
-    const float* zp = pr.z + bb * T * C + c;
-    const float* yp = pr.ys + bb * T * C + c;
-    Raw* gkp = static_cast<Raw*>(pr.gk) + bb * T * C + c;
-    Raw* gvp = static_cast<Raw*>(pr.gv) + bb * T * C + c;
-
-    float Pi = kEmptyP, n = 0.0f;             // scale exponent pi = Pi - n w (anchor Pi = -z)
-    float P = 0.0f, Q = 0.0f;
-    for (int64_t t1 = T; t1 > 0; t1 -= kBwdTokens) {
-        const int cnt = t1 < kBwdTokens ? int(t1) : kBwdTokens;
-        const int64_t t0 = t1 - cnt;
-        float kf[kBwdTokens], vf[kBwdTokens], gf[kBwdTokens], zf[kBwdTokens], yf[kBwdTokens];
+    // ---------------- gw, gu of this (b, column group) ----------------
 #pragma unroll
-        for (int i = 0; i < kBwdTokens; i++) {
-            if (i < cnt) {
-                float x[1];
-                IO::unpack(load_stream(kp + (t0 + i) * C), x); kf[i] = x[0];
-                IO::unpack(load_stream(vp + (t0 + i) * C), x); vf[i] = x[0];
-                IO::unpack(load_stream(gp + (t0 + i) * C), x); gf[i] = x[0];
-                zf[i] = load_stream(zp + (t0 + i) * C);
-                yf[i] = load_stream(yp + (t0 + i) * C);
-            }
-        }
+    for (int q = 0; q < VEC; q++) {
+        s_red[0][wave][lane * VEC + q] = gw[q];
+        s_red[1][wave][lane * VEC + q] = gu[q];
+    }
+    __syncthreads();
+    if (wave == 0 && active) {
 #pragma unroll
-        for (int i = kBwdTokens - 1; i >= 0; i--) {
-            if (i < cnt) {
-                const float k = kf[i], v = vf[i], g = gf[i], z = zf[i], y = yf[i];
-                // gy_t e^{u+k_t} / D_t; u + k rounds as where z was formed, so
-                // the exponent is exactly -log(delta) when the bonus dominates
-                const float ed = g * expf_((u + k) - z);
-                const float eh = expf_(__builtin_fmaf(-n, w, k + Pi)); // e^{k_t} times the scale of P, Q
-                float gv[1], gk[1];
-                gv[0] = __builtin_fmaf(eh, P, ed);
-                gk[0] = __builtin_fmaf(eh, __builtin_fmaf(v, P, -Q), ed * (v - y));
-                gvp[(t0 + i) * C] = IO::pack(gv);
-                gkp[(t0 + i) * C] = IO::pack(gk);
-                // fold token t into P, Q for the earlier tokens; the new term's
-                // exponent is -z_t, e = (pi - w) - (-z_t), anchor-relative
-                const float e = __builtin_fmaf(-(n + 1.0f), w, Pi + z);
-                if (e < 0.0f) {
-                    const float s = expf_(e);
-                    P = __builtin_fmaf(s, P, g);
-                    Q = __builtin_fmaf(s, Q, g * y);
-                    Pi = -z;
-                    n = 0.0f;
-                } else {
-                    const float s = expf_(-e);
-                    P = __builtin_fmaf(s, g, P);
-                    Q = __builtin_fmaf(s * g, y, Q);
-                    n += 1.0f;
-                }
+        for (int q = 0; q < VEC; q++) {
+            float sw = 0.0f, su = 0.0f;
+            for (int v2 = 0; v2 < NWV; v2++) {
+                sw += s_red[0][v2][lane * VEC + q];
+                su += s_red[1][v2][lane * VEC + q];
             }
+            pr.part_w[bb * C + c + q] = sw;
+            pr.part_u[bb * C + c + q] = su;
         }
     }
 }
@@ -203,37 +462,44 @@ __global__ void zero_pair(float* x, float* y, int64_t n) {
     }
 }
 
+size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
 }  // namespace
 
+int backward_vec(int64_t C, int dtype, bool aligned) {
+    return (dtype == kBF16 && C % 2 == 0 && aligned) ? 2 : 1;
+}
+
 size_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C) {
-    const size_t n = size_t(B) * size_t(T) * size_t(C);
+    const size_t nsub = size_t((T + kBwdTokens - 1) / kBwdTokens);
     const size_t cols = size_t(B) * size_t(C);
-    auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-    return up(n * 4) * 2 + up(cols * 4) * 2;
+    return up256(cols * nsub * kCkptFields * 4) + 2 * up256(cols * 4);
 }
 
 hipError_t launch_backward(BackwardProblem pr, void* workspace, hipStream_t stream) {
-    const int64_t cols = pr.B * pr.C;
     if (pr.T == 0) {
         hipLaunchKernelGGL(zero_pair, dim3(unsigned((pr.C + 255) / 256)), dim3(256), 0, stream, pr.gw,
                            pr.gu, pr.C);
         return hipGetLastError();
     }
-    const size_t n = size_t(pr.B) * size_t(pr.T) * size_t(pr.C);
-    auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+    const int64_t cols = pr.B * pr.C;
+    const int64_t nsub = (pr.T + kBwdTokens - 1) / kBwdTokens;
     char* ws = static_cast<char*>(workspace);
-    pr.z = reinterpret_cast<float*>(ws);
-    pr.ys = reinterpret_cast<float*>(ws + up(n * 4));
-    pr.part_w = reinterpret_cast<float*>(ws + 2 * up(n * 4));
-    pr.part_u = reinterpret_cast<float*>(ws + 2 * up(n * 4) + up(size_t(cols) * 4));
-    const dim3 grid(unsigned((cols + 255) / 256)), block(256);
-    if (pr.dtype == kBF16) {
-        hipLaunchKernelGGL(backward_forward_pass<kBF16>, grid, block, 0, stream, pr);
-        hipLaunchKernelGGL(backward_reverse_pass<kBF16>, grid, block, 0, stream, pr);
-    } else {
-        hipLaunchKernelGGL(backward_forward_pass<kF32>, grid, block, 0, stream, pr);
-        hipLaunchKernelGGL(backward_reverse_pass<kF32>, grid, block, 0, stream, pr);
-    }
+    pr.ckpt = reinterpret_cast<float*>(ws);
+    const size_t ck = up256(size_t(cols) * size_t(nsub) * kCkptFields * 4);
+    pr.part_w = reinterpret_cast<float*>(ws + ck);
+    pr.part_u = reinterpret_cast<float*>(ws + ck + up256(size_t(cols) * 4));
+    const int64_t cg = 64 * pr.vec;
+    const int64_t gpr = (pr.C + cg - 1) / cg;
+    const dim3 grid(unsigned(pr.B * gpr));
+    constexpr int NW = 8;
+    const dim3 block(NW * 64);
+    if (pr.dtype == kBF16 && pr.vec == 2)
+        hipLaunchKernelGGL((backward_chained_kernel<kBF16, 2, NW>), grid, block, 0, stream, pr, gpr, nsub);
+    else if (pr.dtype == kBF16)
+        hipLaunchKernelGGL((backward_chained_kernel<kBF16, 1, NW>), grid, block, 0, stream, pr, gpr, nsub);
+    else
+        hipLaunchKernelGGL((backward_chained_kernel<kF32, 1, NW>), grid, block, 0, stream, pr, gpr, nsub);
     hipLaunchKernelGGL(backward_reduce, dim3(unsigned((pr.C + 255) / 256)), dim3(256), 0, stream, pr);
     return hipGetLastError();
 }

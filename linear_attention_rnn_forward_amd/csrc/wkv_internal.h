@@ -64,12 +64,13 @@ struct BackwardProblem {
     const void *k, *v, *gy;        // [B,T,C] dtype
     void *gk, *gv;                 // [B,T,C] dtype
     float *gw, *gu;                // [C]
+    int vec = 1;                   // channels per lane (backward_vec)
     // workspace sections (set by launch_backward)
-    float* z = nullptr;            // [B,T,C] log of each output's weight sum
-    float* ys = nullptr;           // [B,T,C] the outputs, fp32
+    float* ckpt = nullptr;         // [B][T/16][6][C] forward state before each sub-chunk
     float* part_w = nullptr;       // [B,C] per-column gw
     float* part_u = nullptr;       // [B,C] per-column gu
 };
+int backward_vec(int64_t C, int dtype, bool aligned);
 size_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C);
 hipError_t launch_backward(BackwardProblem pr, void* workspace, hipStream_t stream);
 

@@ -205,13 +205,13 @@ def test_session_save_checks_arguments():
 
 
 def test_backward_workspace_size():
-    """Per-token log-normaliser and output (fp32, 8 bytes a token-channel)
-    plus per-column gw, gu partials (8 bytes a column), each section rounded
-    up to 256 bytes."""
+    """The forward state before every 16-token sub-chunk (6 fp32 per column)
+    plus per-column gw, gu partials, each section rounded up to 256 bytes."""
     L = wkv.lib()
-    assert L.wkv_backward_workspace_size(2, 3, 64) == 2 * 1536 + 2 * 512
-    assert L.wkv_backward_workspace_size(16, 4096, 2048) == 8 * 16 * 4096 * 2048 + 8 * 16 * 2048
-    assert L.wkv_backward_workspace_size(1, 1, 1) == 4 * 256
+    assert L.wkv_backward_workspace_size(2, 3, 64) == 3072 + 2 * 512
+    assert L.wkv_backward_workspace_size(2, 17, 64) == 2 * 3072 + 2 * 512
+    assert L.wkv_backward_workspace_size(16, 4096, 2048) == 16 * 2048 * 256 * 24 + 2 * 16 * 2048 * 4
+    assert L.wkv_backward_workspace_size(1, 1, 1) == 3 * 256
     assert L.wkv_backward_workspace_size(0, 8, 8) == 0
     assert L.wkv_backward_workspace_size(1 << 40, 1 << 40, 8) == 0
 
@@ -241,3 +241,4 @@ def test_backward_rejects_bad_arguments():
     assert call(ws_bytes=need - 1) == -4
     assert call(ws=20 * G + 16) == -4              # misaligned
     assert call(ws=6 * G) == -5                    # workspace on gk
+    assert call(C=1 << 26) == -2                   # sub-chunk offsets beyond 32 bits
