@@ -20,15 +20,15 @@
 // handed to the waves round-robin as on the forward's chained path):
 //
 //   phase F  forward in time.  Each wave loads k, v of its sub-chunk and
-//            folds them into a partial state (a, b, a', b') from the empty
-//            history; the carry (the state before the sub-chunk) arrives
+//            sums them into a partial state (a, b, a', b') from the empty
+//            history (max of the exponents, then the sum); the carry (the state before the sub-chunk) arrives
 //            through LDS, carry (+) partial goes on to the next sub-chunk, and
 //            the carry is stored to the workspace as that sub-chunk's
 //            checkpoint.
 //   phase R  backward in time, sub-chunks from the last.  Each wave loads
 //            k, v, gy and its checkpoint, re-runs the forward recurrence over
 //            the sub-chunk (outputs y_t, 1/D_t, the gu and gw terms) and
-//            folds the sub-chunk's (P, Q) contribution into a partial; the
+//            sums the sub-chunk's (P, Q) contribution into a partial; the
 //            (P, Q) carry from the later sub-chunk arrives through LDS,
 //            carry (+) partial goes on to the earlier one, and the tokens are
 //            walked backwards from the carry to write gk, gv.
@@ -38,15 +38,19 @@
 // anchor-relative: (anchor - key) is exact when the two are close, and the
 // count w term is added by one fma at the difference's own magnitude, so no
 // rounding at the keys' magnitude accumulates through the rescalings.  The
-// (P, Q) scan is held against e^{-q_t}, q_t the larger of the two read-out
-// exponents (the history's and u + k_t), with the bounded factor 1/delta_t
-// (delta_t = D_t e^{-q_t} in [1, tokens]) folded into its terms.
+// (P, Q) scan is held against e^{-q_t} with the factor 1/delta_t = e^{q_t} /
+// D_t folded into its terms; q_t is an exponent the read-out already has (the
+// larger of the history's and u + k_t, or the folded state's plus w when the
+// read-out reuses the fold's weights), so delta_t lies in [min(1, e^{u-w}),
+// tokens] and e^{k_i} times the scan's scale stays <= 1.
 //
 // gw, gu are reduced per column over the waves in LDS (fixed order), stored
 // per (b, c), and summed over the batch by a last kernel in batch order: the
 // result does not depend on timing.
 #include "wkv_device.h"
 #include "wkv_internal.h"
+
+#include <type_traits>
 
 namespace wkv {
 namespace {
@@ -134,42 +138,74 @@ struct TokenOut {
     float ed;  // gy_t e^{u+k_t} / D_t
 };
 
-// The forward read-out of one token from state s, its gw, gu terms, its
-// term of the sub-chunk's (P, Q) partial (token index i in the sub-chunk,
-// exponent -q - i w at the sub-chunk start), then the fold-in.
-__device__ __forceinline__ TokenOut forward_detail(FState& s, RState& rg, float k, float v, float g,
-                                                   float w, float u, float fi, float& gw, float& gu) {
+// The forward read-out of one token from state s, its gw, gu terms, then the
+// fold-in.  FUSED (|u - w| <= 44, c = e^{u-w} in range): the read-out reuses
+// the fold's weights, as the forward kernels do -- relative to the folded
+// exponent p' = max(p - w, k), the history weighs al = e^{p-w-p'}, the new
+// token be = e^{k-p'}, and D = e^{p'+w} (al b + be c) -- so one exponential
+// serves both; the (P, Q) exponent is then q = p' + w.  Otherwise the
+// read-out takes its own exponential against q = max(p, u + k).
+template <bool FUSED>
+__device__ __forceinline__ TokenOut forward_detail(FState& s, float k, float v, float g, float w,
+                                                   float u, float c, float& gw, float& gu) {
     TokenOut o;
     const float ak = s.A - k;
-    const float d = __builtin_fmaf(-s.m, w, ak - u);  // p - (u + k)
-    const float x = exp_neg_abs(d);
-    const bool keep = d >= 0.0f;
-    const float al = keep ? 1.0f : x;  // e^{p - q}
-    const float be = keep ? x : 1.0f;  // e^{u + k - q}
-    const float del = __builtin_fmaf(al, s.b, be);
-    const float rd = fast_rcp(del);
-    o.y = __builtin_fmaf(al, s.a, be * v) * rd;
-    o.gr = g * rd;
-    o.ed = o.gr * be;
-    // u + k is rounded as in d's reference point, so q + log(delta) = log D
-    o.q = keep ? __builtin_fmaf(-s.m, w, s.A) : u + k;
-    gu = __builtin_fmaf(o.ed, v - o.y, gu);
-    gw = __builtin_fmaf(-(o.gr * al), __builtin_fmaf(-o.y, s.bp, s.ap), gw);
-    // (P, Q) partial of the sub-chunk, in forward order
-    {
-        const float dr = __builtin_fmaf(-(fi - rg.n), w, -(o.q + rg.Pi));  // new term - running
-        const float xr = exp_neg_abs(dr);
-        const bool nm = dr > 0.0f;
-        const float ar = nm ? xr : 1.0f;
-        const float br = nm ? 1.0f : xr;
-        const float t = br * o.gr;
-        rg.P = __builtin_fmaf(ar, rg.P, t);
-        rg.Q = __builtin_fmaf(ar, rg.Q, t * o.y);
-        rg.Pi = nm ? -o.q : rg.Pi;
-        rg.n = nm ? fi : rg.n;
+    const float e = __builtin_fmaf(-(s.m + 1.0f), w, ak);  // (p - w) - k
+    const float x = exp_neg_abs(e);
+    const bool reset = e < 0.0f;                             // the new key is the maximum
+    const float al = reset ? x : 1.0f;
+    const float be = reset ? 1.0f : x;
+    float rh, bo;  // read-out weights of history and bonus, relative to e^{q}
+    if constexpr (FUSED) {
+        rh = al;
+        bo = be * c;
+        o.q = reset ? k + w : __builtin_fmaf(-s.m, w, s.A);
+    } else {
+        const float d = __builtin_fmaf(-s.m, w, ak - u);  // p - (u + k)
+        const float xr = exp_neg_abs(d);
+        const bool keep = d >= 0.0f;
+        rh = keep ? 1.0f : xr;
+        bo = keep ? xr : 1.0f;
+        // u + k is rounded as in d's reference point
+        o.q = keep ? __builtin_fmaf(-s.m, w, s.A) : u + k;
     }
-    fold_forward(s, k, v, w);
+    const float del = __builtin_fmaf(rh, s.b, bo);
+    const float rd = fast_rcp(del);
+    o.y = __builtin_fmaf(rh, s.a, bo * v) * rd;
+    o.gr = g * rd;
+    o.ed = o.gr * bo;
+    gu = __builtin_fmaf(o.ed, v - o.y, gu);
+    gw = __builtin_fmaf(-(o.gr * rh), __builtin_fmaf(-o.y, s.bp, s.ap), gw);
+    // fold-in: the history decays by e^{-w}, the age-weighted sums gain the
+    // history, the new key enters with weight e^{k}
+    s.ap = al * (s.ap + s.a);
+    s.bp = al * (s.bp + s.b);
+    s.a = __builtin_fmaf(al, s.a, be * v);
+    s.b = __builtin_fmaf(al, s.b, be);
+    s.A = reset ? k : s.A;
+    s.m = reset ? 0.0f : s.m + 1.0f;
     return o;
+}
+
+// The first n tokens of a sub-chunk through forward_detail.
+template <typename IO, int L, int VEC, bool FUSED, typename Raw>
+__device__ __forceinline__ void forward_run(FState (&s)[VEC], const Raw (&kr)[L], const Raw (&vr)[L],
+                                            const Raw (&gyr)[L], const float (&w)[VEC],
+                                            const float (&u)[VEC], const float (&c)[VEC], int n,
+                                            TokenOut (&to)[L][VEC], float (&gw)[VEC],
+                                            float (&gu)[VEC]) {
+#pragma unroll
+    for (int i = 0; i < L; i++) {
+        if (i < n) {
+            float kf[VEC], vf[VEC], gf[VEC];
+            IO::unpack(kr[i], kf);
+            IO::unpack(vr[i], vf);
+            IO::unpack(gyr[i], gf);
+#pragma unroll
+            for (int q = 0; q < VEC; q++)
+                to[i][q] = forward_detail<FUSED>(s[q], kf[q], vf[q], gf[q], w[q], u[q], c[q], gw[q], gu[q]);
+        }
+    }
 }
 
 // One token of the backward walk: gk, gv from the running (P, Q) of the
@@ -215,12 +251,17 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     const bool active = c < pr.C;
     const int64_t T = pr.T, C = pr.C;
 
-    float w[VEC], u[VEC];
+    float w[VEC], u[VEC], cb[VEC];
+    bool fus = true;
 #pragma unroll
     for (int q = 0; q < VEC; q++) {
         w[q] = active ? pr.w[c + q] : 1.0f;
         u[q] = active ? pr.u[c + q] : 0.0f;
+        const float wmu = w[q] - u[q];
+        fus = fus && __builtin_fabsf(wmu) <= kFusedMaxAbsUW;
+        cb[q] = __builtin_amdgcn_exp2f(-wmu * kLog2e);  // e^{u-w}
     }
+    const bool fused = __builtin_amdgcn_ballot_w64(!fus) == 0;
     if (wave == 0) {
 #pragma unroll
         for (int q = 0; q < VEC; q++) {
@@ -271,17 +312,47 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
                 vr[i] = Buf<Raw>::template load<kStreamLoad>(vr_, toff[i], 0);
             }
         }
+        // the sub-chunk from the empty history, max then sum: token i has
+        // exponent x_i = k_i - (n-1-i) w at the sub-chunk's end; the partial's
+        // anchor is the largest, each weight e^{x_i - max}
         FState g[VEC];
+        {
+            float xs[L][VEC], mx[VEC];
 #pragma unroll
-        for (int q = 0; q < VEC; q++) g[q].set_empty();
+            for (int q = 0; q < VEC; q++) mx[q] = kEmptyP;
 #pragma unroll
-        for (int i = 0; i < L; i++) {
-            if (i < n) {
-                float kf[VEC], vf[VEC];
-                IO::unpack(kr[i], kf);
-                IO::unpack(vr[i], vf);
+            for (int i = 0; i < L; i++) {
+                if (i < n) {
+                    float kf[VEC];
+                    IO::unpack(kr[i], kf);
 #pragma unroll
-                for (int q = 0; q < VEC; q++) fold_forward(g[q], kf[q], vf[q], w[q]);
+                    for (int q = 0; q < VEC; q++) {
+                        xs[i][q] = __builtin_fmaf(-float(n - 1 - i), w[q], kf[q]);
+                        mx[q] = max_num(mx[q], xs[i][q]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                g[q].set_empty();
+                g[q].A = mx[q];
+            }
+#pragma unroll
+            for (int i = 0; i < L; i++) {
+                if (i < n) {
+                    float vf[VEC];
+                    IO::unpack(vr[i], vf);
+                    const float age = float(n - 1 - i);
+#pragma unroll
+                    for (int q = 0; q < VEC; q++) {
+                        const float e = __builtin_amdgcn_exp2f((xs[i][q] - mx[q]) * kLog2e);
+                        const float ev = e * vf[q];
+                        g[q].a += ev;
+                        g[q].b += e;
+                        g[q].ap = __builtin_fmaf(age, ev, g[q].ap);
+                        g[q].bp = __builtin_fmaf(age, e, g[q].bp);
+                    }
+                }
             }
         }
         while (__hip_atomic_load(&s_fseq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != int(sc))
@@ -331,94 +402,118 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     float gw[VEC], gu[VEC];
 #pragma unroll
     for (int q = 0; q < VEC; q++) gw[q] = gu[q] = 0.0f;
-    for (int64_t j = wave; j < nsub; j += NWV) {
-        const int64_t sc = nsub - 1 - j;
-        const int64_t t0 = sc * L;
-        const int n = T - t0 >= L ? L : int(T - t0);
-        const int64_t base = gbase + t0 * int64_t(row_bytes);
-        const rsrc_t kr_ = make_rsrc(static_cast<const char*>(pr.k) + base);
-        const rsrc_t vr_ = make_rsrc(static_cast<const char*>(pr.v) + base);
-        const rsrc_t gr_ = make_rsrc(static_cast<const char*>(pr.gy) + base);
-        Raw kr[L], vr[L], gyr[L];
-#pragma unroll
-        for (int i = 0; i < L; i++) {
-            if (i < n) {
-                kr[i] = Buf<Raw>::template load<kStreamLoad>(kr_, toff[i], 0);
-                vr[i] = Buf<Raw>::template load<kStreamLoad>(vr_, toff[i], 0);
-                gyr[i] = Buf<Raw>::template load<kStreamLoad>(gr_, toff[i], 0);
+    // the read-out form is uniform over the workgroup (its waves share the
+    // channels): one copy of the loop per form keeps their registers apart
+    auto reverse_phase = [&](auto fused_tag) {
+        for (int64_t j = wave; j < nsub; j += NWV) {
+            const int64_t sc = nsub - 1 - j;
+            const int64_t t0 = sc * L;
+            const int n = T - t0 >= L ? L : int(T - t0);
+            const int64_t base = gbase + t0 * int64_t(row_bytes);
+            const rsrc_t kr_ = make_rsrc(static_cast<const char*>(pr.k) + base);
+            const rsrc_t vr_ = make_rsrc(static_cast<const char*>(pr.v) + base);
+            const rsrc_t gr_ = make_rsrc(static_cast<const char*>(pr.gy) + base);
+            Raw kr[L], vr[L], gyr[L];
+    #pragma unroll
+            for (int i = 0; i < L; i++) {
+                if (i < n) {
+                    kr[i] = Buf<Raw>::template load<kStreamLoad>(kr_, toff[i], 0);
+                    vr[i] = Buf<Raw>::template load<kStreamLoad>(vr_, toff[i], 0);
+                    gyr[i] = Buf<Raw>::template load<kStreamLoad>(gr_, toff[i], 0);
+                }
             }
-        }
-        FState s[VEC];
-        {
-            const float* ck = ckpt + sc * kCkptFields * C;
-#pragma unroll
+            FState s[VEC];
+            {
+                const float* ck = ckpt + sc * kCkptFields * C;
+    #pragma unroll
+                for (int q = 0; q < VEC; q++) {
+                    s[q].a = ck[0 * C + q];
+                    s[q].b = ck[1 * C + q];
+                    s[q].ap = ck[2 * C + q];
+                    s[q].bp = ck[3 * C + q];
+                    s[q].A = ck[4 * C + q];
+                    s[q].m = ck[5 * C + q];
+                }
+            }
+            TokenOut to[L][VEC];
+            forward_run<IO, L, VEC, decltype(fused_tag)::value>(s, kr, vr, gyr, w, u, cb, n, to, gw, gu);
+            // the sub-chunk's (P, Q) partial, max then sum: token i's term has
+            // exponent -q_i - i w at the sub-chunk's start
+            RState rg[VEC];
+            {
+                float mx[VEC];
+    #pragma unroll
+                for (int q = 0; q < VEC; q++) mx[q] = kEmptyP;
+    #pragma unroll
+                for (int i = 0; i < L; i++)
+                    if (i < n)
+    #pragma unroll
+                        for (int q = 0; q < VEC; q++)
+                            mx[q] = max_num(mx[q], __builtin_fmaf(-float(i), w[q], -to[i][q].q));
+    #pragma unroll
+                for (int q = 0; q < VEC; q++) {
+                    rg[q].set_empty();
+                    rg[q].Pi = mx[q];
+                }
+    #pragma unroll
+                for (int i = 0; i < L; i++) {
+                    if (i < n) {
+    #pragma unroll
+                        for (int q = 0; q < VEC; q++) {
+                            const float xi = __builtin_fmaf(-float(i), w[q], -to[i][q].q);
+                            const float t = __builtin_amdgcn_exp2f((xi - mx[q]) * kLog2e) * to[i][q].gr;
+                            rg[q].P += t;
+                            rg[q].Q = __builtin_fmaf(t, to[i][q].y, rg[q].Q);
+                        }
+                    }
+                }
+            }
+            while (__hip_atomic_load(&s_rseq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != int(j))
+                __builtin_amdgcn_s_sleep(1);
+            RState r[VEC];
+    #pragma unroll
             for (int q = 0; q < VEC; q++) {
-                s[q].a = ck[0 * C + q];
-                s[q].b = ck[1 * C + q];
-                s[q].ap = ck[2 * C + q];
-                s[q].bp = ck[3 * C + q];
-                s[q].A = ck[4 * C + q];
-                s[q].m = ck[5 * C + q];
+                r[q].P = s_rc[0][lane * VEC + q];
+                r[q].Q = s_rc[1][lane * VEC + q];
+                r[q].Pi = s_rc[2][lane * VEC + q];
+                r[q].n = s_rc[3][lane * VEC + q];
             }
-        }
-        RState rg[VEC];
-#pragma unroll
-        for (int q = 0; q < VEC; q++) rg[q].set_empty();
-        TokenOut to[L][VEC];
-#pragma unroll
-        for (int i = 0; i < L; i++) {
-            if (i < n) {
-                float kf[VEC], vf[VEC], gf[VEC];
-                IO::unpack(kr[i], kf);
-                IO::unpack(vr[i], vf);
-                IO::unpack(gyr[i], gf);
-#pragma unroll
-                for (int q = 0; q < VEC; q++)
-                    to[i][q] = forward_detail(s[q], rg[q], kf[q], vf[q], gf[q], w[q], u[q], float(i),
-                                              gw[q], gu[q]);
+            if (sc > 0) {
+    #pragma unroll
+                for (int q = 0; q < VEC; q++) {
+                    RState nr = r[q];
+                    combine_reverse(nr, rg[q], float(n), w[q]);
+                    s_rc[0][lane * VEC + q] = nr.P;
+                    s_rc[1][lane * VEC + q] = nr.Q;
+                    s_rc[2][lane * VEC + q] = nr.Pi;
+                    s_rc[3][lane * VEC + q] = nr.n;
+                }
+                if (lane == 0)
+                    __hip_atomic_store(&s_rseq, int(j + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
-        }
-        while (__hip_atomic_load(&s_rseq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != int(j))
-            __builtin_amdgcn_s_sleep(1);
-        RState r[VEC];
-#pragma unroll
-        for (int q = 0; q < VEC; q++) {
-            r[q].P = s_rc[0][lane * VEC + q];
-            r[q].Q = s_rc[1][lane * VEC + q];
-            r[q].Pi = s_rc[2][lane * VEC + q];
-            r[q].n = s_rc[3][lane * VEC + q];
-        }
-        if (sc > 0) {
-#pragma unroll
-            for (int q = 0; q < VEC; q++) {
-                RState nr = r[q];
-                combine_reverse(nr, rg[q], float(n), w[q]);
-                s_rc[0][lane * VEC + q] = nr.P;
-                s_rc[1][lane * VEC + q] = nr.Q;
-                s_rc[2][lane * VEC + q] = nr.Pi;
-                s_rc[3][lane * VEC + q] = nr.n;
-            }
-            if (lane == 0)
-                __hip_atomic_store(&s_rseq, int(j + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
-        const rsrc_t gkr_ = make_rsrc(static_cast<char*>(pr.gk) + base);
-        const rsrc_t gvr_ = make_rsrc(static_cast<char*>(pr.gv) + base);
-#pragma unroll
-        for (int i = L - 1; i >= 0; i--) {
-            if (i < n) {
-                float kf[VEC], vf[VEC], gkf[VEC], gvf[VEC];
-                IO::unpack(kr[i], kf);
-                IO::unpack(vr[i], vf);
-#pragma unroll
-                for (int q = 0; q < VEC; q++)
-                    reverse_detail(r[q], to[i][q], kf[q], vf[q], w[q], i > 0, gkf[q], gvf[q]);
-                if (active) {
-                    Buf<Raw>::store(IO::pack(gkf), gkr_, toff[i], 0);
-                    Buf<Raw>::store(IO::pack(gvf), gvr_, toff[i], 0);
+            const rsrc_t gkr_ = make_rsrc(static_cast<char*>(pr.gk) + base);
+            const rsrc_t gvr_ = make_rsrc(static_cast<char*>(pr.gv) + base);
+    #pragma unroll
+            for (int i = L - 1; i >= 0; i--) {
+                if (i < n) {
+                    float kf[VEC], vf[VEC], gkf[VEC], gvf[VEC];
+                    IO::unpack(kr[i], kf);
+                    IO::unpack(vr[i], vf);
+    #pragma unroll
+                    for (int q = 0; q < VEC; q++)
+                        reverse_detail(r[q], to[i][q], kf[q], vf[q], w[q], i > 0, gkf[q], gvf[q]);
+                    if (active) {
+                        Buf<Raw>::store(IO::pack(gkf), gkr_, toff[i], 0);
+                        Buf<Raw>::store(IO::pack(gvf), gvr_, toff[i], 0);
+                    }
                 }
             }
         }
-    }
+    };
+    if (fused)
+        reverse_phase(std::integral_constant<bool, true>{});
+    else
+        reverse_phase(std::integral_constant<bool, false>{});
 
     // ---------------- gw, gu of this (b, column group) ----------------
 #pragma unroll

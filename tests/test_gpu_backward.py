@@ -129,7 +129,13 @@ def test_empty_sequence_zeroes_gw_gu(device):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_single_token_closed_form(device, dtype):
-    """wkv_0 = v_0: gv = gy exactly, and k, w, u get no gradient."""
+    """wkv_0 = v_0, so gv = gy and k, w, u get no gradient.  The kernel forms
+    the read-out as (c v) (1/c) with c = e^{u-w} (the fold's weights reused),
+    so y_0 is v_0 within three roundings (one of them the reciprocal's, within
+    1 ulp): |gv - gy| <= 3 * 2^-24 |gy| and |gk|, |gu| <= 4 * 2^-24 |gy v|
+    (per element, and summed over the batch for gu).  Rounded to bf16, gv is
+    gy exactly (gy is a bf16 value and the error is far below half its ulp).
+    gw has no term at all with an empty history: exactly 0."""
     rng = np.random.default_rng(11)
     B, C = 3, 70
     k = rng.normal(0, 3, (B, 1, C)).astype(np.float32)
@@ -140,10 +146,15 @@ def test_single_token_closed_form(device, dtype):
     w = np.exp(rng.uniform(-5, 1, C)).astype(np.float32)
     u = rng.normal(0, 0.5, C).astype(np.float32)
     gk, gv, gw, gu = run_backward(k, v, w, u, g, dtype, device)
-    np.testing.assert_array_equal(gv, g)
-    np.testing.assert_array_equal(gk, 0.0)
+    ulp = 2.0 ** -24
+    gd, vd = g.astype(np.float64), v.astype(np.float64)
+    if dtype == "bf16":
+        np.testing.assert_array_equal(gv, g)
+    else:
+        assert np.all(np.abs(gv - gd) <= 3 * ulp * np.abs(gd))
+    assert np.all(np.abs(gk) <= 4 * ulp * np.abs(gd * vd) * (1 + 2.0 ** -8))
+    assert np.all(np.abs(gu) <= 4 * ulp * np.abs(gd * vd).sum(axis=(0, 1)) * (1 + 1e-6))
     np.testing.assert_array_equal(gw, 0.0)
-    np.testing.assert_array_equal(gu, 0.0)
 
 
 def _cols(B, T, C, seed):
@@ -164,16 +175,34 @@ def test_monotone_keys_move_the_anchor_every_token_or_never(device):
         check(k, v, w, u, g, "f32", device, "ramp")
 
 
-@pytest.mark.parametrize("omega", [-8.0, 0.0, 2.0, 3.7])
+@pytest.mark.parametrize("omega", [-8.0, 0.0, 2.0, 3.7, 4.0])
 def test_decay_extremes(device, omega):
-    """w from e^-8 (a window of thousands of tokens) to e^3.7 = 40 (only the
-    current and the previous token matter)."""
+    """w from e^-8 (a window of thousands of tokens) to e^4 = 55 (only the
+    current and the previous token matter; |u - w| > 44 takes the read-out
+    with its own exponential)."""
     B, T, C = 1, 700, 48
     rng, (v, g) = _cols(B, T, C, 13)
     k = rng.normal(0, 2, (B, T, C)).astype(np.float32)
     w = np.full(C, np.exp(omega), dtype=np.float32)
     u = rng.normal(0, 0.5, C).astype(np.float32)
     check(k, v, w, u, g, "f32", device, f"omega={omega}")
+
+
+def test_mixed_read_out_forms(device):
+    """Column groups whose channels all have |u - w| <= 44 reuse the fold's
+    exponential for the read-out; a group with any other channel takes the
+    separate read-out.  Here the first 64 channels have w = e^4 (and the
+    next 64 a bonus u = 50), the rest ordinary values, in both dtypes'
+    channel grouping."""
+    B, T, C = 2, 150, 300
+    rng, (v, g) = _cols(B, T, C, 16)
+    k = rng.normal(0, 2, (B, T, C)).astype(np.float32)
+    w = np.exp(rng.uniform(-5, 1, C)).astype(np.float32)
+    u = rng.normal(0, 0.5, C).astype(np.float32)
+    w[:64] = np.float32(np.exp(4.0))
+    u[64:128] = 50.0
+    check(k, v, w, u, g, "f32", device, "mixed f32")
+    check(bf16_exact(k), bf16_exact(v), w, u, bf16_exact(g), "bf16", device, "mixed bf16")
 
 
 def test_keys_far_outside_exp_range(device):
