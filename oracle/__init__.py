@@ -31,6 +31,10 @@ What each routine follows (pages cited by address and section):
   ``forward`` / ``step`` (tm_rwkv_math, "Receptance: the gate on the way
   out"), NumPy fp64.  The state is the plain recurrence's.
 
+The matrix-valued-state operator of RWKV-5/6 (Eagle, Finch) has its own
+NumPy fp64 module, ``oracle.matrix_state``, pinned by
+``tests/test_oracle_matrix_pins.py``.
+
 Pins (what ties these to the pages rather than to themselves) live in
 ``tests/test_oracle_pins.py``.  Inputs are promoted exactly to fp64 from
 whatever they are stored as (fp32, or bf16 widened to fp32), so the oracle
