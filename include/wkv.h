@@ -279,6 +279,74 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, int dtype,
                  void *gk, void *gv, float *gw, float *gu,
                  void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Matrix-valued state WKV of RWKV-5 "Eagle" and RWKV-6 "Finch" ([vanos] the
+ * table "Versions: RWKV-4 -> Eagle -> Finch" and the matrix-form recurrence
+ * under it).  Channels are grouped into H heads of WKV_MAT_HEAD_DIM = 64
+ * (C = 64 H; channel c is index c % 64 of head c / 64).  Per batch row and
+ * head, a state S of 64 x 64 (row i: key channel, column j: value channel):
+ *
+ *   S_t = diag(d_t) S_{t-1} + k_t v_t^T,      y_t = r_t^T S_t,
+ *   d_t = exp(-softplus(z_t)) = 1 / (1 + e^{z_t})
+ *
+ * z is the table's decay argument a.b + w: per token for Finch
+ * (WKV_MAT_DECAY_PER_TOKEN, stored like r), per channel for Eagle
+ * (WKV_MAT_DECAY_PER_CHANNEL, fp32).  The page gives no bonus term and no
+ * normalisation for this form; neither is applied.  The state is fp32,
+ * element (i, j) of head h of row b at ((b H + h) 64 + i) 64 + j; a NULL
+ * state input is the zero state.
+ */
+#define WKV_MAT_HEAD_DIM 64
+typedef enum {
+    WKV_MAT_DECAY_PER_CHANNEL = 0,  /* z [C] fp32 (forward), [L,C] fp32 (step)   */
+    WKV_MAT_DECAY_PER_TOKEN = 1     /* z shaped and stored like r                 */
+} wkv_mat_decay;
+
+typedef enum {
+    WKV_MAT_PATH_AUTO = 0,          /* chunked for bf16, token by token for fp32  */
+    WKV_MAT_PATH_CHUNKED = 1,       /* 16-token chunks as dense 16x16x16 products */
+                                    /* on the matrix cores (bf16 operands, fp32   */
+                                    /* accumulation); bf16 storage only          */
+    WKV_MAT_PATH_TOKENWISE = 2      /* the recurrence token by token in fp32      */
+} wkv_mat_path;
+
+/*
+ * Training / prefill form over [B,T,C], and optionally the state after the
+ * last token.
+ *
+ *   B, H >= 1, T >= 0
+ *   r, k, v     [B,T,C] dtype       receptance, keys, values
+ *   z           see wkv_mat_decay
+ *   s_in        [B,H,64,64] fp32    prior state, or NULL (zero)
+ *   s_out       [B,H,64,64] fp32    state after token T-1, or NULL; may be s_in
+ *   y           [B,T,C] dtype       output; must not overlap any input or s_out
+ * r, k, v, z, y must be 8-byte (bf16) or 16-byte (fp32) aligned.  The chunked
+ * path runs a chunk token by token instead, in fp32, when a channel decays by
+ * more than e^{-80} within it.  Results do not depend on timing.
+ */
+int wkv_mat_forward(int64_t B, int64_t T, int64_t H, int dtype,
+                    const void *r, const void *k, const void *v, const void *z, int z_mode,
+                    const float *s_in, float *s_out, void *y, void *stream);
+int wkv_mat_forward_path(int64_t B, int64_t T, int64_t H, int dtype, int path,
+                         const void *r, const void *k, const void *v, const void *z, int z_mode,
+                         const float *s_in, float *s_out, void *y, void *stream);
+
+/*
+ * Decode form: one token for each of L x S rows (layers x sequences), each
+ * of H heads ([vanos] "O(N) Inference Characteristics": one matrix-vector
+ * product against a fixed-size state per token).
+ *
+ *   L, S, H >= 1
+ *   r, k, v     [L,S,C] dtype
+ *   z           [L,S,C] dtype (per token) or [L,C] fp32 (per channel)
+ *   s_in        [L,S,H,64,64] fp32  required
+ *   s_out       [L,S,H,64,64] fp32  required; may be s_in (in place)
+ *   y           [L,S,C] dtype
+ */
+int wkv_mat_step(int64_t L, int64_t S, int64_t H, int dtype,
+                 const void *r, const void *k, const void *v, const void *z, int z_mode,
+                 const float *s_in, float *s_out, void *y, void *stream);
+
 /* Static description of a status code. */
 const char *wkv_status_string(int status);
 
@@ -288,7 +356,7 @@ const char *wkv_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int wkv_abi_version(void);
 
-#define WKV_ABI_VERSION 103
+#define WKV_ABI_VERSION 104
 
 #ifdef __cplusplus
 }

@@ -90,6 +90,12 @@ def lib() -> ctypes.CDLL:
         L.wkv_token_shift.restype = i32
         L.wkv_token_shift.argtypes = [i64, i64, i64, i32] + [vp] * 9 + [vp]
         L.wkv_status_string.restype = ctypes.c_char_p
+        L.wkv_mat_forward.restype = i32
+        L.wkv_mat_forward.argtypes = [i64, i64, i64, i32] + [vp] * 4 + [i32] + [vp] * 4
+        L.wkv_mat_forward_path.restype = i32
+        L.wkv_mat_forward_path.argtypes = [i64, i64, i64, i32, i32] + [vp] * 4 + [i32] + [vp] * 4
+        L.wkv_mat_step.restype = i32
+        L.wkv_mat_step.argtypes = [i64, i64, i64, i32] + [vp] * 4 + [i32] + [vp] * 4
         L.wkv_status_string.argtypes = [i32]
         L.wkv_last_error.restype = ctypes.c_char_p
         L.wkv_last_error.argtypes = []
@@ -405,3 +411,93 @@ def load_session(blob, state, seq, shifts=()):
         check(lib().wkv_session_load(Ln, S, C, dt, seq, _ptr(host), host.numel(), _ptr(a), _ptr(b),
                                      _ptr(p), _ptr_array(list(shifts)), len(shifts), _stream(dev)))
         torch.cuda.current_stream(dev).synchronize()
+
+
+# ---------------------------------------------------------------------------
+# matrix-valued state (RWKV-5 Eagle / RWKV-6 Finch)
+# ---------------------------------------------------------------------------
+
+MAT_HEAD_DIM = 64
+MAT_DECAY_PER_CHANNEL = 0
+MAT_DECAY_PER_TOKEN = 1
+_MAT_PATHS = {"auto": 0, "chunked": 1, "tokenwise": 2}
+
+
+def _mat_z(z, shape_token, shape_channel, dtype, dev):
+    torch = _torch()
+    if tuple(z.shape) == tuple(shape_token):
+        _need(z, "z", shape_token, dtype, dev)
+        return MAT_DECAY_PER_TOKEN
+    _need(z, "z", shape_channel, torch.float32, dev)
+    return MAT_DECAY_PER_CHANNEL
+
+
+def mat_forward(r, k, v, z, state=None, return_state=False, path="auto", out=None,
+                state_out=None):
+    """S_t = diag(d_t) S_{t-1} + k_t v_t^T, y_t = r_t^T S_t, d_t = exp(-softplus(z_t)),
+    per batch row and head of 64 channels (vanos001.github.io "RWKV (Attention-RNN
+    Hybrid)", the versions table and the matrix-form recurrence under it).
+
+    r, k, v: [B,T,C] float32 or bfloat16, C = 64 H.  z: [B,T,C] like r (Finch,
+    per-token decay) or [C] float32 (Eagle, per-channel decay).  state: None
+    (zero) or [B,H,64,64] float32.  path: "auto", "chunked" (bf16 only) or
+    "tokenwise".  Returns y, or (y, S_T) with return_state.
+    """
+    torch = _torch()
+    _need(k, "k")
+    if k.dim() != 3 or k.shape[2] % MAT_HEAD_DIM != 0:
+        raise ValueError("k must be [B,T,C] with C a multiple of 64")
+    B, T, C = k.shape
+    H = C // MAT_HEAD_DIM
+    dev = k.device
+    dt = _dtype_code(k)
+    _need(r, "r", k.shape, k.dtype, dev)
+    _need(v, "v", k.shape, k.dtype, dev)
+    z_mode = _mat_z(z, k.shape, (C,), k.dtype, dev)
+    st_shape = (B, H, MAT_HEAD_DIM, MAT_HEAD_DIM)
+    if state is not None:
+        _need(state, "state", st_shape, torch.float32, dev)
+    if return_state and state_out is None:
+        state_out = torch.empty(st_shape, dtype=torch.float32, device=dev)
+    if state_out is not None:
+        _need(state_out, "state_out", st_shape, torch.float32, dev)
+    y = out if out is not None else torch.empty_like(k)
+    _need(y, "out", k.shape, k.dtype, dev)
+    with torch.cuda.device(dev):
+        check(lib().wkv_mat_forward_path(B, T, H, dt, _MAT_PATHS[path], _ptr(r), _ptr(k), _ptr(v),
+                                         _ptr(z), z_mode, _ptr(state), _ptr(state_out), _ptr(y),
+                                         _stream(dev)))
+    return (y, state_out) if return_state else y
+
+
+def mat_step(state, r, k, v, z, out=None, state_out=None, inplace=False):
+    """One decode token for every (layer, sequence) row and head.
+
+    state: [L,S,H,64,64] float32.  r, k, v: [L,S,C] float32 or bfloat16.
+    z: [L,S,C] like r (per token) or [L,C] float32 (per channel).
+    Returns (y, S').  inplace=True writes S' into `state`.
+    """
+    torch = _torch()
+    _need(k, "k")
+    if k.dim() != 3 or k.shape[2] % MAT_HEAD_DIM != 0:
+        raise ValueError("k must be [L,S,C] with C a multiple of 64")
+    Ln, S, C = k.shape
+    H = C // MAT_HEAD_DIM
+    dev = k.device
+    dt = _dtype_code(k)
+    _need(r, "r", k.shape, k.dtype, dev)
+    _need(v, "v", k.shape, k.dtype, dev)
+    z_mode = _mat_z(z, k.shape, (Ln, C), k.dtype, dev)
+    st_shape = (Ln, S, H, MAT_HEAD_DIM, MAT_HEAD_DIM)
+    _need(state, "state", st_shape, torch.float32, dev)
+    if inplace:
+        state_out = state
+    elif state_out is None:
+        state_out = torch.empty_like(state)
+    _need(state_out, "state_out", st_shape, torch.float32, dev)
+    y = out if out is not None else torch.empty_like(k)
+    _need(y, "out", k.shape, k.dtype, dev)
+    with torch.cuda.device(dev):
+        check(lib().wkv_mat_step(Ln, S, H, dt, _ptr(r), _ptr(k), _ptr(v), _ptr(z), z_mode,
+                                 _ptr(state), _ptr(state_out), _ptr(y), _stream(dev)))
+    return y, state_out

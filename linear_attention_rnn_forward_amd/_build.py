@@ -24,7 +24,7 @@ ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
-SOURCES = ["wkv_api.hip", "wkv_forward.hip", "wkv_step.hip", "wkv_token_shift.hip", "wkv_session.hip", "wkv_backward.hip"]
+SOURCES = ["wkv_api.hip", "wkv_forward.hip", "wkv_step.hip", "wkv_token_shift.hip", "wkv_session.hip", "wkv_backward.hip", "wkv_mat.hip"]
 
 
 def _run(cmd, verbose):

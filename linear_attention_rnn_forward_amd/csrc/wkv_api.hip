@@ -471,4 +471,119 @@ int wkv_token_shift(int64_t B, int64_t T, int64_t C, int dtype, const void* x, c
     return e == hipSuccess ? ok() : hip_fail(e, "token shift launch");
 }
 
+
+}  // extern "C"
+
+namespace {
+
+// Shared checks of the matrix-state calls: nrows token rows of C = 64 H
+// channels, z per token (dtype, like r) or per channel (fp32, zrows x C), a
+// state of nheads 64 x 64 fp32 blocks.
+int mat_check(int dtype, int64_t nrows, int64_t H, const void* r, const void* k, const void* v,
+              const void* z, int z_mode, int64_t zrows, const float* s_in, const float* s_out,
+              int64_t nheads, const void* y, bool same_state_ok) {
+    if (dtype != WKV_F32 && dtype != WKV_BF16) return fail(WKV_ERR_DTYPE, "unknown dtype %d", dtype);
+    if (z_mode != WKV_MAT_DECAY_PER_CHANNEL && z_mode != WKV_MAT_DECAY_PER_TOKEN)
+        return fail(WKV_ERR_ARG, "unknown z_mode %d", z_mode);
+    const int64_t C = H * WKV_MAT_HEAD_DIM;
+    const int64_t io = nrows * C * int64_t(esize(dtype));
+    const int64_t st = nheads * WKV_MAT_HEAD_DIM * WKV_MAT_HEAD_DIM * 4;
+    const int64_t zb = z_mode == WKV_MAT_DECAY_PER_TOKEN ? io : zrows * C * 4;
+    const uintptr_t al = dtype == WKV_BF16 ? 8 : 16;
+    if (nrows > 0) {
+        if (!r || !k || !v || !z || !y) return fail(WKV_ERR_NULL, "r, k, v, z and y are required");
+        if (!aligned(r, al) || !aligned(k, al) || !aligned(v, al) || !aligned(y, al) ||
+            (z_mode == WKV_MAT_DECAY_PER_TOKEN && !aligned(z, al)) || !aligned(z, 4))
+            return fail(WKV_ERR_ARG, "r, k, v, z, y must be %d-byte aligned", int(al));
+    }
+    if ((s_in && !aligned(s_in, 4)) || (s_out && !aligned(s_out, 4)))
+        return fail(WKV_ERR_ARG, "the state arrays must be 4-byte aligned");
+    const Range ins[] = {rng("s_in", s_in, st), rng("r", r, io), rng("k", k, io), rng("v", v, io),
+                         rng("z", z, zb)};
+    const Range ry = rng("y", y, io);
+    for (const Range& ri : ins)
+        if (overlap(ry, ri)) return fail(WKV_ERR_ALIAS, "y overlaps %s", ri.name);
+    const Range so[] = {rng("s_out", s_out, st)};
+    if (int rc = check_state_aliasing(so, 1, ins, 5, same_state_ok)) return rc;
+    if (overlap(so[0], ry)) return fail(WKV_ERR_ALIAS, "s_out overlaps y");
+    return WKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wkv_mat_forward_path(int64_t B, int64_t T, int64_t H, int dtype, int path, const void* r,
+                         const void* k, const void* v, const void* z, int z_mode,
+                         const float* s_in, float* s_out, void* y, void* stream) {
+    if (B < 1 || H < 1 || T < 0)
+        return fail(WKV_ERR_SHAPE, "need B >= 1, T >= 0, H >= 1 (got B=%lld T=%lld H=%lld)",
+                    (long long)B, (long long)T, (long long)H);
+    if (path != WKV_MAT_PATH_AUTO && path != WKV_MAT_PATH_CHUNKED && path != WKV_MAT_PATH_TOKENWISE)
+        return fail(WKV_ERR_ARG, "unknown path %d", path);
+    if (path == WKV_MAT_PATH_CHUNKED && dtype == WKV_F32)
+        return fail(WKV_ERR_UNSUPPORTED, "the chunked matrix-core path takes bf16 storage only");
+    int64_t n = 0;
+    if (!mul3(B, T, H * WKV_MAT_HEAD_DIM, &n) || !mul3(n, 4, 1, &n) ||
+        !mul3(B * H, WKV_MAT_HEAD_DIM * WKV_MAT_HEAD_DIM, 4, &n))
+        return fail(WKV_ERR_SHAPE, "sizes too large");
+    if (B * H > 2147483647) return fail(WKV_ERR_SHAPE, "B*H too large for one launch");
+    if (int rc = mat_check(dtype, B * T, H, r, k, v, z, z_mode, 1, s_in, s_out, B * H, y, true))
+        return rc;
+    wkv::MatProblem pr;
+    pr.B = B;
+    pr.T = T;
+    pr.H = H;
+    pr.dtype = dtype;
+    pr.r = r;
+    pr.k = k;
+    pr.v = v;
+    pr.z = z;
+    pr.z_per_token = z_mode == WKV_MAT_DECAY_PER_TOKEN;
+    pr.s_in = s_in;
+    pr.s_out = s_out;
+    pr.y = y;
+    pr.path = path == WKV_MAT_PATH_TOKENWISE ? 1 : 0;
+    if (T == 0 && s_out == nullptr) return ok();
+    hipError_t e = wkv::launch_mat_forward(pr, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "matrix-state forward launch");
+}
+
+int wkv_mat_forward(int64_t B, int64_t T, int64_t H, int dtype, const void* r, const void* k,
+                    const void* v, const void* z, int z_mode, const float* s_in, float* s_out,
+                    void* y, void* stream) {
+    return wkv_mat_forward_path(B, T, H, dtype, WKV_MAT_PATH_AUTO, r, k, v, z, z_mode, s_in, s_out,
+                                y, stream);
+}
+
+int wkv_mat_step(int64_t L, int64_t S, int64_t H, int dtype, const void* r, const void* k,
+                 const void* v, const void* z, int z_mode, const float* s_in, float* s_out,
+                 void* y, void* stream) {
+    if (L < 1 || S < 1 || H < 1)
+        return fail(WKV_ERR_SHAPE, "need L, S, H >= 1 (got L=%lld S=%lld H=%lld)", (long long)L,
+                    (long long)S, (long long)H);
+    int64_t n = 0;
+    if (!mul3(L, S, H * WKV_MAT_HEAD_DIM * WKV_MAT_HEAD_DIM, &n) || !mul3(n, 4, 1, &n))
+        return fail(WKV_ERR_SHAPE, "sizes too large");
+    if ((L * S * H + 3) / 4 > 2147483647) return fail(WKV_ERR_SHAPE, "too many heads for one launch");
+    if (!s_in || !s_out) return fail(WKV_ERR_NULL, "s_in and s_out are required");
+    if (int rc = mat_check(dtype, L * S, H, r, k, v, z, z_mode, L, s_in, s_out, L * S * H, y, true))
+        return rc;
+    wkv::MatStepProblem pr;
+    pr.L = L;
+    pr.S = S;
+    pr.H = H;
+    pr.dtype = dtype;
+    pr.r = r;
+    pr.k = k;
+    pr.v = v;
+    pr.z = z;
+    pr.z_per_token = z_mode == WKV_MAT_DECAY_PER_TOKEN;
+    pr.s_in = s_in;
+    pr.s_out = s_out;
+    pr.y = y;
+    hipError_t e = wkv::launch_mat_step(pr, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "matrix-state step launch");
+}
+
 }  // extern "C"

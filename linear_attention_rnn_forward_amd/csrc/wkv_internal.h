@@ -84,6 +84,32 @@ struct ShiftProblem {
 };
 hipError_t launch_token_shift(const ShiftProblem& pr, hipStream_t stream);
 
+// Matrix-valued state WKV (RWKV-5/6): head dimension 64, C = 64 H.
+struct MatProblem {
+    int64_t B, T, H;
+    int dtype;
+    const void *r, *k, *v;   // [B,T,C] dtype
+    const void* z;           // [B,T,C] dtype when z_per_token, else [C] fp32
+    int z_per_token;
+    const float* s_in;       // [B,H,64,64] fp32 or null (zero state)
+    float* s_out;            // [B,H,64,64] fp32 or null
+    void* y;                 // [B,T,C] dtype
+    int path;                // 0: chunked matrix-core form (bf16), 1: token by token
+};
+hipError_t launch_mat_forward(const MatProblem& pr, hipStream_t stream);
+
+struct MatStepProblem {
+    int64_t L, S, H;
+    int dtype;
+    const void *r, *k, *v;   // [L,S,C] dtype
+    const void* z;           // [L,S,C] dtype when z_per_token, else [L,C] fp32
+    int z_per_token;
+    const float* s_in;       // [L,S,H,64,64] fp32
+    float* s_out;            // same shape; may equal s_in
+    void* y;                 // [L,S,C] dtype
+};
+hipError_t launch_mat_step(const MatStepProblem& pr, hipStream_t stream);
+
 int device_cu_count();  // CUs of the current device (cached per device)
 
 }  // namespace wkv

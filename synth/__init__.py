@@ -267,3 +267,114 @@ def decode_kv_column(wl: DecodeWorkload, layer: int, seq: int, channels) -> tupl
     tok = np.arange(wl.total_T, dtype=np.uint64)[:, None]
     ctr = decode_counter(wl, layer, seq, tok, ch)
     return philox_normal(ctr, STREAM_K, wl.seed), philox_normal(ctr, STREAM_V, wl.seed)
+
+
+# ----------------------------------------------------------------------------
+# Matrix-valued state (RWKV-5 Eagle / RWKV-6 Finch) workloads
+#
+# r, k, v, z [B,T,C] with C = 64 H.  The pages give no distributions for this
+# variant; the recipe keeps every term of unit scale: r ~ N(0, 1), v ~ N(0, 1),
+# k ~ N(0, 1/8) so that r.k over a 64-channel head has unit variance, and the
+# decay argument z = w_c + N(0, z_token_std) with w_c ~ U(z_lo, z_hi) per
+# channel (d = 1 / (1 + e^z) from 0.99 to 0.07 at the channel means, the span
+# of the RWKV-4 workloads' e^{-w}).  Eagle has no token term: z = w_c [C].
+# ----------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class MatWorkload:
+    """One matrix-state forward workload (decode: B = L * S rows of one token)."""
+    name: str
+    B: int
+    T: int
+    H: int
+    dtype: str                 # storage of r, k, v, y (and of z when per token)
+    seed: int
+    per_token_z: bool          # Finch (True) or Eagle (False)
+    z_range: tuple = (-5.0, 2.0)
+    z_token_std: float = 0.5
+    k_std: float = 0.125
+
+    def resized(self, **kw) -> "MatWorkload":
+        return replace(self, **kw)
+
+    @property
+    def C(self) -> int:
+        return 64 * self.H
+
+    @property
+    def elems(self) -> int:
+        return self.B * self.T * self.C
+
+
+MAT_MAIN = MatWorkload("wkv_mat_forward (Finch) B=16 T=4096 H=32 (C=2048) bf16 r/k/v/z/y, fp32 state",
+                       16, 4096, 32, "bf16", 21, True)
+MAT_EAGLE = MatWorkload("wkv_mat_forward (Eagle) B=16 T=4096 H=32 (C=2048) bf16 r/k/v/y, fp32 z and state",
+                        16, 4096, 32, "bf16", 22, False)
+
+
+@dataclass(frozen=True)
+class MatDecodeWorkload:
+    """wkv_mat_step over [L,S] rows of H heads, a pool of `pool` tokens of
+    inputs replayed in turn."""
+    name: str
+    L: int
+    S: int
+    H: int
+    dtype: str
+    seed: int
+    pool: int
+
+    @property
+    def C(self) -> int:
+        return 64 * self.H
+
+
+MAT_DECODE = MatDecodeWorkload("wkv_mat_step (Finch) L=32 S=64 H=64 (C=4096) fp32 r/k/v/z and state",
+                               32, 64, 64, "f32", 23, 4)
+
+
+@dataclass
+class MatInputs:
+    r: np.ndarray              # [B,T,C] fp32 values as stored (bf16-exact when bf16)
+    k: np.ndarray
+    v: np.ndarray
+    z: np.ndarray              # [B,T,C] (per token) or [C] fp32
+    bits: dict | None          # uint16 bits of r, k, v (and z when per token) for bf16
+
+
+def make_mat_inputs(wl: MatWorkload) -> MatInputs:
+    """Draw w_c, r, k, v, z for `wl` in a fixed order from default_rng(wl.seed)."""
+    rng = np.random.default_rng(wl.seed)
+    B, T, C = wl.B, wl.T, wl.C
+    wc = rng.uniform(wl.z_range[0], wl.z_range[1], size=C).astype(np.float32)
+    r = rng.standard_normal(size=(B, T, C), dtype=np.float32)
+    k = rng.standard_normal(size=(B, T, C), dtype=np.float32) * np.float32(wl.k_std)
+    v = rng.standard_normal(size=(B, T, C), dtype=np.float32)
+    if wl.per_token_z:
+        z = rng.standard_normal(size=(B, T, C), dtype=np.float32) * np.float32(wl.z_token_std)
+        z += wc
+    else:
+        z = wc
+    bits = None
+    if wl.dtype == "bf16":
+        bits = {}
+        names = ("r", "k", "v", "z") if wl.per_token_z else ("r", "k", "v")
+        arrs = {"r": r, "k": k, "v": v, "z": z}
+        for n in names:
+            bits[n] = f32_to_bf16_bits(arrs[n])
+            arrs[n] = bf16_bits_to_f32(bits[n])
+        r, k, v, z = arrs["r"], arrs["k"], arrs["v"], arrs["z"]
+    return MatInputs(r, k, v, z, bits)
+
+
+def make_mat_decode_pool(wl: MatDecodeWorkload) -> MatInputs:
+    """`pool` tokens of r, k, v, z for every row: arrays [pool, L, S, C] fp32."""
+    rng = np.random.default_rng(wl.seed)
+    shape = (wl.pool, wl.L, wl.S, wl.C)
+    wc = rng.uniform(-5.0, 2.0, size=(wl.L, 1, wl.C)).astype(np.float32)
+    r = rng.standard_normal(size=shape, dtype=np.float32)
+    k = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(0.125)
+    v = rng.standard_normal(size=shape, dtype=np.float32)
+    z = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(0.5) + wc
+    return MatInputs(r, k, v, z, None)

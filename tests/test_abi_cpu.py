@@ -32,13 +32,14 @@ def test_header_lists_the_boundary_calls():
     names = _declared("wkv.h")
     for n in ("wkv_forward", "wkv_step", "wkv_token_shift", "wkv_forward_workspace_size",
               "wkv_forward_gated", "wkv_step_gated", "wkv_backward", "wkv_backward_workspace_size",
-              "wkv_status_string", "wkv_last_error"):
+              "wkv_status_string", "wkv_last_error", "wkv_mat_forward", "wkv_mat_forward_path",
+              "wkv_mat_step"):
         assert n in names
 
 
 def test_abi_version_and_status_strings():
     L = wkv.lib()
-    assert L.wkv_abi_version() == 103
+    assert L.wkv_abi_version() == 104
     for code in range(0, -9, -1):
         assert L.wkv_status_string(code).decode()
     assert L.wkv_status_string(-100).decode() == "unknown status"
@@ -242,3 +243,51 @@ def test_backward_rejects_bad_arguments():
     assert call(ws=20 * G + 16) == -4              # misaligned
     assert call(ws=6 * G) == -5                    # workspace on gk
     assert call(C=1 << 26) == -2                   # sub-chunk offsets beyond 32 bits
+
+
+# ---------------------------------------------------------------------------
+# matrix-valued state calls: validation happens before any launch
+# ---------------------------------------------------------------------------
+
+def _mat_fwd(path=0, B=1, T=8, H=2, dtype=1, r=1 * G, k=2 * G, v=3 * G, z=4 * G, z_mode=1,
+             s_in=None, s_out=None, y=5 * G):
+    return wkv.lib().wkv_mat_forward_path(B, T, H, dtype, path, P(r), P(k), P(v), P(z), z_mode,
+                                          P(s_in), P(s_out), P(y), None)
+
+
+def _mat_step(L=2, S=3, H=2, dtype=0, r=1 * G, k=2 * G, v=3 * G, z=4 * G, z_mode=0,
+              s_in=6 * G, s_out=7 * G, y=5 * G):
+    return wkv.lib().wkv_mat_step(L, S, H, dtype, P(r), P(k), P(v), P(z), z_mode, P(s_in),
+                                  P(s_out), P(y), None)
+
+
+def test_mat_forward_rejects_bad_arguments():
+    L = wkv.lib()
+    assert _mat_fwd(dtype=5) == -3
+    assert _mat_fwd(B=0) == -2 and _mat_fwd(H=0) == -2 and _mat_fwd(T=-1) == -2
+    assert _mat_fwd(B=1 << 40, T=1 << 30) == -2
+    assert _mat_fwd(path=7) == -8
+    assert _mat_fwd(z_mode=3) == -8
+    assert _mat_fwd(path=1, dtype=0) == -7          # chunked form: bf16 storage only
+    assert _mat_fwd(r=None) == -1 and _mat_fwd(z=None) == -1 and _mat_fwd(y=None) == -1
+    assert _mat_fwd(k=2 * G + 2) == -8             # misaligned
+    assert _mat_fwd(y=3 * G + 64) == -5            # y overlaps v
+    assert b"y overlaps v" in L.wkv_last_error()
+    # the state out may be the state in, but may not overlap another input
+    assert _mat_fwd(s_in=6 * G, s_out=4 * G) == -5
+    assert _mat_fwd(s_in=6 * G, s_out=6 * G + 256) == -5
+    # T = 0 with no state wanted: nothing to do, nothing launched
+    assert _mat_fwd(T=0, r=None, k=None, v=None, z=None, y=None) == 0
+
+
+def test_mat_step_rejects_bad_arguments():
+    L = wkv.lib()
+    assert _mat_step(dtype=2) == -3
+    assert _mat_step(L=0) == -2 and _mat_step(S=0) == -2 and _mat_step(H=0) == -2
+    assert _mat_step(s_in=None) == -1 and _mat_step(s_out=None) == -1
+    assert _mat_step(v=None) == -1
+    assert _mat_step(z_mode=2) == -8
+    assert _mat_step(dtype=0, r=1 * G + 8) == -8   # fp32 needs 16-byte alignment
+    assert _mat_step(y=2 * G) == -5                # y is k
+    assert _mat_step(s_out=3 * G) == -5            # state out overlaps v
+    assert b"s_out overlaps v" in L.wkv_last_error()

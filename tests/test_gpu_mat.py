@@ -1,0 +1,268 @@
+"""GPU parity of the matrix-valued-state WKV (RWKV-5 Eagle / RWKV-6 Finch:
+S_t = diag(d_t) S_{t-1} + k_t v_t^T, y_t = r_t^T S_t, d_t = exp(-softplus(z_t)))
+against the fp64 oracle (oracle/matrix_state.py).
+
+Error measure: every output is a sum of terms r_t[i] k_s[i] (decay) v_s[j]
+(plus the carried state's), so the rounding error of any fp32 evaluation
+order, and the bf16 rounding of the chunked form's operands, are bounded by a
+multiple of eps times the sum of the terms' magnitudes, which the oracle
+returns with magnitude=True.  The measure is max |x - ref| / max(magnitude,
+1e-30).  Bars: 1e-4 for fp32 storage (token by token in fp32), 2e-2 for bf16
+storage (stored outputs rounded to bf16; the chunked form's operands are bf16
+with fp32 accumulation) -- the same bars as the RWKV-4 operator's.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import matrix_state as ms
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+FLOOR = 1e-30
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _wkv():
+    import linear_attention_rnn_forward_amd as wkv
+    return wkv
+
+
+def to_dev(x, dev, bits=None):
+    torch = _torch()
+    if bits is not None:
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+
+def host(t):
+    return t.float().cpu().numpy()
+
+
+def scaled_err(x, ref, mag):
+    x = np.asarray(x, dtype=np.float64)
+    if x.size == 0:
+        return 0.0
+    return float(np.max(np.abs(x - ref) / np.maximum(mag, FLOOR)))
+
+
+def dev_inputs(x, wl, dev):
+    b = x.bits or {}
+    r = to_dev(x.r, dev, b.get("r"))
+    k = to_dev(x.k, dev, b.get("k"))
+    v = to_dev(x.v, dev, b.get("v"))
+    z = to_dev(x.z, dev, b.get("z")) if wl.per_token_z else to_dev(x.z, dev)
+    return r, k, v, z
+
+
+def run_and_check(x, wl, dev, path, state=None, label=""):
+    torch = _torch()
+    r, k, v, z = dev_inputs(x, wl, dev)
+    s_in = None if state is None else to_dev(state, dev)
+    y, s_out = _wkv().mat_forward(r, k, v, z, state=s_in, return_state=True, path=path)
+    torch.cuda.synchronize()
+    y_ref, s_ref = ms.forward(x.r, x.k, x.v, x.z, state=state)
+    y_mag, s_mag = ms.forward(x.r, x.k, x.v, x.z, state=state, magnitude=True)
+    yh, sh = host(y), host(s_out)
+    assert np.all(np.isfinite(yh)) and np.all(np.isfinite(sh)), label
+    ey = scaled_err(yh, y_ref, y_mag)
+    es = scaled_err(sh, s_ref, s_mag)
+    tol = TOL[wl.dtype]
+    assert ey <= tol, f"{label} path={path}: y scaled err {ey:.3e} > {tol}"
+    assert es <= tol, f"{label} path={path}: state scaled err {es:.3e} > {tol}"
+    return yh, sh, ey, es
+
+
+SMALL = synth.MAT_MAIN.resized(B=2, T=53, H=2)       # 3 whole chunks and a ragged 5
+
+
+@pytest.mark.parametrize("dtype,per_token,path", [
+    ("bf16", True, "chunked"), ("bf16", False, "chunked"), ("bf16", True, "tokenwise"),
+    ("f32", True, "tokenwise"), ("f32", False, "tokenwise"), ("f32", True, "auto"),
+    ("bf16", True, "auto"),
+])
+def test_forward_parity(device, dtype, per_token, path):
+    wl = SMALL.resized(dtype=dtype, per_token_z=per_token, seed=31 + per_token)
+    x = synth.make_mat_inputs(wl)
+    _, _, ey, es = run_and_check(x, wl, device, path, label=f"{dtype} per_token={per_token}")
+    print(f"y err {ey:.2e} state err {es:.2e}")
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (1, 16, 1), (3, 17, 3), (1, 100, 4), (2, 15, 1)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_shapes(device, shape, dtype):
+    B, T, H = shape
+    wl = SMALL.resized(B=B, T=T, H=H, dtype=dtype, seed=40 + T)
+    x = synth.make_mat_inputs(wl)
+    run_and_check(x, wl, device, "auto", label=f"{shape}")
+
+
+@pytest.mark.parametrize("dtype,path", [("bf16", "chunked"), ("f32", "tokenwise")])
+def test_split_and_resume(device, dtype, path):
+    """Two calls joined through the state equal one run (cut inside a chunk)."""
+    torch = _torch()
+    wl = SMALL.resized(B=2, T=70, H=2, dtype=dtype, seed=50)
+    x = synth.make_mat_inputs(wl)
+    r, k, v, z = dev_inputs(x, wl, device)
+    cut = 21
+    y1, s1 = _wkv().mat_forward(r[:, :cut].contiguous(), k[:, :cut].contiguous(),
+                                v[:, :cut].contiguous(), z[:, :cut].contiguous(),
+                                return_state=True, path=path)
+    y2, s2 = _wkv().mat_forward(r[:, cut:].contiguous(), k[:, cut:].contiguous(),
+                                v[:, cut:].contiguous(), z[:, cut:].contiguous(), state=s1,
+                                return_state=True, path=path)
+    torch.cuda.synchronize()
+    y_ref, s_ref = ms.forward(x.r, x.k, x.v, x.z)
+    y_mag, s_mag = ms.forward(x.r, x.k, x.v, x.z, magnitude=True)
+    y = np.concatenate([host(y1), host(y2)], axis=1)
+    assert scaled_err(y, y_ref, y_mag) <= TOL[dtype]
+    assert scaled_err(host(s2), s_ref, s_mag) <= TOL[dtype]
+
+
+def test_empty_sequence_passes_the_state_through(device):
+    torch = _torch()
+    wkv = _wkv()
+    B, H = 2, 3
+    e = torch.empty((B, 0, 64 * H), dtype=torch.bfloat16, device=device)
+    s_in = torch.randn((B, H, 64, 64), device=device)
+    _, s_out = wkv.mat_forward(e, e, e, torch.zeros(64 * H, device=device), state=s_in,
+                               return_state=True)
+    _, s_zero = wkv.mat_forward(e, e, e, torch.zeros(64 * H, device=device), return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(s_out, s_in)
+    assert torch.count_nonzero(s_zero).item() == 0
+
+
+def test_extreme_decay_mixes_chunk_forms(device):
+    """A channel whose decay empties it within a chunk makes that chunk run
+    token by token inside the chunked kernel; its neighbours stay chunked.
+    Also d = 1 (no decay) over many tokens: plain causal linear attention."""
+    wl = SMALL.resized(B=1, T=80, H=2, seed=60)
+    x = synth.make_mat_inputs(wl)
+    z = x.z.copy()
+    z[0, 16:32, 5] = 40.0          # chunk 1: span 16 * 40 > 80
+    z[0, 70:75, 100] = 95.0        # d underflows to 0 inside the last chunk
+    x.z = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(z))
+    x.bits["z"] = synth.f32_to_bf16_bits(z)
+    run_and_check(x, wl, device, "chunked", label="mixed")
+    wl2 = SMALL.resized(B=1, T=300, H=1, seed=61)
+    x2 = synth.make_mat_inputs(wl2)
+    zc = np.full_like(x2.z, -30.0)
+    x2.bits["z"] = synth.f32_to_bf16_bits(zc)
+    x2.z = synth.bf16_bits_to_f32(x2.bits["z"])
+    run_and_check(x2, wl2, device, "chunked", label="no decay")
+
+
+def test_state_input_and_in_place_output(device):
+    torch = _torch()
+    wl = SMALL.resized(B=2, T=40, H=2, seed=70)
+    x = synth.make_mat_inputs(wl)
+    s0 = np.random.default_rng(71).normal(0, 0.5, (2, 2, 64, 64)).astype(np.float32)
+    run_and_check(x, wl, device, "chunked", state=s0, label="state in")
+    r, k, v, z = dev_inputs(x, wl, device)
+    s = to_dev(s0, device)
+    _wkv().mat_forward(r, k, v, z, state=s, state_out=s)     # in place
+    torch.cuda.synchronize()
+    s_ref = ms.forward(x.r, x.k, x.v, x.z, state=s0)[1]
+    s_mag = ms.forward(x.r, x.k, x.v, x.z, state=s0, magnitude=True)[1]
+    assert scaled_err(host(s), s_ref, s_mag) <= TOL["bf16"]
+
+
+def test_deterministic(device):
+    torch = _torch()
+    wl = SMALL.resized(B=2, T=100, H=3, seed=80)
+    x = synth.make_mat_inputs(wl)
+    r, k, v, z = dev_inputs(x, wl, device)
+    y1 = _wkv().mat_forward(r, k, v, z)
+    y2 = _wkv().mat_forward(r, k, v, z)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+# ---------------------------------------------------------------------------
+# decode step
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,per_token", [("f32", True), ("f32", False), ("bf16", True),
+                                             ("bf16", False)])
+def test_step_chain_parity(device, dtype, per_token):
+    """Six chained steps over [L=2, S=3, H=2] rows, state updated in place,
+    against the oracle's step."""
+    torch = _torch()
+    rng = np.random.default_rng(90 + per_token)
+    Ln, S, H = 2, 3, 2
+    C = 64 * H
+    st = rng.normal(0, 0.3, (Ln, S, H, 64, 64))
+    st_dev = to_dev(st, device)
+    st_ref = st.copy()
+    mag = np.abs(st)
+    zc = rng.uniform(-5, 2, (Ln, C)).astype(np.float32)
+    for t in range(6):
+        arrs = {n: rng.normal(0, 0.125 if n == "k" else 1.0, (Ln, S, C)).astype(np.float32)
+                for n in ("r", "k", "v")}
+        arrs["z"] = (rng.normal(0, 0.5, (Ln, S, C)) + zc[:, None, :]).astype(np.float32)
+        bits = {}
+        if dtype == "bf16":
+            for n in arrs:
+                bits[n] = synth.f32_to_bf16_bits(arrs[n])
+                arrs[n] = synth.bf16_bits_to_f32(bits[n])
+        r, k, v = (to_dev(arrs[n], device, bits.get(n)) for n in ("r", "k", "v"))
+        if per_token:
+            z_dev, z_ref = to_dev(arrs["z"], device, bits.get("z")), arrs["z"]
+        else:
+            z_dev, z_ref = to_dev(zc, device), np.broadcast_to(zc[:, None, :], (Ln, S, C))
+        y, _ = _wkv().mat_step(st_dev, r, k, v, z_dev, inplace=True)
+        torch.cuda.synchronize()
+        y_ref, st_ref = ms.step(st_ref, arrs["r"], arrs["k"], arrs["v"], z_ref)
+        y_mag, mag = ms.step(mag, np.abs(arrs["r"]), np.abs(arrs["k"]), np.abs(arrs["v"]), z_ref)
+        assert scaled_err(host(y), y_ref, y_mag) <= TOL[dtype], t
+    assert scaled_err(host(st_dev), st_ref, mag) <= TOL["f32"]
+
+
+def test_step_chain_equals_forward(device):
+    """fp32: T decode steps reproduce the token-by-token forward to 1e-5 of
+    the magnitude scale (the two differ only in where the state is stored)."""
+    torch = _torch()
+    wl = SMALL.resized(B=3, T=24, H=2, dtype="f32", seed=100)
+    x = synth.make_mat_inputs(wl)
+    r, k, v, z = dev_inputs(x, wl, device)
+    y_f, s_f = _wkv().mat_forward(r, k, v, z, return_state=True, path="tokenwise")
+    st = torch.zeros((1, 3, 2, 64, 64), device=device)
+    ys = []
+    for t in range(wl.T):
+        y_t, _ = _wkv().mat_step(st, r[None, :, t].contiguous(), k[None, :, t].contiguous(),
+                                 v[None, :, t].contiguous(), z[None, :, t].contiguous(), inplace=True)
+        ys.append(host(y_t)[0])
+    torch.cuda.synchronize()
+    y_mag, s_mag = ms.forward(x.r, x.k, x.v, x.z, magnitude=True)
+    y_s = np.stack(ys, axis=1)
+    assert scaled_err(y_s, host(y_f), y_mag) <= 1e-5
+    assert scaled_err(host(st)[0], host(s_f), s_mag) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# the full-size workload, in the launch bench.py times, on sampled heads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wl", [synth.MAT_MAIN, synth.MAT_EAGLE], ids=["finch", "eagle"])
+def test_full_size_sampled_heads(device, wl):
+    torch = _torch()
+    x = synth.make_mat_inputs(wl)
+    r, k, v, z = dev_inputs(x, wl, device)
+    y, s = _wkv().mat_forward(r, k, v, z, return_state=True)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (7, 13), (15, 31)):
+        cs = slice(64 * h, 64 * h + 64)
+        zz = x.z[b:b + 1, :, cs] if wl.per_token_z else x.z[cs]
+        args = (x.r[b:b + 1, :, cs], x.k[b:b + 1, :, cs], x.v[b:b + 1, :, cs], zz)
+        y_ref, s_ref = ms.forward(*args)
+        y_mag, s_mag = ms.forward(*args, magnitude=True)
+        ey = scaled_err(host(y[b:b + 1, :, cs]), y_ref, y_mag)
+        es = scaled_err(host(s[b:b + 1, h:h + 1]), s_ref, s_mag)
+        print(f"head ({b},{h}): y err {ey:.2e} state err {es:.2e}")
+        assert ey <= TOL["bf16"] and es <= TOL["bf16"], (b, h, ey, es)
