@@ -15,7 +15,10 @@ Other workloads (--workload): tiny, small_lm, long_ctx (wkv_forward),
 bf16_main_gated (the default workload through wkv_forward_gated, the
 receptance gate fused), bf16_main_backward (wkv_backward over the default
 workload's shape; a step is its three launches), decode (wkv_step over [32,256,4096] fp32),
-token_shift (bf16, B=16 T=4096 C=2048).
+token_shift (bf16, B=16 T=4096 C=2048), mat_main / mat_eagle (the
+matrix-valued-state operator of RWKV-6 Finch / RWKV-5 Eagle, wkv_mat_forward
+over B=16 T=4096 and 32 heads of 64, bf16), mat_decode (wkv_mat_step over
+32 layers x 64 sequences x 64 heads, fp32).
 """
 import argparse
 import hashlib
@@ -32,10 +35,27 @@ METRIC = "WKV forward tokens·channels/s and achieved HBM GB/s (% of peak) at 1 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash() -> str:
+# The sources that define each workload's kernels and their launch geometry
+# (the C ABI layer only validates and dispatches).
+_COMMON_SOURCES = ["wkv_device.h", "wkv_internal.h"]
+_FORWARD_SOURCES = ["wkv_forward.hip"] + _COMMON_SOURCES
+KERNEL_SOURCES = {
+    "tiny": _FORWARD_SOURCES, "small_lm": _FORWARD_SOURCES, "bf16_main": _FORWARD_SOURCES,
+    "bf16_main_gated": _FORWARD_SOURCES, "long_ctx": _FORWARD_SOURCES,
+    "bf16_main_backward": ["wkv_backward.hip"] + _COMMON_SOURCES,
+    "decode": ["wkv_step.hip"] + _COMMON_SOURCES,
+    "token_shift": ["wkv_token_shift.hip"] + _COMMON_SOURCES,
+    "mat_main": ["wkv_mat.hip"] + _COMMON_SOURCES, "mat_eagle": ["wkv_mat.hip"] + _COMMON_SOURCES,
+    "mat_decode": ["wkv_mat.hip"] + _COMMON_SOURCES,
+}
+
+
+def kernel_source_hash(workload: str) -> str:
+    """Hash of the kernel sources of `workload` (every source when unknown)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_rnn_forward_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    names = KERNEL_SOURCES.get(workload) or sorted(os.listdir(csrc))
+    for name in sorted(names):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -51,7 +71,7 @@ def measured_traffic(workload: str):
     except (OSError, ValueError):
         return None
     entry = data.get(workload)
-    if not entry or entry.get("source_hash") != kernel_source_hash():
+    if not entry or entry.get("source_hash") != kernel_source_hash(workload):
         return None
     return entry.get("traffic_bytes_per_launch")
 
@@ -285,6 +305,140 @@ class DecodeBench:
                 "kind": "oracle", "sample": f"10 steps over 4 of the 32 layers ({units} states)"}
 
 
+class MatBench:
+    """wkv_mat_forward (matrix-valued state, RWKV-5/6) over a [B,T,C] batch:
+    r, k, v (and z per token) read, y written; no state in or out."""
+
+    def __init__(self, wl, dev):
+        import numpy as np
+        import torch
+
+        import linear_attention_rnn_forward_amd as wkv
+        import synth
+        self.wl = wl
+        self.wkv = wkv
+        x = synth.make_mat_inputs(wl)
+        self.host = x
+        if wl.dtype == "bf16":
+            dv = lambda n: torch.from_numpy(x.bits[n].view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            dv = lambda n: torch.from_numpy(getattr(x, n)).to(dev)
+        self.r, self.k, self.v = dv("r"), dv("k"), dv("v")
+        self.z = dv("z") if wl.per_token_z else torch.from_numpy(x.z).to(dev)
+        self.y = torch.empty_like(self.k)
+        es = 2 if wl.dtype == "bf16" else 4
+        self.units = wl.B * wl.T * wl.C
+        self.alg_bytes = (5 if wl.per_token_z else 4) * es * self.units + \
+            (0 if wl.per_token_z else 4 * wl.C)
+        self.dtype = "f32"         # fp32 accumulation of bf16 matrix-core products
+
+    def step(self):
+        self.wkv.mat_forward(self.r, self.k, self.v, self.z, out=self.y)
+
+    def check_replay(self):
+        import torch
+        y = self.y.clone()
+        self.step()
+        torch.cuda.synchronize()
+        if not torch.equal(y, self.y):
+            raise RuntimeError("graph replay of wkv_mat_forward differs from the eager launch")
+
+    def config(self):
+        return {"workload": self.wl.name, "B": self.wl.B, "T": self.wl.T, "H": self.wl.H,
+                "C": self.wl.C, "head_dim": 64, "io_dtype": self.wl.dtype, "state_dtype": "f32"}
+
+    def cpu_baseline(self):
+        from threadpoolctl import threadpool_limits
+
+        from oracle import matrix_state as ms
+        x = self.host
+        Ts = 512   # the first 512 tokens of every batch row and head
+        z = x.z[:, :Ts] if self.wl.per_token_z else x.z
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            ms.forward(x.r[:, :Ts], x.k[:, :Ts], x.v[:, :Ts], z)
+            dt = time.perf_counter() - t0
+        n = self.wl.B * Ts * self.wl.C
+        return {"value": n / dt, "unit": "tokens·channels/s", "cores": 1, "kind": "oracle",
+                "sample": f"the first {Ts} tokens of every batch row and head ({n} tokens*channels), "
+                          f"{dt:.2f} s"}
+
+
+class MatDecodeBench:
+    """One wkv_mat_step over [L,S] rows of H heads per step; r, k, v, z of
+    `pool` distinct tokens resident in HBM and used in turn; the state starts
+    at zero and the warm-up steps fill it."""
+
+    def __init__(self, dev):
+        import torch
+
+        import linear_attention_rnn_forward_amd as wkv
+        import synth
+        wl = synth.MAT_DECODE
+        self.wl = wl
+        self.wkv = wkv
+        x = synth.make_mat_decode_pool(wl)
+        self.pool = {n: torch.from_numpy(getattr(x, n)).to(dev) for n in ("r", "k", "v", "z")}
+        self.st = torch.zeros((wl.L, wl.S, wl.H, 64, 64), device=dev)
+        self.y = torch.empty((wl.L, wl.S, wl.C), device=dev)
+        self.i = 0
+        self.units = wl.L * wl.S * wl.C
+        # the state read and written (8 B per element), r, k, v, z read and y written
+        self.alg_bytes = 8 * wl.L * wl.S * wl.H * 64 * 64 + 5 * 4 * self.units
+        self.dtype = "f32"
+
+    def step(self):
+        j = self.i % self.wl.pool
+        p = self.pool
+        self.wkv.mat_step(self.st, p["r"][j], p["k"][j], p["v"][j], p["z"][j], out=self.y,
+                          inplace=True)
+        self.i += 1
+
+    def begin_capture(self):
+        self.i_capture = self.i
+
+    def snapshot(self):
+        self.st_before = self.st.clone()
+
+    def check_replay(self):
+        """The replayed steps, re-run eagerly from the saved state, give the
+        same state and output, bit for bit."""
+        import torch
+        st = self.st_before
+        p = self.pool
+        for n in range(self.i - self.i_capture):
+            j = (self.i_capture + n) % self.wl.pool
+            y, st = self.wkv.mat_step(st, p["r"][j], p["k"][j], p["v"][j], p["z"][j], inplace=True)
+        torch.cuda.synchronize()
+        if not (torch.equal(y, self.y) and torch.equal(st, self.st)):
+            raise RuntimeError("graph replay of the matrix-state decode differs from eager launches")
+        self.st_before = None
+
+    def config(self):
+        wl = self.wl
+        return {"workload": wl.name, "L": wl.L, "S": wl.S, "H": wl.H, "C": wl.C, "head_dim": 64,
+                "io_dtype": "f32", "state_dtype": "f32"}
+
+    def cpu_baseline(self):
+        import numpy as np
+        from threadpoolctl import threadpool_limits
+
+        from oracle import matrix_state as ms
+        wl = self.wl
+        rows = 8   # 8 of the 2048 (layer, sequence) rows, every head, 4 steps
+        p = {n: self.pool[n][:, 0, :rows].cpu().numpy() for n in self.pool}
+        st = np.zeros((rows, wl.H, 64, 64))
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            for j in range(wl.pool):
+                _, st = ms.step(st, p["r"][j], p["k"][j], p["v"][j], p["z"][j])
+            dt = time.perf_counter() - t0
+        n = wl.pool * rows * wl.C
+        return {"value": n / dt, "unit": "tokens·channels/s", "cores": 1, "kind": "oracle",
+                "sample": f"{wl.pool} steps of {rows} of the {wl.L * wl.S} rows ({n} tokens*channels), "
+                          f"{dt:.2f} s"}
+
+
 class CopyBench:
     """A plain device copy of 2 x 256 MiB (torch's copy kernel): known bytes, used
     to scale the HBM counters (FETCH_SIZE, WRITE_SIZE) of the WKV kernels."""
@@ -364,7 +518,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="bf16_main",
                     choices=["tiny", "small_lm", "bf16_main", "bf16_main_gated", "bf16_main_backward",
-                             "long_ctx", "decode", "token_shift", "hbm_copy"])
+                             "long_ctx", "decode", "token_shift", "hbm_copy", "mat_main",
+                             "mat_eagle", "mat_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch each step from Python instead of replaying a HIP graph of the steps")
@@ -389,6 +544,12 @@ def main():
         bench = BackwardBench(synth.BF16_MAIN, dev)
     elif args.workload == "decode":
         bench = DecodeBench(dev)
+    elif args.workload == "mat_main":
+        bench = MatBench(synth.MAT_MAIN, dev)
+    elif args.workload == "mat_eagle":
+        bench = MatBench(synth.MAT_EAGLE, dev)
+    elif args.workload == "mat_decode":
+        bench = MatDecodeBench(dev)
     elif args.workload == "hbm_copy":
         bench = CopyBench(dev)
     else:

@@ -27,6 +27,12 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
 SOURCES = ["wkv_api.hip", "wkv_forward.hip", "wkv_step.hip", "wkv_token_shift.hip", "wkv_session.hip", "wkv_backward.hip", "wkv_mat.hip"]
 
 
+# Per-source flags: the matrix-state kernels keep their MFMA accumulators in
+# ordinary VGPRs (the state is scaled by the vector units between products;
+# accumulator registers would add a copy each way every chunk).
+EXTRA_FLAGS = {"wkv_mat.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -52,7 +58,8 @@ def build(verbose: bool = False) -> None:
     jobs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        jobs.append(([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+        jobs.append(([HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj],
+                     obj))
     synth_obj = os.path.join(objdir, "philox_fill.o")
     jobs.append(([HIPCC, *FLAGS, "-c", SYNTH_SRC, "-o", synth_obj], synth_obj))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:

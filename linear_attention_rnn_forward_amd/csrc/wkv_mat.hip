@@ -12,20 +12,21 @@
 // head); wave w owns value columns [16w, 16w + 16) of the state, which stays
 // in fp32 registers in the accumulator layout of a 16x16 MFMA tile (lane l
 // holds rows 4(l/16) .. 4(l/16)+3 of column l%16 of each of the four 16-row
-// blocks).  The tokens are taken in chunks of 16.  With Lam_t[i] the sum of
-// log d over the chunk's tokens up to and including t, the recurrence
+// blocks).  The tokens are taken in chunks of 16.  With D_t[i] the product of
+// the decays d[i] of the chunk's tokens up to and including t, the recurrence
 // unrolls over a chunk into
 //
-//   y_t = (r_t e^{Lam_t})^T S_0 + sum_{s<=t} [sum_i r_t[i] e^{Lam_t[i]} k_s[i] e^{-Lam_s[i]}] v_s
-//   S_16 = diag(e^{Lam_15}) S_0 + sum_s (k_s e^{Lam_15 - Lam_s}) v_s^T
+//   y_t = (r_t D_t)^T S_0 + sum_{s<=t} [sum_i r_t[i] D_t[i] k_s[i] / D_s[i]] v_s
+//   S_16 = diag(D_15) S_0 + sum_s (k_s D_15 / D_s) v_s^T
 //
 // and every sum over i or s is a dense 16x16x16 product on the matrix cores
 // (bf16 operands, fp32 accumulation): the read-out of the carried state, the
 // chunk's score matrix, its application to the values, and the state update.
-// The factor e^{-Lam_s} is bounded by the chunk's total decay span; a chunk in
-// which some channel's span exceeds kSpanMax (a decay of e^{-80} within 16
-// tokens) is run token by token instead, on the same registers, in fp32.  fp32
-// storage always takes that exact token-by-token form.
+// The prefix products run across the 16 lanes of a row with DPP.  The factor
+// 1/D_s is bounded by the chunk's total decay; a chunk in which some channel
+// decays by more than e^{-80} is run token by token instead, on the same
+// registers, in fp32.  fp32 storage always takes that exact token-by-token
+// form.
 //
 // Decode step: one wave per (row, head); lane j holds column j of the state,
 // which is read, updated and written once: an HBM stream of 8 bytes per state
@@ -38,8 +39,8 @@ namespace {
 
 constexpr int kN = 64;            // head dimension (the page's)
 constexpr int kCT = 16;           // tokens per chunk
-constexpr float kSpanMax = 80.0f; // largest -Lam_15 of a chunk for the factorised form
-constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kMinChunkDecay = 1.8e-35f;  // e^{-80}: the smallest decay over a chunk that
+                                           // the factorised form takes (1/D stays <= e^{80})
 constexpr int kRowPad = kN + 4;   // bf16 row stride of [token][channel] tiles in LDS
 constexpr int kColPad = kCT + 4;  // bf16 row stride of [channel][token] tiles in LDS
 
@@ -49,33 +50,26 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int mat_wave() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int mat_lane() { return threadIdx.x & 63; }
 
-// -softplus(z) = -(max(z, 0) + log1p(e^{-|z|})), with log1p(x) = ln(u) x / (u - 1)
-// for u = 1 + x != 1 (a few ulp where a plain ln(1 + x) would lose x).
-__device__ __forceinline__ float neg_softplus(float z) {
-    const float x = __builtin_amdgcn_exp2f(-__builtin_fabsf(z) * kLog2e);
-    const float u = 1.0f + x;
-    const float l = u == 1.0f ? x
-                              : __builtin_amdgcn_logf(u) * kLn2 * x * __builtin_amdgcn_rcpf(u - 1.0f);
-    return -(max_num(z, 0.0f) + l);
-}
-
 __device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
-// x + (x of the lane n below, within the 16-lane row; 0 for the first n lanes)
+// x * (x of the lane n below, within the 16-lane row; 1 for the first n lanes)
 template <int SH>
-__device__ __forceinline__ float row_shr_add(float x) {
-    const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 | SH, 0xf, 0xf, false);
-    return x + __int_as_float(y);
+__device__ __forceinline__ float row_shr_mul(float x) {
+    const int y = __builtin_amdgcn_update_dpp(0x3f800000, __float_as_int(x), 0x110 | SH, 0xf, 0xf, false);
+    return x * __int_as_float(y);
 }
 
-// inclusive prefix sum over the 16 lanes of each row
-__device__ __forceinline__ float row_scan(float x) {
-    x = row_shr_add<1>(x);
-    x = row_shr_add<2>(x);
-    x = row_shr_add<4>(x);
-    x = row_shr_add<8>(x);
+// inclusive prefix product over the 16 lanes of each row
+__device__ __forceinline__ float row_prod(float x) {
+    x = row_shr_mul<1>(x);
+    x = row_shr_mul<2>(x);
+    x = row_shr_mul<4>(x);
+    x = row_shr_mul<8>(x);
     return x;
 }
+
+// d = exp(-softplus(z)) = 1 / (1 + e^z): 1 for z = -inf, 0 once e^z overflows
+__device__ __forceinline__ float decay_of(float z) { return __builtin_amdgcn_rcpf(1.0f + exp_f(z)); }
 
 // value of lane 15 of this lane's row
 __device__ __forceinline__ float row_last(float x) {
@@ -142,205 +136,318 @@ __device__ __forceinline__ void store_one(void* base, int64_t e, float x) {
 }
 
 struct MatShared {
-    // factorised-form operands, double-buffered by chunk parity
-    uint16_t rq[2][kCT][kRowPad];   // r_t[i] e^{Lam_t[i]}
-    uint16_t kq[2][kCT][kRowPad];   // k_s[i] e^{-Lam_s[i]}
-    uint16_t kdt[2][kN][kColPad];   // k_s[i] e^{Lam_15[i] - Lam_s[i]}, [i][s]
+    // operands of the chunked form, double-buffered by chunk parity
+    uint16_t rq[2][kCT][kRowPad];   // r_t[i] D_t[i]
+    uint16_t kq[2][kCT][kRowPad];   // k_s[i] / D_s[i]
+    uint16_t kdt[2][kN][kColPad];   // k_s[i] D_15[i] / D_s[i], [i][s]
     uint16_t vt[2][kN][kColPad];    // v_s[j], [j][s]
-    float el[2][kN];                // e^{Lam_15[i]}
-    // token-by-token form: r, k, d, v of the chunk in fp32
-    float rf[kCT][kN], kf[kCT][kN], df[kCT][kN], vf[kCT][kN];
-    int exact_chunk;                // index of the last chunk that must run token by token
+    float el[2][kN];                // D_15[i]
+    // fp32 storage (token-by-token form only): r, k, d, v of the chunk, rows
+    // padded so that a wave's 16-byte writes spread over the banks
+    float rf[2][kCT][kN + 4], kf[2][kCT][kN + 4], df[2][kCT][kN + 4], vf[2][kCT][kN + 4];
+    int exact_chunk[2];             // chunk of this parity that must run token by token
 };
 
-// The inputs of one thread for one chunk: four channels of one token.
+// The inputs of one producer thread for one chunk: four channels of one token.
 template <int DT>
 struct ChunkIn {
     typename Quad<DT>::Raw r, k, v, z;
 };
 
+// Unconditional loads (a branch around them would make every later use wait
+// for all outstanding loads); the caller clamps the token to a valid one and
+// masks the padding tokens afterwards.
 template <int DT, bool PER_TOKEN_Z>
-__device__ __forceinline__ void load_chunk(ChunkIn<DT>& in, const MatProblem& pr, int64_t e, bool live) {
+__device__ __forceinline__ void load_chunk(ChunkIn<DT>& in, const MatProblem& pr, int64_t e) {
     using Q = Quad<DT>;
-    if (live) {
-        in.r = Q::load(pr.r, e);
-        in.k = Q::load(pr.k, e);
-        in.v = Q::load(pr.v, e);
-        if constexpr (PER_TOKEN_Z) in.z = Q::load(pr.z, e);
+    in.r = Q::load(pr.r, e);
+    in.k = Q::load(pr.k, e);
+    in.v = Q::load(pr.v, e);
+    if constexpr (PER_TOKEN_Z) in.z = Q::load(pr.z, e);
+}
+
+__device__ __forceinline__ float4 keep_if(bool live, float4 x) {
+    return live ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+__device__ __forceinline__ uint2 keep_if(bool live, uint2 x) { return live ? x : make_uint2(0u, 0u); }
+// padding tokens get z = -inf: d = 1, no decay
+__device__ __forceinline__ float4 pad_z(bool live, float4 x) {
+    const float ni = -__builtin_inff();
+    return live ? x : make_float4(ni, ni, ni, ni);
+}
+__device__ __forceinline__ uint2 pad_z(bool live, uint2 x) {
+    return live ? x : make_uint2(0xff80ff80u, 0xff80ff80u);
+}
+
+// v_s[j] of four channels of one token into the [channel][token] tile: bf16
+// storage is written as stored, fp32 is rounded.
+template <int DT>
+__device__ __forceinline__ void store_vt(uint16_t (*vt)[kColPad], int i0, int tt,
+                                         typename Quad<DT>::Raw raw, const float (&vv)[4]) {
+    if constexpr (DT == kBF16) {
+        vt[i0 + 0][tt] = uint16_t(raw.x & 0xffffu);
+        vt[i0 + 1][tt] = uint16_t(raw.x >> 16);
+        vt[i0 + 2][tt] = uint16_t(raw.y & 0xffffu);
+        vt[i0 + 3][tt] = uint16_t(raw.y >> 16);
     } else {
-        in.r = Q::zero();
-        in.k = Q::zero();
-        in.v = Q::zero();
-        if constexpr (PER_TOKEN_Z) in.z = Q::zero();
+#pragma unroll
+        for (int c = 0; c < 4; c++) vt[i0 + c][tt] = uint16_t(bf16_word(vv[c], 0.0f) & 0xffffu);
     }
 }
 
+__device__ __forceinline__ int chunk_tokens(int64_t T, int64_t ch) {
+    const int64_t left = T - ch * kCT;  // <= 0 past the last chunk
+    return left < kCT ? (left > 0 ? int(left) : 0) : kCT;
+}
+
+// Producer: the operands of chunk ch into LDS buffer ch & 1.  Thread (tt, i0)
+// handles token tt of the chunk and channels i0 .. i0+3.  Chunks past the last
+// one are all padding (no decay, zero keys).
 template <int DT, bool PER_TOKEN_Z, bool EXACT_ONLY>
-__global__ __launch_bounds__(256) void mat_forward_kernel(MatProblem pr) {
+__device__ __forceinline__ void produce_chunk(MatShared& sh, int tt, int i0, int lane,
+                                              const ChunkIn<DT>& cur, const float (&dc)[4],
+                                              int64_t T, int64_t ch) {
     using Q = Quad<DT>;
+    const int buf = int(ch & 1);
+    const bool live = tt < chunk_tokens(T, ch);
+    float rv[4], kv[4], vv[4], dcy[4];
+    const typename Q::Raw vraw = keep_if(live, cur.v);
+    Q::unpack(keep_if(live, cur.r), rv);
+    Q::unpack(keep_if(live, cur.k), kv);
+    Q::unpack(vraw, vv);
+    if constexpr (PER_TOKEN_Z) {
+        float zv[4];
+        Q::unpack(pad_z(live, cur.z), zv);
+#pragma unroll
+        for (int c = 0; c < 4; c++) dcy[c] = decay_of(zv[c]);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; c++) dcy[c] = live ? dc[c] : 1.0f;
+    }
+    if constexpr (EXACT_ONLY) {
+        // the token-by-token form's inputs
+        *reinterpret_cast<float4*>(&sh.rf[buf][tt][i0]) = make_float4(rv[0], rv[1], rv[2], rv[3]);
+        *reinterpret_cast<float4*>(&sh.kf[buf][tt][i0]) = make_float4(kv[0], kv[1], kv[2], kv[3]);
+        *reinterpret_cast<float4*>(&sh.df[buf][tt][i0]) = make_float4(dcy[0], dcy[1], dcy[2], dcy[3]);
+        *reinterpret_cast<float4*>(&sh.vf[buf][tt][i0]) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+    } else {
+        bool wide = false;
+        float rq[4], kq[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            const float D = row_prod(dcy[c]);      // D_t = prod_{tau <= t} d_tau, <= 1
+            const float DL = row_last(D);          // D_15
+            wide = wide || !(DL >= kMinChunkDecay);
+            const float inv = __builtin_amdgcn_rcpf(D);   // <= 1 / D_15
+            rq[c] = rv[c] * D;
+            kq[c] = kv[c] * inv;
+            const float kd = kv[c] * (DL * inv);
+            if (tt == 15) sh.el[buf][i0 + c] = DL;
+            sh.kdt[buf][i0 + c][tt] = uint16_t(bf16_word(kd, 0.0f) & 0xffffu);
+        }
+        store_vt<DT>(sh.vt[buf], i0, tt, vraw, vv);
+        *reinterpret_cast<uint2*>(&sh.rq[buf][tt][i0]) =
+            make_uint2(bf16_word(rq[0], rq[1]), bf16_word(rq[2], rq[3]));
+        *reinterpret_cast<uint2*>(&sh.kq[buf][tt][i0]) =
+            make_uint2(bf16_word(kq[0], kq[1]), bf16_word(kq[2], kq[3]));
+        if (__builtin_amdgcn_ballot_w64(wide) != 0 && lane == 0) sh.exact_chunk[buf] = int(ch);
+    }
+}
+
+// r, k, d of token row e (element offset of its channel 0 in this head) for
+// channels c0 .. c0+3, and v of channel jcol, read from global memory (the
+// rare token-by-token chunk of the chunked kernel).
+template <int DT, bool PER_TOKEN_Z>
+__device__ __forceinline__ void token_inputs(const MatProblem& pr, int64_t e, int64_t zc, int c0,
+                                             float (&r)[4], float (&k)[4], float (&d)[4]) {
+    using Q = Quad<DT>;
+    Q::unpack(Q::load(pr.r, e + c0), r);
+    Q::unpack(Q::load(pr.k, e + c0), k);
+    if constexpr (PER_TOKEN_Z) {
+        float z[4];
+        Q::unpack(Q::load(pr.z, e + c0), z);
+#pragma unroll
+        for (int c = 0; c < 4; c++) d[c] = decay_of(z[c]);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; c++) d[c] = decay_of(static_cast<const float*>(pr.z)[zc + c0 + c]);
+    }
+}
+
+// Consumer: chunk ch from LDS buffer ch & 1 against the state S (accumulator
+// layout: S[b][r] = S[16b + 4g + r][jcol]); writes y of its 16 value columns.
+template <int DT, bool PER_TOKEN_Z, bool EXACT_ONLY>
+__device__ __forceinline__ void consume_chunk(const MatProblem& pr, MatShared& sh, int wave, int g,
+                                              int nn, int64_t row0, int64_t h, int64_t ch,
+                                              float (&S)[4][4]) {
+    using Q = Quad<DT>;
+    const int64_t C = pr.H * kN;
+    const int64_t t0 = ch * kCT;
+    const int n = chunk_tokens(pr.T, ch);
+    const int buf = int(ch & 1);
+    const int jcol = 16 * wave + nn;
+    if (EXACT_ONLY || sh.exact_chunk[buf] == int(ch)) {
+        // ---- token by token, fp32 ----
+        for (int t = 0; t < n; t++) {
+            const int64_t e = (row0 + t0 + t) * C + h * kN;
+            const float vj = EXACT_ONLY ? sh.vf[buf][t][jcol] : load_one<DT>(pr.v, e + jcol);
+            float yp = 0.0f;
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                float dd[4], kk[4], rr[4];
+                if constexpr (EXACT_ONLY) {
+                    const float4 d4 = *reinterpret_cast<const float4*>(&sh.df[buf][t][16 * b + 4 * g]);
+                    const float4 k4 = *reinterpret_cast<const float4*>(&sh.kf[buf][t][16 * b + 4 * g]);
+                    const float4 r4 = *reinterpret_cast<const float4*>(&sh.rf[buf][t][16 * b + 4 * g]);
+                    dd[0] = d4.x; dd[1] = d4.y; dd[2] = d4.z; dd[3] = d4.w;
+                    kk[0] = k4.x; kk[1] = k4.y; kk[2] = k4.z; kk[3] = k4.w;
+                    rr[0] = r4.x; rr[1] = r4.y; rr[2] = r4.z; rr[3] = r4.w;
+                } else {
+                    token_inputs<DT, PER_TOKEN_Z>(pr, e, h * kN, 16 * b + 4 * g, rr, kk, dd);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    S[b][r] = __builtin_fmaf(dd[r], S[b][r], kk[r] * vj);
+                    yp = __builtin_fmaf(rr[r], S[b][r], yp);
+                }
+            }
+            // the four lane groups hold the partial sums over disjoint rows
+            const float y01 = yp + __shfl_xor(yp, 16);
+            const float y = y01 + __shfl_xor(y01, 32);
+            if (g == 0) store_one<DT>(pr.y, e + jcol, y);
+        }
+        return;
+    }
+    if constexpr (!EXACT_ONLY) {
+        // ---- the chunk on the matrix cores ----
+        short4_t rqB[4], kqA[4], kdA[4];
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            rqB[b] = lds4(&sh.rq[buf][nn][16 * b + 4 * g]);
+            kqA[b] = lds4(&sh.kq[buf][nn][16 * b + 4 * g]);
+            kdA[b] = lds4(&sh.kdt[buf][16 * b + nn][4 * g]);
+        }
+        const short4_t vA = lds4(&sh.vt[buf][jcol][4 * g]);
+        float4_t yacc = {0.f, 0.f, 0.f, 0.f};
+        float4_t aacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            yacc = mfma16(pack4(S[b][0], S[b][1], S[b][2], S[b][3]), rqB[b], yacc);
+            aacc = mfma16(kqA[b], rqB[b], aacc);
+        }
+        // aacc[r] = score of key token s = 4g + r for query token nn; causal mask s <= t
+        float am[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) am[r] = (4 * g + r <= nn) ? aacc[r] : 0.0f;
+        yacc = mfma16(vA, pack4(am[0], am[1], am[2], am[3]), yacc);
+        // yacc[r] = y[token nn][column 16 wave + 4g + r]
+        if (nn < n) {
+            const float yo[4] = {yacc[0], yacc[1], yacc[2], yacc[3]};
+            Q::store(pr.y, (row0 + t0 + nn) * C + h * kN + 16 * wave + 4 * g, yo);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const float4 e4 = *reinterpret_cast<const float4*>(&sh.el[buf][16 * b + 4 * g]);
+            float4_t c = {S[b][0] * e4.x, S[b][1] * e4.y, S[b][2] * e4.z, S[b][3] * e4.w};
+            c = mfma16(kdA[b], vA, c);
+#pragma unroll
+            for (int r = 0; r < 4; r++) S[b][r] = c[r];
+        }
+    }
+}
+
+// Chunks in flight per producer thread: the inputs of the next kPrefetch
+// chunks are loaded into registers while the current one is processed.
+constexpr int kPrefetch = 4;
+
+// One workgroup of 8 waves per (batch row, head).  Waves 4..7 produce the
+// operands of chunk c+1 while waves 0..3 consume chunk c (matrix-core products
+// and the state); one barrier per chunk hands the double-buffered LDS over.
+template <int DT, bool PER_TOKEN_Z, bool EXACT_ONLY>
+__global__ __launch_bounds__(512, 4) void mat_forward_kernel(MatProblem pr) {
     __shared__ MatShared sh;
     const int wave = mat_wave();
     const int lane = mat_lane();
-    const int64_t H = pr.H, T = pr.T, C = H * kN;
-    const int64_t bb = blockIdx.x / H;
-    const int64_t h = blockIdx.x - bb * H;
-
-    // phase-1 role: token tt of the chunk, channels i0 .. i0+3
+    const bool producer = wave >= 4;
+    const int64_t T = pr.T, C = pr.H * kN;
+    const int64_t bb = blockIdx.x / pr.H;
+    const int64_t h = blockIdx.x - bb * pr.H;
+    const int64_t row0 = bb * T;
+    const int64_t nch = (T + kCT - 1) / kCT;
+    // producer role: token tt of a chunk, channels i0 .. i0+3
     const int tt = lane & 15;
-    const int i0 = 4 * (4 * wave + (lane >> 4));
-    // matrix-core role: lane group g, column nn of the wave's 16 value columns
+    const int i0 = 4 * (4 * (wave & 3) + (lane >> 4));
+    // consumer role: lane group g, column nn of the wave's 16 value columns
     const int g = lane >> 4;
     const int nn = lane & 15;
-    const int jcol = 16 * wave + nn;
+    const int jcol = 16 * (wave & 3) + nn;
 
-    // state: S[b][r] = S[16b + 4g + r][jcol]
     float S[4][4];
-    const int64_t sbase = (bb * H + h) * int64_t(kN * kN);
+    const int64_t sbase = (bb * pr.H + h) * int64_t(kN * kN);
+    if (!producer) {
 #pragma unroll
-    for (int b = 0; b < 4; b++)
+        for (int b = 0; b < 4; b++)
 #pragma unroll
-        for (int r = 0; r < 4; r++)
-            S[b][r] = pr.s_in ? pr.s_in[sbase + int64_t(16 * b + 4 * g + r) * kN + jcol] : 0.0f;
-
-    // per-channel decay (Eagle): log d once
-    float lc[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int r = 0; r < 4; r++)
+                S[b][r] = pr.s_in ? pr.s_in[sbase + int64_t(16 * b + 4 * g + r) * kN + jcol] : 0.0f;
+    }
+    // per-channel decay (Eagle): d once
+    float dc[4] = {1.f, 1.f, 1.f, 1.f};
     if constexpr (!PER_TOKEN_Z) {
+        if (producer) {
 #pragma unroll
-        for (int c = 0; c < 4; c++) lc[c] = neg_softplus(static_cast<const float*>(pr.z)[h * kN + i0 + c]);
+            for (int c = 0; c < 4; c++) dc[c] = decay_of(static_cast<const float*>(pr.z)[h * kN + i0 + c]);
+        }
     }
-    if (threadIdx.x == 0) sh.exact_chunk = -1;
+    if (threadIdx.x < 2) sh.exact_chunk[threadIdx.x] = -1;
+    // the state and decay loads complete here (s_waitcnt vmcnt(0) as an
+    // instruction the compiler's wait insertion sees), so that the waits inside
+    // the chunk loop only count the prefetch ring's loads
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
 
-    const int64_t nch = (T + kCT - 1) / kCT;
-    const int64_t row0 = bb * T;  // first token row of this batch row
-    ChunkIn<DT> nxt;
-    if (nch > 0) load_chunk<DT, PER_TOKEN_Z>(nxt, pr, (row0 + tt) * C + h * kN + i0, tt < T);
-
-    for (int64_t ch = 0; ch < nch; ch++) {
-        const int64_t t0 = ch * kCT;
-        const int n = T - t0 < kCT ? int(T - t0) : kCT;
-        const bool live = tt < n;
-        const ChunkIn<DT> cur = nxt;
-        if (ch + 1 < nch)
-            load_chunk<DT, PER_TOKEN_Z>(nxt, pr, (row0 + t0 + kCT + tt) * C + h * kN + i0,
-                                        t0 + kCT + tt < T);
-        const int buf = int(ch & 1);
-
-        // ---- phase 1: log decay, its prefix over the chunk, operands ----
-        float rv[4], kv[4], vv[4], lam[4], lamL[4];
-        Q::unpack(cur.r, rv);
-        Q::unpack(cur.k, kv);
-        Q::unpack(cur.v, vv);
-        float lg[4];
-        if constexpr (PER_TOKEN_Z) {
-            float zv[4];
-            Q::unpack(cur.z, zv);
+    // element offset of token tt of chunk ch (ch >= 0), clamped to the last
+    // token; only called when T >= 1
+    const int64_t e0 = row0 * C + h * kN + i0;
+    auto elem = [&](int64_t ch) {
+        const int64_t t = ch * kCT + tt;
+        return e0 + (t < T ? t : T - 1) * C;
+    };
+    // The producers keep a ring of kPrefetch chunks in registers: slot p is
+    // consumed, then reloaded in place with the chunk kPrefetch ahead.  Loads
+    // are unconditional (chunks past the last one load the last token; their
+    // values are masked as padding).  In the interval of chunk q the producers
+    // prepare q while the consumers process q - 1.  The two roles run separate
+    // loops (so that neither holds the other's registers) with the same number
+    // of barriers; nothing happens for T = 0.
+    if (nch > 0) {
+        if (producer) {
+            // the first pass only loads (a prologue outside the loop would
+            // reach the loop with the slots loaded in another order, and the
+            // waits would then cover every load in flight)
+            ChunkIn<DT> ring[kPrefetch];
+            for (int64_t q0 = -kPrefetch; q0 <= nch; q0 += kPrefetch) {
 #pragma unroll
-            for (int c = 0; c < 4; c++) lg[c] = live ? neg_softplus(zv[c]) : 0.0f;
-        } else {
-#pragma unroll
-            for (int c = 0; c < 4; c++) lg[c] = live ? lc[c] : 0.0f;
-        }
-#pragma unroll
-        for (int c = 0; c < 4; c++) {
-            lam[c] = row_scan(lg[c]);
-            lamL[c] = row_last(lam[c]);
-        }
-        if constexpr (!EXACT_ONLY) {
-            bool wide = false;
-            float rq[4], kq[4], kd[4];
-#pragma unroll
-            for (int c = 0; c < 4; c++) {
-                wide = wide || !(-lamL[c] <= kSpanMax);
-                const float ep = exp_f(lam[c]);     // <= 1
-                const float en = exp_f(-lam[c]);    // <= e^{span}
-                const float eL = exp_f(lamL[c]);
-                rq[c] = rv[c] * ep;
-                kq[c] = kv[c] * en;
-                kd[c] = kv[c] * (eL * en);
-                if (tt == 15) sh.el[buf][i0 + c] = eL;
-                sh.kdt[buf][i0 + c][tt] = uint16_t(bf16_word(kd[c], 0.0f) & 0xffffu);
-                sh.vt[buf][i0 + c][tt] = uint16_t(bf16_word(vv[c], 0.0f) & 0xffffu);
-            }
-            *reinterpret_cast<uint2*>(&sh.rq[buf][tt][i0]) =
-                make_uint2(bf16_word(rq[0], rq[1]), bf16_word(rq[2], rq[3]));
-            *reinterpret_cast<uint2*>(&sh.kq[buf][tt][i0]) =
-                make_uint2(bf16_word(kq[0], kq[1]), bf16_word(kq[2], kq[3]));
-            if (__builtin_amdgcn_ballot_w64(wide) != 0 && lane == 0) sh.exact_chunk = int(ch);
-        }
-        __syncthreads();
-        const bool exact = EXACT_ONLY || sh.exact_chunk == int(ch);
-
-        if (exact) {
-            // ---- token by token, fp32 ----
-#pragma unroll
-            for (int c = 0; c < 4; c++) {
-                sh.rf[tt][i0 + c] = rv[c];
-                sh.kf[tt][i0 + c] = kv[c];
-                sh.df[tt][i0 + c] = exp_f(lg[c]);
-                sh.vf[tt][i0 + c] = vv[c];
-            }
-            __syncthreads();
-            for (int t = 0; t < n; t++) {
-                const float vj = sh.vf[t][jcol];
-                float yp = 0.0f;
-#pragma unroll
-                for (int b = 0; b < 4; b++) {
-                    const float4 d4 = *reinterpret_cast<const float4*>(&sh.df[t][16 * b + 4 * g]);
-                    const float4 k4 = *reinterpret_cast<const float4*>(&sh.kf[t][16 * b + 4 * g]);
-                    const float4 r4 = *reinterpret_cast<const float4*>(&sh.rf[t][16 * b + 4 * g]);
-                    const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-                    const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
-                    const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
-#pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        S[b][r] = __builtin_fmaf(dd[r], S[b][r], kk[r] * vj);
-                        yp = __builtin_fmaf(rr[r], S[b][r], yp);
-                    }
+                for (int p = 0; p < kPrefetch; p++) {
+                    const int64_t q = q0 + p;
+                    if (q0 >= 0) produce_chunk<DT, PER_TOKEN_Z, EXACT_ONLY>(sh, tt, i0, lane, ring[p], dc, T, q);
+                    load_chunk<DT, PER_TOKEN_Z>(ring[p], pr, elem(q + kPrefetch));
+                    if (q0 >= 0) __syncthreads();
                 }
-                // the four lane groups hold the partial sums over disjoint rows
-                const float y01 = yp + __shfl_xor(yp, 16);
-                const float y = y01 + __shfl_xor(y01, 32);
-                if (g == 0) store_one<DT>(pr.y, (row0 + t0 + t) * C + h * kN + jcol, y);
             }
-            __syncthreads();
-        } else if constexpr (!EXACT_ONLY) {
-            // ---- the chunk on the matrix cores ----
-            short4_t rqB[4], kqA[4], kdA[4];
+        } else {
+            for (int64_t q0 = 0; q0 <= nch; q0 += kPrefetch) {
 #pragma unroll
-            for (int b = 0; b < 4; b++) {
-                rqB[b] = lds4(&sh.rq[buf][nn][16 * b + 4 * g]);
-                kqA[b] = lds4(&sh.kq[buf][nn][16 * b + 4 * g]);
-                kdA[b] = lds4(&sh.kdt[buf][16 * b + nn][4 * g]);
-            }
-            const short4_t vA = lds4(&sh.vt[buf][jcol][4 * g]);
-            float4_t yacc = {0.f, 0.f, 0.f, 0.f};
-            float4_t aacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int b = 0; b < 4; b++) {
-                yacc = mfma16(pack4(S[b][0], S[b][1], S[b][2], S[b][3]), rqB[b], yacc);
-                aacc = mfma16(kqA[b], rqB[b], aacc);
-            }
-            // aacc[r] = score of key token s = 4g + r for query token nn; causal mask s <= t
-            float am[4];
-#pragma unroll
-            for (int r = 0; r < 4; r++) am[r] = (4 * g + r <= nn) ? aacc[r] : 0.0f;
-            yacc = mfma16(vA, pack4(am[0], am[1], am[2], am[3]), yacc);
-            // yacc[r] = y[token nn][column 16 wave + 4g + r]
-            if (nn < n) {
-                const float yo[4] = {yacc[0], yacc[1], yacc[2], yacc[3]};
-                Q::store(pr.y, (row0 + t0 + nn) * C + h * kN + 16 * wave + 4 * g, yo);
-            }
-#pragma unroll
-            for (int b = 0; b < 4; b++) {
-                const float4 e4 = *reinterpret_cast<const float4*>(&sh.el[buf][16 * b + 4 * g]);
-                float4_t c = {S[b][0] * e4.x, S[b][1] * e4.y, S[b][2] * e4.z, S[b][3] * e4.w};
-                c = mfma16(kdA[b], vA, c);
-#pragma unroll
-                for (int r = 0; r < 4; r++) S[b][r] = c[r];
+                for (int p = 0; p < kPrefetch; p++) {
+                    const int64_t q = q0 + p;
+                    if (q >= 1 && q <= nch)
+                        consume_chunk<DT, PER_TOKEN_Z, EXACT_ONLY>(pr, sh, wave, g, nn, row0, h, q - 1, S);
+                    __syncthreads();
+                }
             }
         }
     }
-    if (pr.s_out) {
+    if (!producer && pr.s_out) {
 #pragma unroll
         for (int b = 0; b < 4; b++)
 #pragma unroll
@@ -365,7 +472,7 @@ __global__ __launch_bounds__(256) void mat_step_kernel(MatStepProblem pr) {
     const float v = load_one<DT>(pr.v, e);
     const float z = PER_TOKEN_Z ? load_one<DT>(pr.z, e)
                                 : static_cast<const float*>(pr.z)[layer * C + h * kN + lane];
-    const float d = exp_f(neg_softplus(z));
+    const float d = decay_of(z);
     const int64_t sb = head * int64_t(kN * kN) + lane;
     float s[kN];
 #pragma unroll
@@ -388,7 +495,7 @@ __global__ __launch_bounds__(256) void mat_step_kernel(MatStepProblem pr) {
 }  // namespace
 
 hipError_t launch_mat_forward(const MatProblem& pr, hipStream_t stream) {
-    const dim3 grid(unsigned(pr.B * pr.H)), block(256);
+    const dim3 grid(unsigned(pr.B * pr.H)), block(512);
     const bool exact = pr.dtype == kF32 || pr.path == 1;
 #define WKV_MAT_FWD(DT, PT, EX) hipLaunchKernelGGL((mat_forward_kernel<DT, PT, EX>), grid, block, 0, stream, pr)
     if (pr.dtype == kF32) {

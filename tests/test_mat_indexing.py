@@ -1,0 +1,97 @@
+"""Host check of the matrix-state kernels' addressing (csrc/wkv_mat.hip).
+
+The element offsets each thread of mat_forward_kernel and mat_step_kernel
+forms are recomputed here from the same formulas, for every workgroup and
+thread of small launches, and checked against the arrays' bounds -- including
+T = 0, where the forward must not load at all (its token clamp needs a token),
+and the chunks past the last one that its 4-deep prefetch ring loads.
+CPU only.
+"""
+import numpy as np
+import pytest
+
+N = 64        # head dimension
+CT = 16       # tokens per chunk
+PREFETCH = 4  # chunks in the register ring
+
+
+def forward_offsets(B, T, H):
+    """(loads, stores, state) element offsets of mat_forward_kernel: 512
+    threads per (batch row, head); waves 4..7 load (producers), waves 0..3
+    store y and hold the state (consumers)."""
+    C = H * N
+    loads, stores, state = [], [], []
+    nch = (T + CT - 1) // CT
+    for blk in range(B * H):
+        bb, h = divmod(blk, H)
+        row0 = bb * T
+        for thr in range(512):
+            wave, lane = divmod(thr, 64)
+            producer = wave >= 4
+            tt, i0 = lane & 15, 4 * (4 * (wave & 3) + (lane >> 4))
+            g, nn = lane >> 4, lane & 15
+            jcol = 16 * (wave & 3) + nn
+            if producer:
+                if nch == 0:
+                    continue
+                e0 = row0 * C + h * N + i0
+                q0 = -PREFETCH
+                while q0 <= nch:
+                    for p in range(PREFETCH):
+                        t = (q0 + p + PREFETCH) * CT + tt
+                        t = t if t < T else T - 1
+                        loads.extend(e0 + t * C + q for q in range(4))
+                    q0 += PREFETCH
+                continue
+            for b in range(4):
+                for r in range(4):
+                    state.append((bb * H + h) * N * N + (16 * b + 4 * g + r) * N + jcol)
+            for ch in range(nch):
+                t0 = ch * CT
+                n = max(0, min(CT, T - t0))
+                if nn < n:   # chunked form's output
+                    stores.extend((row0 + t0 + nn) * C + h * N + 16 * (wave & 3) + 4 * g + q
+                                  for q in range(4))
+                for t in range(n):    # token-by-token form: its inputs read from global memory
+                    e = (row0 + t0 + t) * C + h * N
+                    stores.append(e + jcol)
+                    loads.append(e + jcol)
+                    loads.extend(e + 16 * b + 4 * g + q for b in range(4) for q in range(4))
+    return np.array(loads, dtype=np.int64), np.array(stores, dtype=np.int64), np.array(state)
+
+
+@pytest.mark.parametrize("B,T,H", [(2, 0, 3), (1, 1, 1), (1, 15, 2), (2, 16, 1), (1, 17, 1),
+                                   (2, 53, 2), (1, 100, 1), (1, 129, 1)])
+def test_forward_addresses_stay_in_bounds(B, T, H):
+    loads, stores, state = forward_offsets(B, T, H)
+    n_io = B * T * H * N
+    if T == 0:
+        assert loads.size == 0 and stores.size == 0
+        assert state.min() >= 0 and state.max() < B * H * N * N
+        return
+    else:
+        assert loads.min() >= 0 and loads.max() < n_io
+        assert stores.min() >= 0 and stores.max() < n_io
+        # every output element is written
+        assert np.array_equal(np.unique(stores), np.arange(n_io))
+    assert state.min() >= 0 and state.max() < B * H * N * N
+    assert np.array_equal(np.unique(state), np.arange(B * H * N * N))
+
+
+@pytest.mark.parametrize("L,S,H", [(1, 1, 1), (2, 3, 2), (1, 1, 5)])
+def test_step_addresses_stay_in_bounds(L, S, H):
+    C = H * N
+    heads = L * S * H
+    io, st = [], []
+    for blk in range((heads + 3) // 4):
+        for thr in range(256):
+            head = blk * 4 + thr // 64
+            lane = thr & 63
+            if head >= heads:
+                continue
+            row, h = divmod(head, H)
+            io.append(row * C + h * N + lane)
+            st.extend(head * N * N + lane + i * N for i in range(N))
+    io, st = np.array(io), np.array(st)
+    assert np.array_equal(np.unique(io), np.arange(L * S * C))
+    assert np.array_equal(np.unique(st), np.arange(heads * N * N))
