@@ -52,11 +52,26 @@ __device__ __forceinline__ int mat_lane() { return threadIdx.x & 63; }
 
 __device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
-// x * (x of the lane n below, within the 16-lane row; 1 for the first n lanes)
+// x * (x of the lane SH below, within the 16-lane row), in place: the first
+// SH lanes of each row have no source and keep x (v_mul_f32_dpp without
+// bound_ctrl leaves such lanes unwritten).  The s_nop covers the two wait
+// states a DPP read needs after a vector write of its source.
 template <int SH>
 __device__ __forceinline__ float row_shr_mul(float x) {
-    const int y = __builtin_amdgcn_update_dpp(0x3f800000, __float_as_int(x), 0x110 | SH, 0xf, 0xf, false);
-    return x * __int_as_float(y);
+    float y;
+    if constexpr (SH == 1)
+        asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %1, %2 row_shr:1 row_mask:0xf bank_mask:0xf"
+                     : "=v"(y) : "v"(x), "v"(x), "0"(x));
+    else if constexpr (SH == 2)
+        asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %1, %2 row_shr:2 row_mask:0xf bank_mask:0xf"
+                     : "=v"(y) : "v"(x), "v"(x), "0"(x));
+    else if constexpr (SH == 4)
+        asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %1, %2 row_shr:4 row_mask:0xf bank_mask:0xf"
+                     : "=v"(y) : "v"(x), "v"(x), "0"(x));
+    else
+        asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %1, %2 row_shr:8 row_mask:0xf bank_mask:0xf"
+                     : "=v"(y) : "v"(x), "v"(x), "0"(x));
+    return y;
 }
 
 // inclusive prefix product over the 16 lanes of each row
@@ -68,14 +83,17 @@ __device__ __forceinline__ float row_prod(float x) {
     return x;
 }
 
+// value of lane 15 of this lane's row (DPP row_newbcast)
+__device__ __forceinline__ float row_last(float x) {
+    float y;
+    asm volatile("s_nop 1\n\tv_mov_b32_dpp %0, %1 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+                 : "=v"(y) : "v"(x));
+    return y;
+}
+
 // d = exp(-softplus(z)) = 1 / (1 + e^z): 1 for z = -inf, 0 once e^z overflows
 __device__ __forceinline__ float decay_of(float z) { return __builtin_amdgcn_rcpf(1.0f + exp_f(z)); }
 
-// value of lane 15 of this lane's row
-__device__ __forceinline__ float row_last(float x) {
-    const int src = (mat_lane() | 15) << 2;
-    return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(x)));
-}
 
 __device__ __forceinline__ uint32_t bf16_word(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
@@ -90,6 +108,17 @@ __device__ __forceinline__ short4_t lds4(const uint16_t* p) {
 
 __device__ __forceinline__ float4_t mfma16(short4_t a, short4_t b, float4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// 16x16x32: lane l supplies k = 8(l/16) .. 8(l/16)+7 of its row (A) or column
+// (B); the eight values are the two 4-value halves lo, hi.
+__device__ __forceinline__ float4_t mfma32(short4_t alo, short4_t ahi, short4_t blo, short4_t bhi,
+                                           float4_t c) {
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7));
+    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // Four consecutive channels of one token in storage type DT.
@@ -145,6 +174,7 @@ struct MatShared {
     // fp32 storage (token-by-token form only): r, k, d, v of the chunk, rows
     // padded so that a wave's 16-byte writes spread over the banks
     float rf[2][kCT][kN + 4], kf[2][kCT][kN + 4], df[2][kCT][kN + 4], vf[2][kCT][kN + 4];
+    uint16_t yt[2][kCT][kRowPad];   // y of a chunk (chunked form), written out one chunk later
     int exact_chunk[2];             // chunk of this parity that must run token by token
 };
 
@@ -275,9 +305,11 @@ __device__ __forceinline__ void token_inputs(const MatProblem& pr, int64_t e, in
 }
 
 // Consumer: chunk ch from LDS buffer ch & 1 against the state S (accumulator
-// layout: S[b][r] = S[16b + 4g + r][jcol]); writes y of its 16 value columns.
+// layout: S[b][r] = S[16b + 4g + r][jcol]).  The token-by-token form writes y
+// of its 16 value columns to global memory at once; the chunked form leaves
+// it in the tile yt[ch & 1] and returns true (store_tile writes it out).
 template <int DT, bool PER_TOKEN_Z, bool EXACT_ONLY>
-__device__ __forceinline__ void consume_chunk(const MatProblem& pr, MatShared& sh, int wave, int g,
+__device__ __forceinline__ bool consume_chunk(const MatProblem& pr, MatShared& sh, int wave, int g,
                                               int nn, int64_t row0, int64_t h, int64_t ch,
                                               float (&S)[4][4]) {
     using Q = Quad<DT>;
@@ -286,6 +318,19 @@ __device__ __forceinline__ void consume_chunk(const MatProblem& pr, MatShared& s
     const int n = chunk_tokens(pr.T, ch);
     const int buf = int(ch & 1);
     const int jcol = 16 * wave + nn;
+    // The chunked form's operands are read before the choice of form, so that
+    // their LDS latency overlaps the flag's (reading them is harmless when the
+    // chunk runs token by token).
+    short4_t rqB[4], kqA[4], kdA[4], vA;
+    if constexpr (!EXACT_ONLY) {
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            rqB[b] = lds4(&sh.rq[buf][nn][16 * b + 4 * g]);
+            kqA[b] = lds4(&sh.kq[buf][nn][16 * b + 4 * g]);
+            kdA[b] = lds4(&sh.kdt[buf][16 * b + nn][4 * g]);
+        }
+        vA = lds4(&sh.vt[buf][jcol][4 * g]);
+    }
     if (EXACT_ONLY || sh.exact_chunk[buf] == int(ch)) {
         // ---- token by token, fp32 ----
         for (int t = 0; t < n; t++) {
@@ -316,44 +361,64 @@ __device__ __forceinline__ void consume_chunk(const MatProblem& pr, MatShared& s
             const float y = y01 + __shfl_xor(y01, 32);
             if (g == 0) store_one<DT>(pr.y, e + jcol, y);
         }
-        return;
+        return false;
     }
     if constexpr (!EXACT_ONLY) {
         // ---- the chunk on the matrix cores ----
-        short4_t rqB[4], kqA[4], kdA[4];
-#pragma unroll
-        for (int b = 0; b < 4; b++) {
-            rqB[b] = lds4(&sh.rq[buf][nn][16 * b + 4 * g]);
-            kqA[b] = lds4(&sh.kq[buf][nn][16 * b + 4 * g]);
-            kdA[b] = lds4(&sh.kdt[buf][16 * b + nn][4 * g]);
-        }
-        const short4_t vA = lds4(&sh.vt[buf][jcol][4 * g]);
         float4_t yacc = {0.f, 0.f, 0.f, 0.f};
         float4_t aacc = {0.f, 0.f, 0.f, 0.f};
+        // the contraction over the 64 key channels as two 16x16x32 products:
+        // lane group g supplies rows 16b + 4g .. +3 of blocks b = 2m, 2m+1 (its
+        // own state registers), and the same channels of rq and kq
 #pragma unroll
-        for (int b = 0; b < 4; b++) {
-            yacc = mfma16(pack4(S[b][0], S[b][1], S[b][2], S[b][3]), rqB[b], yacc);
-            aacc = mfma16(kqA[b], rqB[b], aacc);
+        for (int m = 0; m < 2; m++) {
+            const short4_t s0 = pack4(S[2 * m][0], S[2 * m][1], S[2 * m][2], S[2 * m][3]);
+            const short4_t s1 = pack4(S[2 * m + 1][0], S[2 * m + 1][1], S[2 * m + 1][2], S[2 * m + 1][3]);
+            yacc = mfma32(s0, s1, rqB[2 * m], rqB[2 * m + 1], yacc);
+            aacc = mfma32(kqA[2 * m], kqA[2 * m + 1], rqB[2 * m], rqB[2 * m + 1], aacc);
         }
         // aacc[r] = score of key token s = 4g + r for query token nn; causal mask s <= t
         float am[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) am[r] = (4 * g + r <= nn) ? aacc[r] : 0.0f;
         yacc = mfma16(vA, pack4(am[0], am[1], am[2], am[3]), yacc);
-        // yacc[r] = y[token nn][column 16 wave + 4g + r]
-        if (nn < n) {
-            const float yo[4] = {yacc[0], yacc[1], yacc[2], yacc[3]};
-            Q::store(pr.y, (row0 + t0 + nn) * C + h * kN + 16 * wave + 4 * g, yo);
-        }
+        // yacc[r] = y[token nn][column 16 wave + 4g + r], into the tile: a
+        // wave's direct stores would write 32 bytes of each of 16 rows
+        *reinterpret_cast<uint2*>(&sh.yt[buf][nn][16 * wave + 4 * g]) =
+            make_uint2(bf16_word(yacc[0], yacc[1]), bf16_word(yacc[2], yacc[3]));
+        // S <- diag(D_15) S + Kd^T V: the product does not wait for D_15
+        float4_t upd[4];
+#pragma unroll
+        for (int b = 0; b < 4; b++) upd[b] = mfma16(kdA[b], vA, float4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int b = 0; b < 4; b++) {
             const float4 e4 = *reinterpret_cast<const float4*>(&sh.el[buf][16 * b + 4 * g]);
-            float4_t c = {S[b][0] * e4.x, S[b][1] * e4.y, S[b][2] * e4.z, S[b][3] * e4.w};
-            c = mfma16(kdA[b], vA, c);
-#pragma unroll
-            for (int r = 0; r < 4; r++) S[b][r] = c[r];
+            S[b][0] = __builtin_fmaf(S[b][0], e4.x, upd[b][0]);
+            S[b][1] = __builtin_fmaf(S[b][1], e4.y, upd[b][1]);
+            S[b][2] = __builtin_fmaf(S[b][2], e4.z, upd[b][2]);
+            S[b][3] = __builtin_fmaf(S[b][3], e4.w, upd[b][3]);
         }
     }
+    return true;
+}
+
+// The y tile of chunk ch (n valid rows) from LDS to global memory in whole
+// rows: consumer thread ct writes 4 channels of row ct / 16, so a wave writes
+// 4 rows of 128 bytes per instruction.
+// (read_tile issues the LDS read early; write_tile stores it once it is needed.)
+__device__ __forceinline__ uint2 read_tile(MatShared& sh, int ct, int64_t ch) {
+    return *reinterpret_cast<const uint2*>(&sh.yt[ch & 1][ct >> 4][(ct & 15) * 4]);
+}
+__device__ __forceinline__ void write_tile(const MatProblem& pr, uint2 v, int ct, int64_t row0,
+                                           int64_t h, int64_t ch, int n) {
+    const int row = ct >> 4;
+    if (row < n)
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(pr.y) + (row0 + ch * kCT + row) * pr.H * kN +
+                                  h * kN + (ct & 15) * 4) = v;
+}
+__device__ __forceinline__ void store_tile(const MatProblem& pr, MatShared& sh, int ct,
+                                           int64_t row0, int64_t h, int64_t ch, int n) {
+    write_tile(pr, read_tile(sh, ct, ch), ct, row0, h, ch, n);
 }
 
 // Chunks in flight per producer thread: the inputs of the next kPrefetch
@@ -420,6 +485,7 @@ __global__ __launch_bounds__(512, 4) void mat_forward_kernel(MatProblem pr) {
     // prepare q while the consumers process q - 1.  The two roles run separate
     // loops (so that neither holds the other's registers) with the same number
     // of barriers; nothing happens for T = 0.
+    int64_t pend = -1;  // consumers: chunk whose y tile is still to be written
     if (nch > 0) {
         if (producer) {
             // the first pass only loads (a prologue outside the loop would
@@ -436,17 +502,28 @@ __global__ __launch_bounds__(512, 4) void mat_forward_kernel(MatProblem pr) {
                 }
             }
         } else {
+            // the y tile of the chunk consumed in the previous interval is
+            // written out in this one (after the barrier that completes it)
             for (int64_t q0 = 0; q0 <= nch; q0 += kPrefetch) {
 #pragma unroll
                 for (int p = 0; p < kPrefetch; p++) {
                     const int64_t q = q0 + p;
-                    if (q >= 1 && q <= nch)
-                        consume_chunk<DT, PER_TOKEN_Z, EXACT_ONLY>(pr, sh, wave, g, nn, row0, h, q - 1, S);
+                    const int64_t prev = pend;
+                    uint2 tile = make_uint2(0u, 0u);
+                    if (prev >= 0) tile = read_tile(sh, int(threadIdx.x), prev);
+                    pend = -1;
+                    if (q >= 1 && q <= nch &&
+                        consume_chunk<DT, PER_TOKEN_Z, EXACT_ONLY>(pr, sh, wave, g, nn, row0, h, q - 1, S))
+                        pend = q - 1;
+                    if (prev >= 0) write_tile(pr, tile, int(threadIdx.x), row0, h, prev, chunk_tokens(T, prev));
                     __syncthreads();
                 }
             }
         }
     }
+    // both roles: the last tile, if still pending, after one more barrier
+    __syncthreads();
+    if (pend >= 0) store_tile(pr, sh, int(threadIdx.x), row0, h, pend, chunk_tokens(T, pend));
     if (!producer && pr.s_out) {
 #pragma unroll
         for (int b = 0; b < 4; b++)

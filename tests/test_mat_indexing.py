@@ -49,9 +49,10 @@ def forward_offsets(B, T, H):
             for ch in range(nch):
                 t0 = ch * CT
                 n = max(0, min(CT, T - t0))
-                if nn < n:   # chunked form's output
-                    stores.extend((row0 + t0 + nn) * C + h * N + 16 * (wave & 3) + 4 * g + q
-                                  for q in range(4))
+                ct = wave * 64 + lane   # chunked form's output: the y tile in whole rows
+                row, cg = ct >> 4, (ct & 15) * 4
+                if row < n:
+                    stores.extend((row0 + t0 + row) * C + h * N + cg + q for q in range(4))
                 for t in range(n):    # token-by-token form: its inputs read from global memory
                     e = (row0 + t0 + t) * C + h * N
                     stores.append(e + jcol)
