@@ -553,7 +553,7 @@ __global__ __launch_bounds__(256) void mat_step_kernel(MatStepProblem pr) {
     const int64_t sb = head * int64_t(kN * kN) + lane;
     float s[kN];
 #pragma unroll
-    for (int i = 0; i < kN; i++) s[i] = pr.s_in[sb + i * kN];
+    for (int i = 0; i < kN; i++) s[i] = __builtin_nontemporal_load(pr.s_in + sb + i * kN);
     float y = 0.0f;
 #pragma unroll
     for (int i = 0; i < kN; i++) {
