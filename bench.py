@@ -133,19 +133,26 @@ class ForwardBench:
         return {"workload": name, "B": self.wl.B, "T": self.wl.T, "C": self.wl.C,
                 "io_dtype": self.io, "state_dtype": "f32"}
 
-    def cpu_baseline(self):
+    def cpu_baseline(self, min_seconds=10.0):
+        """The oracle over the whole workload, repeated until about
+        min_seconds of wall time have passed."""
         import oracle
         x = self.host
+        passes = 0
         t0 = time.perf_counter()
-        if self.gated:
-            oracle.forward_gated(x.k, x.v, self.r_host, x.w, x.u)
-        else:
-            oracle.forward(x.k, x.v, x.w, x.u)
-        dt = time.perf_counter() - t0
-        return {"value": self.units / dt, "unit": "tokens·channels/s", "cores": oracle.threads(),
-                "kind": "oracle",
-                "sample": f"the full workload ({self.units} tokens*channels), one pass, "
-                          f"{dt:.2f} s including fp64 conversion"}
+        while True:
+            if self.gated:
+                oracle.forward_gated(x.k, x.v, self.r_host, x.w, x.u)
+            else:
+                oracle.forward(x.k, x.v, x.w, x.u)
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+        return {"value": passes * self.units / dt, "unit": "tokens·channels/s",
+                "cores": oracle.threads(), "kind": "oracle",
+                "sample": f"the full workload ({self.units} tokens*channels), {passes} passes, "
+                          f"{dt:.1f} s including fp64 conversion"}
 
 
 class BackwardBench:

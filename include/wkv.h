@@ -342,6 +342,8 @@ int wkv_mat_forward_path(int64_t B, int64_t T, int64_t H, int dtype, int path,
  *   s_in        [L,S,H,64,64] fp32  required
  *   s_out       [L,S,H,64,64] fp32  required; may be s_in (in place)
  *   y           [L,S,C] dtype
+ * r, k, v, z, y must be 8-byte (bf16) or 16-byte (fp32) aligned, s_in and
+ * s_out 16-byte aligned.
  */
 int wkv_mat_step(int64_t L, int64_t S, int64_t H, int dtype,
                  const void *r, const void *k, const void *v, const void *z, int z_mode,

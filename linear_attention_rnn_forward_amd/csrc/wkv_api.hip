@@ -567,6 +567,8 @@ int wkv_mat_step(int64_t L, int64_t S, int64_t H, int dtype, const void* r, cons
         return fail(WKV_ERR_SHAPE, "sizes too large");
     if ((L * S * H + 3) / 4 > 2147483647) return fail(WKV_ERR_SHAPE, "too many heads for one launch");
     if (!s_in || !s_out) return fail(WKV_ERR_NULL, "s_in and s_out are required");
+    if (!aligned(s_in, 16) || !aligned(s_out, 16))
+        return fail(WKV_ERR_ARG, "the decode state arrays must be 16-byte aligned");
     if (int rc = mat_check(dtype, L * S, H, r, k, v, z, z_mode, L, s_in, s_out, L * S * H, y, true))
         return rc;
     wkv::MatStepProblem pr;

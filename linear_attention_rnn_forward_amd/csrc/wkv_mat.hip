@@ -28,9 +28,8 @@
 // registers, in fp32.  fp32 storage always takes that exact token-by-token
 // form.
 //
-// Decode step: one wave per (row, head); lane j holds column j of the state,
-// which is read, updated and written once: an HBM stream of 8 bytes per state
-// element and token.
+// Decode step: one wave per (row, head); each state element is read, updated
+// and written once: an HBM stream of 8 bytes per state element and token.
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
@@ -533,40 +532,74 @@ __global__ __launch_bounds__(512, 4) void mat_forward_kernel(MatProblem pr) {
     }
 }
 
-// One token for every (row, head): lane j holds column j of the head's state.
+// One token for every (row, head), one wave per head.  Lane (rg, cq) holds
+// columns 4cq .. 4cq+3 of rows 4m + rg (m = 0 .. 15), so each of the wave's
+// 16 loads and stores of the state covers 4 whole rows (1 KB).  The decay,
+// key and receptance of the 64 key channels pass through LDS, ordered so that
+// a lane's 16 rows are contiguous.
 template <int DT, bool PER_TOKEN_Z>
 __global__ __launch_bounds__(256) void mat_step_kernel(MatStepProblem pr) {
+    __shared__ float tab[4][3][kN];  // per wave: d, k, r of key channel 4m + rg at rg * 16 + m
+    const int wave = mat_wave();
     const int lane = mat_lane();
-    const int64_t head = int64_t(blockIdx.x) * 4 + mat_wave();
     const int64_t H = pr.H, C = H * kN;
-    if (head >= pr.L * pr.S * H) return;
-    const int64_t row = head / H;          // l * S + s
-    const int64_t h = head - row * H;
+    const int64_t head = int64_t(blockIdx.x) * 4 + wave;
+    const bool live = head < pr.L * pr.S * H;
+    const int64_t row = live ? head / H : 0;  // l * S + s
+    const int64_t h = live ? head - row * H : 0;
     const int64_t layer = row / pr.S;
-    const int64_t e = row * C + h * kN + lane;
-    const float r = load_one<DT>(pr.r, e);
-    const float k = load_one<DT>(pr.k, e);
-    const float v = load_one<DT>(pr.v, e);
-    const float z = PER_TOKEN_Z ? load_one<DT>(pr.z, e)
-                                : static_cast<const float*>(pr.z)[layer * C + h * kN + lane];
-    const float d = decay_of(z);
-    const int64_t sb = head * int64_t(kN * kN) + lane;
-    float s[kN];
+    const int64_t e0 = row * C + h * kN;
+    if (live) {
+        // lane = key channel
+        const float z = PER_TOKEN_Z ? load_one<DT>(pr.z, e0 + lane)
+                                    : static_cast<const float*>(pr.z)[layer * C + h * kN + lane];
+        const int slot = (lane & 3) * 16 + (lane >> 2);
+        tab[wave][0][slot] = decay_of(z);
+        tab[wave][1][slot] = load_one<DT>(pr.k, e0 + lane);
+        tab[wave][2][slot] = load_one<DT>(pr.r, e0 + lane);
+    }
+    __syncthreads();
+    if (!live) return;
+    const int rg = lane >> 4;
+    const int cq = lane & 15;
+    float vv[4];
+    Quad<DT>::unpack(Quad<DT>::load(pr.v, e0 + 4 * cq), vv);
+    const int64_t sb = head * int64_t(kN * kN) + int64_t(rg) * kN + 4 * cq;
+    float4 st[16];
 #pragma unroll
-    for (int i = 0; i < kN; i++) s[i] = __builtin_nontemporal_load(pr.s_in + sb + i * kN);
-    float y = 0.0f;
+    for (int m = 0; m < 16; m++)
+        st[m] = load_stream(reinterpret_cast<const float4*>(pr.s_in + sb + m * 4 * kN));
+    float y[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kN; i++) {
-        // d, k, r of key channel i, from lane i (wave-uniform)
-        const float di = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), i));
-        const float ki = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k), i));
-        const float ri = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), i));
-        s[i] = __builtin_fmaf(di, s[i], ki * v);
-        y = __builtin_fmaf(ri, s[i], y);
+    for (int q4 = 0; q4 < 4; q4++) {
+        const float4 d4 = *reinterpret_cast<const float4*>(&tab[wave][0][rg * 16 + 4 * q4]);
+        const float4 k4 = *reinterpret_cast<const float4*>(&tab[wave][1][rg * 16 + 4 * q4]);
+        const float4 r4 = *reinterpret_cast<const float4*>(&tab[wave][2][rg * 16 + 4 * q4]);
+        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+        const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            float4& s4 = st[4 * q4 + j];   // row 4 (4 q4 + j) + rg
+            s4.x = __builtin_fmaf(dd[j], s4.x, kk[j] * vv[0]);
+            s4.y = __builtin_fmaf(dd[j], s4.y, kk[j] * vv[1]);
+            s4.z = __builtin_fmaf(dd[j], s4.z, kk[j] * vv[2]);
+            s4.w = __builtin_fmaf(dd[j], s4.w, kk[j] * vv[3]);
+            y[0] = __builtin_fmaf(rr[j], s4.x, y[0]);
+            y[1] = __builtin_fmaf(rr[j], s4.y, y[1]);
+            y[2] = __builtin_fmaf(rr[j], s4.z, y[2]);
+            y[3] = __builtin_fmaf(rr[j], s4.w, y[3]);
+        }
     }
 #pragma unroll
-    for (int i = 0; i < kN; i++) pr.s_out[sb + i * kN] = s[i];
-    store_one<DT>(pr.y, e, y);
+    for (int m = 0; m < 16; m++) *reinterpret_cast<float4*>(pr.s_out + sb + m * 4 * kN) = st[m];
+    // the four row groups hold partial sums over disjoint rows
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        const float y01 = y[c] + __shfl_xor(y[c], 16);
+        y[c] = y01 + __shfl_xor(y01, 32);
+    }
+    if (rg == 0) Quad<DT>::store(pr.y, e0 + 4 * cq, y);
 }
 
 }  // namespace

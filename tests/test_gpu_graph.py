@@ -131,3 +131,63 @@ def test_token_shift_graph_replay(device):
         assert all(torch.equal(a, b) for a, b in zip(out, ref)), rep
         wkv.token_shift(x.flip(1).contiguous(), *mus)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("path", ["chunked", "tokenwise"])
+def test_mat_forward_graph_replay(device, path):
+    """The matrix-valued-state forward recorded once and replayed three
+    times, with eager launches on other inputs in between: every replay
+    equals the eager result bit for bit (no timing-dependent order)."""
+    import linear_attention_rnn_forward_amd as wkv
+    torch = _torch()
+    wl = synth.MAT_MAIN.resized(B=2, T=77, H=2, seed=41)
+    x = synth.make_mat_inputs(wl)
+    dev_b = lambda n: torch.from_numpy(x.bits[n].view(np.int16)).to(device).view(torch.bfloat16)
+    r, k, v, z = (dev_b(n) for n in ("r", "k", "v", "z"))
+    y = torch.empty_like(k)
+    s_out = torch.empty((2, 2, 64, 64), device=device)
+    run = lambda: wkv.mat_forward(r, k, v, z, out=y, state_out=s_out, path=path)
+    run()
+    torch.cuda.synchronize()
+    y_eager, s_eager = y.clone(), s_out.clone()
+    g, _ = _capture(run)
+    other = synth.make_mat_inputs(wl.resized(seed=42))
+    r2, k2, v2, z2 = (torch.from_numpy(other.bits[n].view(np.int16)).to(device).view(torch.bfloat16)
+                      for n in ("r", "k", "v", "z"))
+    for _ in range(3):
+        wkv.mat_forward(r2, k2, v2, z2, out=torch.empty_like(k2), path=path)
+        y.zero_()
+        s_out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager) and torch.equal(s_out, s_eager)
+
+
+def test_mat_step_graph_replay(device):
+    """Four decode steps recorded in one graph (state updated in place) and
+    replayed from the same starting state: bit for bit the eager chain."""
+    import linear_attention_rnn_forward_amd as wkv
+    torch = _torch()
+    g_ = torch.Generator(device="cpu").manual_seed(43)
+    Ln, S, H = 2, 3, 2
+    C = 64 * H
+    toks = [tuple(torch.randn((Ln, S, C), generator=g_).to(device) for _ in range(4)) for _ in range(4)]
+    st0 = (torch.randn((Ln, S, H, 64, 64), generator=g_) * 0.3).to(device)
+    st = st0.clone()
+    y = torch.empty((Ln, S, C), device=device)
+
+    def run():
+        for r, k, v, z in toks:
+            wkv.mat_step(st, r, k, v, z, out=y, inplace=True)
+
+    run()
+    torch.cuda.synchronize()
+    y_eager, st_eager = y.clone(), st.clone()
+    st.copy_(st0)
+    g, _ = _capture(run)   # the capture warm-up also runs the steps once
+    for _ in range(3):
+        st.copy_(st0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager) and torch.equal(st, st_eager)

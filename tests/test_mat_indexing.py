@@ -81,9 +81,12 @@ def test_forward_addresses_stay_in_bounds(B, T, H):
 
 @pytest.mark.parametrize("L,S,H", [(1, 1, 1), (2, 3, 2), (1, 1, 5)])
 def test_step_addresses_stay_in_bounds(L, S, H):
+    """mat_step_kernel: wave = head; lane (rg, cq) reads and writes columns
+    4cq .. 4cq+3 of rows 4m + rg of the head's state; the key-channel table is
+    read with one element per lane; y is written by the lanes of row group 0."""
     C = H * N
     heads = L * S * H
-    io, st = [], []
+    io_loads, y_stores, st = [], [], []
     for blk in range((heads + 3) // 4):
         for thr in range(256):
             head = blk * 4 + thr // 64
@@ -91,8 +94,16 @@ def test_step_addresses_stay_in_bounds(L, S, H):
             if head >= heads:
                 continue
             row, h = divmod(head, H)
-            io.append(row * C + h * N + lane)
-            st.extend(head * N * N + lane + i * N for i in range(N))
-    io, st = np.array(io), np.array(st)
-    assert np.array_equal(np.unique(io), np.arange(L * S * C))
+            e0 = row * C + h * N
+            io_loads.append(e0 + lane)                          # z, k, r of key channel lane
+            rg, cq = lane >> 4, lane & 15
+            io_loads.extend(e0 + 4 * cq + q for q in range(4))  # v of the lane's columns
+            sb = head * N * N + rg * N + 4 * cq
+            st.extend(sb + m * 4 * N + q for m in range(16) for q in range(4))
+            if rg == 0:
+                y_stores.extend(e0 + 4 * cq + q for q in range(4))
+    io_loads, y_stores, st = np.array(io_loads), np.array(y_stores), np.array(st)
+    assert io_loads.min() >= 0 and io_loads.max() < L * S * C
+    assert np.array_equal(np.unique(y_stores), np.arange(L * S * C))
     assert np.array_equal(np.unique(st), np.arange(heads * N * N))
+    assert st.size == heads * N * N            # each state element once
