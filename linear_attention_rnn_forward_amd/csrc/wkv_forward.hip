@@ -724,7 +724,10 @@ __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProble
                         rr, make_rsrc(static_cast<const char*>(pr.r) + base), voff, row_bytes, n);
             }
         }
-        // the carry of this sub-chunk, then the next one's
+        // the carry of this sub-chunk, then the next one's.  The hand-off is
+        // the workgroup's critical path (every wave waits on it in turn), so
+        // the wave runs it at raised issue priority over the others' passes.
+        __builtin_amdgcn_s_setprio(3);
         while (__hip_atomic_load(&s_seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != int(sc))
             __builtin_amdgcn_s_sleep(1);
         Part<VEC> x;
@@ -748,6 +751,7 @@ __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProble
             if (lane == 0)
                 __hip_atomic_store(&s_seq, int(sc + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int q = 0; q < VEC; q++) { s.a[q] = x.a[q]; s.b[q] = x.b[q]; s.A[q] = x.A[q]; s.m[q] = x.m[q]; }
         const rsrc_t yr_ = make_rsrc(static_cast<char*>(pr.y) + base);
