@@ -51,45 +51,6 @@ __device__ __forceinline__ int mat_lane() { return threadIdx.x & 63; }
 
 __device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
-// x * (x of the lane SH below, within the 16-lane row), in place: the first
-// SH lanes of each row have no source and keep x (v_mul_f32_dpp without
-// bound_ctrl leaves such lanes unwritten).  The s_nop covers the two wait
-// states a DPP read needs after a vector write of its source.
-template <int SH>
-__device__ __forceinline__ float row_shr_mul(float x) {
-    float y;
-    if constexpr (SH == 1)
-        asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %1, %2 row_shr:1 row_mask:0xf bank_mask:0xf"
-                     : "=v"(y) : "v"(x), "v"(x), "0"(x));
-    else if constexpr (SH == 2)
-        asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %1, %2 row_shr:2 row_mask:0xf bank_mask:0xf"
-                     : "=v"(y) : "v"(x), "v"(x), "0"(x));
-    else if constexpr (SH == 4)
-        asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %1, %2 row_shr:4 row_mask:0xf bank_mask:0xf"
-                     : "=v"(y) : "v"(x), "v"(x), "0"(x));
-    else
-        asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %1, %2 row_shr:8 row_mask:0xf bank_mask:0xf"
-                     : "=v"(y) : "v"(x), "v"(x), "0"(x));
-    return y;
-}
-
-// inclusive prefix product over the 16 lanes of each row
-__device__ __forceinline__ float row_prod(float x) {
-    x = row_shr_mul<1>(x);
-    x = row_shr_mul<2>(x);
-    x = row_shr_mul<4>(x);
-    x = row_shr_mul<8>(x);
-    return x;
-}
-
-// value of lane 15 of this lane's row (DPP row_newbcast)
-__device__ __forceinline__ float row_last(float x) {
-    float y;
-    asm volatile("s_nop 1\n\tv_mov_b32_dpp %0, %1 row_newbcast:15 row_mask:0xf bank_mask:0xf"
-                 : "=v"(y) : "v"(x));
-    return y;
-}
-
 // d = exp(-softplus(z)) = 1 / (1 + e^z): 1 for z = -inf, 0 once e^z overflows
 __device__ __forceinline__ float decay_of(float z) { return __builtin_amdgcn_rcpf(1.0f + exp_f(z)); }
 
@@ -163,18 +124,21 @@ __device__ __forceinline__ void store_one(void* base, int64_t e, float x) {
     else static_cast<uint16_t*>(base)[e] = uint16_t(bf16_word(x, 0.0f) & 0xffffu);
 }
 
-struct MatShared {
-    // operands of the chunked form, double-buffered by chunk parity
-    uint16_t rq[2][kCT][kRowPad];   // r_t[i] D_t[i]
-    uint16_t kq[2][kCT][kRowPad];   // k_s[i] / D_s[i]
-    uint16_t kdt[2][kN][kColPad];   // k_s[i] D_15[i] / D_s[i], [i][s]
-    uint16_t vt[2][kN][kColPad];    // v_s[j], [j][s]
-    float el[2][kN];                // D_15[i]
-    // fp32 storage (token-by-token form only): r, k, d, v of the chunk, rows
-    // padded so that a wave's 16-byte writes spread over the banks
+// The operand tiles of one chunk (chunked form) and its y tile.
+struct ChunkOps {
+    uint16_t rq[kCT][kRowPad];    // r_t[i] D_t[i]
+    uint16_t kq[kCT][kRowPad];    // k_s[i] / D_s[i]
+    uint16_t kdt[kN][kColPad];    // k_s[i] D_15[i] / D_s[i], [i][s]
+    uint16_t vt[kN][kColPad];     // v_s[j], [j][s]
+    float el[kN];                 // D_15[i]
+    uint16_t yt[kCT][kRowPad];    // y of the chunk, written out afterwards
+};
+
+// The token-by-token kernel's fp32 inputs of a chunk, double-buffered by
+// chunk parity; rows padded so that a wave's 16-byte writes spread over the
+// banks.
+struct TokShared {
     float rf[2][kCT][kN + 4], kf[2][kCT][kN + 4], df[2][kCT][kN + 4], vf[2][kCT][kN + 4];
-    uint16_t yt[2][kCT][kRowPad];   // y of a chunk (chunked form), written out one chunk later
-    int exact_chunk[2];             // chunk of this parity that must run token by token
 };
 
 // The inputs of one producer thread for one chunk: four channels of one token.
@@ -208,42 +172,24 @@ __device__ __forceinline__ uint2 pad_z(bool live, uint2 x) {
     return live ? x : make_uint2(0xff80ff80u, 0xff80ff80u);
 }
 
-// v_s[j] of four channels of one token into the [channel][token] tile: bf16
-// storage is written as stored, fp32 is rounded.
-template <int DT>
-__device__ __forceinline__ void store_vt(uint16_t (*vt)[kColPad], int i0, int tt,
-                                         typename Quad<DT>::Raw raw, const float (&vv)[4]) {
-    if constexpr (DT == kBF16) {
-        vt[i0 + 0][tt] = uint16_t(raw.x & 0xffffu);
-        vt[i0 + 1][tt] = uint16_t(raw.x >> 16);
-        vt[i0 + 2][tt] = uint16_t(raw.y & 0xffffu);
-        vt[i0 + 3][tt] = uint16_t(raw.y >> 16);
-    } else {
-#pragma unroll
-        for (int c = 0; c < 4; c++) vt[i0 + c][tt] = uint16_t(bf16_word(vv[c], 0.0f) & 0xffffu);
-    }
-}
-
 __device__ __forceinline__ int chunk_tokens(int64_t T, int64_t ch) {
     const int64_t left = T - ch * kCT;  // <= 0 past the last chunk
     return left < kCT ? (left > 0 ? int(left) : 0) : kCT;
 }
 
-// Producer: the operands of chunk ch into LDS buffer ch & 1.  Thread (tt, i0)
-// handles token tt of the chunk and channels i0 .. i0+3.  Chunks past the last
-// one are all padding (no decay, zero keys).
-template <int DT, bool PER_TOKEN_Z, bool EXACT_ONLY>
-__device__ __forceinline__ void produce_chunk(MatShared& sh, int tt, int i0, int lane,
-                                              const ChunkIn<DT>& cur, const float (&dc)[4],
-                                              int64_t T, int64_t ch) {
+// Producer of the token-by-token kernel: the fp32 inputs of chunk ch into LDS
+// buffer ch & 1.  Thread (tt, i0) handles token tt of the chunk and channels
+// i0 .. i0+3.  Chunks past the last one are all padding (no decay, zero keys).
+template <int DT, bool PER_TOKEN_Z>
+__device__ __forceinline__ void stage_chunk(TokShared& sh, int tt, int i0, const ChunkIn<DT>& cur,
+                                            const float (&dc)[4], int64_t T, int64_t ch) {
     using Q = Quad<DT>;
     const int buf = int(ch & 1);
     const bool live = tt < chunk_tokens(T, ch);
     float rv[4], kv[4], vv[4], dcy[4];
-    const typename Q::Raw vraw = keep_if(live, cur.v);
+    Q::unpack(keep_if(live, cur.v), vv);
     Q::unpack(keep_if(live, cur.r), rv);
     Q::unpack(keep_if(live, cur.k), kv);
-    Q::unpack(vraw, vv);
     if constexpr (PER_TOKEN_Z) {
         float zv[4];
         Q::unpack(pad_z(live, cur.z), zv);
@@ -253,34 +199,10 @@ __device__ __forceinline__ void produce_chunk(MatShared& sh, int tt, int i0, int
 #pragma unroll
         for (int c = 0; c < 4; c++) dcy[c] = live ? dc[c] : 1.0f;
     }
-    if constexpr (EXACT_ONLY) {
-        // the token-by-token form's inputs
-        *reinterpret_cast<float4*>(&sh.rf[buf][tt][i0]) = make_float4(rv[0], rv[1], rv[2], rv[3]);
-        *reinterpret_cast<float4*>(&sh.kf[buf][tt][i0]) = make_float4(kv[0], kv[1], kv[2], kv[3]);
-        *reinterpret_cast<float4*>(&sh.df[buf][tt][i0]) = make_float4(dcy[0], dcy[1], dcy[2], dcy[3]);
-        *reinterpret_cast<float4*>(&sh.vf[buf][tt][i0]) = make_float4(vv[0], vv[1], vv[2], vv[3]);
-    } else {
-        bool wide = false;
-        float rq[4], kq[4];
-#pragma unroll
-        for (int c = 0; c < 4; c++) {
-            const float D = row_prod(dcy[c]);      // D_t = prod_{tau <= t} d_tau, <= 1
-            const float DL = row_last(D);          // D_15
-            wide = wide || !(DL >= kMinChunkDecay);
-            const float inv = __builtin_amdgcn_rcpf(D);   // <= 1 / D_15
-            rq[c] = rv[c] * D;
-            kq[c] = kv[c] * inv;
-            const float kd = kv[c] * (DL * inv);
-            if (tt == 15) sh.el[buf][i0 + c] = DL;
-            sh.kdt[buf][i0 + c][tt] = uint16_t(bf16_word(kd, 0.0f) & 0xffffu);
-        }
-        store_vt<DT>(sh.vt[buf], i0, tt, vraw, vv);
-        *reinterpret_cast<uint2*>(&sh.rq[buf][tt][i0]) =
-            make_uint2(bf16_word(rq[0], rq[1]), bf16_word(rq[2], rq[3]));
-        *reinterpret_cast<uint2*>(&sh.kq[buf][tt][i0]) =
-            make_uint2(bf16_word(kq[0], kq[1]), bf16_word(kq[2], kq[3]));
-        if (__builtin_amdgcn_ballot_w64(wide) != 0 && lane == 0) sh.exact_chunk[buf] = int(ch);
-    }
+    *reinterpret_cast<float4*>(&sh.rf[buf][tt][i0]) = make_float4(rv[0], rv[1], rv[2], rv[3]);
+    *reinterpret_cast<float4*>(&sh.kf[buf][tt][i0]) = make_float4(kv[0], kv[1], kv[2], kv[3]);
+    *reinterpret_cast<float4*>(&sh.df[buf][tt][i0]) = make_float4(dcy[0], dcy[1], dcy[2], dcy[3]);
+    *reinterpret_cast<float4*>(&sh.vf[buf][tt][i0]) = make_float4(vv[0], vv[1], vv[2], vv[3]);
 }
 
 // r, k, d of token row e (element offset of its channel 0 in this head) for
@@ -303,133 +225,117 @@ __device__ __forceinline__ void token_inputs(const MatProblem& pr, int64_t e, in
     }
 }
 
-// Consumer: chunk ch from LDS buffer ch & 1 against the state S (accumulator
-// layout: S[b][r] = S[16b + 4g + r][jcol]).  The token-by-token form writes y
-// of its 16 value columns to global memory at once; the chunked form leaves
-// it in the tile yt[ch & 1] and returns true (store_tile writes it out).
-template <int DT, bool PER_TOKEN_Z, bool EXACT_ONLY>
-__device__ __forceinline__ bool consume_chunk(const MatProblem& pr, MatShared& sh, int wave, int g,
-                                              int nn, int64_t row0, int64_t h, int64_t ch,
-                                              float (&S)[4][4]) {
-    using Q = Quad<DT>;
+// The chunked form's operands of one consumer lane: rows 16b + 4g .. +3 of
+// its token nn (rq, kq), key channels 16b + nn over tokens 4g .. +3 (kd), and
+// value column jcol over the same tokens (v).
+struct FastOps {
+    short4_t rqB[4], kqA[4], kdA[4], vA;
+};
+
+__device__ __forceinline__ void read_ops(const ChunkOps& op, int g, int nn, int jcol, FastOps& f) {
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+        f.rqB[b] = lds4(&op.rq[nn][16 * b + 4 * g]);
+        f.kqA[b] = lds4(&op.kq[nn][16 * b + 4 * g]);
+        f.kdA[b] = lds4(&op.kdt[16 * b + nn][4 * g]);
+    }
+    f.vA = lds4(&op.vt[jcol][4 * g]);
+}
+
+// One chunk on the matrix cores against the state S (accumulator layout:
+// S[b][r] = S[16b + 4g + r][jcol]); y of the wave's 16 value columns goes to
+// the tile op.yt.
+__device__ __forceinline__ void consume_fast(ChunkOps& op, const FastOps& f, int wave, int g, int nn,
+                                             float (&S)[4][4]) {
+    float4_t yacc = {0.f, 0.f, 0.f, 0.f};
+    float4_t aacc = {0.f, 0.f, 0.f, 0.f};
+    // the contraction over the 64 key channels as two 16x16x32 products:
+    // lane group g supplies rows 16b + 4g .. +3 of blocks b = 2m, 2m+1 (its
+    // own state registers), and the same channels of rq and kq
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+        const short4_t s0 = pack4(S[2 * m][0], S[2 * m][1], S[2 * m][2], S[2 * m][3]);
+        const short4_t s1 = pack4(S[2 * m + 1][0], S[2 * m + 1][1], S[2 * m + 1][2], S[2 * m + 1][3]);
+        yacc = mfma32(s0, s1, f.rqB[2 * m], f.rqB[2 * m + 1], yacc);
+        aacc = mfma32(f.kqA[2 * m], f.kqA[2 * m + 1], f.rqB[2 * m], f.rqB[2 * m + 1], aacc);
+    }
+    // aacc[r] = score of key token s = 4g + r for query token nn; causal mask s <= t
+    float am[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) am[r] = (4 * g + r <= nn) ? aacc[r] : 0.0f;
+    yacc = mfma16(f.vA, pack4(am[0], am[1], am[2], am[3]), yacc);
+    // yacc[r] = y[token nn][column 16 wave + 4g + r], into the tile: a
+    // wave's direct stores would write 32 bytes of each of 16 rows
+    *reinterpret_cast<uint2*>(&op.yt[nn][16 * wave + 4 * g]) =
+        make_uint2(bf16_word(yacc[0], yacc[1]), bf16_word(yacc[2], yacc[3]));
+    // S <- diag(D_15) S + Kd^T V: the product does not wait for D_15
+    float4_t upd[4];
+#pragma unroll
+    for (int b = 0; b < 4; b++) upd[b] = mfma16(f.kdA[b], f.vA, float4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+        const float4 e4 = *reinterpret_cast<const float4*>(&op.el[16 * b + 4 * g]);
+        S[b][0] = __builtin_fmaf(S[b][0], e4.x, upd[b][0]);
+        S[b][1] = __builtin_fmaf(S[b][1], e4.y, upd[b][1]);
+        S[b][2] = __builtin_fmaf(S[b][2], e4.z, upd[b][2]);
+        S[b][3] = __builtin_fmaf(S[b][3], e4.w, upd[b][3]);
+    }
+}
+
+// One chunk token by token in fp32, y of the wave's 16 value columns written
+// to global memory at once.  FROM_LDS: the inputs are the fp32 arrays of
+// buffer buf (fp32 storage); otherwise they are read from global memory (the
+// rare chunk of the chunked kernel whose decay is too steep for it).
+template <int DT, bool PER_TOKEN_Z, bool FROM_LDS>
+__device__ __forceinline__ void consume_tokens(const MatProblem& pr, const TokShared* sh, int buf, int g,
+                                               int jcol, int64_t row0, int64_t h, int64_t ch,
+                                               float (&S)[4][4]) {
     const int64_t C = pr.H * kN;
     const int64_t t0 = ch * kCT;
     const int n = chunk_tokens(pr.T, ch);
-    const int buf = int(ch & 1);
-    const int jcol = 16 * wave + nn;
-    // The chunked form's operands are read before the choice of form, so that
-    // their LDS latency overlaps the flag's (reading them is harmless when the
-    // chunk runs token by token).
-    short4_t rqB[4], kqA[4], kdA[4], vA;
-    if constexpr (!EXACT_ONLY) {
+    for (int t = 0; t < n; t++) {
+        const int64_t e = (row0 + t0 + t) * C + h * kN;
+        float vj;
+        if constexpr (FROM_LDS) vj = sh->vf[buf][t][jcol];
+        else vj = load_one<DT>(pr.v, e + jcol);
+        float yp = 0.0f;
 #pragma unroll
         for (int b = 0; b < 4; b++) {
-            rqB[b] = lds4(&sh.rq[buf][nn][16 * b + 4 * g]);
-            kqA[b] = lds4(&sh.kq[buf][nn][16 * b + 4 * g]);
-            kdA[b] = lds4(&sh.kdt[buf][16 * b + nn][4 * g]);
-        }
-        vA = lds4(&sh.vt[buf][jcol][4 * g]);
-    }
-    if (EXACT_ONLY || sh.exact_chunk[buf] == int(ch)) {
-        // ---- token by token, fp32 ----
-        for (int t = 0; t < n; t++) {
-            const int64_t e = (row0 + t0 + t) * C + h * kN;
-            const float vj = EXACT_ONLY ? sh.vf[buf][t][jcol] : load_one<DT>(pr.v, e + jcol);
-            float yp = 0.0f;
-#pragma unroll
-            for (int b = 0; b < 4; b++) {
-                float dd[4], kk[4], rr[4];
-                if constexpr (EXACT_ONLY) {
-                    const float4 d4 = *reinterpret_cast<const float4*>(&sh.df[buf][t][16 * b + 4 * g]);
-                    const float4 k4 = *reinterpret_cast<const float4*>(&sh.kf[buf][t][16 * b + 4 * g]);
-                    const float4 r4 = *reinterpret_cast<const float4*>(&sh.rf[buf][t][16 * b + 4 * g]);
-                    dd[0] = d4.x; dd[1] = d4.y; dd[2] = d4.z; dd[3] = d4.w;
-                    kk[0] = k4.x; kk[1] = k4.y; kk[2] = k4.z; kk[3] = k4.w;
-                    rr[0] = r4.x; rr[1] = r4.y; rr[2] = r4.z; rr[3] = r4.w;
-                } else {
-                    token_inputs<DT, PER_TOKEN_Z>(pr, e, h * kN, 16 * b + 4 * g, rr, kk, dd);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    S[b][r] = __builtin_fmaf(dd[r], S[b][r], kk[r] * vj);
-                    yp = __builtin_fmaf(rr[r], S[b][r], yp);
-                }
+            float dd[4], kk[4], rr[4];
+            if constexpr (FROM_LDS) {
+                const float4 d4 = *reinterpret_cast<const float4*>(&sh->df[buf][t][16 * b + 4 * g]);
+                const float4 k4 = *reinterpret_cast<const float4*>(&sh->kf[buf][t][16 * b + 4 * g]);
+                const float4 r4 = *reinterpret_cast<const float4*>(&sh->rf[buf][t][16 * b + 4 * g]);
+                dd[0] = d4.x; dd[1] = d4.y; dd[2] = d4.z; dd[3] = d4.w;
+                kk[0] = k4.x; kk[1] = k4.y; kk[2] = k4.z; kk[3] = k4.w;
+                rr[0] = r4.x; rr[1] = r4.y; rr[2] = r4.z; rr[3] = r4.w;
+            } else {
+                token_inputs<DT, PER_TOKEN_Z>(pr, e, h * kN, 16 * b + 4 * g, rr, kk, dd);
             }
-            // the four lane groups hold the partial sums over disjoint rows
-            const float y01 = yp + __shfl_xor(yp, 16);
-            const float y = y01 + __shfl_xor(y01, 32);
-            if (g == 0) store_one<DT>(pr.y, e + jcol, y);
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                S[b][r] = __builtin_fmaf(dd[r], S[b][r], kk[r] * vj);
+                yp = __builtin_fmaf(rr[r], S[b][r], yp);
+            }
         }
-        return false;
+        // the four lane groups hold the partial sums over disjoint rows
+        const float y01 = yp + __shfl_xor(yp, 16);
+        const float y = y01 + __shfl_xor(y01, 32);
+        if (g == 0) store_one<DT>(pr.y, e + jcol, y);
     }
-    if constexpr (!EXACT_ONLY) {
-        // ---- the chunk on the matrix cores ----
-        float4_t yacc = {0.f, 0.f, 0.f, 0.f};
-        float4_t aacc = {0.f, 0.f, 0.f, 0.f};
-        // the contraction over the 64 key channels as two 16x16x32 products:
-        // lane group g supplies rows 16b + 4g .. +3 of blocks b = 2m, 2m+1 (its
-        // own state registers), and the same channels of rq and kq
-#pragma unroll
-        for (int m = 0; m < 2; m++) {
-            const short4_t s0 = pack4(S[2 * m][0], S[2 * m][1], S[2 * m][2], S[2 * m][3]);
-            const short4_t s1 = pack4(S[2 * m + 1][0], S[2 * m + 1][1], S[2 * m + 1][2], S[2 * m + 1][3]);
-            yacc = mfma32(s0, s1, rqB[2 * m], rqB[2 * m + 1], yacc);
-            aacc = mfma32(kqA[2 * m], kqA[2 * m + 1], rqB[2 * m], rqB[2 * m + 1], aacc);
-        }
-        // aacc[r] = score of key token s = 4g + r for query token nn; causal mask s <= t
-        float am[4];
-#pragma unroll
-        for (int r = 0; r < 4; r++) am[r] = (4 * g + r <= nn) ? aacc[r] : 0.0f;
-        yacc = mfma16(vA, pack4(am[0], am[1], am[2], am[3]), yacc);
-        // yacc[r] = y[token nn][column 16 wave + 4g + r], into the tile: a
-        // wave's direct stores would write 32 bytes of each of 16 rows
-        *reinterpret_cast<uint2*>(&sh.yt[buf][nn][16 * wave + 4 * g]) =
-            make_uint2(bf16_word(yacc[0], yacc[1]), bf16_word(yacc[2], yacc[3]));
-        // S <- diag(D_15) S + Kd^T V: the product does not wait for D_15
-        float4_t upd[4];
-#pragma unroll
-        for (int b = 0; b < 4; b++) upd[b] = mfma16(kdA[b], vA, float4_t{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int b = 0; b < 4; b++) {
-            const float4 e4 = *reinterpret_cast<const float4*>(&sh.el[buf][16 * b + 4 * g]);
-            S[b][0] = __builtin_fmaf(S[b][0], e4.x, upd[b][0]);
-            S[b][1] = __builtin_fmaf(S[b][1], e4.y, upd[b][1]);
-            S[b][2] = __builtin_fmaf(S[b][2], e4.z, upd[b][2]);
-            S[b][3] = __builtin_fmaf(S[b][3], e4.w, upd[b][3]);
-        }
-    }
-    return true;
-}
-
-// The y tile of chunk ch (n valid rows) from LDS to global memory in whole
-// rows: consumer thread ct writes 4 channels of row ct / 16, so a wave writes
-// 4 rows of 128 bytes per instruction.
-// (read_tile issues the LDS read early; write_tile stores it once it is needed.)
-__device__ __forceinline__ uint2 read_tile(MatShared& sh, int ct, int64_t ch) {
-    return *reinterpret_cast<const uint2*>(&sh.yt[ch & 1][ct >> 4][(ct & 15) * 4]);
-}
-__device__ __forceinline__ void write_tile(const MatProblem& pr, uint2 v, int ct, int64_t row0,
-                                           int64_t h, int64_t ch, int n) {
-    const int row = ct >> 4;
-    if (row < n)
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(pr.y) + (row0 + ch * kCT + row) * pr.H * kN +
-                                  h * kN + (ct & 15) * 4) = v;
-}
-__device__ __forceinline__ void store_tile(const MatProblem& pr, MatShared& sh, int ct,
-                                           int64_t row0, int64_t h, int64_t ch, int n) {
-    write_tile(pr, read_tile(sh, ct, ch), ct, row0, h, ch, n);
 }
 
 // Chunks in flight per producer thread: the inputs of the next kPrefetch
 // chunks are loaded into registers while the current one is processed.
 constexpr int kPrefetch = 4;
 
-// One workgroup of 8 waves per (batch row, head).  Waves 4..7 produce the
-// operands of chunk c+1 while waves 0..3 consume chunk c (matrix-core products
-// and the state); one barrier per chunk hands the double-buffered LDS over.
-template <int DT, bool PER_TOKEN_Z, bool EXACT_ONLY>
-__global__ __launch_bounds__(512, 4) void mat_forward_kernel(MatProblem pr) {
-    __shared__ MatShared sh;
+// Token-by-token form (fp32 storage, or on request): one workgroup of 8 waves
+// per (batch row, head).  Waves 4..7 stage the fp32 inputs of chunk c+1 in LDS
+// while waves 0..3 run chunk c token by token against their 16 value columns
+// of the state; one barrier per chunk hands the double-buffered LDS over.
+template <int DT, bool PER_TOKEN_Z>
+__global__ __launch_bounds__(512, 4) void mat_forward_tokens_kernel(MatProblem pr) {
+    __shared__ TokShared sh;
     const int wave = mat_wave();
     const int lane = mat_lane();
     const bool producer = wave >= 4;
@@ -441,10 +347,9 @@ __global__ __launch_bounds__(512, 4) void mat_forward_kernel(MatProblem pr) {
     // producer role: token tt of a chunk, channels i0 .. i0+3
     const int tt = lane & 15;
     const int i0 = 4 * (4 * (wave & 3) + (lane >> 4));
-    // consumer role: lane group g, column nn of the wave's 16 value columns
+    // consumer role: lane group g, column jcol of the state
     const int g = lane >> 4;
-    const int nn = lane & 15;
-    const int jcol = 16 * (wave & 3) + nn;
+    const int jcol = 16 * (wave & 3) + (lane & 15);
 
     float S[4][4];
     const int64_t sbase = (bb * pr.H + h) * int64_t(kN * kN);
@@ -463,12 +368,10 @@ __global__ __launch_bounds__(512, 4) void mat_forward_kernel(MatProblem pr) {
             for (int c = 0; c < 4; c++) dc[c] = decay_of(static_cast<const float*>(pr.z)[h * kN + i0 + c]);
         }
     }
-    if (threadIdx.x < 2) sh.exact_chunk[threadIdx.x] = -1;
     // the state and decay loads complete here (s_waitcnt vmcnt(0) as an
     // instruction the compiler's wait insertion sees), so that the waits inside
     // the chunk loop only count the prefetch ring's loads
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
 
     // element offset of token tt of chunk ch (ch >= 0), clamped to the last
     // token; only called when T >= 1
@@ -478,13 +381,12 @@ __global__ __launch_bounds__(512, 4) void mat_forward_kernel(MatProblem pr) {
         return e0 + (t < T ? t : T - 1) * C;
     };
     // The producers keep a ring of kPrefetch chunks in registers: slot p is
-    // consumed, then reloaded in place with the chunk kPrefetch ahead.  Loads
+    // staged, then reloaded in place with the chunk kPrefetch ahead.  Loads
     // are unconditional (chunks past the last one load the last token; their
     // values are masked as padding).  In the interval of chunk q the producers
-    // prepare q while the consumers process q - 1.  The two roles run separate
-    // loops (so that neither holds the other's registers) with the same number
-    // of barriers; nothing happens for T = 0.
-    int64_t pend = -1;  // consumers: chunk whose y tile is still to be written
+    // stage q while the consumers run q - 1.  The two roles run separate loops
+    // (so that neither holds the other's registers) with the same number of
+    // barriers; nothing happens for T = 0.
     if (nch > 0) {
         if (producer) {
             // the first pass only loads (a prologue outside the loop would
@@ -495,40 +397,382 @@ __global__ __launch_bounds__(512, 4) void mat_forward_kernel(MatProblem pr) {
 #pragma unroll
                 for (int p = 0; p < kPrefetch; p++) {
                     const int64_t q = q0 + p;
-                    if (q0 >= 0) produce_chunk<DT, PER_TOKEN_Z, EXACT_ONLY>(sh, tt, i0, lane, ring[p], dc, T, q);
+                    if (q0 >= 0) stage_chunk<DT, PER_TOKEN_Z>(sh, tt, i0, ring[p], dc, T, q);
                     load_chunk<DT, PER_TOKEN_Z>(ring[p], pr, elem(q + kPrefetch));
                     if (q0 >= 0) __syncthreads();
                 }
             }
         } else {
-            // the y tile of the chunk consumed in the previous interval is
-            // written out in this one (after the barrier that completes it)
             for (int64_t q0 = 0; q0 <= nch; q0 += kPrefetch) {
 #pragma unroll
                 for (int p = 0; p < kPrefetch; p++) {
                     const int64_t q = q0 + p;
-                    const int64_t prev = pend;
-                    uint2 tile = make_uint2(0u, 0u);
-                    if (prev >= 0) tile = read_tile(sh, int(threadIdx.x), prev);
-                    pend = -1;
-                    if (q >= 1 && q <= nch &&
-                        consume_chunk<DT, PER_TOKEN_Z, EXACT_ONLY>(pr, sh, wave, g, nn, row0, h, q - 1, S))
-                        pend = q - 1;
-                    if (prev >= 0) write_tile(pr, tile, int(threadIdx.x), row0, h, prev, chunk_tokens(T, prev));
+                    if (q >= 1 && q <= nch)
+                        consume_tokens<DT, PER_TOKEN_Z, true>(pr, &sh, int((q - 1) & 1), g, jcol, row0, h, q - 1, S);
                     __syncthreads();
                 }
             }
         }
     }
-    // both roles: the last tile, if still pending, after one more barrier
-    __syncthreads();
-    if (pend >= 0) store_tile(pr, sh, int(threadIdx.x), row0, h, pend, chunk_tokens(T, pend));
     if (!producer && pr.s_out) {
 #pragma unroll
         for (int b = 0; b < 4; b++)
 #pragma unroll
             for (int r = 0; r < 4; r++)
                 pr.s_out[sbase + int64_t(16 * b + 4 * g + r) * kN + jcol] = S[b][r];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Chunked form with a ring of operand tiles (bf16 storage).
+//
+// One workgroup of 8 waves per (batch row, head), as in the token-by-token
+// kernel, but the two roles are not in lockstep: producer wave p (waves 4..7) prepares chunks p, p + 4,
+// p + 8, ... on its own, each into ring slot (chunk mod 4), while the four
+// consumer waves take the chunks in order.  Per slot, `ready` names the chunk
+// whose operands are in it and `done` counts the consumer waves' completions
+// of its chunks (4 per chunk), so chunk q may be written once it reaches
+// 4 (q / 4).  The producer that takes a slot over first writes the previous
+// chunk's y tile out of it, which keeps the stores off the consumers' path.
+// The flags live in LDS; waits poll them.
+//
+// A producer lane (g, n) = (lane / 16, lane % 16) holds tokens 4g .. 4g+3 of
+// its chunk for channels 4n .. 4n+3, so each of its loads covers four whole
+// 128-byte rows of the head: the decay products run along its own four tokens,
+// then across the four lane groups.
+// ---------------------------------------------------------------------------
+
+constexpr int kSlots = 4;                       // ring slots: one per producer wave
+constexpr uint64_t kRingSpinTicks = 20000000;   // 200 ms of the 100 MHz real-time counter
+constexpr int kProducerSleep = 4;               // producers wait for a free slot at a slower poll
+
+struct MatRing {
+    ChunkOps slot[kSlots];
+    int ready[kSlots];   // chunk whose operands the slot holds (-1: none yet)
+    int done[kSlots];    // consumer waves' completions of the slot's chunks, in all
+    int exact[kSlots];   // 1 when the slot's chunk must run token by token
+    int gave_up;         // set once a wait timed out: no later wait blocks
+};
+
+// Wait until *f == want.  The wait is bounded, and once one wait of the
+// workgroup has given up no other blocks: a slip in the hand-over would give
+// wrong results rather than a workgroup that does not end.
+// SLEEP: the pause between polls (units of 64 cycles).
+template <int SLEEP>
+__device__ __forceinline__ void ring_wait(MatRing& sh, int* f, int want) {
+    if (__hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == want) return;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (uint32_t i = 1;; i++) {
+        __builtin_amdgcn_s_sleep(SLEEP);
+        if (__hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == want) return;
+        // the clock and the give-up flag are looked at every 16th poll
+        if ((i & 15) == 0) {
+            if (__hip_atomic_load(&sh.gave_up, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) return;
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kRingSpinTicks) {
+                __hip_atomic_store(&sh.gave_up, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                return;
+            }
+        }
+    }
+}
+
+// The raw bf16 inputs of one chunk held by a producer lane: word pair j is
+// token 4g + j, channels 4n .. 4n+3.
+struct RawChunk {
+    u32x2_t r[4], k[4], v[4], z[4];
+};
+
+// Buffer descriptor of chunk q of one array: its first row at channel h * 64.
+// Rows past the sequence end read as zero (the descriptor's size stops at the
+// last valid row's head channels); chunks past the last one read nothing.
+__device__ __forceinline__ rsrc_t ring_rsrc(const void* base, int64_t row0, int64_t T, int64_t C,
+                                            int64_t h, int64_t q, int64_t nch) {
+    const bool in = q < nch;
+    const int64_t t0 = in ? q * kCT : 0;
+    const int64_t rows = in ? (T - t0 < kCT ? T - t0 : kCT) : 0;
+    const int64_t row_bytes = C * 2;
+    const int num = rows == kCT ? -1 : int(rows > 0 ? rows * row_bytes - h * kN * 2 : 0);
+    const char* p = static_cast<const char*>(base) + ((row0 + t0) * C + h * kN) * 2;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, num, 0x00020000);
+}
+
+// The loads of chunk q: voff[j] is the byte offset of the lane's word pair j
+// (token 4g + j, channel 4n) from the chunk's first row.  The whole offset is
+// in the vector operand, where the descriptor's size check applies to it.
+template <bool PER_TOKEN_Z>
+__device__ __forceinline__ void ring_load(RawChunk& x, const MatProblem& pr, int64_t row0, int64_t h,
+                                          int64_t q, int64_t nch, const uint32_t (&voff)[4]) {
+    const int64_t T = pr.T, C = pr.H * kN;
+    const rsrc_t rr = ring_rsrc(pr.r, row0, T, C, h, q, nch);
+    const rsrc_t kr = ring_rsrc(pr.k, row0, T, C, h, q, nch);
+    const rsrc_t vr = ring_rsrc(pr.v, row0, T, C, h, q, nch);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        x.r[j] = __builtin_amdgcn_raw_buffer_load_b64(rr, voff[j], 0u, kStreamLoad);
+        x.k[j] = __builtin_amdgcn_raw_buffer_load_b64(kr, voff[j], 0u, kStreamLoad);
+        x.v[j] = __builtin_amdgcn_raw_buffer_load_b64(vr, voff[j], 0u, kStreamLoad);
+    }
+    if constexpr (PER_TOKEN_Z) {
+        const rsrc_t zr = ring_rsrc(pr.z, row0, T, C, h, q, nch);
+#pragma unroll
+        for (int j = 0; j < 4; j++) x.z[j] = __builtin_amdgcn_raw_buffer_load_b64(zr, voff[j], 0u, kStreamLoad);
+    }
+}
+
+__device__ __forceinline__ void unpack_bf16x4(u32x2_t w, float (&x)[4]) {
+    x[0] = __uint_as_float(w.x << 16);
+    x[1] = __uint_as_float(w.x & 0xffff0000u);
+    x[2] = __uint_as_float(w.y << 16);
+    x[3] = __uint_as_float(w.y & 0xffff0000u);
+}
+
+// Value of lane `src` of the wave.
+__device__ __forceinline__ float lane_value(float x, int src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
+}
+
+// Producer: the operand tiles of chunk q from the lane's raw inputs into ring
+// slot q mod kSlots, once the slot is free; then the slot is published.
+// The y tile of chunk q, consumed from slot s, to global memory in whole
+// 128-byte rows (a token-by-token chunk has written y already).
+__device__ __forceinline__ void ring_store_tile(const MatProblem& pr, MatRing& sh, int s, int64_t q, int lane,
+                                                int64_t row0, int64_t h) {
+    if (sh.exact[s] != 0) return;
+    const int64_t C = pr.H * kN;
+    const int g = lane >> 4, nn = lane & 15;
+    const int n = chunk_tokens(pr.T, q);
+    const ChunkOps& op = sh.slot[s];
+    uint2 yv[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) yv[i] = *reinterpret_cast<const uint2*>(&op.yt[4 * i + g][4 * nn]);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int row = 4 * i + g;
+        if (row < n)
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(pr.y) + (row0 + q * kCT + row) * C + h * kN + 4 * nn) =
+                yv[i];
+    }
+}
+
+template <bool PER_TOKEN_Z>
+__device__ __forceinline__ void ring_produce(const MatProblem& pr, MatRing& sh, const RawChunk& x,
+                                             const float (&dc)[4], int lane, int64_t row0, int64_t h,
+                                             int64_t q) {
+    const int64_t T = pr.T;
+    const int g = lane >> 4, n = lane & 15;
+    const int s = int(q % kSlots);
+    // the slot is free once the consumers are done with the chunk four back;
+    // that chunk's y tile goes out first (the chunks ahead leave time for it)
+    ring_wait<kProducerSleep>(sh, &sh.done[s], 4 * int(q / kSlots));
+    if (q >= kSlots) ring_store_tile(pr, sh, s, q - kSlots, lane, row0, h);
+    const int live = chunk_tokens(T, q);   // tokens of the chunk; 4g + j >= live is padding
+    // decays d[j][c] of token 4g + j, channel 4n + c; padding tokens do not decay
+    float d[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        if constexpr (PER_TOKEN_Z) {
+            float zv[4];
+            unpack_bf16x4(x.z[j], zv);
+#pragma unroll
+            for (int c = 0; c < 4; c++) d[j][c] = decay_of(4 * g + j < live ? zv[c] : -__builtin_inff());
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; c++) d[j][c] = 4 * g + j < live ? dc[c] : 1.0f;
+        }
+    }
+    // D[j][c] = product of the chunk's decays up to token 4g + j: along the
+    // lane's own tokens, then the products of the lane groups before it
+    float D[4][4], DL[4];
+    bool wide = false;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        D[0][c] = d[0][c];
+#pragma unroll
+        for (int j = 1; j < 4; j++) D[j][c] = D[j - 1][c] * d[j][c];
+        // (the lane reads are taken by every lane: a read from a lane that
+        // is switched off returns nothing useful)
+        const float t = D[3][c];                                         // group g's product
+        const float u1 = lane_value(t, lane - 16);
+        const float t1 = g >= 1 ? t * u1 : t;                            // groups g-1 .. g
+        const float u2 = lane_value(t1, lane - 32);
+        const float t2 = g >= 2 ? t1 * u2 : t1;                          // groups 0 .. g
+        const float before = lane_value(t2, lane - 16);                  // groups 0 .. g-1
+        const float e = g >= 1 ? before : 1.0f;
+        DL[c] = lane_value(t2, 48 + n);                                  // the whole chunk
+#pragma unroll
+        for (int j = 0; j < 4; j++) D[j][c] *= e;
+        wide = wide || !(DL[c] >= kMinChunkDecay);
+    }
+    // rq = r D, kq = k / D, kd = k D_15 / D in bf16
+    uint32_t rq[4][2], kq[4][2], kd[4][2];   // [token j][channel pair]; kd: [channel c][token pair]
+    float kdv[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        float rv[4], kv[4], q4[4], r4[4];
+        unpack_bf16x4(x.r[j], rv);
+        unpack_bf16x4(x.k[j], kv);
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            const float inv = __builtin_amdgcn_rcpf(D[j][c]);
+            r4[c] = rv[c] * D[j][c];
+            q4[c] = kv[c] * inv;
+            kdv[j][c] = q4[c] * DL[c];
+        }
+        rq[j][0] = bf16_word(r4[0], r4[1]);
+        rq[j][1] = bf16_word(r4[2], r4[3]);
+        kq[j][0] = bf16_word(q4[0], q4[1]);
+        kq[j][1] = bf16_word(q4[2], q4[3]);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        kd[c][0] = bf16_word(kdv[0][c], kdv[1][c]);
+        kd[c][1] = bf16_word(kdv[2][c], kdv[3][c]);
+    }
+    // v as stored, regrouped from [token][channel] to [channel][token] words:
+    // channel c of tokens 0, 1 (then 2, 3) = 16-bit half c of words j, j + 1
+    uint32_t vt[4][2];
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+#pragma unroll
+        for (int p = 0; p < 2; p++) {
+            const uint32_t lo = (c < 2) ? x.v[2 * p].x : x.v[2 * p].y;
+            const uint32_t hi = (c < 2) ? x.v[2 * p + 1].x : x.v[2 * p + 1].y;
+            // selector: bytes of hi are 4..7, of lo 0..3; low half of a word is bytes 0, 1
+            vt[c][p] = (c & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u) : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
+    }
+    const bool exact = __builtin_amdgcn_ballot_w64(wide) != 0;
+
+    ChunkOps& op = sh.slot[s];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        *reinterpret_cast<uint2*>(&op.rq[4 * g + j][4 * n]) = make_uint2(rq[j][0], rq[j][1]);
+        *reinterpret_cast<uint2*>(&op.kq[4 * g + j][4 * n]) = make_uint2(kq[j][0], kq[j][1]);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        *reinterpret_cast<uint2*>(&op.kdt[4 * n + c][4 * g]) = make_uint2(kd[c][0], kd[c][1]);
+        *reinterpret_cast<uint2*>(&op.vt[4 * n + c][4 * g]) = make_uint2(vt[c][0], vt[c][1]);
+    }
+    if (g == 0) *reinterpret_cast<float4*>(&op.el[4 * n]) = make_float4(DL[0], DL[1], DL[2], DL[3]);
+    if (lane == 0) {
+        sh.exact[s] = exact ? 1 : 0;
+        __hip_atomic_store(&sh.ready[s], int(q), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+}
+
+// A consumer wave is done with the chunk in slot s (its operand reads and its
+// part of the y tile complete before the count).
+__device__ __forceinline__ void ring_finish(MatRing& sh, int s, int lane) {
+    if (lane == 0) __hip_atomic_fetch_add(&sh.done[s], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+template <bool PER_TOKEN_Z>
+__global__ __launch_bounds__(512, 4) void mat_forward_ring_kernel(MatProblem pr) {
+    __shared__ MatRing sh;
+    const int wave = mat_wave();
+    const int lane = mat_lane();
+    const bool producer = wave >= 4;
+    const int64_t T = pr.T, C = pr.H * kN;
+    const int64_t bb = blockIdx.x / pr.H;
+    const int64_t h = blockIdx.x - bb * pr.H;
+    const int64_t row0 = bb * T;
+    const int64_t nch = (T + kCT - 1) / kCT;
+    const int g = lane >> 4;
+    const int nn = lane & 15;
+
+    float S[4][4];
+    const int64_t sbase = (bb * pr.H + h) * int64_t(kN * kN);
+    const int jcol = 16 * (wave & 3) + nn;
+    if (!producer) {
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                S[b][r] = pr.s_in ? pr.s_in[sbase + int64_t(16 * b + 4 * g + r) * kN + jcol] : 0.0f;
+    }
+    // per-channel decay (Eagle) of the producer lane's channels 4 nn .. 4 nn + 3
+    float dc[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (!PER_TOKEN_Z) {
+        if (producer) {
+#pragma unroll
+            for (int c = 0; c < 4; c++) dc[c] = decay_of(static_cast<const float*>(pr.z)[h * kN + 4 * nn + c]);
+        }
+    }
+    if (threadIdx.x == 0) sh.gave_up = 0;
+    if (threadIdx.x < kSlots) {
+        sh.ready[threadIdx.x] = -1;
+        sh.done[threadIdx.x] = 0;
+        sh.exact[threadIdx.x] = 0;
+    }
+    // the state and decay loads complete here (s_waitcnt vmcnt(0) as an
+    // instruction the compiler's wait insertion sees), so that the waits in
+    // the loops only count the loads of the chunks in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+
+    if (producer) {
+        const int p = wave - 4;
+        const uint32_t row_bytes = uint32_t(C * 2);
+        uint32_t voff[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) voff[j] = uint32_t(4 * g + j) * row_bytes + uint32_t(8 * nn);
+        // two register sets: the wave's next chunk loads while this one is prepared
+        RawChunk xa, xb;
+        ring_load<PER_TOKEN_Z>(xa, pr, row0, h, p, nch, voff);
+        for (int64_t q = p; q < nch; q += 2 * kSlots) {
+            ring_load<PER_TOKEN_Z>(xb, pr, row0, h, q + kSlots, nch, voff);
+            ring_produce<PER_TOKEN_Z>(pr, sh, xa, dc, lane, row0, h, q);
+            if (q + kSlots >= nch) break;
+            ring_load<PER_TOKEN_Z>(xa, pr, row0, h, q + 2 * kSlots, nch, voff);
+            ring_produce<PER_TOKEN_Z>(pr, sh, xb, dc, lane, row0, h, q + kSlots);
+        }
+        // the wave's last chunk: its y tile once the consumers are done with it
+        if (p < nch) {
+            const int64_t last = p + (nch - 1 - p) / kSlots * kSlots;
+            ring_wait<kProducerSleep>(sh, &sh.done[p], 4 * int(last / kSlots + 1));
+            ring_store_tile(pr, sh, p, last, lane, row0, h);
+        }
+    } else {
+        // chunks in pairs: the two chunks' products are independent but for
+        // the state, so their latencies overlap
+        for (int64_t q = 0; q < nch; q += 2) {
+            const int64_t q1 = q + 1;
+            const bool two = q1 < nch;
+            const int s0 = int(q % kSlots), s1 = int(q1 % kSlots);
+            ring_wait<1>(sh, &sh.ready[s0], int(q));
+            if (two) ring_wait<1>(sh, &sh.ready[s1], int(q1));
+            const bool fast0 = sh.exact[s0] == 0;
+            const bool fast1 = two && sh.exact[s1] == 0;
+            if (fast0 && fast1) {
+                FastOps f0, f1;
+                read_ops(sh.slot[s0], g, nn, jcol, f0);
+                read_ops(sh.slot[s1], g, nn, jcol, f1);
+                consume_fast(sh.slot[s0], f0, wave, g, nn, S);
+                consume_fast(sh.slot[s1], f1, wave, g, nn, S);
+            } else {
+                // one chunk at a time (the last one, or a token-by-token one)
+                for (int i = 0; i < (two ? 2 : 1); i++) {
+                    const int si = i == 0 ? s0 : s1;
+                    if (i == 0 ? fast0 : fast1) {
+                        FastOps f;
+                        read_ops(sh.slot[si], g, nn, jcol, f);
+                        consume_fast(sh.slot[si], f, wave, g, nn, S);
+                    } else {
+                        consume_tokens<kBF16, PER_TOKEN_Z, false>(pr, nullptr, 0, g, jcol, row0, h, q + i, S);
+                    }
+                }
+            }
+            ring_finish(sh, s0, lane);
+            if (two) ring_finish(sh, s1, lane);
+        }
+        if (pr.s_out) {
+#pragma unroll
+            for (int b = 0; b < 4; b++)
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    pr.s_out[sbase + int64_t(16 * b + 4 * g + r) * kN + jcol] = S[b][r];
+        }
     }
 }
 
@@ -606,19 +850,22 @@ __global__ __launch_bounds__(256) void mat_step_kernel(MatStepProblem pr) {
 
 hipError_t launch_mat_forward(const MatProblem& pr, hipStream_t stream) {
     const dim3 grid(unsigned(pr.B * pr.H)), block(512);
-    const bool exact = pr.dtype == kF32 || pr.path == 1;
-#define WKV_MAT_FWD(DT, PT, EX) hipLaunchKernelGGL((mat_forward_kernel<DT, PT, EX>), grid, block, 0, stream, pr)
+    // the ring kernel's byte offsets within a chunk are 32-bit
+    const bool tokens = pr.dtype == kF32 || pr.path == 1 || pr.H * kN * 2 * kCT >= (int64_t(1) << 31);
+#define WKV_MAT_TOK(DT, PT) hipLaunchKernelGGL((mat_forward_tokens_kernel<DT, PT>), grid, block, 0, stream, pr)
+#define WKV_MAT_RING(PT) hipLaunchKernelGGL((mat_forward_ring_kernel<PT>), grid, block, 0, stream, pr)
     if (pr.dtype == kF32) {
-        if (pr.z_per_token) WKV_MAT_FWD(kF32, true, true);
-        else WKV_MAT_FWD(kF32, false, true);
-    } else if (exact) {
-        if (pr.z_per_token) WKV_MAT_FWD(kBF16, true, true);
-        else WKV_MAT_FWD(kBF16, false, true);
+        if (pr.z_per_token) WKV_MAT_TOK(kF32, true);
+        else WKV_MAT_TOK(kF32, false);
+    } else if (tokens) {
+        if (pr.z_per_token) WKV_MAT_TOK(kBF16, true);
+        else WKV_MAT_TOK(kBF16, false);
     } else {
-        if (pr.z_per_token) WKV_MAT_FWD(kBF16, true, false);
-        else WKV_MAT_FWD(kBF16, false, false);
+        if (pr.z_per_token) WKV_MAT_RING(true);
+        else WKV_MAT_RING(false);
     }
-#undef WKV_MAT_FWD
+#undef WKV_MAT_TOK
+#undef WKV_MAT_RING
     return hipGetLastError();
 }
 

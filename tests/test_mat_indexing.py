@@ -1,6 +1,7 @@
 """Host check of the matrix-state kernels' addressing (csrc/wkv_mat.hip).
 
-The element offsets each thread of mat_forward_kernel and mat_step_kernel
+The element offsets each thread of mat_forward_tokens_kernel,
+mat_forward_ring_kernel and mat_step_kernel
 forms are recomputed here from the same formulas, for every workgroup and
 thread of small launches, and checked against the arrays' bounds -- including
 T = 0, where the forward must not load at all (its token clamp needs a token),
@@ -16,8 +17,8 @@ PREFETCH = 4  # chunks in the register ring
 
 
 def forward_offsets(B, T, H):
-    """(loads, stores, state) element offsets of mat_forward_kernel: 512
-    threads per (batch row, head); waves 4..7 load (producers), waves 0..3
+    """(loads, stores, state) element offsets of mat_forward_tokens_kernel:
+    512 threads per (batch row, head); waves 4..7 load (producers), waves 0..3
     store y and hold the state (consumers)."""
     C = H * N
     loads, stores, state = [], [], []
@@ -49,15 +50,9 @@ def forward_offsets(B, T, H):
             for ch in range(nch):
                 t0 = ch * CT
                 n = max(0, min(CT, T - t0))
-                ct = wave * 64 + lane   # chunked form's output: the y tile in whole rows
-                row, cg = ct >> 4, (ct & 15) * 4
-                if row < n:
-                    stores.extend((row0 + t0 + row) * C + h * N + cg + q for q in range(4))
-                for t in range(n):    # token-by-token form: its inputs read from global memory
-                    e = (row0 + t0 + t) * C + h * N
-                    stores.append(e + jcol)
-                    loads.append(e + jcol)
-                    loads.extend(e + 16 * b + 4 * g + q for b in range(4) for q in range(4))
+                for t in range(n):    # y of column jcol, token by token
+                    if g == 0:
+                        stores.append((row0 + t0 + t) * C + h * N + jcol)
     return np.array(loads, dtype=np.int64), np.array(stores, dtype=np.int64), np.array(state)
 
 
@@ -107,3 +102,87 @@ def test_step_addresses_stay_in_bounds(L, S, H):
     assert np.array_equal(np.unique(y_stores), np.arange(L * S * C))
     assert np.array_equal(np.unique(st), np.arange(heads * N * N))
     assert st.size == heads * N * N            # each state element once
+
+
+def ring_offsets(B, T, H, per_token_z=True, strict_size=True):
+    """Byte offsets of mat_forward_ring_kernel (bf16): the producer loads of
+    every (batch row, head), with the buffer descriptor's size check applied
+    (strict_size: an access is dropped unless it ends within the size; else
+    only when it starts at or past it), the operand-tile writes, and the y
+    stores of the chunked form.  Returns (loads, y_stores, tile_writes)."""
+    C = H * N
+    row_bytes = 2 * C
+    nch = (T + CT - 1) // CT
+    loads, ystores, tiles = [], [], []
+    for blk in range(B * H):
+        bb, h = divmod(blk, H)
+        row0 = bb * T
+        for p in range(4):                       # producer wave p (waves 4..7)
+            chunks = []
+            q = p
+            chunks.append(q)                     # the first load, before the loop
+            while q < nch:
+                chunks.append(q + 4)             # prefetch into the other set
+                if q + 4 >= nch:
+                    break
+                chunks.append(q + 8)
+                q += 8
+            for q in chunks:
+                inside = q < nch
+                t0 = q * CT if inside else 0
+                rows = min(CT, T - t0) if inside else 0
+                base = ((row0 + t0) * C + h * N) * 2
+                size = None if rows == CT else (rows * row_bytes - h * N * 2 if rows > 0 else 0)
+                for lane in range(64):
+                    g, n = lane >> 4, lane & 15
+                    for j in range(4):
+                        off = (4 * g + j) * row_bytes + 8 * n
+                        if size is not None:
+                            dropped = off + 8 > size if strict_size else off >= size
+                            if dropped:
+                                continue
+                        loads.append(((base + off) // 2, bb, h))
+            for q in range(p, nch, 4):
+                for lane in range(64):
+                    g, n = lane >> 4, lane & 15
+                    for j in range(4):
+                        tiles.append(("rq", 4 * g + j, 4 * n))
+                    for c in range(4):
+                        tiles.append(("kdt", 4 * n + c, 4 * g))
+        for q in range(nch):
+            live = min(CT, T - q * CT)
+            for lane in range(64):
+                g, nn = lane >> 4, lane & 15
+                for i in range(4):
+                    row = 4 * i + g
+                    if row < live:
+                        e = (row0 + q * CT + row) * C + h * N + 4 * nn
+                        ystores.extend(e + c for c in range(4))
+    return np.array(loads, dtype=np.int64).reshape(-1, 3), np.array(ystores, dtype=np.int64), tiles
+
+
+@pytest.mark.parametrize("strict", [True, False])
+@pytest.mark.parametrize("B,T,H", [(2, 0, 3), (1, 1, 1), (1, 5, 2), (2, 16, 1), (1, 17, 3),
+                                   (2, 53, 2), (1, 100, 1), (2, 129, 2)])
+def test_ring_addresses_stay_in_bounds(B, T, H, strict):
+    loads, ystores, tiles = ring_offsets(B, T, H, strict_size=strict)
+    n_io = B * T * H * N
+    if T == 0:
+        assert loads.size == 0 and ystores.size == 0
+        return
+    # every load lands on the workgroup's own batch row and head (so never on
+    # a token past T), and every element is loaded
+    el, bb, h = loads[:, 0], loads[:, 1], loads[:, 2]
+    assert el.min() >= 0 and el.max() + 3 < n_io
+    C = H * N
+    assert np.array_equal(el // C // T, bb)
+    assert np.array_equal((el % C) // N, h)
+    assert np.array_equal(np.unique(el // 4 * 4), np.arange(0, n_io, 4))
+    # each y element written exactly once
+    assert ystores.size == n_io
+    assert np.array_equal(np.sort(ystores), np.arange(n_io))
+    for name, r, c in tiles:
+        if name == "rq":
+            assert 0 <= r < CT and 0 <= c and c + 3 < N
+        else:
+            assert 0 <= r < N and 0 <= c and c + 3 < CT
