@@ -534,24 +534,29 @@ __device__ __forceinline__ float lane_value(float x, int src) {
 // Producer: the operand tiles of chunk q from the lane's raw inputs into ring
 // slot q mod kSlots, once the slot is free; then the slot is published.
 // The y tile of chunk q, consumed from slot s, to global memory in whole
-// 128-byte rows (a token-by-token chunk has written y already).
-__device__ __forceinline__ void ring_store_tile(const MatProblem& pr, MatRing& sh, int s, int64_t q, int lane,
-                                                int64_t row0, int64_t h) {
-    if (sh.exact[s] != 0) return;
-    const int64_t C = pr.H * kN;
+// 128-byte rows.  Nothing is written when `any` is false (no chunk) or the
+// chunk ran token by token (y is out already): the stores then go through a
+// zero-size descriptor, and rows past the sequence end past the descriptor's
+// size, so that the four stores are issued on every path (a branch around
+// them would make later waits for the loads wait for every store as well).
+__device__ __forceinline__ void ring_store_tile(const MatProblem& pr, MatRing& sh, int s, int64_t q, bool any,
+                                                int lane, int64_t row0, int64_t h) {
+    const int64_t C = pr.H * kN, T = pr.T;
     const int g = lane >> 4, nn = lane & 15;
-    const int n = chunk_tokens(pr.T, q);
+    const bool write = any && sh.exact[s] == 0;
+    const int64_t t0 = any ? q * kCT : 0;
+    const int64_t rows = T - t0 < kCT ? T - t0 : kCT;
+    const uint32_t row_bytes = uint32_t(C * 2);
+    const int num = !write ? 0 : (rows == kCT ? -1 : int(rows * int64_t(row_bytes) - h * kN * 2));
+    char* p = static_cast<char*>(pr.y) + ((row0 + t0) * C + h * kN) * 2;
+    const rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(p, (short)0, num, 0x00020000);
     const ChunkOps& op = sh.slot[s];
-    uint2 yv[4];
+    u32x2_t yv[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) yv[i] = *reinterpret_cast<const uint2*>(&op.yt[4 * i + g][4 * nn]);
+    for (int i = 0; i < 4; i++) yv[i] = *reinterpret_cast<const u32x2_t*>(&op.yt[4 * i + g][4 * nn]);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int row = 4 * i + g;
-        if (row < n)
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(pr.y) + (row0 + q * kCT + row) * C + h * kN + 4 * nn) =
-                yv[i];
-    }
+    for (int i = 0; i < 4; i++)
+        __builtin_amdgcn_raw_buffer_store_b64(yv[i], yr, uint32_t(4 * i + g) * row_bytes + uint32_t(8 * nn), 0u, 0);
 }
 
 template <bool PER_TOKEN_Z>
@@ -564,7 +569,7 @@ __device__ __forceinline__ void ring_produce(const MatProblem& pr, MatRing& sh, 
     // the slot is free once the consumers are done with the chunk four back;
     // that chunk's y tile goes out first (the chunks ahead leave time for it)
     ring_wait<kProducerSleep>(sh, &sh.done[s], 4 * int(q / kSlots));
-    if (q >= kSlots) ring_store_tile(pr, sh, s, q - kSlots, lane, row0, h);
+    ring_store_tile(pr, sh, s, q - kSlots, q >= kSlots, lane, row0, h);
     const int live = chunk_tokens(T, q);   // tokens of the chunk; 4g + j >= live is padding
     // decays d[j][c] of token 4g + j, channel 4n + c; padding tokens do not decay
     float d[4][4];
@@ -731,7 +736,7 @@ __global__ __launch_bounds__(512, 4) void mat_forward_ring_kernel(MatProblem pr)
         if (p < nch) {
             const int64_t last = p + (nch - 1 - p) / kSlots * kSlots;
             ring_wait<kProducerSleep>(sh, &sh.done[p], 4 * int(last / kSlots + 1));
-            ring_store_tile(pr, sh, p, last, lane, row0, h);
+            ring_store_tile(pr, sh, p, last, true, lane, row0, h);
         }
     } else {
         // chunks in pairs: the two chunks' products are independent but for
