@@ -427,9 +427,9 @@ __global__ __launch_bounds__(512, 4) void mat_forward_tokens_kernel(MatProblem p
 // Chunked form with a ring of operand tiles (bf16 storage).
 //
 // One workgroup of 8 waves per (batch row, head), as in the token-by-token
-// kernel, but the two roles are not in lockstep: producer wave p (waves 4..7) prepares chunks p, p + 4,
-// p + 8, ... on its own, each into ring slot (chunk mod 4), while the four
-// consumer waves take the chunks in order.  Per slot, `ready` names the chunk
+// kernel, but the two roles are not in lockstep: producer wave p (waves
+// 4..7) prepares chunks p, p + 4, p + 8, ... on its own, each into ring slot
+// (chunk mod 4), while the four consumer waves take the chunks in order.  Per slot, `ready` names the chunk
 // whose operands are in it and `done` counts the consumer waves' completions
 // of its chunks (4 per chunk), so chunk q may be written once it reaches
 // 4 (q / 4).  The producer that takes a slot over first writes the previous
@@ -531,8 +531,6 @@ __device__ __forceinline__ float lane_value(float x, int src) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
 
-// Producer: the operand tiles of chunk q from the lane's raw inputs into ring
-// slot q mod kSlots, once the slot is free; then the slot is published.
 // The y tile of chunk q, consumed from slot s, to global memory in whole
 // 128-byte rows.  Nothing is written when `any` is false (no chunk) or the
 // chunk ran token by token (y is out already): the stores then go through a
@@ -559,6 +557,8 @@ __device__ __forceinline__ void ring_store_tile(const MatProblem& pr, MatRing& s
         __builtin_amdgcn_raw_buffer_store_b64(yv[i], yr, uint32_t(4 * i + g) * row_bytes + uint32_t(8 * nn), 0u, 0);
 }
 
+// Producer: the operand tiles of chunk q from the lane's raw inputs into ring
+// slot q mod kSlots, once the slot is free; then the slot is published.
 template <bool PER_TOKEN_Z>
 __device__ __forceinline__ void ring_produce(const MatProblem& pr, MatRing& sh, const RawChunk& x,
                                              const float (&dc)[4], int lane, int64_t row0, int64_t h,
