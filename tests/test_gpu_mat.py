@@ -184,6 +184,32 @@ def test_deterministic(device):
     assert torch.equal(y1, y2)
 
 
+def test_ordinary_chunks_take_the_matrix_cores(device):
+    """On inputs whose decay over a chunk stays above e^-80 every chunk takes
+    the factorised form (bf16 operands on the matrix cores), not the
+    token-by-token fallback.  The final state (fp32, never rounded to the
+    storage type) tells the two apart: the factorised form's error is that of
+    its bf16 operands, the token-by-token form's that of fp32 arithmetic on
+    the same inputs.  A chunk-form decision that went wrong would keep the
+    results correct and only show up as a much slower kernel."""
+    torch = _torch()
+    wl = SMALL.resized(B=2, T=96, H=2, seed=110)
+    x = synth.make_mat_inputs(wl)
+    # every chunk's decay product stays above e^-80
+    zmax = np.max(x.z.astype(np.float64))
+    assert 16 * np.log1p(np.exp(zmax)) < 80.0
+    r, k, v, z = dev_inputs(x, wl, device)
+    s_ref = ms.forward(x.r, x.k, x.v, x.z)[1]
+    s_mag = ms.forward(x.r, x.k, x.v, x.z, magnitude=True)[1]
+    errs = {}
+    for path in ("chunked", "tokenwise"):
+        _, s_out = _wkv().mat_forward(r, k, v, z, return_state=True, path=path)
+        torch.cuda.synchronize()
+        errs[path] = scaled_err(host(s_out), s_ref, s_mag)
+    assert errs["tokenwise"] < 1e-5, errs
+    assert 1e-4 < errs["chunked"] <= TOL["bf16"], errs
+
+
 # ---------------------------------------------------------------------------
 # decode step
 # ---------------------------------------------------------------------------
