@@ -1,0 +1,125 @@
+"""GPU parity past 32-bit element and byte offsets.
+
+Inputs of more than 2^31 elements (more than 4 GiB per bf16 array) are made
+on the device by the counter-based generator of synth.device, and sampled
+channels are made again on the host from the same counters, so that the fp64
+oracle can run on those channels over the whole sequence.  Every kernel
+forms its addresses from 64-bit bases and 32-bit offsets inside a tile or
+chunk; these tests run the paths on arrays where a 32-bit element or byte
+offset over the whole array would wrap.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import matrix_state as ms
+from oracle.compare import guarded_rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _wkv():
+    import linear_attention_rnn_forward_amd as wkv
+    return wkv
+
+
+def device_normal_bf16(n_rows, C, stream, seed, device, scale=1.0, offset=None):
+    """[n_rows, C] bf16 on the device: element (t, c) is philox_normal of
+    counter t * C + c (times scale, plus offset[c] when given)."""
+    import synth.device as sd
+    torch = _torch()
+    tmp = torch.empty((n_rows, C), dtype=torch.float32, device=device)
+    sd.fill_normal(tmp, (1, 1, n_rows, C), (0, 0, C, 1), 0, stream, seed)
+    if scale != 1.0:
+        tmp.mul_(scale)
+    if offset is not None:
+        tmp.add_(torch.from_numpy(offset).to(device)[None, :])
+    out = tmp.to(torch.bfloat16)
+    del tmp
+    return out
+
+
+def host_columns_bf16(n_rows, C, channels, stream, seed, scale=1.0, offset=None):
+    """The same values for the given channels, [n_rows, len(channels)], as the
+    device rounds them: fp32 value (scaled, offset) rounded to bf16."""
+    t = np.arange(n_rows, dtype=np.uint64)[:, None]
+    ch = np.asarray(channels, dtype=np.uint64)[None, :]
+    x = synth.philox_normal(t * np.uint64(C) + ch, stream, seed)
+    if scale != 1.0:
+        x = (x * np.float32(scale)).astype(np.float32)
+    if offset is not None:
+        x = (x + offset[np.asarray(channels)][None, :].astype(np.float32)).astype(np.float32)
+    return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x))
+
+
+@pytest.mark.parametrize("path", ["auto", "chained"])
+def test_forward_past_32_bit_offsets(device, path):
+    """bf16 [1, 2^20 + 37, 2304]: 2.42e9 elements, 4.8 GB per array."""
+    torch = _torch()
+    T, C, seed = (1 << 20) + 37, 2304, 77
+    assert T * C > 2 ** 31 and 2 * T * C > 2 ** 32
+    k = device_normal_bf16(T, C, synth.STREAM_K, seed, device)
+    v = device_normal_bf16(T, C, synth.STREAM_V, seed, device)
+    rng = np.random.default_rng(seed)
+    w = np.exp(rng.uniform(-5.0, 1.0, C)).astype(np.float32)
+    u = rng.normal(0.0, 0.5, C).astype(np.float32)
+    y, (a, b, p) = _wkv().forward(k.view(1, T, C), v.view(1, T, C), torch.from_numpy(w).to(device),
+                                  torch.from_numpy(u).to(device), return_state=True, path=path)
+    cs = [0, 1, 127, 128, 1151, 2048, 2302, 2303]   # lanes, strips, the last channels
+    idx = torch.tensor(cs, device=device)
+    ys = y[0].index_select(1, idx).float().cpu().numpy()
+    state = [s[0].index_select(0, idx).cpu().numpy() for s in (a, b, p)]
+    del y, k, v
+    torch.cuda.synchronize()
+    kh = host_columns_bf16(T, C, cs, synth.STREAM_K, seed)
+    vh = host_columns_bf16(T, C, cs, synth.STREAM_V, seed)
+    y_ref, (a_ref, b_ref, p_ref) = oracle.forward(kh[None], vh[None], w[cs], u[cs])
+    err = guarded_rel_err(ys, y_ref[0], 1.0)
+    print(f"path={path}: {ys.shape[0]} tokens x {ys.shape[1]} channels, y err {err:.3e}")
+    assert err <= TOL_BF16, f"path={path}: y err {err:.3e}"
+    # the final state, in the form that does not depend on the anchor
+    for got, want in ((state[0] * np.exp(state[2] - p_ref[0]), a_ref[0]),
+                      (state[1] * np.exp(state[2] - p_ref[0]), b_ref[0])):
+        assert np.max(np.abs(got - want) / np.maximum(np.abs(want), 1.0)) <= TOL_BF16
+
+
+def test_mat_forward_past_32_bit_offsets(device):
+    """Finch bf16 [1, 2^15 + 5, 1024 heads] (C = 65536): 2.15e9 elements; two
+    sampled heads against the fp64 oracle over the whole sequence."""
+    torch = _torch()
+    T, H, seed = (1 << 15) + 5, 1024, 91
+    C = 64 * H
+    assert T * C > 2 ** 31
+    rng = np.random.default_rng(seed)
+    zc = rng.uniform(-5.0, 2.0, C).astype(np.float32)
+    r = device_normal_bf16(T, C, 0, seed, device)
+    k = device_normal_bf16(T, C, 1, seed, device, scale=0.125)
+    v = device_normal_bf16(T, C, 2, seed, device)
+    z = device_normal_bf16(T, C, 3, seed, device, scale=0.5, offset=zc)
+    y, s_out = _wkv().mat_forward(r.view(1, T, C), k.view(1, T, C), v.view(1, T, C), z.view(1, T, C),
+                                  return_state=True)
+    heads = [0, H - 1]
+    cols = [64 * h + i for h in heads for i in range(64)]
+    idx = torch.tensor(cols, device=device)
+    ys = y[0].index_select(1, idx).float().cpu().numpy()
+    ss = s_out[0, heads].cpu().numpy()
+    del y, r, k, v, z
+    torch.cuda.synchronize()
+    rh = host_columns_bf16(T, C, cols, 0, seed)
+    kh = host_columns_bf16(T, C, cols, 1, seed, scale=0.125)
+    vh = host_columns_bf16(T, C, cols, 2, seed)
+    zh = host_columns_bf16(T, C, cols, 3, seed, scale=0.5, offset=zc)
+    y_ref, s_ref = ms.forward(rh[None], kh[None], vh[None], zh[None])
+    y_mag, s_mag = ms.forward(rh[None], kh[None], vh[None], zh[None], magnitude=True)
+    ey = float(np.max(np.abs(ys - y_ref[0]) / np.maximum(y_mag[0], 1e-30)))
+    es = float(np.max(np.abs(ss - s_ref[0]) / np.maximum(s_mag[0], 1e-30)))
+    print(f"{ys.shape[0]} tokens x {ys.shape[1]} channels: y err {ey:.3e}, state err {es:.3e}")
+    assert ey <= TOL_BF16 and es <= TOL_BF16, (ey, es)
