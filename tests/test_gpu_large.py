@@ -89,6 +89,7 @@ def test_forward_past_32_bit_offsets(device, path):
     for got, want in ((state[0] * np.exp(state[2] - p_ref[0]), a_ref[0]),
                       (state[1] * np.exp(state[2] - p_ref[0]), b_ref[0])):
         assert np.max(np.abs(got - want) / np.maximum(np.abs(want), 1.0)) <= TOL_BF16
+    torch.cuda.empty_cache()
 
 
 def test_mat_forward_past_32_bit_offsets(device):
@@ -113,6 +114,7 @@ def test_mat_forward_past_32_bit_offsets(device):
     ss = s_out[0, heads].cpu().numpy()
     del y, r, k, v, z
     torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     rh = host_columns_bf16(T, C, cols, 0, seed)
     kh = host_columns_bf16(T, C, cols, 1, seed, scale=0.125)
     vh = host_columns_bf16(T, C, cols, 2, seed)
@@ -123,3 +125,53 @@ def test_mat_forward_past_32_bit_offsets(device):
     es = float(np.max(np.abs(ss - s_ref[0]) / np.maximum(s_mag[0], 1e-30)))
     print(f"{ys.shape[0]} tokens x {ys.shape[1]} channels: y err {ey:.3e}, state err {es:.3e}")
     assert ey <= TOL_BF16 and es <= TOL_BF16, (ey, es)
+
+
+def device_normal_f32(shape, stream, seed, device):
+    """fp32 on the device: element n (row-major) is philox_normal of counter n."""
+    import synth.device as sd
+    torch = _torch()
+    n_rows = int(np.prod(shape[:-1]))
+    out = torch.empty(shape, dtype=torch.float32, device=device)
+    sd.fill_normal(out, (1, 1, n_rows, shape[-1]), (0, 0, shape[-1], 1), 0, stream, seed)
+    return out
+
+
+def test_step_past_32_bit_offsets(device):
+    """One decode step over fp32 [L=8, S=8200, C=32768] (2.15e9 elements per
+    array), the state updated in place; sampled rows against the oracle."""
+    torch = _torch()
+    Ln, S, C, seed = 8, 8200, 32768, 93
+    shape = (Ln, S, C)
+    assert Ln * S * C > 2 ** 31
+    k = device_normal_f32(shape, 0, seed, device)
+    v = device_normal_f32(shape, 1, seed, device)
+    a = device_normal_f32(shape, 2, seed, device)
+    b = device_normal_f32(shape, 3, seed, device).abs_().add_(1.0)
+    p = device_normal_f32(shape, 4, seed, device)
+    rng = np.random.default_rng(seed)
+    w = np.exp(rng.uniform(-5.0, 1.0, (Ln, C))).astype(np.float32)
+    u = rng.normal(0.0, 0.5, (Ln, C)).astype(np.float32)
+    y, _ = _wkv().step((a, b, p), k, v, torch.from_numpy(w).to(device), torch.from_numpy(u).to(device),
+                       inplace=True)
+    # sampled (layer, sequence) rows, every channel of each: the last row of
+    # the array among them
+    rows = [(0, 0), (3, 4097), (Ln - 1, S - 1)]
+    got = {name: np.stack([t[l, s].cpu().numpy() for l, s in rows]) for name, t in
+           (("y", y), ("a", a), ("b", b), ("p", p))}
+    del k, v, a, b, p, y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    flat = [(l * S + s) * C for l, s in rows]
+    cnt = np.array(flat, dtype=np.uint64)[:, None] + np.arange(C, dtype=np.uint64)[None, :]
+    kh, vh, ah, bh, ph = (synth.philox_normal(cnt, st, seed) for st in range(5))
+    bh = np.abs(bh) + np.float32(1.0)
+    lay = [l for l, _ in rows]
+    y_ref, (a_ref, b_ref, p_ref) = oracle.step((ah[:, None], bh[:, None], ph[:, None]), kh[:, None], vh[:, None],
+                                               w[lay], u[lay])
+    # the state (exponent p) is compared in the form that does not depend on it
+    err_y = guarded_rel_err(got["y"], y_ref[:, 0], 1.0)
+    assert err_y <= 1e-4, err_y
+    sc = np.exp(got["p"].astype(np.float64) - p_ref[:, 0])
+    for g, r in ((got["a"] * sc, a_ref[:, 0]), (got["b"] * sc, b_ref[:, 0])):
+        assert np.max(np.abs(g - r) / np.maximum(np.abs(r), 1.0)) <= 1e-4
