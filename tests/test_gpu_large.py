@@ -171,7 +171,70 @@ def test_step_past_32_bit_offsets(device):
                                                w[lay], u[lay])
     # the state (exponent p) is compared in the form that does not depend on it
     err_y = guarded_rel_err(got["y"], y_ref[:, 0], 1.0)
+    print(f"{len(rows)} rows x {C} channels: y err {err_y:.3e}")
     assert err_y <= 1e-4, err_y
     sc = np.exp(got["p"].astype(np.float64) - p_ref[:, 0])
     for g, r in ((got["a"] * sc, a_ref[:, 0]), (got["b"] * sc, b_ref[:, 0])):
         assert np.max(np.abs(g - r) / np.maximum(np.abs(r), 1.0)) <= 1e-4
+
+
+def test_token_shift_past_32_bit_offsets(device):
+    """Token shift over bf16 [1, 2^20 + 37, 2304]; sampled channels against
+    the oracle over the whole sequence."""
+    torch = _torch()
+    T, C, seed = (1 << 20) + 37, 2304, 95
+    assert T * C > 2 ** 31
+    x = device_normal_bf16(T, C, 0, seed, device)
+    rng = np.random.default_rng(seed)
+    mus = [rng.uniform(0.0, 1.0, C).astype(np.float32) for _ in range(3)]
+    outs = _wkv().token_shift(x.view(1, T, C), *(torch.from_numpy(m).to(device) for m in mus),
+                              return_last=True)
+    cs = [0, 3, 4, 1151, 2300, 2303]
+    idx = torch.tensor(cs, device=device)
+    got = [o[0].index_select(1, idx).float().cpu().numpy() for o in outs[:3]]
+    last = outs[3][0].index_select(0, idx).float().cpu().numpy()
+    del x, outs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    xh = host_columns_bf16(T, C, cs, 0, seed)
+    ref = oracle.token_shift(xh[None], *(m[cs] for m in mus))
+    for g, r in zip(got, ref[:3]):
+        err = float(np.max(np.abs(g - r[0]) / np.maximum(np.abs(r[0]), 1.0)))
+        assert err <= 2.0 ** -8, err
+    np.testing.assert_array_equal(last, ref[3][0])
+
+
+def test_mat_step_past_32_bit_offsets(device):
+    """One matrix-state decode step, fp32, [L=8, S=128, H=520]: a state of
+    2.18e9 elements updated in place; three sampled heads against the oracle."""
+    torch = _torch()
+    Ln, S, H, seed = 8, 128, 520, 97
+    C = 64 * H
+    assert Ln * S * H * 64 * 64 > 2 ** 31
+    import synth.device as sd
+    st = torch.empty((Ln, S, H, 64, 64), dtype=torch.float32, device=device)
+    sd.fill_normal(st, (1, 1, Ln * S * H * 64, 64), (0, 0, 64, 1), 0, 4, seed)
+    st.mul_(0.3)
+    r, k, v = (device_normal_f32((Ln, S, C), s_, seed, device) for s_ in range(3))
+    k.mul_(0.125)
+    z = device_normal_f32((Ln, S, C), 3, seed, device)
+    _wkv().mat_step(st, r, k, v, z, inplace=True)
+    picks = [(0, 0, 0), (3, 77, 259), (Ln - 1, S - 1, H - 1)]
+    got_s = np.stack([st[l, s, h].cpu().numpy() for l, s, h in picks])
+    del st
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    # the same inputs on the host for the picked heads
+    def host_f32(stream, flat_start, n):
+        cnt = np.uint64(flat_start) + np.arange(n, dtype=np.uint64)
+        return synth.philox_normal(cnt, stream, seed)
+    for i, (l, s, h) in enumerate(picks):
+        row = l * S + s
+        s0 = (host_f32(4, ((row * H + h) * 64) * 64, 64 * 64) * np.float32(0.3)).astype(np.float32)
+        rr, kk, vv, zz = (host_f32(st_, row * C + 64 * h, 64) for st_ in range(4))
+        kk = (kk * np.float32(0.125)).astype(np.float32)
+        _, s_ref = ms.step(s0.reshape(1, 64, 64), rr, kk, vv, zz)
+        _, s_mag = ms.step(np.abs(s0).reshape(1, 64, 64), np.abs(rr), np.abs(kk), np.abs(vv), zz)
+        err = float(np.max(np.abs(got_s[i] - s_ref.reshape(64, 64)) / np.maximum(s_mag.reshape(64, 64), 1e-30)))
+        print(f"head {(l, s, h)}: state err {err:.3e}")
+        assert err <= 1e-4, (l, s, h, err)
