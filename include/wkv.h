@@ -322,7 +322,8 @@ typedef enum {
  *   y           [B,T,C] dtype       output; must not overlap any input or s_out
  * r, k, v, z, y must be 8-byte (bf16) or 16-byte (fp32) aligned.  The chunked
  * path runs a chunk token by token instead, in fp32, when a channel decays by
- * more than e^{-80} within it.  Results do not depend on timing.
+ * more than e^{-80} within it, and the whole call so when 16 rows of C bf16
+ * values reach 2 GiB (C >= 2^26).  Results do not depend on timing.
  */
 int wkv_mat_forward(int64_t B, int64_t T, int64_t H, int dtype,
                     const void *r, const void *k, const void *v, const void *z, int z_mode,
