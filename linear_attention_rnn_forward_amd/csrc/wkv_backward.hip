@@ -159,7 +159,9 @@ __device__ __forceinline__ TokenOut forward_detail(FState& s, float k, float v, 
     if constexpr (FUSED) {
         rh = al;
         bo = be * c;
-        o.q = reset ? k + w : __builtin_fmaf(-s.m, w, s.A);
+        // the folded exponent plus w: k + w on a reset, else A - m w (the
+        // same roundings either way: fma(1, w, k) is k + w)
+        o.q = __builtin_fmaf(reset ? 1.0f : -s.m, w, reset ? k : s.A);
     } else {
         const float d = __builtin_fmaf(-s.m, w, ak - u);  // p - (u + k)
         const float xr = exp_neg_abs(d);
@@ -332,10 +334,13 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
                     }
                 }
             }
+            // e^{x_i - max}; a rounding of max * log2e scales every term alike
+            float mxl[VEC];
 #pragma unroll
             for (int q = 0; q < VEC; q++) {
                 g[q].set_empty();
                 g[q].A = mx[q];
+                mxl[q] = mx[q] * kLog2e;
             }
 #pragma unroll
             for (int i = 0; i < L; i++) {
@@ -345,7 +350,7 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
                     const float age = float(n - 1 - i);
 #pragma unroll
                     for (int q = 0; q < VEC; q++) {
-                        const float e = __builtin_amdgcn_exp2f((xs[i][q] - mx[q]) * kLog2e);
+                        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[i][q], kLog2e, -mxl[q]));
                         const float ev = e * vf[q];
                         g[q].a += ev;
                         g[q].b += e;
@@ -450,10 +455,12 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     #pragma unroll
                         for (int q = 0; q < VEC; q++)
                             mx[q] = max_num(mx[q], __builtin_fmaf(-float(i), w[q], -to[i][q].q));
+                float mxl[VEC];
     #pragma unroll
                 for (int q = 0; q < VEC; q++) {
                     rg[q].set_empty();
                     rg[q].Pi = mx[q];
+                    mxl[q] = mx[q] * kLog2e;
                 }
     #pragma unroll
                 for (int i = 0; i < L; i++) {
@@ -461,7 +468,7 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     #pragma unroll
                         for (int q = 0; q < VEC; q++) {
                             const float xi = __builtin_fmaf(-float(i), w[q], -to[i][q].q);
-                            const float t = __builtin_amdgcn_exp2f((xi - mx[q]) * kLog2e) * to[i][q].gr;
+                            const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(xi, kLog2e, -mxl[q])) * to[i][q].gr;
                             rg[q].P += t;
                             rg[q].Q = __builtin_fmaf(t, to[i][q].y, rg[q].Q);
                         }
