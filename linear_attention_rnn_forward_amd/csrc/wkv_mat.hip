@@ -8,25 +8,25 @@
 //   d_t = exp(-softplus(z_t)),  z_t = a.b + w (the table's decay argument;
 //                                per token for Finch, per channel for Eagle)
 //
-// Forward (training / prefill form): one workgroup of 4 waves per (batch row,
-// head); wave w owns value columns [16w, 16w + 16) of the state, which stays
-// in fp32 registers in the accumulator layout of a 16x16 MFMA tile (lane l
-// holds rows 4(l/16) .. 4(l/16)+3 of column l%16 of each of the four 16-row
-// blocks).  The tokens are taken in chunks of 16.  With D_t[i] the product of
-// the decays d[i] of the chunk's tokens up to and including t, the recurrence
-// unrolls over a chunk into
+// Forward (training / prefill form): one workgroup of 8 waves per (batch row,
+// head).  Consumer wave w (waves 0..3) owns value columns [16w, 16w + 16) of
+// the state, which stays in fp32 registers in the accumulator layout of a
+// 16x16 MFMA tile (lane l holds rows 4(l/16) .. 4(l/16)+3 of column l%16 of
+// each of the four 16-row blocks); waves 4..7 prepare the chunks' operands.
+// The tokens are taken in chunks of 16.  With D_t[i] the product of the decays
+// d[i] of the chunk's tokens up to and including t, the recurrence unrolls
+// over a chunk into
 //
 //   y_t = (r_t D_t)^T S_0 + sum_{s<=t} [sum_i r_t[i] D_t[i] k_s[i] / D_s[i]] v_s
 //   S_16 = diag(D_15) S_0 + sum_s (k_s D_15 / D_s) v_s^T
 //
-// and every sum over i or s is a dense 16x16x16 product on the matrix cores
-// (bf16 operands, fp32 accumulation): the read-out of the carried state, the
+// and every sum over i or s is a dense product on the matrix cores (bf16
+// operands, fp32 accumulation): the read-out of the carried state, the
 // chunk's score matrix, its application to the values, and the state update.
-// The prefix products run across the 16 lanes of a row with DPP.  The factor
-// 1/D_s is bounded by the chunk's total decay; a chunk in which some channel
-// decays by more than e^{-80} is run token by token instead, on the same
-// registers, in fp32.  fp32 storage always takes that exact token-by-token
-// form.
+// The factor 1/D_s is bounded by the chunk's total decay; a chunk in which
+// some channel decays by more than e^{-80} is run token by token instead, in
+// fp32.  fp32 storage takes the token-by-token form throughout (its own
+// kernel).
 //
 // Decode step: one wave per (row, head); each state element is read, updated
 // and written once: an HBM stream of 8 bytes per state element and token.
