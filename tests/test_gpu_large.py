@@ -238,3 +238,30 @@ def test_mat_step_past_32_bit_offsets(device):
         err = float(np.max(np.abs(got_s[i] - s_ref.reshape(64, 64)) / np.maximum(s_mag.reshape(64, 64), 1e-30)))
         print(f"head {(l, s, h)}: state err {err:.3e}")
         assert err <= 1e-4, (l, s, h, err)
+
+
+def test_gated_forward_past_32_bit_offsets(device):
+    """The receptance-gated forward over bf16 [1, 2^20 + 37, 2304] (auto path);
+    sampled channels against the oracle's forward_gated."""
+    torch = _torch()
+    T, C, seed = (1 << 20) + 37, 2304, 99
+    assert T * C > 2 ** 31
+    k = device_normal_bf16(T, C, 0, seed, device)
+    v = device_normal_bf16(T, C, 1, seed, device)
+    r = device_normal_bf16(T, C, 2, seed, device)
+    rng = np.random.default_rng(seed)
+    w = np.exp(rng.uniform(-5.0, 1.0, C)).astype(np.float32)
+    u = rng.normal(0.0, 0.5, C).astype(np.float32)
+    o = _wkv().forward(k.view(1, T, C), v.view(1, T, C), torch.from_numpy(w).to(device),
+                       torch.from_numpy(u).to(device), r=r.view(1, T, C))
+    cs = [0, 2, 129, 1151, 2303]
+    idx = torch.tensor(cs, device=device)
+    os_ = o[0].index_select(1, idx).float().cpu().numpy()
+    del o, k, v, r
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    kh, vh, rh = (host_columns_bf16(T, C, cs, st, seed) for st in range(3))
+    o_ref, _ = oracle.forward_gated(kh[None], vh[None], rh[None], w[cs], u[cs])
+    err = guarded_rel_err(os_, o_ref[0], 1.0)
+    print(f"gated: {os_.shape[0]} tokens x {os_.shape[1]} channels, err {err:.3e}")
+    assert err <= TOL_BF16, err
