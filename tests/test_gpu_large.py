@@ -265,3 +265,42 @@ def test_gated_forward_past_32_bit_offsets(device):
     err = guarded_rel_err(os_, o_ref[0], 1.0)
     print(f"gated: {os_.shape[0]} tokens x {os_.shape[1]} channels, err {err:.3e}")
     assert err <= TOL_BF16, err
+
+
+def test_backward_past_32_bit_offsets(device):
+    """The backward over bf16 [1, 2^20 + 37, 2304] with gy non-zero in the
+    first 96 tokens only: every gradient then comes from those tokens, so
+    gk, gv of the first 96 and gw, gu match the oracle on that prefix (sampled
+    channels), and gk, gv of every later token -- up to the end of arrays
+    past 4 GiB -- are exactly zero."""
+    torch = _torch()
+    T, C, seed, P = (1 << 20) + 37, 2304, 101, 96
+    assert T * C > 2 ** 31
+    k = device_normal_bf16(T, C, 0, seed, device)
+    v = device_normal_bf16(T, C, 1, seed, device)
+    gy = torch.zeros((T, C), dtype=torch.bfloat16, device=device)
+    gy[:P] = device_normal_bf16(P, C, 2, seed, device)
+    rng = np.random.default_rng(seed)
+    w = np.exp(rng.uniform(-5.0, 1.0, C)).astype(np.float32)
+    u = rng.normal(0.0, 0.5, C).astype(np.float32)
+    gk, gv, gw, gu = _wkv().backward(k.view(1, T, C), v.view(1, T, C), torch.from_numpy(w).to(device),
+                                     torch.from_numpy(u).to(device), gy.view(1, T, C))
+    cs = [0, 1, 255, 1152, 2303]
+    idx = torch.tensor(cs, device=device)
+    head = [g[0, :P].index_select(1, idx).float().cpu().numpy() for g in (gk, gv)]
+    tail_nonzero = [int(torch.count_nonzero(g[0, P:]).item()) for g in (gk, gv)]
+    gwu = [g.index_select(0, idx).cpu().numpy() for g in (gw, gu)]
+    del k, v, gy, gk, gv
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    assert tail_nonzero == [0, 0], tail_nonzero
+    kh, vh, gh = (host_columns_bf16(P, C, cs, st, seed) for st in range(3))
+    gk_ref, gv_ref, gw_ref, gu_ref = oracle.backward(kh[None], vh[None], w[cs], u[cs], gh[None])
+    mags = oracle.backward(kh[None], vh[None], w[cs], u[cs], gh[None], magnitude=True)
+    # gw, gu are fp32 sums (the bar of the backward's own tests)
+    for name, got, ref, mag, tol in (("gk", head[0], gk_ref[0], mags[0][0], TOL_BF16),
+                                     ("gv", head[1], gv_ref[0], mags[1][0], TOL_BF16),
+                                     ("gw", gwu[0], gw_ref, mags[2], 1e-4), ("gu", gwu[1], gu_ref, mags[3], 1e-4)):
+        err = float(np.max(np.abs(got - ref) / np.maximum(mag, 1e-30)))
+        print(f"backward {name}: err {err:.3e}")
+        assert err <= tol, (name, err)
