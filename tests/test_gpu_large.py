@@ -47,6 +47,16 @@ def device_normal_bf16(n_rows, C, stream, seed, device, scale=1.0, offset=None):
     return out
 
 
+def device_normal_f32(shape, stream, seed, device):
+    """fp32 on the device: element n (row-major) is philox_normal of counter n."""
+    import synth.device as sd
+    torch = _torch()
+    n_rows = int(np.prod(shape[:-1]))
+    out = torch.empty(shape, dtype=torch.float32, device=device)
+    sd.fill_normal(out, (1, 1, n_rows, shape[-1]), (0, 0, shape[-1], 1), 0, stream, seed)
+    return out
+
+
 def host_columns_bf16(n_rows, C, channels, stream, seed, scale=1.0, offset=None):
     """The same values for the given channels, [n_rows, len(channels)], as the
     device rounds them: fp32 value (scaled, offset) rounded to bf16."""
@@ -60,14 +70,19 @@ def host_columns_bf16(n_rows, C, channels, stream, seed, scale=1.0, offset=None)
     return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x))
 
 
-@pytest.mark.parametrize("path", ["auto", "chained"])
-def test_forward_past_32_bit_offsets(device, path):
-    """bf16 [1, 2^20 + 37, 2304]: 2.42e9 elements, 4.8 GB per array."""
+@pytest.mark.parametrize("path,dtype", [("auto", "bf16"), ("chained", "bf16"), ("auto", "f32")])
+def test_forward_past_32_bit_offsets(device, path, dtype):
+    """[1, 2^20 + 37, 2304]: 2.42e9 elements, 4.8 GB per bf16 array (9.7 GB
+    in fp32)."""
     torch = _torch()
     T, C, seed = (1 << 20) + 37, 2304, 77
     assert T * C > 2 ** 31 and 2 * T * C > 2 ** 32
-    k = device_normal_bf16(T, C, synth.STREAM_K, seed, device)
-    v = device_normal_bf16(T, C, synth.STREAM_V, seed, device)
+    if dtype == "bf16":
+        k = device_normal_bf16(T, C, synth.STREAM_K, seed, device)
+        v = device_normal_bf16(T, C, synth.STREAM_V, seed, device)
+    else:
+        k = device_normal_f32((T, C), synth.STREAM_K, seed, device)
+        v = device_normal_f32((T, C), synth.STREAM_V, seed, device)
     rng = np.random.default_rng(seed)
     w = np.exp(rng.uniform(-5.0, 1.0, C)).astype(np.float32)
     u = rng.normal(0.0, 0.5, C).astype(np.float32)
@@ -79,16 +94,22 @@ def test_forward_past_32_bit_offsets(device, path):
     state = [s[0].index_select(0, idx).cpu().numpy() for s in (a, b, p)]
     del y, k, v
     torch.cuda.synchronize()
-    kh = host_columns_bf16(T, C, cs, synth.STREAM_K, seed)
-    vh = host_columns_bf16(T, C, cs, synth.STREAM_V, seed)
+    if dtype == "bf16":
+        kh = host_columns_bf16(T, C, cs, synth.STREAM_K, seed)
+        vh = host_columns_bf16(T, C, cs, synth.STREAM_V, seed)
+    else:
+        t = np.arange(T, dtype=np.uint64)[:, None] * np.uint64(C) + np.asarray(cs, dtype=np.uint64)[None, :]
+        kh = synth.philox_normal(t, synth.STREAM_K, seed)
+        vh = synth.philox_normal(t, synth.STREAM_V, seed)
+    tol = TOL_BF16 if dtype == "bf16" else 1e-4
     y_ref, (a_ref, b_ref, p_ref) = oracle.forward(kh[None], vh[None], w[cs], u[cs])
     err = guarded_rel_err(ys, y_ref[0], 1.0)
-    print(f"path={path}: {ys.shape[0]} tokens x {ys.shape[1]} channels, y err {err:.3e}")
-    assert err <= TOL_BF16, f"path={path}: y err {err:.3e}"
+    print(f"path={path} {dtype}: {ys.shape[0]} tokens x {ys.shape[1]} channels, y err {err:.3e}")
+    assert err <= tol, f"path={path}: y err {err:.3e}"
     # the final state, in the form that does not depend on the anchor
     for got, want in ((state[0] * np.exp(state[2] - p_ref[0]), a_ref[0]),
                       (state[1] * np.exp(state[2] - p_ref[0]), b_ref[0])):
-        assert np.max(np.abs(got - want) / np.maximum(np.abs(want), 1.0)) <= TOL_BF16
+        assert np.max(np.abs(got - want) / np.maximum(np.abs(want), 1.0)) <= tol
     torch.cuda.empty_cache()
 
 
@@ -125,16 +146,6 @@ def test_mat_forward_past_32_bit_offsets(device):
     es = float(np.max(np.abs(ss - s_ref[0]) / np.maximum(s_mag[0], 1e-30)))
     print(f"{ys.shape[0]} tokens x {ys.shape[1]} channels: y err {ey:.3e}, state err {es:.3e}")
     assert ey <= TOL_BF16 and es <= TOL_BF16, (ey, es)
-
-
-def device_normal_f32(shape, stream, seed, device):
-    """fp32 on the device: element n (row-major) is philox_normal of counter n."""
-    import synth.device as sd
-    torch = _torch()
-    n_rows = int(np.prod(shape[:-1]))
-    out = torch.empty(shape, dtype=torch.float32, device=device)
-    sd.fill_normal(out, (1, 1, n_rows, shape[-1]), (0, 0, shape[-1], 1), 0, stream, seed)
-    return out
 
 
 def test_step_past_32_bit_offsets(device):
