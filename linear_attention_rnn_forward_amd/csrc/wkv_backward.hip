@@ -72,22 +72,6 @@ struct FState {
     }
 };
 
-// Fold token (k, v) into s: the history decays by e^{-w}, the age-weighted
-// sums gain the history, the new key enters with weight e^{k}.
-__device__ __forceinline__ void fold_forward(FState& s, float k, float v, float w) {
-    const float e = __builtin_fmaf(-(s.m + 1.0f), w, s.A - k);  // (p - w) - k
-    const float x = exp_neg_abs(e);
-    const bool reset = e < 0.0f;                                  // the new key is the maximum
-    const float al = reset ? x : 1.0f;
-    const float be = reset ? 1.0f : x;
-    s.ap = al * (s.ap + s.a);
-    s.bp = al * (s.bp + s.b);
-    s.a = __builtin_fmaf(al, s.a, be * v);
-    s.b = __builtin_fmaf(al, s.b, be);
-    s.A = reset ? k : s.A;
-    s.m = reset ? 0.0f : s.m + 1.0f;
-}
-
 // X <- X (+) G, G the state of the n tokens after X from the empty history.
 // Over n tokens X's terms gain n in age: a' -> e^{-n w} (a' + n a).
 __device__ __forceinline__ void combine_forward(FState& x, const FState& g, float n, float w) {
