@@ -441,16 +441,18 @@ int wkv_token_shift(int64_t B, int64_t T, int64_t C, int dtype, const void* x, c
             if (overlap(r_out[i], r_out[j]))
                 return fail(WKV_ERR_ALIAS, "%s overlaps %s", r_out[i].name, r_out[j].name);
     }
+    // the widest lane access (16 bytes at most) that C and every array allow
     int vec = 1;
-    for (int cand : {4, 2}) {
+    for (int cand : {8, 4, 2}) {
         const uintptr_t a = uintptr_t(cand) * uintptr_t(es);
-        if (C % cand == 0 && aligned(x, a) && aligned(xr, a) && aligned(xk, a) && aligned(xv, a) &&
-            aligned(x_prev, a) && aligned(x_last, a)) {
+        if (a <= 16 && C % cand == 0 && aligned(x, a) && aligned(xr, a) && aligned(xk, a) &&
+            aligned(xv, a) && aligned(x_prev, a) && aligned(x_last, a)) {
             vec = cand;
             break;
         }
     }
-    if (double(B) * double((T + 31) / 32) * double(C / vec) / 256.0 > 2147483647.0)
+    if (double(B) * double((T + wkv::kShiftTokens - 1) / wkv::kShiftTokens) * double(C / vec) / 256.0 >
+        2147483647.0)
         return fail(WKV_ERR_SHAPE, "too many elements for one launch");
     wkv::ShiftProblem pr;
     pr.B = B;

@@ -294,6 +294,20 @@ struct Io<kBF16, 4> {
     static __device__ __forceinline__ Raw zero() { return make_uint2(0u, 0u); }
 };
 
+template <>
+struct Io<kBF16, 8> {
+    using Raw = uint4;
+    static __device__ __forceinline__ void unpack(Raw r, float (&x)[8]) {
+        x[0] = bf16_lo(r.x); x[1] = bf16_hi(r.x); x[2] = bf16_lo(r.y); x[3] = bf16_hi(r.y);
+        x[4] = bf16_lo(r.z); x[5] = bf16_hi(r.z); x[6] = bf16_lo(r.w); x[7] = bf16_hi(r.w);
+    }
+    static __device__ __forceinline__ Raw pack(const float (&x)[8]) {
+        return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                          pack_bf16x2(x[6], x[7]));
+    }
+    static __device__ __forceinline__ Raw zero() { return make_uint4(0u, 0u, 0u, 0u); }
+};
+
 // ---------------------------------------------------------------------------
 // Buffer addressing: a wave-uniform base in a buffer resource (SGPRs), a
 // per-lane byte offset (VGPR, fixed for the kernel) and a per-token byte

@@ -74,10 +74,16 @@ int backward_vec(int64_t C, int dtype, bool aligned);
 size_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C);
 hipError_t launch_backward(BackwardProblem pr, void* workspace, hipStream_t stream);
 
+// Tokens per lane in the token shift: each lane reads the row before its run
+// once more, so short runs cost 1/kShiftTokens of x again but give the
+// stream many more independent lanes (8 measured fastest on the bf16 [16,
+// 4096, 2048] shift among 4..64).
+constexpr int kShiftTokens = 8;
+
 struct ShiftProblem {
     int64_t B, T, C;
     int dtype;
-    int vec;  // 4, 2 or 1 channels per lane, dividing C, arrays aligned for it
+    int vec;  // 8 (bf16 only), 4, 2 or 1 channels per lane, dividing C, arrays aligned for it
     const void *x, *x_prev;
     const float *mu_r, *mu_k, *mu_v;
     void *xr, *xk, *xv, *x_last;

@@ -15,8 +15,6 @@
 namespace wkv {
 namespace {
 
-constexpr int kShiftTokens = 32;
-
 template <int DT, int VEC>
 __global__ __launch_bounds__(256) void token_shift_kernel(ShiftProblem pr, int64_t lanes_per_row,
                                                           int64_t runs) {
@@ -109,6 +107,7 @@ hipError_t launch_token_shift(const ShiftProblem& pr, hipStream_t stream) {
         return hipGetLastError();
     }
     if (pr.dtype == kBF16) {
+        if (pr.vec == 8) return launch_vec<kBF16, 8>(pr, stream);
         if (pr.vec == 4) return launch_vec<kBF16, 4>(pr, stream);
         if (pr.vec == 2) return launch_vec<kBF16, 2>(pr, stream);
         return launch_vec<kBF16, 1>(pr, stream);

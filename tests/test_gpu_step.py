@@ -107,7 +107,8 @@ def test_step_chain_matches_forward(device, dtype, path):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("shape", [(1, 1, 4), (2, 33, 64), (3, 100, 130), (1, 70, 7), (2, 0, 8)],
+@pytest.mark.parametrize("shape", [(1, 1, 4), (2, 33, 64), (3, 100, 130), (1, 70, 7), (2, 0, 8),
+                                   (2, 41, 24), (2, 19, 12), (1, 9, 8)],
                          ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("with_prev", [False, True])
 def test_token_shift_matches_oracle(device, shape, dtype, with_prev):
@@ -127,6 +128,28 @@ def test_token_shift_matches_oracle(device, shape, dtype, with_prev):
     for got, want in zip((xr, xk, xv), ref[:3]):
         assert guarded_rel_err(host(got), want, 1.0) <= tol
     np.testing.assert_array_equal(host(last), ref[3])
+
+
+
+@pytest.mark.parametrize("offset", [1, 2, 4])
+def test_token_shift_on_unaligned_views(device, offset):
+    """Arrays that start 2, 4 or 8 bytes past a 16-byte boundary take the
+    narrower lane accesses (1, 2 or 4 channels); results match the oracle."""
+    import linear_attention_rnn_forward_amd as wkv
+    torch = _torch()
+    B, T, C = 2, 37, 64
+    rng = np.random.default_rng(77 + offset)
+    n = B * T * C
+    flat = torch.from_numpy(rng.normal(0, 1, n + offset).astype(np.float32)).to(device).to(torch.bfloat16)
+    x = flat[offset:].view(B, T, C)
+    mus = [rng.uniform(0, 1, C).astype(np.float32) for _ in range(3)]
+    outs = [torch.empty(n + offset, device=device, dtype=torch.bfloat16) for _ in range(3)]
+    out = tuple(o[offset:].view(B, T, C) for o in outs)
+    wkv.token_shift(x, *(dev_f32(m, device) for m in mus), out=out)
+    torch.cuda.synchronize()
+    ref = oracle.token_shift(host(x), *mus)
+    for got, want in zip(out, ref[:3]):
+        assert guarded_rel_err(host(got), want, 1.0) <= 2.0 ** -8
 
 
 def test_device_generator_matches_host(device):
