@@ -42,33 +42,43 @@ int wkv_oracle_threads(void)
 }
 
 /*
- * One token of the stabilised recurrence for one channel.
- * Read-out, then fold-in, exactly as [aiwiki] "wkv_step" (code listing under
- * "What it gives up") and [tm-math] "Numerical stability: carry the exponent":
- *   q  = max(p, u+k)
- *   y  = (e^{p-q} a + e^{u+k-q} v) / (e^{p-q} b + e^{u+k-q})
- *   p' = max(p-w, k)
- *   a' = e^{p-w-p'} a + e^{k-p'} v
- *   b' = e^{p-w-p'} b + e^{k-p'}
- * The current token enters the read-out with the bonus u and is not yet in
- * the state; it enters the state without u.
+ * Two terms with log-weights x1 and x2, brought to a common scale: returns
+ * the larger exponent m and sets *e1 = e^{x1-m}, *e2 = e^{x2-m} (both <= 1,
+ * one of them exactly 1).  This is the shift that keeps every exp argument
+ * <= 0 ([tm-math] "Numerical stability: carry the exponent").
+ */
+static double scaled_weights(double x1, double x2, double *e1, double *e2)
+{
+    double m = fmax(x1, x2);
+    *e1 = exp(x1 - m);
+    *e2 = exp(x2 - m);
+    return m;
+}
+
+/*
+ * One token of one channel on the state (a, b, p), whose true sums are
+ * e^p*a (weighted values) and e^p*b (weights) ([tm-math] "Numerical
+ * stability: carry the exponent"; the sums themselves are those of "The WKV
+ * operator: attention with a fixed decay").
+ *
+ * Output: the history, at log-weight p, mixed with the current value, at
+ * log-weight u + k (the bonus applies to the current token only and is not
+ * stored).  State: the history decays by one token (log-weight p - w) and
+ * the current value joins it at log-weight k; the larger of the two becomes
+ * the new exponent.
  */
 static double stabilised_token(double *a, double *b, double *p,
                                double k, double v, double w, double u)
 {
-    double q = fmax(*p, u + k);
-    double e1 = exp(*p - q);
-    double e2 = exp(u + k - q);
-    double y = (e1 * *a + e2 * v) / (e1 * *b + e2);
+    double hist, cur;   /* scaled weights of the history and of the current token */
 
-    double q2 = fmax(*p - w, k);
-    double f1 = exp(*p - w - q2);
-    double f2 = exp(k - q2);
-    double a_next = f1 * *a + f2 * v;
-    double b_next = f1 * *b + f2;
-    *a = a_next;
-    *b = b_next;
-    *p = q2;
+    scaled_weights(*p, u + k, &hist, &cur);
+    double y = (hist * *a + cur * v) / (hist * *b + cur);
+
+    double p_next = scaled_weights(*p - w, k, &hist, &cur);
+    *a = hist * *a + cur * v;
+    *b = hist * *b + cur;
+    *p = p_next;
     return y;
 }
 

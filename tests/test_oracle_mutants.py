@@ -20,20 +20,19 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json"
 
 MUTANTS = {
     # fold-in decays with the wrong sign (the negative-w convention applied to positive w)
-    "decay_sign": ("double q2 = fmax(*p - w, k);\n    double f1 = exp(*p - w - q2);",
-                   "double q2 = fmax(*p + w, k);\n    double f1 = exp(*p + w - q2);"),
+    "decay_sign": ("scaled_weights(*p - w, k, &hist, &cur)", "scaled_weights(*p + w, k, &hist, &cur)"),
     # read-out forgets the current-token bonus
-    "no_bonus": ("double e2 = exp(u + k - q);", "double e2 = exp(k - q);"),
+    "no_bonus": ("scaled_weights(*p, u + k, &hist, &cur)", "scaled_weights(*p, k, &hist, &cur)"),
     # read-out decays the history once too often
-    "extra_decay": ("double e1 = exp(*p - q);", "double e1 = exp(*p - w - q);"),
+    "extra_decay": ("scaled_weights(*p, u + k, &hist, &cur)", "scaled_weights(*p - w, u + k, &hist, &cur)"),
     # numerator takes a where v belongs
-    "transposed_av": ("double y = (e1 * *a + e2 * v)", "double y = (e1 * v + e2 * *a)"),
+    "transposed_av": ("double y = (hist * *a + cur * v)", "double y = (hist * v + cur * *a)"),
     # state update adds the bonus too
-    "bonus_in_state": ("double f2 = exp(k - q2);", "double f2 = exp(u + k - q2);"),
-    # running maximum ignores the decay (the ratio survives, the state's p does not)
-    "max_without_decay": ("double q2 = fmax(*p - w, k);", "double q2 = fmax(*p, k);"),
+    "bonus_in_state": ("scaled_weights(*p - w, k, &hist, &cur)", "scaled_weights(*p - w, u + k, &hist, &cur)"),
+    # the common scale is not the larger exponent (the ratio survives, the state's p does not)
+    "scale_not_max": ("double m = fmax(x1, x2);", "double m = x2;"),
     # denominator drops the history
-    "den_no_history": ("/ (e1 * *b + e2);", "/ (e2);"),
+    "den_no_history": ("/ (hist * *b + cur);", "/ (cur);"),
     # decay per channel read with the batch index
     "wrong_param_index": ("stabilised_token(&a, &b, &p, k[i], v[i], w[c], u[c])",
                           "stabilised_token(&a, &b, &p, k[i], v[i], w[bb], u[c])"),
