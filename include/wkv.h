@@ -103,7 +103,9 @@ size_t wkv_forward_workspace_size_path(int64_t B, int64_t T, int64_t C, int dtyp
  * Operator", training mode; [multigrid] "Prefill, decode, ...": prefill
  * yields the state after the last prompt token).
  *
- *   B >= 1, T >= 0, C >= 1
+ *   B >= 1, T >= 0, C >= 1; C * sizeof(dtype) * 33 + 512 < 2^32 (a block of
+ *               up to 32 token rows is addressed with 32-bit byte offsets;
+ *               larger C returns WKV_ERR_SHAPE)
  *   w, u        [C] fp32            decay rate (> 0) and bonus
  *   k, v        [B,T,C] dtype       keys, values
  *   y           [B,T,C] dtype       output; must not overlap k, v, w, u or the state
@@ -167,9 +169,14 @@ int wkv_forward_gated(int64_t B, int64_t T, int64_t C, int dtype, int path,
  *   a_in, b_in, p_in    [L,S,C] fp32  required (use p = -inf for an empty history)
  *   a_out, b_out, p_out [L,S,C] fp32  required; each may equal its *_in (in place),
  *                                     but must not partially overlap any array
- * The state is rounded to fp32 after every step (its exponent p once per
- * token), so a chain of steps follows wkv_forward's outputs to within that
- * rounding (about 1e-6 relative for keys of unit scale).
+ * The state is rounded to fp32 after every step.  Its exponent p_out is an
+ * anchor, not necessarily the running maximum: it stays where it is until a
+ * new key exceeds it (then p_out = k exactly) or the decayed sums fall below
+ * 2^-40 (then it moves down by 28), and the decay e^{-w} is applied to
+ * a_out, b_out instead.  Any (a, b, p) with the same e^p a and e^p b is the
+ * same state, and every call accepts any such state.  This keeps the
+ * per-token roundings from all going one way, so a chain of steps follows
+ * wkv_forward's outputs to a few 1e-6 relative, also behind keys near +40.
  */
 int wkv_step(int64_t L, int64_t S, int64_t C, int dtype,
              const float *w, const float *u,
@@ -314,7 +321,8 @@ typedef enum {
  * Training / prefill form over [B,T,C], and optionally the state after the
  * last token.
  *
- *   B, H >= 1, T >= 0
+ *   B, H >= 1, T >= 0; H * 64 * 4 * 17 < 2^32 (rows of a chunk are addressed with
+ *               32-bit byte offsets; larger H returns WKV_ERR_SHAPE)
  *   r, k, v     [B,T,C] dtype       receptance, keys, values
  *   z           see wkv_mat_decay
  *   s_in        [B,H,64,64] fp32    prior state, or NULL (zero)
@@ -359,7 +367,23 @@ const char *wkv_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int wkv_abi_version(void);
 
-#define WKV_ABI_VERSION 104
+/*
+ * Bounded waits that gave up, on the current device, since the library was
+ * loaded.  Two kernels wait on work of other waves or workgroups: the chunked
+ * forward path's look-back over earlier tiles, and the matrix-state forward's
+ * ring of operand slots.  Each wait is bounded (200 ms) so that a kernel
+ * always ends; a wait that gives up is never expected, and when it happens the
+ * results it would have fed are written as NaN (the chunked path: the tile and
+ * every later tile of its column group; the ring: the head's y and s_out),
+ * the chunked path also sets the uint32 error word at byte offset 4 of its
+ * workspace (cleared by every call), and the count read here grows by one.
+ *   count    host pointer, receives the count
+ * Synchronous: copies from device memory after the device's prior work (do
+ * not call during stream capture).  Returns WKV_OK or WKV_ERR_NULL/WKV_ERR_HIP.
+ */
+int wkv_bounded_wait_failures(uint64_t *count);
+
+#define WKV_ABI_VERSION 105
 
 #ifdef __cplusplus
 }

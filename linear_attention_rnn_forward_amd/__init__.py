@@ -101,8 +101,18 @@ def lib() -> ctypes.CDLL:
         L.wkv_last_error.argtypes = []
         L.wkv_abi_version.restype = i32
         L.wkv_abi_version.argtypes = []
+        L.wkv_bounded_wait_failures.restype = i32
+        L.wkv_bounded_wait_failures.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
         _lib = L
     return _lib
+
+
+def bounded_wait_failures() -> int:
+    """Bounded waits (chunked look-back, matrix ring) that gave up on the
+    current device since the library was loaded; synchronous."""
+    n = ctypes.c_uint64(0)
+    check(lib().wkv_bounded_wait_failures(ctypes.byref(n)))
+    return int(n.value)
 
 
 def check(status: int) -> None:

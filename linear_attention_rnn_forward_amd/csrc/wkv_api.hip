@@ -100,6 +100,10 @@ int forward_impl(int64_t B, int64_t T, int64_t C, int dtype, int path, const flo
     int64_t n = 0;
     if (!mul3(B, T, C, &n) || !mul3(n, 4, 1, &n) || !mul3(B, C, 12, &n))
         return fail(WKV_ERR_SHAPE, "B*T*C too large");
+    // every kernel addresses the tokens of one block (at most 32 rows) from
+    // a 64-bit base with 32-bit byte offsets
+    if (double(C) * double(esize(dtype)) * 33.0 + 512.0 > 4294967295.0)
+        return fail(WKV_ERR_SHAPE, "C too large for 32-bit offsets within a block of tokens");
     const bool has_in = a_in || b_in || p_in;
     const bool has_out = a_out || b_out || p_out;
     if (has_in && !(a_in && b_in && p_in)) return fail(WKV_ERR_NULL, "a_in, b_in, p_in: all or none");
@@ -207,6 +211,17 @@ int device_cu_count() {
 extern "C" {
 
 int wkv_abi_version(void) { return WKV_ABI_VERSION; }
+
+int wkv_bounded_wait_failures(uint64_t* count) {
+    if (!count) return fail(WKV_ERR_NULL, "count is required");
+    uint64_t a = 0, b = 0;
+    hipError_t e = wkv::read_chunk_wait_failures(&a);
+    if (e != hipSuccess) return hip_fail(e, "reading the look-back failure count");
+    e = wkv::read_ring_wait_failures(&b);
+    if (e != hipSuccess) return hip_fail(e, "reading the ring failure count");
+    *count = a + b;
+    return ok();
+}
 
 const char* wkv_status_string(int status) {
     switch (status) {
@@ -530,6 +545,9 @@ int wkv_mat_forward_path(int64_t B, int64_t T, int64_t H, int dtype, int path, c
         !mul3(B * H, WKV_MAT_HEAD_DIM * WKV_MAT_HEAD_DIM, 4, &n))
         return fail(WKV_ERR_SHAPE, "sizes too large");
     if (B * H > 2147483647) return fail(WKV_ERR_SHAPE, "B*H too large for one launch");
+    // rows of a chunk of tokens are addressed with 32-bit byte offsets
+    if (double(H) * WKV_MAT_HEAD_DIM * 4.0 * 17.0 > 4294967295.0)
+        return fail(WKV_ERR_SHAPE, "H too large for 32-bit offsets within a chunk of tokens");
     if (int rc = mat_check(dtype, B * T, H, r, k, v, z, z_mode, 1, s_in, s_out, B * H, y, true))
         return rc;
     wkv::MatProblem pr;

@@ -165,27 +165,53 @@ __device__ __forceinline__ void combine(float& xa, float& xb, float& xA, float& 
     xm = keep ? xm2 : gm;
 }
 
-// Decode step: the state is stored after every token, so its exponent is
-// rounded once per token (p' = fl(p - w) when the history keeps the maximum).
-// GATED as in frame_token: gd = 1 + e^{-r}.
+// Decode step.  The state is stored after every token, so whatever it holds
+// is rounded once per token.  Storing p' = fl(p - w) would round the
+// exponent of the whole history at every token, and with w fixed that
+// rounding goes the same way token after token: the history's weight drifts
+// against every new key (1e-4 after a few hundred tokens behind a key near
+// +40).  Instead the exponent is an anchor that stays where it is while no
+// new key exceeds it, and the decay is applied to the sums: a, b are
+// multiplied by D = e^{-w} every token.  Those roundings change from token to
+// token and do not add up in one direction.  D itself is held as hi + lo
+// (from an fp64 exp), since a fixed error in D would again act on every token
+// alike.  The anchor moves:
+//   - up to k, exactly, when a new key exceeds it (the history is rescaled
+//     by e^{p-k} <= 1);
+//   - down by kStepReanchor when the decayed sums fall below 2^-40, so that
+//     new keys never underflow against a stale anchor.  This happens about
+//     once every kStepReanchor / w tokens.
+// The state is any (a, b, p) with the same e^p a and e^p b, so p need not be
+// the running maximum.  GATED as in frame_token: gd = 1 + e^{-r}.
+constexpr float kStepReanchor = 28.0f;                  // natural-log units
+constexpr float kStepExpReanchor = 1.44625706e12f;      // e^28, rounded to fp32
+constexpr float kStepLowSum = 9.094947e-13f;            // 2^-40
+
 template <bool GATED = false>
 __device__ __forceinline__ float decode_token(float& a, float& b, float& p, float k, float v,
                                               float w, float u, float gd = 1.0f) {
-    const float pw = p - w;
-    const float d = pw - k;
-    const float e = exp_neg_abs(d);
-    const bool keep = d >= 0.0f;
-    const float alpha = keep ? 1.0f : e;
-    const float beta = keep ? e : 1.0f;
-    const float t1 = alpha * a;
+    const double dd = exp(-double(w));
+    const float dhi = float(dd);
+    const float dlo = float(dd - double(dhi));
+    const float x = k - p;                   // new key against the anchor
+    const float e = exp_neg_abs(x);
+    const bool keep = x <= 0.0f;             // the anchor stays
+    const float alpha = keep ? 1.0f : e;     // history moved to an anchor at k
+    const float beta = keep ? e : 1.0f;      // weight of the new token
+    float ta = alpha * a;
+    float tb = alpha * b;
+    ta = __builtin_fmaf(ta, dhi, ta * dlo);  // decayed by one token
+    tb = __builtin_fmaf(tb, dhi, tb * dlo);
     const float wmu = w - u;
     float y;
     if (__builtin_fabsf(wmu) <= kFusedMaxAbsUW) {
+        // read-out weights are the fold-in weights times (D, e^{u-w})
         const float delta = beta * __builtin_amdgcn_exp2f(-wmu * kLog2e);
-        const float den = __builtin_fmaf(alpha, b, delta);
-        y = __builtin_fmaf(delta, v, t1) * fast_rcp(GATED ? den * gd : den);
+        const float den = tb + delta;
+        y = __builtin_fmaf(delta, v, ta) * fast_rcp(GATED ? den * gd : den);
     } else {
-        const float dr = d + wmu;
+        // read-out as written: history at exponent p against u + k
+        const float dr = -x - u;
         const float er = exp_neg_abs(dr);
         const bool kr = dr >= 0.0f;
         const float ar = kr ? 1.0f : er;
@@ -193,9 +219,19 @@ __device__ __forceinline__ float decode_token(float& a, float& b, float& p, floa
         const float den = __builtin_fmaf(ar, b, br);
         y = __builtin_fmaf(br, v, ar * a) * fast_rcp(GATED ? den * gd : den);
     }
-    a = __builtin_fmaf(beta, v, t1);
-    b = __builtin_fmaf(alpha, b, beta);
-    p = keep ? pw : k;
+    a = __builtin_fmaf(beta, v, ta);
+    b = tb + beta;
+    p = keep ? p : k;
+    // downward re-anchor: p - 28 with its rounding error (TwoSum) folded
+    // into the factor e^{28 + err} that a and b take
+    const bool low = b < kStepLowSum;
+    const float ps = p - kStepReanchor;
+    const float z = ps - p;
+    const float err = (p - (ps - z)) + (-kStepReanchor - z);
+    const float f = __builtin_fmaf(kStepExpReanchor, err, kStepExpReanchor);
+    a = low ? a * f : a;
+    b = low ? b * f : b;
+    p = low ? ps : p;
     return y;
 }
 

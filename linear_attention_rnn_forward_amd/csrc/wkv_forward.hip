@@ -59,6 +59,10 @@ constexpr int kChainTokens = WKV_CHAIN_TOKENS;   // tokens per sub-chunk on the 
 constexpr int kFrameTokens = WKV_FRAME_TOKENS;   // tokens per frame of the running maximum
 constexpr uint64_t kSpinTicks = 20000000;  // 200 ms at 100 MHz
 
+// Count of look-back waits that gave up, on this device, since the library
+// was loaded (read by wkv_bounded_wait_failures()).
+__device__ unsigned int g_chunk_wait_failures;
+
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
@@ -367,10 +371,23 @@ __device__ void look_back(const ChunkArgs& ca, int64_t g, int64_t j, int tile_to
         }
         compiler_fence();
         if (f == 0) {
-            // never expected: record it and continue with what we have, so the
-            // kernel still terminates
-            if (lane == 0) atomicOr(ca.error, 1u);
-            x = sfx;
+            // never expected.  The kernel still terminates, and the miss is
+            // made visible: the carry becomes NaN, so this tile's outputs and
+            // (through its inclusive prefix) every later tile's of the column
+            // group are NaN; the workspace error word and the device's
+            // failure count record it.
+            if (lane == 0) {
+                atomicOr(ca.error, 1u);
+                atomicAdd(&g_chunk_wait_failures, 1u);
+            }
+            const float nan = __builtin_nanf("");
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                x.a[q] = nan;
+                x.b[q] = nan;
+                x.A[q] = 0.0f;
+                x.m[q] = 0.0f;
+            }
             return;
         }
         const int kind = f == kInclusive ? 1 : 0;
@@ -948,6 +965,14 @@ hipError_t launch_forward_chunked(const ForwardProblem& pr, void* workspace, hip
     else
         launch_chunked_t<false>(pr, ca, pl.vec, grid, stream);
     return hipGetLastError();
+}
+
+hipError_t read_chunk_wait_failures(uint64_t* count) {
+    unsigned int n = 0;
+    const hipError_t e = hipMemcpyFromSymbol(&n, HIP_SYMBOL(g_chunk_wait_failures), sizeof(n), 0,
+                                             hipMemcpyDeviceToHost);
+    *count = n;
+    return e;
 }
 
 hipError_t launch_state_passthrough(const ForwardProblem& pr, hipStream_t stream) {

@@ -42,6 +42,10 @@ hipError_t launch_forward_chunked(const ForwardProblem& pr, void* workspace, hip
 hipError_t launch_forward_chained(const ForwardProblem& pr, hipStream_t stream);
 // T == 0: state_out = state_in (or the empty state).
 hipError_t launch_state_passthrough(const ForwardProblem& pr, hipStream_t stream);
+// Bounded waits that gave up on the current device since the library was
+// loaded: the chunked forward's look-back, the matrix forward's ring.
+hipError_t read_chunk_wait_failures(uint64_t* count);
+hipError_t read_ring_wait_failures(uint64_t* count);
 
 struct StepProblem {
     int64_t L, S, C;

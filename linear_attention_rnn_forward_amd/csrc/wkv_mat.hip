@@ -446,6 +446,10 @@ constexpr int kSlots = 4;                       // ring slots: one per producer 
 constexpr uint64_t kRingSpinTicks = 20000000;   // 200 ms of the 100 MHz real-time counter
 constexpr int kProducerSleep = 4;               // producers wait for a free slot at a slower poll
 
+// Count of ring workgroups whose bounded waits gave up, on this device, since
+// the library was loaded (read by wkv_bounded_wait_failures()).
+__device__ unsigned int g_ring_wait_failures;
+
 struct MatRing {
     ChunkOps slot[kSlots];
     int ready[kSlots];   // chunk whose operands the slot holds (-1: none yet)
@@ -455,8 +459,9 @@ struct MatRing {
 };
 
 // Wait until *f == want.  The wait is bounded, and once one wait of the
-// workgroup has given up no other blocks: a slip in the hand-over would give
-// wrong results rather than a workgroup that does not end.
+// workgroup has given up no other blocks: a slip in the hand-over ends the
+// workgroup, which then writes NaN over its outputs and state and counts
+// itself in g_ring_wait_failures (never expected; see the end of the kernel).
 // SLEEP: the pause between polls (units of 64 cycles).
 template <int SLEEP>
 __device__ __forceinline__ void ring_wait(MatRing& sh, int* f, int want) {
@@ -779,6 +784,18 @@ __global__ __launch_bounds__(512, 4) void mat_forward_ring_kernel(MatProblem pr)
                     pr.s_out[sbase + int64_t(16 * b + 4 * g + r) * kN + jcol] = S[b][r];
         }
     }
+    // every wave gets here (all waits are bounded).  A wait that gave up
+    // leaves the head's results unusable: they are overwritten with NaN, so
+    // no check of finite outputs can miss it, and the miss is counted.
+    __syncthreads();
+    if (__hip_atomic_load(&sh.gave_up, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) {
+        uint16_t* y = static_cast<uint16_t*>(pr.y);
+        for (int64_t t = threadIdx.x / kN; t < T; t += blockDim.x / kN)
+            y[(row0 + t) * C + h * kN + threadIdx.x % kN] = 0x7FC0u;   // bf16 NaN
+        if (pr.s_out)
+            for (int e = threadIdx.x; e < kN * kN; e += blockDim.x) pr.s_out[sbase + e] = __builtin_nanf("");
+        if (threadIdx.x == 0) atomicAdd(&g_ring_wait_failures, 1u);
+    }
 }
 
 // One token for every (row, head), one wave per head.  Lane (rg, cq) holds
@@ -852,6 +869,14 @@ __global__ __launch_bounds__(256) void mat_step_kernel(MatStepProblem pr) {
 }
 
 }  // namespace
+
+hipError_t read_ring_wait_failures(uint64_t* count) {
+    unsigned int n = 0;
+    const hipError_t e = hipMemcpyFromSymbol(&n, HIP_SYMBOL(g_ring_wait_failures), sizeof(n), 0,
+                                             hipMemcpyDeviceToHost);
+    *count = n;
+    return e;
+}
 
 hipError_t launch_mat_forward(const MatProblem& pr, hipStream_t stream) {
     const dim3 grid(unsigned(pr.B * pr.H)), block(512);

@@ -5,8 +5,10 @@
 //
 // Purely elementwise: every element reads k, v, a, b, p and writes y, a', b',
 // p'.  VEC adjacent channels per lane with vector loads.  The per-element
-// arithmetic is decode_token() from wkv_device.h: natural-log exponents and
-// one rounding of p per token (the state is stored between tokens).
+// arithmetic is decode_token() from wkv_device.h: natural-log exponents, the
+// exponent held as an anchor that moves only to an exact new maximum (or
+// rarely down), and the decay applied to a, b as e^{-w} in hi + lo parts, so
+// that no rounding repeats the same way token after token.
 #include "wkv_device.h"
 #include "wkv_internal.h"
 

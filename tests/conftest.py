@@ -15,9 +15,21 @@ def pytest_configure(config):
 @pytest.fixture(autouse=True)
 def _announce_gpu_case(request):
     # name the case before any GPU work, so a run that dies names its test
-    if request.node.get_closest_marker("gpu") is not None:
+    gpu = request.node.get_closest_marker("gpu") is not None
+    if gpu:
         print(f"\n[gpu case] {request.node.nodeid}", flush=True)
     yield
+    # no bounded wait (chunked look-back, matrix ring) may have given up
+    # during a GPU test: its results would be NaN and counted here
+    if gpu and "device" in request.fixturenames:
+        import linear_attention_rnn_forward_amd as wkv
+        before = request.config.stash.get(_WAIT_KEY, 0)
+        now = wkv.bounded_wait_failures()
+        request.config.stash[_WAIT_KEY] = now
+        assert now == before, f"{now - before} bounded wait(s) gave up during {request.node.nodeid}"
+
+
+_WAIT_KEY = pytest.StashKey[int]()
 
 
 @pytest.fixture(scope="session")

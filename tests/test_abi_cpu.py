@@ -33,13 +33,13 @@ def test_header_lists_the_boundary_calls():
     for n in ("wkv_forward", "wkv_step", "wkv_token_shift", "wkv_forward_workspace_size",
               "wkv_forward_gated", "wkv_step_gated", "wkv_backward", "wkv_backward_workspace_size",
               "wkv_status_string", "wkv_last_error", "wkv_mat_forward", "wkv_mat_forward_path",
-              "wkv_mat_step"):
+              "wkv_mat_step", "wkv_bounded_wait_failures"):
         assert n in names
 
 
 def test_abi_version_and_status_strings():
     L = wkv.lib()
-    assert L.wkv_abi_version() == 104
+    assert L.wkv_abi_version() == 105
     for code in range(0, -9, -1):
         assert L.wkv_status_string(code).decode()
     assert L.wkv_status_string(-100).decode() == "unknown status"
@@ -64,6 +64,11 @@ def test_forward_rejects_bad_arguments():
     assert _fwd(dtype=7) == -3
     assert _fwd(B=0) == -2 and _fwd(C=0) == -2 and _fwd(T=-1) == -2
     assert _fwd(B=1 << 40, T=1 << 40) == -2
+    # a block of 32 token rows must stay within 32-bit byte offsets
+    for dtype, es in ((0, 4), (1, 2)):
+        c_max = (4294967295 - 512) // (33 * es)
+        assert _fwd(C=c_max + 1, T=1, dtype=dtype) == -2
+        assert b"32-bit offsets" in L.wkv_last_error()
     assert _fwd(path=9) == -8
     assert _fwd(k=None) == -1 and _fwd(w=None) == -1
     assert _fwd(a_in=6 * G) == -1          # state in: all or none

@@ -52,9 +52,14 @@ def check_forward(x, dtype, dev, path, state=None, check_state=True, tol=None):
     err = guarded_rel_err(yh, y_ref, g)
     assert err <= (tol or TOL[dtype]), f"path={path} guarded rel err {err:.3e}"
     if check_state:
+        # the state is fp32 whatever the storage: the fp32 bar (or the case's
+        # own, where exponents are so large that their fp32 spacing sets it),
+        # on the sums rescaled to the oracle's exponent and on the exponent
+        state_tol = max(TOL["f32"], tol or 0.0)
         ea, eb, ep = state_mismatch(tuple(host(s) for s in st), st_ref)
-        assert ea <= 10 * TOL["f32"] and eb <= 10 * TOL["f32"], (ea, eb)
-        assert ep <= 1e-3, ep
+        print(f"path={path} y err {err:.2e}; state a {ea:.2e} b {eb:.2e} p {ep:.2e}")
+        assert ea <= state_tol and eb <= state_tol, (ea, eb)
+        assert ep <= state_tol, ep
     return yh, y_ref, err
 
 
@@ -257,3 +262,20 @@ def test_paths_agree(device):
         assert guarded_rel_err(host(yc), host(ys), 1.0) <= 2.0 ** -7
         ea, eb, ep = state_mismatch(tuple(host(s) for s in stc), tuple(host(s) for s in sts))
         assert ea <= 1e-4 and eb <= 1e-4 and ep <= 1e-4
+
+
+def test_chunked_workspace_error_word_stays_clear(device):
+    """The chunked path's look-back waits are bounded; one that gives up sets
+    the uint32 error word at byte offset 4 of the workspace (and writes NaN).
+    On an ordinary run it stays 0, also when the workspace held garbage."""
+    import linear_attention_rnn_forward_amd as wkv
+    torch = _torch()
+    x = synth.make_forward_inputs(synth.TINY.resized(B=2, T=5000, C=192, seed=8))
+    k, v, w, u = gpu_inputs(x, device)
+    need = wkv.workspace_size(2, 5000, 192, wkv.F32, "chunked")
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=device)
+    y = wkv.forward(k, v, w, u, path="chunked", workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[4:8].view(torch.int32).item()) == 0
+    y_ref, _ = oracle.forward(x.k, x.v, x.w, x.u)
+    assert guarded_rel_err(host(y), y_ref, rms(x.v)) <= TOL["f32"]

@@ -58,3 +58,68 @@ def test_save_load_round_trip_and_resume(device, dtype):
         y, fresh = wkv.step(fresh, ks[t][:, perm].contiguous(), vs[t][:, perm].contiguous(), w, u)
         torch.cuda.synchronize()
         assert torch.equal(y[:, 3], ys[t][:, 1]), t
+
+
+def _decode_blob(blob, Ln, C):
+    """a, b, p [L, C] from a session blob: a 64-byte header (magic "WKVS",
+    version, L, C, dtype, number of shift arrays), then a, b, p as fp32
+    [L][C] each, little-endian."""
+    raw = bytes(blob)
+    assert raw[:4] == b"WKVS"
+    L_, C_ = np.frombuffer(raw[8:24], dtype="<i8")
+    assert (L_, C_) == (Ln, C)
+    body = np.frombuffer(raw[64:64 + 12 * Ln * C], dtype="<f4").reshape(3, Ln, C)
+    return tuple(body[i].astype(np.float64) for i in range(3))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_resume_matches_the_oracle(device, dtype):
+    """A resumed session continues as the oracle does: the oracle, started
+    from the a, b, p read back out of the saved bytes, and the oracle run
+    without a break both give the resumed slot's outputs (1e-4 guarded
+    relative for fp32 storage, 2e-2 for bf16), on keys with 1% at +40."""
+    import linear_attention_rnn_forward_amd as wkv
+    import oracle
+    from oracle.compare import guarded_rel_err
+    torch = _torch()
+    rng = np.random.default_rng(93)
+    Ln, S, C, T = 2, 3, 130, 64
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    w = np.exp(rng.uniform(-5, 1, (Ln, C))).astype(np.float32)
+    u = rng.normal(0, 0.5, (Ln, C)).astype(np.float32)
+    kh = rng.normal(0, 1, (T, Ln, S, C)).astype(np.float32)
+    kh[rng.random(kh.shape) < 0.01] = 40.0
+    vh = rng.normal(0, 1, (T, Ln, S, C)).astype(np.float32)
+    ks = torch.from_numpy(kh).to(device).to(tdt)
+    vs = torch.from_numpy(vh).to(device).to(tdt)
+    kh, vh = ks.float().cpu().numpy(), vs.float().cpu().numpy()   # as stored
+    wd, ud = torch.from_numpy(w).to(device), torch.from_numpy(u).to(device)
+    st = tuple(torch.full((Ln, S, C), f, device=device) for f in (0.0, 0.0, float("-inf")))
+    half = T // 2
+    for t in range(half):
+        _, st = wkv.step(st, ks[t], vs[t], wd, ud)
+    blob = wkv.save_session(st, 2)
+    torch.cuda.synchronize()
+    # resume sequence 2 in slot 0 of a fresh batch
+    fresh = tuple(torch.full((Ln, S, C), f, device=device) for f in (0.0, 0.0, float("-inf")))
+    wkv.load_session(blob, fresh, 0)
+    perm = [2, 0, 1]
+    got = []
+    for t in range(half, T):
+        y, fresh = wkv.step(fresh, ks[t][:, perm].contiguous(), vs[t][:, perm].contiguous(), wd, ud)
+        got.append(y[:, 0].float().cpu().numpy())
+    torch.cuda.synchronize()
+    got = np.stack(got)                                    # [T - half, L, C]
+    tol = 2e-2 if dtype == "bf16" else 1e-4
+    # the oracle from the saved bytes
+    st_o = tuple(x[:, None, :] for x in _decode_blob(blob, Ln, C))   # [L, 1, C]
+    ref = []
+    for t in range(half, T):
+        y_o, st_o = oracle.step(st_o, kh[t][:, 2:3], vh[t][:, 2:3], w, u)
+        ref.append(y_o[:, 0])
+    ref = np.stack(ref)
+    assert guarded_rel_err(got, ref, 1.0) <= tol
+    # the oracle without a break (its forward over all T tokens, per layer)
+    for l in range(Ln):
+        y_full, _ = oracle.forward(kh[:, l, 2][None], vh[:, l, 2][None], w[l], u[l])
+        assert guarded_rel_err(got[:, l], y_full[0, half:], 1.0) <= tol, l

@@ -48,8 +48,9 @@ def test_step_matches_oracle(device, C, dtype):
         torch.cuda.synchronize()
         tol = 2e-2 if dtype == "bf16" else 1e-4
         assert guarded_rel_err(host(y), y_o, 1.0) <= tol, t
-        ea, eb, ep = state_mismatch(tuple(host(s) for s in st), st_o)
-        assert ea <= 1e-4 and eb <= 1e-4 and ep <= 1e-4
+        # the decode state keeps its own anchor: compared at the oracle's exponent
+        ea, eb, _ = state_mismatch(tuple(host(s) for s in st), st_o)
+        assert ea <= 1e-4 and eb <= 1e-4
 
 
 def test_step_in_place(device):
@@ -78,8 +79,7 @@ def test_step_in_place(device):
 def test_step_chain_matches_forward(device, dtype, path):
     """A chain of decode steps reproduces wkv_forward's outputs and final state
     (1e-5 guarded relative for fp32 storage; bf16 outputs may sit one bf16
-    rounding apart).  The decode state is stored after every token, so its
-    exponent is rounded once per step; the forward paths keep it exact."""
+    rounding apart)."""
     import linear_attention_rnn_forward_amd as wkv
     torch = _torch()
     B, T, C = 6, 300, 192
@@ -101,9 +101,9 @@ def test_step_chain_matches_forward(device, dtype, path):
     y_chain = torch.stack(ys, dim=1)
     tol = 1e-5 if dtype == "f32" else 2.0 ** -7
     assert guarded_rel_err(host(y_chain), host(y_f), 1.0) <= tol
-    # the chain's exponent carries one rounding per step; the forward's does not
-    ea, eb, ep = state_mismatch(tuple(host(s[0]) for s in st), tuple(host(s) for s in st_f))
-    assert ea <= 1e-4 and eb <= 1e-4 and ep <= 1e-4, (ea, eb, ep)
+    # the chain's state keeps its own anchor: compared at the forward's exponent
+    ea, eb, _ = state_mismatch(tuple(host(s[0]) for s in st), tuple(host(s) for s in st_f))
+    assert ea <= 1e-4 and eb <= 1e-4, (ea, eb)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -173,3 +173,58 @@ def test_device_generator_matches_host(device):
     ctr = synth.decode_counter(wl, lay, seq, tok, ch)
     np.testing.assert_array_equal(out_k.cpu().numpy(), synth.philox_normal(ctr, synth.STREAM_K, wl.seed))
     np.testing.assert_array_equal(out_v.cpu().numpy(), synth.philox_normal(ctr, synth.STREAM_V, wl.seed))
+
+
+# ---------------------------------------------------------------------------
+# the decode chain on keys the pages warn about: 1% of keys at +40
+# ([tm-math] "Numerical stability: carry the exponent"), long enough for the
+# state's exponent to sit behind a large key for hundreds of tokens
+# ---------------------------------------------------------------------------
+
+def _spiky_chain(device, B, T, C, seed, gated):
+    import linear_attention_rnn_forward_amd as wkv
+    torch = _torch()
+    x = synth.make_forward_inputs(synth.TINY.resized(B=B, T=T, C=C, seed=seed))
+    k, v = dev_f32(x.k, device), dev_f32(x.v, device)
+    w, u = dev_f32(x.w, device), dev_f32(x.u, device)
+    r_host = rd = None
+    if gated:
+        r_host, _ = synth.make_receptance(synth.TINY.resized(B=B, T=T, C=C, seed=seed))
+        rd = dev_f32(r_host, device)
+    y_f, st_f = wkv.forward(k, v, w, u, return_state=True, r=rd)
+    wl, ul = w[None].contiguous(), u[None].contiguous()
+    st = tuple(torch.full((1, B, C), f, device=device) for f in (0.0, 0.0, float("-inf")))
+    ys = []
+    for t in range(T):
+        rt = None if rd is None else rd[:, t][None].contiguous()
+        y, st = wkv.step(st, k[:, t][None].contiguous(), v[:, t][None].contiguous(), wl, ul, r=rt)
+        ys.append(y[0])
+    torch.cuda.synchronize()
+    y_chain = host(torch.stack(ys, dim=1))
+    if gated:
+        y_ref, st_ref = oracle.forward_gated(x.k, x.v, r_host, x.w, x.u)
+    else:
+        y_ref, st_ref = oracle.forward(x.k, x.v, x.w, x.u)
+    assert np.all(np.isfinite(y_chain))
+    e_fwd = guarded_rel_err(y_chain, host(y_f), 1.0)
+    e_orc = guarded_rel_err(y_chain, y_ref, 1.0)
+    e_fwd_orc = guarded_rel_err(host(y_f), y_ref, 1.0)
+    ea, eb, _ = state_mismatch(tuple(host(s[0]) for s in st), st_ref)
+    print(f"spiky chain B={B} T={T} C={C} gated={gated}: chain vs forward {e_fwd:.2e}, "
+          f"chain vs oracle {e_orc:.2e}, forward vs oracle {e_fwd_orc:.2e}, state {ea:.2e} {eb:.2e}")
+    return e_fwd, e_orc, ea, eb
+
+
+@pytest.mark.parametrize("gated", [False, True], ids=["plain", "gated"])
+@pytest.mark.parametrize("shape", [(4, 256, 64), (2, 1024, 256)], ids=["T256", "T1024"])
+def test_step_chain_on_spiky_keys(device, shape, gated):
+    """The decode chain follows wkv_forward to 1e-5 (guarded relative) and the
+    oracle to 1e-4 on the overflow-probe recipe, where a key of +40 dominates
+    the history for hundreds of tokens; the chain's final state equals the
+    oracle's to 1e-4 (compared at the oracle's exponent: the decode state
+    keeps its own anchor, which need not be the running maximum)."""
+    B, T, C = shape
+    e_fwd, e_orc, ea, eb = _spiky_chain(device, B, T, C, 300 + T, gated)
+    assert e_fwd <= 1e-5
+    assert e_orc <= 1e-4
+    assert ea <= 1e-4 and eb <= 1e-4
