@@ -130,21 +130,24 @@ class ForwardBench:
 
     def config(self):
         name = self.wl.name + (", receptance gate fused (o = sigmoid(r) * wkv)" if self.gated else "")
+        code = self.wkv.BF16 if self.io == "bf16" else self.wkv.F32
         return {"workload": name, "B": self.wl.B, "T": self.wl.T, "C": self.wl.C,
-                "io_dtype": self.io, "state_dtype": "f32"}
+                "io_dtype": self.io, "state_dtype": "f32",
+                "path": self.wkv.auto_path(self.wl.B, self.wl.T, self.wl.C, code)}
 
     def cpu_baseline(self, min_seconds=10.0):
         """The oracle over the whole workload, repeated until about
-        min_seconds of wall time have passed."""
+        min_seconds of wall time have passed; its last output is kept for the
+        run's parity figure."""
         import oracle
         x = self.host
         passes = 0
         t0 = time.perf_counter()
         while True:
             if self.gated:
-                oracle.forward_gated(x.k, x.v, self.r_host, x.w, x.u)
+                self.y_oracle, _ = oracle.forward_gated(x.k, x.v, self.r_host, x.w, x.u)
             else:
-                oracle.forward(x.k, x.v, x.w, x.u)
+                self.y_oracle, _ = oracle.forward(x.k, x.v, x.w, x.u)
             passes += 1
             dt = time.perf_counter() - t0
             if dt >= min_seconds:
@@ -153,6 +156,18 @@ class ForwardBench:
                 "cores": oracle.threads(), "kind": "oracle",
                 "sample": f"the full workload ({self.units} tokens*channels), {passes} passes, "
                           f"{dt:.1f} s including fp64 conversion"}
+
+    def parity(self):
+        """Max guarded relative error of the timed run's output against the
+        oracle's over the whole workload (guard: RMS of v), if the oracle ran."""
+        y_ref = getattr(self, "y_oracle", None)
+        if y_ref is None:
+            return None
+        from oracle.compare import guarded_rel_err, rms
+        err = guarded_rel_err(self.y.float().cpu().numpy(), y_ref, rms(self.host.v))
+        return {"max_guarded_rel_err": float(f"{err:.3e}"),
+                "bar": 2e-2 if self.io == "bf16" else 1e-4,
+                "against": "fp64 oracle, whole workload"}
 
 
 class BackwardBench:
@@ -518,6 +533,43 @@ class TokenShiftBench:
                 "kind": "oracle", "sample": "2 of the 16 batch rows"}
 
 
+def step_spread(bench, stream, n):
+    """min / median / max duration of n eager steps, HIP events recorded on
+    the launch stream between consecutive steps (launched back to back)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(n):
+        bench.step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    d = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n))
+    return {"min": round(d[0], 2), "median": round(d[n // 2], 2), "max": round(d[-1], 2), "n": n,
+            "from": "eager steps right after the timed replay, HIP events between steps"}
+
+
+def copy_ceiling(nbytes, dev, stream, n=20):
+    """GB/s of a plain device copy moving nbytes in all (nbytes / 2 read,
+    nbytes / 2 written): the rate this device gives a simple stream."""
+    import torch
+    half = max(int(nbytes // 2) // 4, 1)
+    x = torch.ones(half, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(n):
+        y.copy_(x)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t = ev0.elapsed_time(ev1) / 1e3 / n
+    return 2 * 4 * half / t / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -606,8 +658,10 @@ def main():
     # timed region, divided by the launch count
     avg_kernel_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
 
+    spread = step_spread(bench, stream, args.steps)
     value = bench.units * args.steps / elapsed
     achieved = bench.alg_bytes / avg_kernel_s / 1e9
+    copy_gbs = copy_ceiling(bench.alg_bytes, dev, stream)
     traffic = measured_traffic(args.workload)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -620,13 +674,18 @@ def main():
         cpu = bench.cpu_baseline()
         if cpu is not None:
             cpu["value"] = float(f"{cpu['value']:.4g}")
+    parity = getattr(bench, "parity", lambda: None)()
     line = {"metric": METRIC, "value": float(f"{value:.6g}"), "unit": "tokens·channels/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": bench.dtype, "data": "synthetic",
             "config": dict(bench.config(), launch="hip graph of the timed steps" if graph is not None
                            else "one launch per step"),
-            "roofline": roofline, "cpu_baseline": cpu}
+            "roofline": roofline, "cpu_baseline": cpu,
+            "step_us": spread,
+            "copy_ceiling": {"GB/s": round(copy_gbs, 1), "frac": round(achieved / copy_gbs, 4),
+                             "bytes": bench.alg_bytes, "kernel": "torch device copy, same bytes"},
+            "parity": parity}
     print(json.dumps(line), flush=True)
 
 

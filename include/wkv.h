@@ -96,6 +96,11 @@ size_t wkv_forward_workspace_size(int64_t B, int64_t T, int64_t C, int dtype);
 /* Same, for an explicitly chosen path. */
 size_t wkv_forward_workspace_size_path(int64_t B, int64_t T, int64_t C, int dtype, int path);
 
+/* The wkv_path (WKV_PATH_SERIAL, _CHUNKED or _CHAINED) that wkv_forward takes
+ * for these sizes on the current device, with k, v, y 4-byte aligned (for
+ * reports and tests).  Negative wkv_status for invalid sizes or dtype. */
+int wkv_forward_auto_path(int64_t B, int64_t T, int64_t C, int dtype);
+
 /*
  * Training / prefill form: y for every position, and optionally the state
  * after the last token ([tm-math] "Why it collapses into a recurrence": one

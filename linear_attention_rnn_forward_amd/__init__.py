@@ -101,10 +101,19 @@ def lib() -> ctypes.CDLL:
         L.wkv_last_error.argtypes = []
         L.wkv_abi_version.restype = i32
         L.wkv_abi_version.argtypes = []
+        L.wkv_forward_auto_path.restype = i32
+        L.wkv_forward_auto_path.argtypes = [i64, i64, i64, i32]
         L.wkv_bounded_wait_failures.restype = i32
         L.wkv_bounded_wait_failures.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
         _lib = L
     return _lib
+
+
+def auto_path(B: int, T: int, C: int, dtype: int = F32) -> str:
+    """The execution path wkv_forward takes for these sizes on the current device."""
+    code = lib().wkv_forward_auto_path(B, T, C, dtype)
+    check(min(code, 0))
+    return {v: k for k, v in _PATHS.items()}[code]
 
 
 def bounded_wait_failures() -> int:

@@ -262,6 +262,20 @@ size_t wkv_forward_workspace_size_path(int64_t B, int64_t T, int64_t C, int dtyp
     return wkv::forward_workspace_bytes(B, T, C, dtype, path);
 }
 
+int wkv_forward_auto_path(int64_t B, int64_t T, int64_t C, int dtype) {
+    if (B < 1 || C < 1 || T < 0) return fail(WKV_ERR_SHAPE, "need B >= 1, T >= 0, C >= 1");
+    if (dtype != WKV_F32 && dtype != WKV_BF16) return fail(WKV_ERR_DTYPE, "unknown dtype %d", dtype);
+    int64_t n = 0;
+    if (!mul3(B, T, C, &n)) return fail(WKV_ERR_SHAPE, "B*T*C too large");
+    wkv::ForwardProblem pr{};
+    pr.B = B;
+    pr.T = T;
+    pr.C = C;
+    pr.dtype = dtype;
+    pr.vec = wkv::pick_forward_vec(C, dtype, true);
+    return wkv::choose_forward_path(pr, wkv::device_cu_count());
+}
+
 size_t wkv_forward_workspace_size(int64_t B, int64_t T, int64_t C, int dtype) {
     return wkv_forward_workspace_size_path(B, T, C, dtype, WKV_PATH_AUTO);
 }

@@ -61,6 +61,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kEmptyP = -1.0e38f;      // the empty history's exponent
 constexpr float kEmptyIn = -1.0e30f;     // state inputs at or below this are empty
 constexpr float kFusedMaxAbsUW = 44.0f;  // |u - w| bound for the fused read-out
+constexpr float kNarrowMaxAbsUW = 13.8f; // |u - w| bound (c within [2^-20, 2^20]) for frame weights
 
 enum : int { kF32 = 0, kBF16 = 1 };
 
@@ -83,6 +84,12 @@ __device__ __forceinline__ float max_num(float a, float b) {
     return r;
 }
 
+__device__ __forceinline__ float max3_num(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ float min_num(float a, float b) {
     float r;
     asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
@@ -95,6 +102,7 @@ struct Chan {
     float wmu;   // w - u
     float c;     // e^{u-w}
     bool fused;  // fused read-out allowed
+    bool narrow; // c within [2^-20, 2^20]: the frame-weight output pass applies
 };
 
 __device__ __forceinline__ Chan make_chan(float w, float u) {
@@ -102,6 +110,7 @@ __device__ __forceinline__ Chan make_chan(float w, float u) {
     ch.w = w;
     ch.wmu = w - u;
     ch.fused = __builtin_fabsf(ch.wmu) <= kFusedMaxAbsUW;
+    ch.narrow = __builtin_fabsf(ch.wmu) <= kNarrowMaxAbsUW;
     ch.c = __builtin_amdgcn_exp2f(ch.fused ? -ch.wmu * kLog2e : 0.0f);
     return ch;
 }

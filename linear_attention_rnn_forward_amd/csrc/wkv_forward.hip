@@ -169,7 +169,7 @@ __device__ __forceinline__ void run_block(Lane<VEC>& s, const typename Io<DT, VE
                                                        float(i % F + 1), keep, GATED ? gd[q] : 1.0f);
                 all_keep[q] = all_keep[q] && keep;
             }
-            if (active) Buf<Raw>::store(IO::pack(yf), yr_, voff + uint32_t(i) * row_bytes, 0u);
+            if (active) Buf<Raw>::store(IO::pack(yf), yr_, voff, uint32_t(i) * row_bytes);
         }
     }
     // the last frame starts at token f0 of the block
@@ -502,6 +502,272 @@ __device__ __forceinline__ void chunk_aggregate(const Lane<VEC>& s,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Frame weights: the output pass reuses the aggregate pass's exponentials.
+//
+// Inside a frame of F tokens the decay rides on the keys: in frame
+// coordinates token i's key is x_i = k_i + (i + 1) w and the history (the
+// state before the frame's first token, exponent H) decays no further
+// (wkv_device.h, 4.).  The aggregate pass already forms e_i = e^{x_i - M}
+// against the frame's largest key M.  Against G = max(H, M) the history
+// takes alpha = e^{H-G} and the frame's tokens beta e_i with beta = e^{M-G}
+// (one of the two is exactly 1), and token by token
+//   y_i = (a + beta e_i c v_i) / (b + beta e_i c),  a += beta e_i v_i,
+//   b += beta e_i,  starting from a = alpha a_H, b = alpha b_H,  c = e^{u-w}
+// (the read-out of wkv_device.h 3. with the frame's weights fixed): no
+// exponential, running maximum or select per token.  A history that keeps
+// the maximum is not rescaled at all, as in frame_token.
+//
+// Fixing the weights for a whole frame needs them in range: the largest
+// term of every prefix must stay a normal number, i.e. alpha (the history
+// has b >= 1) or beta e_0 at least 2^-100 (with c >= 2^-20 the read-out's
+// denominator stays above 2^-120).  A frame whose first token and history
+// both sit more than 69 (natural-log units) below a later key of the frame
+// fails that; if any lane of the wave does, the wave runs that frame token
+// by token with the running maximum (frame_token), its keys read again.  On
+// the bf16 workload (1 in 1000 keys at +-40) about 1 frame in 100 of a wave
+// takes that path.
+// ---------------------------------------------------------------------------
+
+constexpr float kFrameTermMin = 7.88860905e-31f;  // 2^-100
+constexpr float kFrameHistMax = 1.8446744e19f;    // 2^64: the history's weight against M_f
+
+template <int VEC, int L>
+struct FrameW {
+    float e[L][VEC];                  // e^{x_i - M_f}
+    float M[L / kFrameTokens][VEC];   // frame maxima M_f (natural-log units)
+};
+
+// Weights of a full block of L tokens (pass 1: frame keys and maxima; pass 2:
+// e_i, with frame sums folded into g, the block's state from the empty
+// history in anchor form).
+template <int DT, int VEC, int L>
+__device__ __forceinline__ void chunk_weights(const Lane<VEC>& s,
+                                              const typename Io<DT, VEC>::Raw (&kr)[L],
+                                              const typename Io<DT, VEC>::Raw (&vr)[L],
+                                              FrameW<VEC, L>& fw, Part<VEC>& g) {
+    using IO = Io<DT, VEC>;
+    constexpr int F = kFrameTokens, NF = L / F;
+    static_assert(L % F == 0 && F % 2 == 0, "whole frames of an even length");
+#pragma unroll
+    for (int f = 0; f < NF; f++) {
+#pragma unroll
+        for (int j = 0; j < F; j += 2) {
+            const int i = f * F + j;
+            float k0[VEC], k1[VEC];
+            IO::unpack(kr[i], k0);
+            IO::unpack(kr[i + 1], k1);
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                const float x0 = __builtin_fmaf(float(j + 1), s.ch[q].w, k0[q]);
+                const float x1 = __builtin_fmaf(float(j + 2), s.ch[q].w, k1[q]);
+                fw.e[i][q] = x0;
+                fw.e[i + 1][q] = x1;
+                fw.M[f][q] = j == 0 ? max_num(x0, x1) : max3_num(fw.M[f][q], x0, x1);
+            }
+        }
+    }
+#pragma unroll
+    for (int f = 0; f < NF; f++) {
+        float sa[VEC], sb[VEC];
+#pragma unroll
+        for (int q = 0; q < VEC; q++) { sa[q] = 0.0f; sb[q] = 0.0f; }
+#pragma unroll
+        for (int j = 0; j < F; j++) {
+            const int i = f * F + j;
+            float vf[VEC];
+            IO::unpack(vr[i], vf);
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                // the difference first: exact 0 for the frame's largest key
+                const float e = __builtin_amdgcn_exp2f((fw.e[i][q] - fw.M[f][q]) * kLog2e);
+                fw.e[i][q] = e;
+                sb[q] += e;
+                sa[q] = __builtin_fmaf(e, vf[q], sa[q]);
+            }
+        }
+        // frame f spans F tokens; its state in anchor form is (sa, sb, M_f, F)
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            if (f == 0) {
+                g.a[q] = sa[q];
+                g.b[q] = sb[q];
+                g.A[q] = fw.M[0][q];
+                g.m[q] = float(F);
+            } else {
+                combine(g.a[q], g.b[q], g.A[q], g.m[q], sa[q], sb[q], fw.M[f][q], float(F), float(F),
+                        s.ch[q].w);
+            }
+        }
+    }
+}
+
+// The outputs of a full block of L tokens from the state in s (anchor form),
+// with the weights of chunk_weights; see above.  kr_, voff, row_bytes: where
+// the block's keys are, for a frame that must run token by token.
+template <int DT, int VEC, int L, bool GATED>
+__device__ __forceinline__ void run_block_weights(Lane<VEC>& s, const FrameW<VEC, L>& fw,
+                                                  const typename Io<DT, VEC>::Raw (&vr)[L],
+                                                  const typename Io<DT, VEC>::Raw (&rr)[L],
+                                                  rsrc_t kr_, rsrc_t yr_, uint32_t voff,
+                                                  uint32_t row_bytes, bool active) {
+    using IO = Io<DT, VEC>;
+    using Raw = typename IO::Raw;
+    constexpr int F = kFrameTokens, NF = L / F;
+#pragma unroll
+    for (int f = 0; f < NF; f++) {
+        float alpha[VEC], beta[VEC], H[VEC], hist[VEC];
+        bool keep[VEC];
+        bool ok = true, ok_anchor = true;
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            H[q] = __builtin_fmaf(-s.m[q], s.ch[q].w, s.A[q]);  // history exponent
+            const float d = H[q] - fw.M[f][q];
+            // the range checks look at the history's whole weight (factor * b),
+            // so that a state whose b is far from 1 is safe too
+            if constexpr (DT == kBF16) {
+                // the history's factor against M_f (either side of 1)
+                hist[q] = __builtin_amdgcn_exp2f(d * kLog2e);
+                const float hb = hist[q] * s.b[q];
+                ok_anchor = ok_anchor && hb <= kFrameHistMax &&
+                            max_num(hb, fw.e[f * F][q]) >= kFrameTermMin;
+            } else {
+                const float e = exp_neg_abs(d);
+                keep[q] = d >= 0.0f;
+                alpha[q] = keep[q] ? 1.0f : e;
+                beta[q] = keep[q] ? e : 1.0f;
+                ok = ok && max_num(alpha[q] * s.b[q], beta[q] * fw.e[f * F][q]) >= kFrameTermMin;
+            }
+        }
+        if (DT == kBF16 && __builtin_amdgcn_ballot_w64(!ok_anchor) == 0) {
+            // bf16 storage: the frame's anchor is M_f whichever side keeps the
+            // maximum, so the weights need no factor; the history is rescaled
+            // by e^{H - M_f} <= 2^64 every frame (a rounding per frame, far
+            // below one bf16 rounding of the output)
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                s.a[q] *= hist[q];
+                s.b[q] *= hist[q];
+            }
+#pragma unroll
+            for (int j = 0; j < F; j++) {
+                const int i = f * F + j;
+                float vf[VEC], yf[VEC], gd[VEC];
+                IO::unpack(vr[i], vf);
+                if constexpr (GATED) {
+                    float rf[VEC];
+                    IO::unpack(rr[i], rf);
+#pragma unroll
+                    for (int q = 0; q < VEC; q++) gd[q] = gate_den(rf[q]);
+                }
+#pragma unroll
+                for (int q = 0; q < VEC; q++) {
+                    const float e = fw.e[i][q];
+                    const float ec = e * s.ch[q].c;
+                    const float den = s.b[q] + ec;
+                    yf[q] = __builtin_fmaf(ec, vf[q], s.a[q]) * fast_rcp(GATED ? den * gd[q] : den);
+                    s.a[q] = __builtin_fmaf(e, vf[q], s.a[q]);
+                    s.b[q] += e;
+                }
+                if (active) Buf<Raw>::store(IO::pack(yf), yr_, voff, uint32_t(i) * row_bytes);
+            }
+#pragma unroll
+            for (int q = 0; q < VEC; q++) { s.A[q] = fw.M[f][q]; s.m[q] = float(F); }
+        } else if (DT != kBF16 && __builtin_amdgcn_ballot_w64(!ok) == 0) {
+            float ct[VEC];
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                s.a[q] *= alpha[q];
+                s.b[q] *= alpha[q];
+                ct[q] = beta[q] * s.ch[q].c;
+            }
+#pragma unroll
+            for (int j = 0; j < F; j++) {
+                const int i = f * F + j;
+                float vf[VEC], yf[VEC], gd[VEC];
+                IO::unpack(vr[i], vf);
+                if constexpr (GATED) {
+                    float rf[VEC];
+                    IO::unpack(rr[i], rf);
+#pragma unroll
+                    for (int q = 0; q < VEC; q++) gd[q] = gate_den(rf[q]);
+                }
+#pragma unroll
+                for (int q = 0; q < VEC; q++) {
+                    const float et = fw.e[i][q] * beta[q];
+                    const float ec = fw.e[i][q] * ct[q];
+                    const float den = s.b[q] + ec;
+                    yf[q] = __builtin_fmaf(ec, vf[q], s.a[q]) * fast_rcp(GATED ? den * gd[q] : den);
+                    s.a[q] = __builtin_fmaf(et, vf[q], s.a[q]);
+                    s.b[q] += et;
+                }
+                if (active) Buf<Raw>::store(IO::pack(yf), yr_, voff, uint32_t(i) * row_bytes);
+            }
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                s.A[q] = keep[q] ? s.A[q] : fw.M[f][q];
+                s.m[q] = keep[q] ? s.m[q] + float(F) : float(F);
+            }
+        } else {
+            // token by token with the running maximum, the frame's keys read again
+            float kas[VEC];
+            bool all_keep[VEC];
+#pragma unroll
+            for (int q = 0; q < VEC; q++) { kas[q] = H[q]; all_keep[q] = true; }
+#pragma unroll
+            for (int j = 0; j < F; j++) {
+                const int i = f * F + j;
+                float kf[VEC], vf[VEC], yf[VEC], gd[VEC];
+                IO::unpack(Buf<Raw>::template load<kDefaultLoad>(kr_, voff + uint32_t(i) * row_bytes, 0u), kf);
+                IO::unpack(vr[i], vf);
+                if constexpr (GATED) {
+                    float rf[VEC];
+                    IO::unpack(rr[i], rf);
+#pragma unroll
+                    for (int q = 0; q < VEC; q++) gd[q] = gate_den(rf[q]);
+                }
+#pragma unroll
+                for (int q = 0; q < VEC; q++) {
+                    bool kp;
+                    yf[q] = frame_token<true, GATED>(s.a[q], s.b[q], kas[q], kf[q], vf[q], s.ch[q],
+                                                     float(j + 1), kp, GATED ? gd[q] : 1.0f);
+                    all_keep[q] = all_keep[q] && kp;
+                }
+                if (active) Buf<Raw>::store(IO::pack(yf), yr_, voff, uint32_t(i) * row_bytes);
+            }
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                s.A[q] = all_keep[q] ? s.A[q] : kas[q];
+                s.m[q] = all_keep[q] ? s.m[q] + float(F) : float(F);
+            }
+        }
+    }
+}
+
+// Materialise the weights and the aggregate here (an empty asm that takes
+// and returns each of them in a register, ordered with the hand-off's
+// volatile accesses).
+template <int VEC, int L>
+__device__ __forceinline__ void pin_weights(FrameW<VEC, L>& fw, Part<VEC>& g) {
+#pragma unroll
+    for (int i = 0; i < L; i++)
+#pragma unroll
+        for (int q = 0; q < VEC; q++) asm volatile("" : "+v"(fw.e[i][q]));
+#pragma unroll
+    for (int q = 0; q < VEC; q++)
+        asm volatile("" : "+v"(g.a[q]), "+v"(g.b[q]), "+v"(g.A[q]), "+v"(g.m[q]));
+}
+
+// All channels of the wave may use the frame-weight output pass (fused
+// read-out with c in [2^-20, 2^20]).
+template <int VEC>
+__device__ __forceinline__ bool wave_all_narrow(const Lane<VEC>& s) {
+    bool f = true;
+#pragma unroll
+    for (int q = 0; q < VEC; q++) f = f && s.ch[q].narrow;
+    return __builtin_amdgcn_ballot_w64(!f) == 0;
+}
+
 template <int DT, int VEC, bool GATED>
 __global__ __launch_bounds__(kChunkWaves * 64) void forward_chunked_kernel(ForwardProblem pr,
                                                                            ChunkArgs ca) {
@@ -675,6 +941,43 @@ __global__ __launch_bounds__(kChunkWaves * 64) void forward_chunked_kernel(Forwa
 // does not depend on timing.
 // ---------------------------------------------------------------------------
 
+// The carry of sub-chunk sc (the state before it) into s, and carry (+) gw
+// (its n tokens) handed on to sub-chunk sc + 1 and returned in `after` (the
+// state after the sub-chunk, anchored at the running maximum).  The hand-off is the
+// workgroup's critical path (every wave waits on it in turn), so the wave
+// runs it at raised issue priority over the others' passes.
+template <int VEC>
+__device__ __forceinline__ void chain_handoff(Lane<VEC>& s, const Part<VEC>& gw, int n, int64_t sc,
+                                              int64_t nsub, float (&s_carry)[4][64 * VEC],
+                                              int* s_seq, int lane, Part<VEC>& after) {
+    __builtin_amdgcn_s_setprio(3);
+    while (__hip_atomic_load(s_seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != int(sc))
+        __builtin_amdgcn_s_sleep(1);
+    Part<VEC> x;
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        x.a[q] = s_carry[0][lane * VEC + q];
+        x.b[q] = s_carry[1][lane * VEC + q];
+        x.A[q] = s_carry[2][lane * VEC + q];
+        x.m[q] = s_carry[3][lane * VEC + q];
+    }
+    after = x;
+    after.absorb(gw, float(n), s);
+    if (sc + 1 < nsub) {
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            s_carry[0][lane * VEC + q] = after.a[q];
+            s_carry[1][lane * VEC + q] = after.b[q];
+            s_carry[2][lane * VEC + q] = after.A[q];
+            s_carry[3][lane * VEC + q] = after.m[q];
+        }
+        if (lane == 0) __hip_atomic_store(s_seq, int(sc + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int q = 0; q < VEC; q++) { s.a[q] = x.a[q]; s.b[q] = x.b[q]; s.A[q] = x.A[q]; s.m[q] = x.m[q]; }
+}
+
 template <int DT, int VEC, int NWV, bool GATED>
 __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProblem pr, int64_t gpr,
                                                                    int64_t nsub) {
@@ -715,18 +1018,38 @@ __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProble
     const uint32_t voff = active ? uint32_t(lane) * uint32_t(sizeof(Raw)) : 0u;
     const int64_t gbase = (bb * T * pr.C + c0) * es;
     const bool fused = wave_all_fused(s);
+    const bool narrow = wave_all_narrow(s);
 
     for (int64_t sc = wave; sc < nsub; sc += NWV) {
         const int64_t t0 = sc * L;
         const int n = T - t0 >= L ? L : int(T - t0);
         const int64_t base = gbase + t0 * int64_t(row_bytes);
-        Raw kr[L], vr[L], rr[GATED ? L : 1];
-        Part<VEC> gw;
-        {
-            const rsrc_t kr_ = make_rsrc(static_cast<const char*>(pr.k) + base);
-            const rsrc_t vr_ = make_rsrc(static_cast<const char*>(pr.v) + base);
-            // the receptance is needed only after the carry: its loads are
-            // issued after the aggregate, to overlap the wait for the carry
+        Part<VEC> after;   // the state after this sub-chunk (exported after the last)
+        const rsrc_t kr_ = make_rsrc(static_cast<const char*>(pr.k) + base);
+        const rsrc_t vr_ = make_rsrc(static_cast<const char*>(pr.v) + base);
+        const rsrc_t yr_ = make_rsrc(static_cast<char*>(pr.y) + base);
+        // the receptance is needed only after the carry: its loads are issued
+        // after the aggregate, to overlap the wait for the carry
+        if (narrow && n == L) {
+            // frame weights: the keys are done with after the aggregate pass
+            Raw kr[L], vr[L], rr[GATED ? L : 1];
+            FrameW<VEC, L> fw;
+            Part<VEC> gw;
+            chunk_load<DT, VEC, L, true, kStreamLoad>(kr, vr, kr_, vr_, voff, row_bytes, n);
+            chunk_weights<DT, VEC, L>(s, kr, vr, fw, gw);
+            if constexpr (GATED)
+                chunk_load_one<DT, VEC, L, true, kStreamLoad>(
+                    rr, make_rsrc(static_cast<const char*>(pr.r) + base), voff, row_bytes, n);
+            // the weights and the aggregate are finished before the wait for the
+            // carry: left to itself the compiler sinks them below it, onto the
+            // chain of hand-offs that every wave of the workgroup waits on
+            pin_weights(fw, gw);
+            chain_handoff<VEC>(s, gw, n, sc, nsub, s_carry, &s_seq, lane, after);
+            run_block_weights<DT, VEC, L, GATED>(s, fw, vr, gated_rr<GATED>(rr, kr), kr_, yr_, voff,
+                                                 row_bytes, active);
+        } else {
+            Raw kr[L], vr[L], rr[GATED ? L : 1];
+            Part<VEC> gw;
             if (n == L) {
                 chunk_load<DT, VEC, L, true, kStreamLoad>(kr, vr, kr_, vr_, voff, row_bytes, n);
                 chunk_aggregate<DT, VEC, L, true, !GATED>(s, kr, vr, n, gw);
@@ -740,51 +1063,25 @@ __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProble
                     chunk_load_one<DT, VEC, L, false, kStreamLoad>(
                         rr, make_rsrc(static_cast<const char*>(pr.r) + base), voff, row_bytes, n);
             }
-        }
-        // the carry of this sub-chunk, then the next one's.  The hand-off is
-        // the workgroup's critical path (every wave waits on it in turn), so
-        // the wave runs it at raised issue priority over the others' passes.
-        __builtin_amdgcn_s_setprio(3);
-        while (__hip_atomic_load(&s_seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != int(sc))
-            __builtin_amdgcn_s_sleep(1);
-        Part<VEC> x;
-#pragma unroll
-        for (int q = 0; q < VEC; q++) {
-            x.a[q] = s_carry[0][lane * VEC + q];
-            x.b[q] = s_carry[1][lane * VEC + q];
-            x.A[q] = s_carry[2][lane * VEC + q];
-            x.m[q] = s_carry[3][lane * VEC + q];
-        }
-        if (sc + 1 < nsub) {
-            Part<VEC> nx = x;
-            nx.absorb(gw, float(n), s);
-#pragma unroll
-            for (int q = 0; q < VEC; q++) {
-                s_carry[0][lane * VEC + q] = nx.a[q];
-                s_carry[1][lane * VEC + q] = nx.b[q];
-                s_carry[2][lane * VEC + q] = nx.A[q];
-                s_carry[3][lane * VEC + q] = nx.m[q];
+            chain_handoff<VEC>(s, gw, n, sc, nsub, s_carry, &s_seq, lane, after);
+            const Raw (&rg)[L] = gated_rr<GATED>(rr, kr);
+            if (n == L) {
+                if (fused)
+                    run_block<DT, VEC, L, true, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
+                else
+                    run_block<DT, VEC, L, false, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
+            } else {
+                if (fused)
+                    run_block<DT, VEC, L, true, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
+                else
+                    run_block<DT, VEC, L, false, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
             }
-            if (lane == 0)
-                __hip_atomic_store(&s_seq, int(sc + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
-        __builtin_amdgcn_s_setprio(0);
+        if (sc == nsub - 1 && active && pr.a_out != nullptr) {
 #pragma unroll
-        for (int q = 0; q < VEC; q++) { s.a[q] = x.a[q]; s.b[q] = x.b[q]; s.A[q] = x.A[q]; s.m[q] = x.m[q]; }
-        const rsrc_t yr_ = make_rsrc(static_cast<char*>(pr.y) + base);
-        const Raw (&rg)[L] = gated_rr<GATED>(rr, kr);
-        if (n == L) {
-            if (fused)
-                run_block<DT, VEC, L, true, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
-            else
-                run_block<DT, VEC, L, false, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
-        } else {
-            if (fused)
-                run_block<DT, VEC, L, true, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
-            else
-                run_block<DT, VEC, L, false, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
+            for (int q = 0; q < VEC; q++) { s.a[q] = after.a[q]; s.b[q] = after.b[q]; s.A[q] = after.A[q]; s.m[q] = after.m[q]; }
+            store_state(s, pr, bb * pr.C + c);
         }
-        if (sc == nsub - 1 && active && pr.a_out != nullptr) store_state(s, pr, bb * pr.C + c);
     }
 }
 

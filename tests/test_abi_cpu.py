@@ -33,7 +33,7 @@ def test_header_lists_the_boundary_calls():
     for n in ("wkv_forward", "wkv_step", "wkv_token_shift", "wkv_forward_workspace_size",
               "wkv_forward_gated", "wkv_step_gated", "wkv_backward", "wkv_backward_workspace_size",
               "wkv_status_string", "wkv_last_error", "wkv_mat_forward", "wkv_mat_forward_path",
-              "wkv_mat_step", "wkv_bounded_wait_failures"):
+              "wkv_mat_step", "wkv_bounded_wait_failures", "wkv_forward_auto_path"):
         assert n in names
 
 
@@ -115,6 +115,17 @@ def test_workspace_sizes():
     n = L.wkv_forward_workspace_size_path(1, 65536, 4096, 0, 2)
     assert 256 < n < 128 << 20
     assert L.wkv_forward_workspace_size_path(0, 10, 10, 0, 2) == 0
+
+
+def test_auto_path_query():
+    # without a visible device the library assumes 256 compute units (MI355X)
+    assert wkv.auto_path(16, 4096, 2048, wkv.BF16) == "chained"   # 256 column groups
+    assert wkv.auto_path(1, 65536, 4096, wkv.F32) == "chunked"    # 64 column groups
+    assert wkv.auto_path(256, 512, 4096, wkv.F32) == "serial"     # 16384 column groups
+    assert wkv.auto_path(1, 16, 64, wkv.F32) == "serial"          # a single block
+    L = wkv.lib()
+    assert L.wkv_forward_auto_path(0, 8, 8, 0) == -2
+    assert L.wkv_forward_auto_path(1, 8, 8, 5) == -3
 
 
 def _fwd_gated(path=0, B=1, T=8, C=64, dtype=0, w=1 * G, u=2 * G, k=3 * G, v=4 * G, r=6 * G, o=5 * G,
