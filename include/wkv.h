@@ -139,6 +139,28 @@ int wkv_forward_path(int64_t B, int64_t T, int64_t C, int dtype, int path,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * wkv_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * takes no workspace; where the chosen path needs one (the chunked path), it
+ * uses a fixed device array of WKV_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every device it runs on until the process ends.  Sizes whose
+ * workspace (wkv_forward_workspace_size) exceeds that return WKV_ERR_WORKSPACE.
+ * The call allocates nothing and frees nothing; each call clears what it uses
+ * of the array with a kernel of its own.  All calls on one device share the
+ * array, so calls that may overlap on one device (different streams without
+ * ordering between them) race: order them on one stream.  Arguments, outputs
+ * and other errors are those of wkv_forward.
+ */
+#define WKV_NOALLOC_SCRATCH_BYTES (40u << 20)
+
+int wkv_forward_noalloc(int64_t B, int64_t T, int64_t C, int dtype,
+                        const float *w, const float *u,
+                        const void *k, const void *v, void *y,
+                        const float *a_in, const float *b_in, const float *p_in,
+                        float *a_out, float *b_out, float *p_out,
+                        void *stream);
+
+/*
  * Training / prefill form with the receptance gate fused on the way out
  * ([tm-math] "Receptance: the gate on the way out"): for every position
  *

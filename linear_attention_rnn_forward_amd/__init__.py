@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
         L.wkv_last_error.argtypes = []
         L.wkv_abi_version.restype = i32
         L.wkv_abi_version.argtypes = []
+        L.wkv_forward_noalloc.restype = i32
+        L.wkv_forward_noalloc.argtypes = [i64, i64, i64, i32] + [vp] * 11 + [vp]
         L.wkv_forward_auto_path.restype = i32
         L.wkv_forward_auto_path.argtypes = [i64, i64, i64, i32]
         L.wkv_bounded_wait_failures.restype = i32
@@ -253,6 +255,36 @@ def forward(k, v, w, u, state=None, return_state=False, path="auto", out=None, s
     if return_state or state_out is not None:
         return y, (a_out, b_out, p_out)
     return y
+
+
+def forward_noalloc(k, v, w, u, out, state=None, state_out=None):
+    """wkv_forward without a workspace and without allocating anything: the
+    chunked path uses the library's fixed device array (wkv_forward_noalloc).
+    The caller passes every output: out [B,T,C] (dtype of k) and, if the
+    final state is wanted, state_out = (a, b, p) [B,C] float32.  Returns out."""
+    torch = _torch()
+    _need(k, "k")
+    if k.dim() != 3:
+        raise ValueError("k must be [B,T,C]")
+    B, T, C = k.shape
+    dev = k.device
+    dt = _dtype_code(k)
+    _need(v, "v", k.shape, k.dtype, dev)
+    _need(w, "w", (C,), torch.float32, dev)
+    _need(u, "u", (C,), torch.float32, dev)
+    _need(out, "out", k.shape, k.dtype, dev)
+    a_in = b_in = p_in = a_out = b_out = p_out = None
+    if state is not None:
+        a_in, b_in, p_in = (_need(x, n, (B, C), torch.float32, dev)
+                            for x, n in zip(state, ("a_in", "b_in", "p_in")))
+    if state_out is not None:
+        a_out, b_out, p_out = (_need(x, n, (B, C), torch.float32, dev)
+                               for x, n in zip(state_out, ("a_out", "b_out", "p_out")))
+    with torch.cuda.device(dev):
+        check(lib().wkv_forward_noalloc(B, T, C, dt, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(out),
+                                        _ptr(a_in), _ptr(b_in), _ptr(p_in), _ptr(a_out),
+                                        _ptr(b_out), _ptr(p_out), _stream(dev)))
+    return out
 
 
 def backward_workspace_size(B: int, T: int, C: int) -> int:

@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "wkv_internal.h"
@@ -278,6 +279,65 @@ int wkv_forward_auto_path(int64_t B, int64_t T, int64_t C, int dtype) {
 
 size_t wkv_forward_workspace_size(int64_t B, int64_t T, int64_t C, int dtype) {
     return wkv_forward_workspace_size_path(B, T, C, dtype, WKV_PATH_AUTO);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Scratch memory of wkv_forward_noalloc: a fixed device array, one copy per
+// device, that stands in for the chunked path's workspace.  Host code never
+// uses the array's name as an address (it is a host-side stand-in): the
+// device address of this device's copy comes from hipGetSymbolAddress, once
+// per device, and only that pointer is handed to the kernels.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) unsigned char scratch[WKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::atomic<void*> g_scratch_ptr[64];
+std::mutex g_scratch_mutex;
+
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(WKV_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the scratch array");
+            if (p == nullptr) return fail(WKV_ERR_HIP, "hipGetSymbolAddress gave no scratch address");
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return WKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wkv_forward_noalloc(int64_t B, int64_t T, int64_t C, int dtype, const float* w, const float* u,
+                        const void* k, const void* v, void* y, const float* a_in, const float* b_in,
+                        const float* p_in, float* a_out, float* b_out, float* p_out, void* stream) {
+    // the sizes are validated in full by forward_impl; here only the scratch need
+    const size_t need = wkv_forward_workspace_size(B, T, C, dtype);
+    if (need > size_t(WKV_NOALLOC_SCRATCH_BYTES))
+        return fail(WKV_ERR_WORKSPACE,
+                    "these sizes need %zu bytes of scratch; wkv_forward_noalloc has %zu "
+                    "(use wkv_forward with a workspace)",
+                    need, size_t(WKV_NOALLOC_SCRATCH_BYTES));
+    void* ws = nullptr;
+    if (need > 0)
+        if (int rc = scratch_address(&ws)) return rc;
+    return forward_impl(B, T, C, dtype, WKV_PATH_AUTO, w, u, k, v, nullptr, y, a_in, b_in, p_in,
+                        a_out, b_out, p_out, ws, need > 0 ? size_t(WKV_NOALLOC_SCRATCH_BYTES) : 0,
+                        stream, false);
 }
 
 int wkv_forward(int64_t B, int64_t T, int64_t C, int dtype, const float* w, const float* u,

@@ -307,3 +307,17 @@ def test_mat_step_rejects_bad_arguments():
     assert _mat_step(y=2 * G) == -5                # y is k
     assert _mat_step(s_out=3 * G) == -5            # state out overlaps v
     assert b"s_out overlaps v" in L.wkv_last_error()
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch():
+    L = wkv.lib()
+    P_ = ctypes.c_void_p
+    def call(B, T, C, dtype=0):
+        return L.wkv_forward_noalloc(B, T, C, dtype, P_(1 * G), P_(2 * G), P_(3 * G), P_(4 * G),
+                                     P_(5 * G), None, None, None, None, None, None, None)
+    # long context at 16x the channels: its chunked workspace is far beyond 40 MiB
+    assert L.wkv_forward_workspace_size(1, 1 << 20, 8192, 0) > 40 << 20
+    assert call(1, 1 << 20, 8192) == -4
+    assert b"scratch" in L.wkv_last_error()
+    # invalid sizes are reported as such
+    assert call(0, 8, 8) == -2
