@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from oracle.compare import guarded_rel_err, prefix_hull_violation, rms, state_mismatch
+from oracle.compare import guarded_rel_err, prefix_hull_violation, rel_err_where_large, rms, state_mismatch
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +38,7 @@ def host(t):
     return t.float().cpu().numpy()
 
 
-def check_forward(x, dtype, dev, path, state=None, check_state=True, tol=None):
+def check_forward(x, dtype, dev, path, state=None, check_state=True, tol=None, plain_bar=True):
     import linear_attention_rnn_forward_amd as wkv
     torch = _torch()
     k, v, w, u = gpu_inputs(x, dev)
@@ -51,6 +51,14 @@ def check_forward(x, dtype, dev, path, state=None, check_state=True, tol=None):
     assert np.all(np.isfinite(yh))
     err = guarded_rel_err(yh, y_ref, g)
     assert err <= (tol or TOL[dtype]), f"path={path} guarded rel err {err:.3e}"
+    if tol is None and plain_bar:
+        # the guard only takes over near zero crossings: outputs down to a
+        # tenth of the values' scale are held to the plain relative bar
+        # (cases with their own tolerance derive it for the guarded measure;
+        # extreme decays opt out, see test_decay_extremes)
+        err_large = rel_err_where_large(yh, y_ref, 0.1 * g)
+        print(f"path={path} plain relative error where |y| >= 0.1 rms(v): {err_large:.2e}")
+        assert err_large <= TOL[dtype], f"path={path} relative err {err_large:.3e}"
     if check_state:
         # the state is fp32 whatever the storage: the fp32 bar (or the case's
         # own, where exponents are so large that their fp32 spacing sets it),
@@ -231,7 +239,10 @@ def test_decay_extremes(device, path):
     x.w[:16] = 1e-6
     x.w[16:32] = 50.0
     x.w[32:48] = np.float32(np.exp(-9.0))
-    check_forward(x, "f32", device, path)
+    # w = 50 moves a key by up to 8 w = 400 inside a frame, where fp32 numbers
+    # are 3e-5 apart: the guarded bar holds, plain relative error near
+    # |y| = 0.1 reaches about 1e-4
+    check_forward(x, "f32", device, path, plain_bar=False)
 
 
 @pytest.mark.parametrize("path", ["serial", "chained"])
