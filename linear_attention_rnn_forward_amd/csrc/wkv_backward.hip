@@ -31,7 +31,11 @@
 //            sums the sub-chunk's (P, Q) contribution into a partial; the
 //            (P, Q) carry from the later sub-chunk arrives through LDS,
 //            carry (+) partial goes on to the earlier one, and the tokens are
-//            walked backwards from the carry to write gk, gv.
+//            walked backwards from the carry to write gk, gv.  Full
+//            sub-chunks of channels with c = e^{u-w} in [2^-20, 2^20] run in
+//            frames of 8 tokens with one exponential per token (below);
+//            sub-chunks whose values leave the frames' range, and ragged
+//            ones, run token by token.
 //
 // Stabilisation: every scale is an exponent in anchor form, anchor - count w,
 // and every weight an exponential of a non-positive difference formed
@@ -216,6 +220,471 @@ __device__ __forceinline__ void reverse_detail(RState& r, const TokenOut& o, flo
     }
 }
 
+// ---------------------------------------------------------------------------
+// Frame weights in the backward walk (full sub-chunks of channels with the
+// fused read-out and c = e^{u-w} in [2^-20, 2^20]).
+//
+// Inside a frame of kBwdFrame tokens the decay rides on the keys: in frame
+// coordinates token i's key is x_i = k_i + (i + 1) w, the history (exponent
+// H) decays no further, and against one anchor G = max(H, M) per frame (M the
+// frame's largest key) every weight is e_i = e^{x_i - G} <= 1 and the
+// history's factor e^{H - G} <= 1 ([tm-math] "Why it collapses into a
+// recurrence").  Token by token, with den_i = b + e_i c:
+//   D_t = e^{G - i w} den_i,   y = (a + e_i c v) / den_i,
+//   gy / D_t = e^{-(G - i w)} gr,  gr = gy / den_i,
+//   gy e^{u+k} / D_t = gr e_i c,   (A'_t - y B'_t) / D_t = (a' - y b') / den_i,
+//   a' += a, b' += b, a += e_i v, b += e_i
+// and for the walk backwards, with S, SQ the sums of gr, gr y over the later
+// tokens of the frame plus the later frames' carried in:
+//   e^{k_t} P_t = e_t S,   e^{k_t} Q_t = e_t SQ.
+// A frame's (S, SQ) goes on to the frame before it with the factor
+// e^{G_prev - F w - G} <= 1 (the next frame's anchor is at least the previous
+// one's, decayed over the frame), and to the sub-chunk before through the
+// carry's anchor form as (S, SQ) at exponent -G of the first frame.  No
+// exponential per token but the weight itself.
+//
+// Fixed weights need the values in range for every lane that holds a channel
+// (lanes past the last channel compute on stand-in data and are not asked;
+// their results are never stored): the first prefix of
+// each frame (the history, whose b is at least 1 against its own exponent,
+// or the first token) at least 2^-100 of the anchor (so every den is a
+// normal number), every token's weight normal, and every gy / den at most
+// 2^100 (so the walk's sums cannot overflow).  A sub-chunk that fails any runs token by token
+// (forward_detail, reverse_detail); so does a walk whose carried-in sums
+// overflow.
+// ---------------------------------------------------------------------------
+
+constexpr int kBwdFrame = 8;
+constexpr int kBwdFrames = kBwdTokens / kBwdFrame;
+constexpr float kBwdTermMin = 7.88860905e-31f;   // 2^-100
+constexpr float kBwdWeightMin = 1.17549435e-38f; // 2^-126, fp32's smallest normal
+constexpr float kBwdGrMax = 1.26765060e30f;      // 2^100
+
+// Per token and channel of a frame-weight sub-chunk the walk needs the
+// weight against the frame's anchor (kept in registers) and the output y
+// and gy / den.  Those two sit in registers (FrameYG) or, for two channels a
+// lane, in a per-wave LDS stash (16 tokens x 64 lanes x 16 bytes): the walk
+// runs after the hand-off, and holding them across it would take the whole
+// register file.
+template <int VEC>
+struct FrameYG {
+    float y[kBwdTokens][VEC], gr[kBwdTokens][VEC];
+};
+template <int VEC, bool STASH>
+struct FrameStore;
+template <int VEC>
+struct FrameStore<VEC, false> {
+    FrameYG<VEC> r;
+    __device__ __forceinline__ void put(int i, const float (&y)[VEC], const float (&gr)[VEC]) {
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            r.y[i][q] = y[q];
+            r.gr[i][q] = gr[q];
+        }
+    }
+    __device__ __forceinline__ void get(int i, float (&y)[VEC], float (&gr)[VEC]) const {
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            y[q] = r.y[i][q];
+            gr[q] = r.gr[i][q];
+        }
+    }
+};
+template <>
+struct FrameStore<2, true> {
+    float4* p;  // this wave's stash, [token][lane]
+    int lane;
+    __device__ __forceinline__ void put(int i, const float (&y)[2], const float (&gr)[2]) {
+        p[i * 64 + lane] = make_float4(y[0], gr[0], y[1], gr[1]);
+    }
+    __device__ __forceinline__ void get(int i, float (&y)[2], float (&gr)[2]) const {
+        const float4 t = p[i * 64 + lane];
+        y[0] = t.x;
+        gr[0] = t.y;
+        y[1] = t.z;
+        gr[1] = t.w;
+    }
+};
+
+// The forward re-run of a full sub-chunk in frames from the checkpoint s0: the
+// sub-chunk's gw, gu terms (returned in gw, gu, for the caller to add once the
+// walk has succeeded too) and its own (P, Q) partial.  Returns false for the
+// whole wave when some lane's values leave the range.
+template <typename IO, int L, int VEC, typename Raw, typename Store>
+__device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw (&kr)[L],
+                                             const Raw (&vr)[L], const Raw (&gyr)[L],
+                                             const float (&w)[VEC], const float (&c)[VEC],
+                                             float (&te)[L][VEC], Store& st, float (&G)[kBwdFrames][VEC],
+                                             float (&rho)[kBwdFrames][VEC], RState (&rg)[VEC],
+                                             float (&gw)[VEC], float (&gu)[VEC], bool active) {
+    constexpr int F = kBwdFrame, NF = kBwdFrames;
+    static_assert(L == F * NF, "whole frames");
+    float M[NF][VEC];
+    // frame keys and frame maxima; then e^{x - M}
+#pragma unroll
+    for (int f = 0; f < NF; f++) {
+#pragma unroll
+        for (int j = 0; j < F; j++) {
+            const int i = f * F + j;
+            float kf[VEC];
+            IO::unpack(kr[i], kf);
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                const float x = __builtin_fmaf(float(j + 1), w[q], kf[q]);
+                te[i][q] = x;
+                M[f][q] = j == 0 ? x : max_num(M[f][q], x);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < F; j++) {
+            const int i = f * F + j;
+#pragma unroll
+            for (int q = 0; q < VEC; q++)
+                te[i][q] = __builtin_amdgcn_exp2f((te[i][q] - M[f][q]) * kLog2e);
+        }
+    }
+    float a[VEC], b[VEC], ap[VEC], bp[VEC], H[VEC], gwt[VEC], gut[VEC], sg[NF][VEC], sq[NF][VEC];
+    float grmax = 0.0f, emin = 1.0f;
+    bool ok = true;
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        a[q] = s0[q].a;
+        b[q] = s0[q].b;
+        ap[q] = s0[q].ap;
+        bp[q] = s0[q].bp;
+        H[q] = __builtin_fmaf(-s0[q].m, w[q], s0[q].A);
+        gwt[q] = 0.0f;
+        gut[q] = 0.0f;
+    }
+#pragma unroll
+    for (int f = 0; f < NF; f++) {
+        float beta[VEC];
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            const float d = H[q] - M[f][q];
+            const float e = exp_neg_abs(d);
+            const bool keep = d >= 0.0f;
+            const float alpha = keep ? 1.0f : e;
+            beta[q] = keep ? e : 1.0f;
+            G[f][q] = keep ? H[q] : M[f][q];
+            ok &= max_num(alpha * b[q], beta[q] * te[f * F][q]) >= kBwdTermMin;
+            a[q] *= alpha;
+            b[q] *= alpha;
+            ap[q] *= alpha;
+            bp[q] *= alpha;
+            sg[f][q] = 0.0f;
+            sq[f][q] = 0.0f;
+        }
+        if (__builtin_amdgcn_ballot_w64(!ok & active) != 0) return false;
+#pragma unroll
+        for (int j = 0; j < F; j++) {
+            const int i = f * F + j;
+            float vf[VEC], gf[VEC];
+            IO::unpack(vr[i], vf);
+            IO::unpack(gyr[i], gf);
+            float yt[VEC], grt[VEC];
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                const float et = te[i][q] * beta[q];
+                const float ec = et * c[q];
+                const float rd = fast_rcp(b[q] + ec);
+                const float y = __builtin_fmaf(ec, vf[q], a[q]) * rd;
+                const float gr = gf[q] * rd;
+                gut[q] = __builtin_fmaf(gr * ec, vf[q] - y, gut[q]);
+                gwt[q] = __builtin_fmaf(-gr, __builtin_fmaf(-y, bp[q], ap[q]), gwt[q]);
+                ap[q] += a[q];
+                bp[q] += b[q];
+                a[q] = __builtin_fmaf(et, vf[q], a[q]);
+                b[q] += et;
+                sg[f][q] += gr;
+                sq[f][q] = __builtin_fmaf(gr, y, sq[f][q]);
+                grmax = max_num(grmax, __builtin_fabsf(gr));
+                emin = min_num(emin, et);
+                te[i][q] = et;
+                yt[q] = y;
+                grt[q] = gr;
+            }
+            st.put(i, yt, grt);
+            // token after token: left free, the scheduler runs the cheap
+            // prefix chains ahead over the frame and holds every token's
+            // values at once
+#pragma unroll
+            for (int q = 0; q < VEC; q++)
+                asm volatile("" : "+v"(a[q]), "+v"(b[q]), "+v"(ap[q]), "+v"(bp[q]), "+v"(gwt[q]),
+                             "+v"(gut[q]), "+v"(sg[f][q]), "+v"(sq[f][q]));
+        }
+#pragma unroll
+        for (int q = 0; q < VEC; q++) H[q] = __builtin_fmaf(-float(F), w[q], G[f][q]);  // next frame's
+    }
+    // gy / den beyond 2^100 (or not finite), or a weight below fp32's
+    // smallest normal, for some lane: token by token.  A token's gk, gv are
+    // its weight times the walk's sums, and a flushed or subnormal weight
+    // would lose their relative precision however large the sums are
+    if (__builtin_amdgcn_ballot_w64((!(grmax <= kBwdGrMax) | !(emin >= kBwdWeightMin)) & active) != 0)
+        return false;
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        // rho[f]: frame f+1's sums carried into frame f, e^{G_f - F w - G_{f+1}} <= 1
+#pragma unroll
+        for (int f = 0; f + 1 < NF; f++)
+            rho[f][q] = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(-float(F), w[q], G[f][q] - G[f + 1][q]) * kLog2e);
+        float P = sg[NF - 1][q], Q = sq[NF - 1][q];
+#pragma unroll
+        for (int f = NF - 2; f >= 0; f--) {
+            P = __builtin_fmaf(rho[f][q], P, sg[f][q]);
+            Q = __builtin_fmaf(rho[f][q], Q, sq[f][q]);
+        }
+        rg[q].P = P;
+        rg[q].Q = Q;
+        rg[q].Pi = -G[0][q];
+        rg[q].n = 0.0f;
+        gw[q] = gwt[q];
+        gu[q] = gut[q];
+    }
+    return true;
+}
+
+// The walk of a frame-weight sub-chunk from the carry r after it (exponent
+// r.Pi - r.n w at the sub-chunk's last token): gk, gv of every token.  Returns
+// false, writing nothing, when the carried-in sums overflow fp32 for some
+// lane of the wave.
+template <typename IO, int L, int VEC, typename Raw, typename Store>
+__device__ __forceinline__ bool frames_walk(const RState (&r)[VEC], const float (&te)[L][VEC],
+                                            const Store& st,
+                                            const float (&G)[kBwdFrames][VEC],
+                                            const float (&rho)[kBwdFrames][VEC], const Raw (&vr)[L],
+                                            const float (&w)[VEC], const float (&c)[VEC],
+                                            rsrc_t gkr_, rsrc_t gvr_, const uint32_t (&toff)[L],
+                                            bool active) {
+    constexpr int F = kBwdFrame, NF = kBwdFrames;
+    float S[VEC], SQ[VEC];
+    bool ok = true;
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        // e^{G_last - F w + exponent of the carry}, applied in two halves:
+        // the factor alone may overflow where its product with the carry
+        // (a tiny P after a small gy) does not
+        const float x = __builtin_fmaf(-(r[q].n + float(F)), w[q], G[NF - 1][q] + r[q].Pi);
+        const float h = __builtin_amdgcn_exp2f(x * (0.5f * kLog2e));
+        S[q] = (h * r[q].P) * h;
+        SQ[q] = (h * r[q].Q) * h;
+        ok &= __builtin_isfinite(S[q]) & __builtin_isfinite(SQ[q]);
+    }
+    if (__builtin_amdgcn_ballot_w64(!ok & active) != 0) return false;
+#pragma unroll
+    for (int f = NF - 1; f >= 0; f--) {
+        if (f < NF - 1) {
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                S[q] *= rho[f][q];
+                SQ[q] *= rho[f][q];
+            }
+        }
+#pragma unroll
+        for (int j = F - 1; j >= 0; j--) {
+            const int i = f * F + j;
+            float vf[VEC], gkf[VEC], gvf[VEC], yt[VEC], grt[VEC];
+            IO::unpack(vr[i], vf);
+            st.get(i, yt, grt);
+#pragma unroll
+            for (int q = 0; q < VEC; q++) {
+                const float e = te[i][q];
+                const float ed = grt[q] * (e * c[q]);
+                gvf[q] = __builtin_fmaf(e, S[q], ed);
+                gkf[q] = __builtin_fmaf(ed, vf[q] - yt[q], e * __builtin_fmaf(vf[q], S[q], -SQ[q]));
+                S[q] += grt[q];
+                SQ[q] = __builtin_fmaf(grt[q], yt[q], SQ[q]);
+            }
+            if (active) {
+                Buf<Raw>::store(IO::pack(gkf), gkr_, toff[i], 0);
+                Buf<Raw>::store(IO::pack(gvf), gvr_, toff[i], 0);
+            }
+        }
+    }
+    return true;
+}
+
+// Per-lane constants of the backward walk, passed by value.
+template <int VEC>
+struct Lanes {
+    float w[VEC], u[VEC], c[VEC];  // decay, bonus, e^{u-w}
+    uint32_t voff, row_bytes;      // byte offset of this lane's channels, of one token
+    int lane;
+    bool active;
+};
+
+// The (P, Q) hand-off through LDS: wait for the carry after sub-chunk sc
+// (wave order j), read it into r and pass carry (+) partial on to the
+// sub-chunk before.  s_rc holds four rows (P, Q, Pi, n) of 64 VEC floats.
+template <int VEC>
+__device__ __forceinline__ void rev_handoff(float* s_rc, int* s_rseq, const Lanes<VEC>& ln,
+                                            const RState (&rg)[VEC], RState (&r)[VEC], int64_t j,
+                                            int64_t sc, int n) {
+    constexpr int CG = 64 * VEC;
+    while (__hip_atomic_load(s_rseq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != int(j))
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        const int x = ln.lane * VEC + q;
+        r[q].P = s_rc[0 * CG + x];
+        r[q].Q = s_rc[1 * CG + x];
+        r[q].Pi = s_rc[2 * CG + x];
+        r[q].n = s_rc[3 * CG + x];
+    }
+    if (sc > 0) {
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            const int x = ln.lane * VEC + q;
+            RState nr = r[q];
+            combine_reverse(nr, rg[q], float(n), ln.w[q]);
+            s_rc[0 * CG + x] = nr.P;
+            s_rc[1 * CG + x] = nr.Q;
+            s_rc[2 * CG + x] = nr.Pi;
+            s_rc[3 * CG + x] = nr.n;
+        }
+        if (ln.lane == 0)
+            __hip_atomic_store(s_rseq, int(j + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+}
+
+// The checkpoint (state before the sub-chunk) of this lane's channels.
+template <int VEC>
+__device__ __forceinline__ void load_checkpoint(FState (&s)[VEC], const float* ck, int64_t C) {
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        s[q].a = ck[0 * C + q];
+        s[q].b = ck[1 * C + q];
+        s[q].ap = ck[2 * C + q];
+        s[q].bp = ck[3 * C + q];
+        s[q].A = ck[4 * C + q];
+        s[q].m = ck[5 * C + q];
+    }
+}
+
+// A carry taken by the hand-off, kept in LDS (four rows of 64 per channel).
+template <int VEC>
+__device__ __forceinline__ void keep_carry(float* slot, int lane, const RState (&r)[VEC]) {
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        slot[(q * 4 + 0) * 64 + lane] = r[q].P;
+        slot[(q * 4 + 1) * 64 + lane] = r[q].Q;
+        slot[(q * 4 + 2) * 64 + lane] = r[q].Pi;
+        slot[(q * 4 + 3) * 64 + lane] = r[q].n;
+    }
+}
+
+template <int VEC>
+struct GradWU {
+    float gw[VEC], gu[VEC];
+};
+
+// One sub-chunk token by token: the forward re-run from the checkpoint, the
+// (P, Q) partial and the hand-off (unless the carry was already taken and
+// kept in `slot`), the walk backwards.  Returns the sub-chunk's gw, gu terms.
+template <typename IO, int L, int VEC, bool FUSED>
+__device__ __forceinline__ GradWU<VEC> token_subchunk(const char* kb, const char* vb, const char* gyb,
+                                                      char* gkb, char* gvb, const float* ck, int64_t C,
+                                                      Lanes<VEC> ln, int n, int64_t j, int64_t sc,
+                                                      float* s_rc, int* s_rseq, const float* slot,
+                                                      bool have_carry) {
+    using Raw = typename IO::Raw;
+    const rsrc_t kr_ = make_rsrc(kb);
+    const rsrc_t vr_ = make_rsrc(vb);
+    const rsrc_t gr_ = make_rsrc(gyb);
+    Raw kr[L], vr[L], gyr[L];
+#pragma unroll
+    for (int i = 0; i < L; i++) {
+        if (i < n) {
+            const uint32_t o = ln.voff + uint32_t(i) * ln.row_bytes;
+            kr[i] = Buf<Raw>::template load<kStreamLoad>(kr_, o, 0);
+            vr[i] = Buf<Raw>::template load<kStreamLoad>(vr_, o, 0);
+            gyr[i] = Buf<Raw>::template load<kStreamLoad>(gr_, o, 0);
+        }
+    }
+    FState s[VEC];
+    load_checkpoint(s, ck, C);
+    GradWU<VEC> g;
+#pragma unroll
+    for (int q = 0; q < VEC; q++) g.gw[q] = g.gu[q] = 0.0f;
+    TokenOut to[L][VEC];
+    forward_run<IO, L, VEC, FUSED>(s, kr, vr, gyr, ln.w, ln.u, ln.c, n, to, g.gw, g.gu);
+    RState r[VEC];
+    if (have_carry) {
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            r[q].P = slot[(q * 4 + 0) * 64 + ln.lane];
+            r[q].Q = slot[(q * 4 + 1) * 64 + ln.lane];
+            r[q].Pi = slot[(q * 4 + 2) * 64 + ln.lane];
+            r[q].n = slot[(q * 4 + 3) * 64 + ln.lane];
+        }
+    } else {
+        // the sub-chunk's (P, Q) partial, max then sum: token i's term has
+        // exponent -q_i - i w at the sub-chunk's start
+        RState rg[VEC];
+        float mx[VEC];
+#pragma unroll
+        for (int q = 0; q < VEC; q++) mx[q] = kEmptyP;
+#pragma unroll
+        for (int i = 0; i < L; i++)
+            if (i < n)
+#pragma unroll
+                for (int q = 0; q < VEC; q++)
+                    mx[q] = max_num(mx[q], __builtin_fmaf(-float(i), ln.w[q], -to[i][q].q));
+        float mxl[VEC];
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            rg[q].set_empty();
+            rg[q].Pi = mx[q];
+            mxl[q] = mx[q] * kLog2e;
+        }
+#pragma unroll
+        for (int i = 0; i < L; i++) {
+            if (i < n) {
+#pragma unroll
+                for (int q = 0; q < VEC; q++) {
+                    const float xi = __builtin_fmaf(-float(i), ln.w[q], -to[i][q].q);
+                    const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(xi, kLog2e, -mxl[q])) * to[i][q].gr;
+                    rg[q].P += t;
+                    rg[q].Q = __builtin_fmaf(t, to[i][q].y, rg[q].Q);
+                }
+            }
+        }
+        rev_handoff(s_rc, s_rseq, ln, rg, r, j, sc, n);
+    }
+    // the walk backwards from the carry r after the sub-chunk
+    const rsrc_t gkr_ = make_rsrc(gkb);
+    const rsrc_t gvr_ = make_rsrc(gvb);
+#pragma unroll
+    for (int i = L - 1; i >= 0; i--) {
+        if (i < n) {
+            float kf[VEC], vf[VEC], gkf[VEC], gvf[VEC];
+            IO::unpack(kr[i], kf);
+            IO::unpack(vr[i], vf);
+#pragma unroll
+            for (int q = 0; q < VEC; q++)
+                reverse_detail(r[q], to[i][q], kf[q], vf[q], ln.w[q], i > 0, gkf[q], gvf[q]);
+            if (ln.active) {
+                const uint32_t o = ln.voff + uint32_t(i) * ln.row_bytes;
+                Buf<Raw>::store(IO::pack(gkf), gkr_, o, 0);
+                Buf<Raw>::store(IO::pack(gvf), gvr_, o, 0);
+            }
+        }
+    }
+    return g;
+}
+
+// The same as a call of its own, for the frame loop's fallback: inlined
+// there, its registers and the frame path's would be allocated as one.
+template <typename IO, int L, int VEC, bool FUSED>
+__device__ __attribute__((noinline)) GradWU<VEC> token_subchunk_call(
+    const char* kb, const char* vb, const char* gyb, char* gkb, char* gvb, const float* ck, int64_t C,
+    Lanes<VEC> ln, int n, int64_t j, int64_t sc, float* s_rc, int* s_rseq, const float* slot,
+    bool have_carry) {
+    return token_subchunk<IO, L, VEC, FUSED>(kb, vb, gyb, gkb, gvb, ck, C, ln, n, j, sc, s_rc, s_rseq,
+                                             slot, have_carry);
+}
+
 template <int DT, int VEC, int NWV>
 __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProblem pr, int64_t gpr,
                                                                     int64_t nsub) {
@@ -227,6 +696,12 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     __shared__ float s_rc[4][CG];            // reverse carry after sub-chunk nsub-1-s_rseq
     __shared__ float s_red[2][NWV][CG];      // per-wave gw, gu
     __shared__ int s_fseq, s_rseq;
+    // y, gy / den of the frame path's sub-chunk, per wave (two channels a lane)
+    constexpr bool STASH = VEC == 2;
+    __shared__ float4 s_stash[STASH ? NWV : 1][STASH ? L * 64 : 1];
+    // a carry the frame path has taken but could not use, per wave (in the
+    // stash, free by then, when there is one)
+    __shared__ float s_keep[STASH ? 1 : NWV][STASH ? 1 : 4 * VEC * 64];
 
     const int wave = bwd_wave_id();
     const int lane = bwd_lane_id();
@@ -248,6 +723,10 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
         cb[q] = __builtin_amdgcn_exp2f(-wmu * kLog2e);  // e^{u-w}
     }
     const bool fused = __builtin_amdgcn_ballot_w64(!fus) == 0;
+    bool nar = true;
+#pragma unroll
+    for (int q = 0; q < VEC; q++) nar = nar && __builtin_fabsf(w[q] - u[q]) <= kNarrowMaxAbsUW;
+    const bool narrow = __builtin_amdgcn_ballot_w64(!nar) == 0;
     if (wave == 0) {
 #pragma unroll
         for (int q = 0; q < VEC; q++) {
@@ -281,7 +760,9 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     for (int i = 0; i < L; i++) toff[i] = voff + uint32_t(i) * row_bytes;
     const int64_t gbase = (bb * T * C + c0) * es;
     // checkpoints: [B][nsub][field][C] fp32
-    float* ckpt = pr.ckpt + bb * nsub * kCkptFields * C + c;
+    // (lanes past the last channel read the group's first channel: stand-in
+    // data inside the workspace, never stored)
+    float* ckpt = pr.ckpt + bb * nsub * kCkptFields * C + (active ? c : c0);
 
     // ---------------- phase F: forward carries and checkpoints ----------------
     for (int64_t sc = wave; sc < nsub; sc += NWV) {
@@ -391,120 +872,115 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     float gw[VEC], gu[VEC];
 #pragma unroll
     for (int q = 0; q < VEC; q++) gw[q] = gu[q] = 0.0f;
+    Lanes<VEC> ln;
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        ln.w[q] = w[q];
+        ln.u[q] = u[q];
+        ln.c[q] = cb[q];
+    }
+    ln.voff = voff;
+    ln.row_bytes = row_bytes;
+    ln.lane = lane;
+    ln.active = active;
+    float* rc = &s_rc[0][0];
+    // a carry the frame path has taken but could not use: in the stash (free
+    // by then) when there is one
+    float* slot;
+    if constexpr (STASH)
+        slot = reinterpret_cast<float*>(s_stash[wave]);
+    else
+        slot = s_keep[wave];
+    // sub-chunk sc in wave order j: its bases
+    auto at = [&](const void* p, int64_t sc) __attribute__((always_inline)) {
+        return static_cast<const char*>(p) + gbase + sc * L * int64_t(row_bytes);
+    };
+    auto at_out = [&](void* p, int64_t sc) __attribute__((always_inline)) {
+        return static_cast<char*>(p) + gbase + sc * L * int64_t(row_bytes);
+    };
+    auto add = [&](const GradWU<VEC>& g) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < VEC; q++) {
+            gw[q] += g.gw[q];
+            gu[q] += g.gu[q];
+        }
+    };
     // the read-out form is uniform over the workgroup (its waves share the
     // channels): one copy of the loop per form keeps their registers apart
-    auto reverse_phase = [&](auto fused_tag) {
+    if (fused && narrow) {
+        // frame weights for full sub-chunks; the others, and sub-chunks whose
+        // values leave the frames' range, token by token through a call
         for (int64_t j = wave; j < nsub; j += NWV) {
             const int64_t sc = nsub - 1 - j;
             const int64_t t0 = sc * L;
             const int n = T - t0 >= L ? L : int(T - t0);
-            const int64_t base = gbase + t0 * int64_t(row_bytes);
-            const rsrc_t kr_ = make_rsrc(static_cast<const char*>(pr.k) + base);
-            const rsrc_t vr_ = make_rsrc(static_cast<const char*>(pr.v) + base);
-            const rsrc_t gr_ = make_rsrc(static_cast<const char*>(pr.gy) + base);
-            Raw kr[L], vr[L], gyr[L];
-    #pragma unroll
-            for (int i = 0; i < L; i++) {
-                if (i < n) {
+            const float* ck = ckpt + sc * kCkptFields * C;
+            bool have_carry = false;  // the hand-off has run
+            if (n == L) {
+                const rsrc_t kr_ = make_rsrc(at(pr.k, sc));
+                const rsrc_t vr_ = make_rsrc(at(pr.v, sc));
+                const rsrc_t gr_ = make_rsrc(at(pr.gy, sc));
+                Raw kr[L], vr[L], gyr[L];
+#pragma unroll
+                for (int i = 0; i < L; i++) {
                     kr[i] = Buf<Raw>::template load<kStreamLoad>(kr_, toff[i], 0);
                     vr[i] = Buf<Raw>::template load<kStreamLoad>(vr_, toff[i], 0);
                     gyr[i] = Buf<Raw>::template load<kStreamLoad>(gr_, toff[i], 0);
                 }
-            }
-            FState s[VEC];
-            {
-                const float* ck = ckpt + sc * kCkptFields * C;
-    #pragma unroll
-                for (int q = 0; q < VEC; q++) {
-                    s[q].a = ck[0 * C + q];
-                    s[q].b = ck[1 * C + q];
-                    s[q].ap = ck[2 * C + q];
-                    s[q].bp = ck[3 * C + q];
-                    s[q].A = ck[4 * C + q];
-                    s[q].m = ck[5 * C + q];
+                FState s[VEC];
+                load_checkpoint(s, ck, C);
+                float te[L][VEC];
+                FrameStore<VEC, STASH> st;
+                if constexpr (STASH) {
+                    st.p = s_stash[wave];
+                    st.lane = lane;
                 }
-            }
-            TokenOut to[L][VEC];
-            forward_run<IO, L, VEC, decltype(fused_tag)::value>(s, kr, vr, gyr, w, u, cb, n, to, gw, gu);
-            // the sub-chunk's (P, Q) partial, max then sum: token i's term has
-            // exponent -q_i - i w at the sub-chunk's start
-            RState rg[VEC];
-            {
-                float mx[VEC];
-    #pragma unroll
-                for (int q = 0; q < VEC; q++) mx[q] = kEmptyP;
-    #pragma unroll
-                for (int i = 0; i < L; i++)
-                    if (i < n)
-    #pragma unroll
-                        for (int q = 0; q < VEC; q++)
-                            mx[q] = max_num(mx[q], __builtin_fmaf(-float(i), w[q], -to[i][q].q));
-                float mxl[VEC];
-    #pragma unroll
-                for (int q = 0; q < VEC; q++) {
-                    rg[q].set_empty();
-                    rg[q].Pi = mx[q];
-                    mxl[q] = mx[q] * kLog2e;
-                }
-    #pragma unroll
-                for (int i = 0; i < L; i++) {
-                    if (i < n) {
-    #pragma unroll
+                float G[kBwdFrames][VEC], rho[kBwdFrames][VEC], gwt[VEC], gut[VEC];
+                RState rg[VEC];
+                if (frames_rerun<IO, L, VEC>(s, kr, vr, gyr, w, cb, te, st, G, rho, rg, gwt, gut, active)) {
+                    RState r[VEC];
+                    rev_handoff(rc, &s_rseq, ln, rg, r, j, sc, n);
+                    const rsrc_t gkr_ = make_rsrc(at_out(pr.gk, sc));
+                    const rsrc_t gvr_ = make_rsrc(at_out(pr.gv, sc));
+                    if (frames_walk<IO, L, VEC>(r, te, st, G, rho, vr, w, cb, gkr_, gvr_, toff, active)) {
+#pragma unroll
                         for (int q = 0; q < VEC; q++) {
-                            const float xi = __builtin_fmaf(-float(i), w[q], -to[i][q].q);
-                            const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(xi, kLog2e, -mxl[q])) * to[i][q].gr;
-                            rg[q].P += t;
-                            rg[q].Q = __builtin_fmaf(t, to[i][q].y, rg[q].Q);
+                            gw[q] += gwt[q];
+                            gu[q] += gut[q];
                         }
+                        continue;
                     }
+                    // the carried-in sums overflow: the walk token by token
+                    // from the kept carry
+                    keep_carry(slot, lane, r);
+                    have_carry = true;
                 }
             }
-            while (__hip_atomic_load(&s_rseq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != int(j))
-                __builtin_amdgcn_s_sleep(1);
-            RState r[VEC];
-    #pragma unroll
-            for (int q = 0; q < VEC; q++) {
-                r[q].P = s_rc[0][lane * VEC + q];
-                r[q].Q = s_rc[1][lane * VEC + q];
-                r[q].Pi = s_rc[2][lane * VEC + q];
-                r[q].n = s_rc[3][lane * VEC + q];
-            }
-            if (sc > 0) {
-    #pragma unroll
-                for (int q = 0; q < VEC; q++) {
-                    RState nr = r[q];
-                    combine_reverse(nr, rg[q], float(n), w[q]);
-                    s_rc[0][lane * VEC + q] = nr.P;
-                    s_rc[1][lane * VEC + q] = nr.Q;
-                    s_rc[2][lane * VEC + q] = nr.Pi;
-                    s_rc[3][lane * VEC + q] = nr.n;
-                }
-                if (lane == 0)
-                    __hip_atomic_store(&s_rseq, int(j + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
-            const rsrc_t gkr_ = make_rsrc(static_cast<char*>(pr.gk) + base);
-            const rsrc_t gvr_ = make_rsrc(static_cast<char*>(pr.gv) + base);
-    #pragma unroll
-            for (int i = L - 1; i >= 0; i--) {
-                if (i < n) {
-                    float kf[VEC], vf[VEC], gkf[VEC], gvf[VEC];
-                    IO::unpack(kr[i], kf);
-                    IO::unpack(vr[i], vf);
-    #pragma unroll
-                    for (int q = 0; q < VEC; q++)
-                        reverse_detail(r[q], to[i][q], kf[q], vf[q], w[q], i > 0, gkf[q], gvf[q]);
-                    if (active) {
-                        Buf<Raw>::store(IO::pack(gkf), gkr_, toff[i], 0);
-                        Buf<Raw>::store(IO::pack(gvf), gvr_, toff[i], 0);
-                    }
-                }
-            }
+            add(token_subchunk_call<IO, L, VEC, true>(at(pr.k, sc), at(pr.v, sc), at(pr.gy, sc),
+                                                      at_out(pr.gk, sc), at_out(pr.gv, sc), ck, C, ln, n,
+                                                      j, sc, rc, &s_rseq, slot, have_carry));
         }
-    };
-    if (fused)
-        reverse_phase(std::integral_constant<bool, true>{});
-    else
-        reverse_phase(std::integral_constant<bool, false>{});
+    } else if (fused) {
+        for (int64_t j = wave; j < nsub; j += NWV) {
+            const int64_t sc = nsub - 1 - j;
+            const int64_t t0 = sc * L;
+            const int n = T - t0 >= L ? L : int(T - t0);
+            add(token_subchunk<IO, L, VEC, true>(at(pr.k, sc), at(pr.v, sc), at(pr.gy, sc),
+                                                 at_out(pr.gk, sc), at_out(pr.gv, sc),
+                                                 ckpt + sc * kCkptFields * C, C, ln, n, j, sc, rc,
+                                                 &s_rseq, slot, false));
+        }
+    } else {
+        for (int64_t j = wave; j < nsub; j += NWV) {
+            const int64_t sc = nsub - 1 - j;
+            const int64_t t0 = sc * L;
+            const int n = T - t0 >= L ? L : int(T - t0);
+            add(token_subchunk<IO, L, VEC, false>(at(pr.k, sc), at(pr.v, sc), at(pr.gy, sc),
+                                                  at_out(pr.gk, sc), at_out(pr.gv, sc),
+                                                  ckpt + sc * kCkptFields * C, C, ln, n, j, sc, rc,
+                                                  &s_rseq, slot, false));
+        }
+    }
 
     // ---------------- gw, gu of this (b, column group) ----------------
 #pragma unroll
