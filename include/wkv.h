@@ -299,8 +299,8 @@ int wkv_session_load(int64_t L, int64_t S, int64_t C, int dtype, int64_t seq,
  *   gw, gu      [C] fp32            outputs; zero when T = 0
  *   workspace   device memory of wkv_backward_workspace_size(B, T, C) bytes,
  *               256-byte aligned (NULL allowed when T = 0); it holds the
- *               forward state before every 16-token sub-chunk (6 fp32 per
- *               channel, 1.5 bytes per token-channel) and per-column partial
+ *               forward state before every 16-token sub-chunk (4 fp32 per
+ *               channel, 1 byte per token-channel) and per-column partial
  *               sums, and is overwritten
  * No output may overlap any input, another output or the workspace.
  * Arithmetic is fp32 with every exponential of a non-positive argument;
@@ -312,6 +312,43 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, int dtype,
                  const void *k, const void *v, const void *gy,
                  void *gk, void *gv, float *gw, float *gu,
                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The training pair that reads k and v once less.  wkv_backward first re-runs
+ * the forward recurrence over every token to recover the state before each
+ * 16-token sub-chunk; a forward that is run anyway can save those states as
+ * it goes, and the backward then starts from them.  Same operator, same
+ * results to rounding as wkv_forward + wkv_backward.
+ *
+ * wkv_forward_save: wkv_forward from the empty history (no state in or out)
+ * that also writes
+ *   states      [B][ceil(T/16)][4][C] fp32 device array,
+ *               wkv_saved_states_bytes(B, T, C) bytes, 4-byte aligned: for
+ *               sub-chunk s (tokens 16 s .. 16 s + 15) of row b the
+ *               recurrence's state before its first token, in the anchor
+ *               form (a, b, A, m): the history sums scaled by e^{-p},
+ *               p = A - m w.  No chunk of it may overlap an input or y.
+ * It always runs the chained path (one workgroup per group of 64 or 128
+ * channels of a row); k, v, y, w, u and the errors are as for wkv_forward.
+ *
+ * wkv_backward_saved: wkv_backward with `states` from wkv_forward_save for
+ * the same (k, v, w, u, B, T, C, dtype), read and not written.  Its
+ * workspace (wkv_backward_saved_workspace_size(B, C) bytes, 256-byte
+ * aligned, NULL allowed when T = 0) holds only the per-column partial sums.
+ * States from other inputs give gradients of nothing in particular; the
+ * call cannot tell.
+ */
+#define WKV_SAVED_STATE_TOKENS 16
+size_t wkv_saved_states_bytes(int64_t B, int64_t T, int64_t C);
+int wkv_forward_save(int64_t B, int64_t T, int64_t C, int dtype,
+                     const float *w, const float *u, const void *k, const void *v,
+                     void *y, float *states, void *stream);
+size_t wkv_backward_saved_workspace_size(int64_t B, int64_t C);
+int wkv_backward_saved(int64_t B, int64_t T, int64_t C, int dtype,
+                       const float *w, const float *u,
+                       const void *k, const void *v, const void *gy, const float *states,
+                       void *gk, void *gv, float *gw, float *gu,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Matrix-valued state WKV of RWKV-5 "Eagle" and RWKV-6 "Finch" ([vanos] the
@@ -410,7 +447,7 @@ int wkv_abi_version(void);
  */
 int wkv_bounded_wait_failures(uint64_t *count);
 
-#define WKV_ABI_VERSION 105
+#define WKV_ABI_VERSION 106
 
 #ifdef __cplusplus
 }

@@ -87,6 +87,14 @@ def lib() -> ctypes.CDLL:
         L.wkv_backward_workspace_size.argtypes = [i64, i64, i64]
         L.wkv_backward.restype = i32
         L.wkv_backward.argtypes = [i64, i64, i64, i32] + [vp] * 9 + [vp, sz, vp]
+        L.wkv_saved_states_bytes.restype = sz
+        L.wkv_saved_states_bytes.argtypes = [i64, i64, i64]
+        L.wkv_forward_save.restype = i32
+        L.wkv_forward_save.argtypes = [i64, i64, i64, i32] + [vp] * 6 + [vp]
+        L.wkv_backward_saved_workspace_size.restype = sz
+        L.wkv_backward_saved_workspace_size.argtypes = [i64, i64]
+        L.wkv_backward_saved.restype = i32
+        L.wkv_backward_saved.argtypes = [i64, i64, i64, i32] + [vp] * 10 + [vp, sz, vp]
         L.wkv_token_shift.restype = i32
         L.wkv_token_shift.argtypes = [i64, i64, i64, i32] + [vp] * 9 + [vp]
         L.wkv_status_string.restype = ctypes.c_char_p
@@ -292,13 +300,49 @@ def backward_workspace_size(B: int, T: int, C: int) -> int:
     return int(lib().wkv_backward_workspace_size(B, T, C))
 
 
-def backward(k, v, w, u, gy, out=None, workspace=None):
+SAVED_STATE_TOKENS = 16
+
+
+def saved_states_shape(B: int, T: int, C: int):
+    """Shape of forward_save's states: [B, ceil(T/16), 4, C] float32."""
+    return (B, (T + SAVED_STATE_TOKENS - 1) // SAVED_STATE_TOKENS, 4, C)
+
+
+def forward_save(k, v, w, u, out=None, states=None):
+    """forward(k, v, w, u) from the empty history that also saves the state
+    before every 16-token sub-chunk (wkv_forward_save), for backward(...,
+    states=...).  Returns (y, states); states is [B, ceil(T/16), 4, C]
+    float32."""
+    torch = _torch()
+    _need(k, "k")
+    if k.dim() != 3:
+        raise ValueError("k must be [B,T,C]")
+    B, T, C = k.shape
+    dev = k.device
+    dt = _dtype_code(k)
+    _need(v, "v", k.shape, k.dtype, dev)
+    _need(w, "w", (C,), torch.float32, dev)
+    _need(u, "u", (C,), torch.float32, dev)
+    y = out if out is not None else torch.empty_like(k)
+    _need(y, "out", k.shape, k.dtype, dev)
+    shape = saved_states_shape(B, T, C)
+    if states is None:
+        states = torch.empty(shape, dtype=torch.float32, device=dev)
+    _need(states, "states", shape, torch.float32, dev)
+    with torch.cuda.device(dev):
+        check(lib().wkv_forward_save(B, T, C, dt, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                     _ptr(states), _stream(dev)))
+    return y, states
+
+
+def backward(k, v, w, u, gy, out=None, workspace=None, states=None):
     """Gradients of sum(gy * forward(k, v, w, u)) from the empty history.
 
     k, v, gy: [B,T,C] float32 or bfloat16 (same dtype); w, u: [C] float32.
     Returns (gk, gv, gw, gu): gk, gv [B,T,C] in the dtype of k, gw, gu [C]
     float32 (summed over batch and tokens).  out: optional preallocated
-    (gk, gv, gw, gu).
+    (gk, gv, gw, gu).  states: the states forward_save saved for the same
+    inputs (wkv_backward_saved: k, v are then read once less), or None.
     """
     torch = _torch()
     _need(k, "k")
@@ -320,14 +364,28 @@ def backward(k, v, w, u, gy, out=None, workspace=None):
     _need(gv, "gv", k.shape, k.dtype, dev)
     _need(gw, "gw", (C,), torch.float32, dev)
     _need(gu, "gu", (C,), torch.float32, dev)
-    need = int(lib().wkv_backward_workspace_size(B, T, C))
+    if states is not None:
+        _need(states, "states", saved_states_shape(B, T, C), torch.float32, dev)
+        need = int(lib().wkv_backward_saved_workspace_size(B, C))
+    else:
+        need = int(lib().wkv_backward_workspace_size(B, T, C))
     ws = workspace if workspace is not None else _workspace(dev, need)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     with torch.cuda.device(dev):
-        check(lib().wkv_backward(B, T, C, dt, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy),
-                                 _ptr(gk), _ptr(gv), _ptr(gw), _ptr(gu), _ptr(ws), ws_bytes,
-                                 _stream(dev)))
+        if states is not None:
+            check(lib().wkv_backward_saved(B, T, C, dt, _ptr(w), _ptr(u), _ptr(k), _ptr(v),
+                                           _ptr(gy), _ptr(states), _ptr(gk), _ptr(gv), _ptr(gw),
+                                           _ptr(gu), _ptr(ws), ws_bytes, _stream(dev)))
+        else:
+            check(lib().wkv_backward(B, T, C, dt, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy),
+                                     _ptr(gk), _ptr(gv), _ptr(gw), _ptr(gu), _ptr(ws), ws_bytes,
+                                     _stream(dev)))
     return gk, gv, gw, gu
+
+
+def backward_saved_workspace_size(B: int, C: int) -> int:
+    """Bytes of workspace wkv_backward_saved needs."""
+    return int(lib().wkv_backward_saved_workspace_size(B, C))
 
 
 def step(state, k, v, w, u, out=None, state_out=None, inplace=False, r=None):

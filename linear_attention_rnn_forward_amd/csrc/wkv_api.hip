@@ -85,12 +85,18 @@ int check_state_aliasing(const Range* outs, int nouts, const Range* ins, int nin
     return WKV_OK;
 }
 
+// Bytes of the saved states of a [B, T, C] problem: fp32 [B][ceil(T/16)][4][C].
+int64_t saved_state_bytes(int64_t B, int64_t T, int64_t C) {
+    return B * ((T + WKV_SAVED_STATE_TOKENS - 1) / WKV_SAVED_STATE_TOKENS) * 4 * C * 4;
+}
+
 // r == nullptr: plain forward; else the gated form (y = sigmoid(r) * wkv).
+// states != nullptr (chained path, empty history): the carries are saved too.
 int forward_impl(int64_t B, int64_t T, int64_t C, int dtype, int path, const float* w,
                  const float* u, const void* k, const void* v, const void* r, void* y,
                  const float* a_in, const float* b_in, const float* p_in, float* a_out,
                  float* b_out, float* p_out, void* workspace, size_t workspace_bytes, void* stream,
-                 bool gated) {
+                 bool gated, float* states = nullptr) {
     if (dtype != WKV_F32 && dtype != WKV_BF16) return fail(WKV_ERR_DTYPE, "unknown dtype %d", dtype);
     if (path != WKV_PATH_AUTO && path != WKV_PATH_SERIAL && path != WKV_PATH_CHUNKED &&
         path != WKV_PATH_CHAINED)
@@ -128,6 +134,15 @@ int forward_impl(int64_t B, int64_t T, int64_t C, int dtype, int path, const flo
     if (int rc = check_state_aliasing(r_out, 3, r_in, 8, true)) return rc;
     for (const Range& ro : r_out)
         if (overlap(ro, r_y)) return fail(WKV_ERR_ALIAS, "%s overlaps y", ro.name);
+    if (states != nullptr) {
+        const Range r_st = rng("states", states, saved_state_bytes(B, T, C));
+        for (const Range& ri : r_in)
+            if (overlap(r_st, ri)) return fail(WKV_ERR_ALIAS, "states overlaps %s", ri.name);
+        for (const Range& ro : r_out)
+            if (overlap(r_st, ro)) return fail(WKV_ERR_ALIAS, "states overlaps %s", ro.name);
+        if (overlap(r_st, r_y)) return fail(WKV_ERR_ALIAS, "states overlaps y");
+        if (!aligned(states, 4)) return fail(WKV_ERR_ARG, "states must be 4-byte aligned");
+    }
 
     wkv::ForwardProblem pr;
     pr.B = B;
@@ -148,6 +163,7 @@ int forward_impl(int64_t B, int64_t T, int64_t C, int dtype, int path, const flo
     pr.b_out = b_out;
     pr.p_out = p_out;
     pr.r = gated ? r : nullptr;
+    pr.states = states;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     if (T == 0) {
@@ -446,12 +462,17 @@ size_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C) {
     if (B < 1 || C < 1 || T < 0) return 0;
     int64_t n = 0;
     if (!mul3(B, T, C, &n) || !mul3(n, 8, 1, &n)) return 0;
-    return wkv::backward_workspace_bytes(B, T, C);
+    return wkv::backward_workspace_bytes(B, T, C, false);
 }
 
-int wkv_backward(int64_t B, int64_t T, int64_t C, int dtype, const float* w, const float* u,
-                 const void* k, const void* v, const void* gy, void* gk, void* gv, float* gw,
-                 float* gu, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// states != nullptr: the saved checkpoints of wkv_forward_save.
+int backward_impl(int64_t B, int64_t T, int64_t C, int dtype, const float* w, const float* u,
+                  const void* k, const void* v, const void* gy, const float* states, void* gk,
+                  void* gv, float* gw, float* gu, void* workspace, size_t workspace_bytes,
+                  void* stream) {
     if (dtype != WKV_F32 && dtype != WKV_BF16) return fail(WKV_ERR_DTYPE, "unknown dtype %d", dtype);
     if (B < 1 || C < 1 || T < 0)
         return fail(WKV_ERR_SHAPE, "need B >= 1, T >= 0, C >= 1 (got B=%lld T=%lld C=%lld)",
@@ -468,9 +489,12 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, int dtype, const float* w, con
     if (double(C) * 4.0 * 17.0 > 4294967295.0)
         return fail(WKV_ERR_SHAPE, "C too large for 32-bit offsets within a sub-chunk");
     const int64_t io = n * int64_t(esize(dtype));
+    const bool saved = states != nullptr;
+    if (saved && T > 0 && !aligned(states, 4)) return fail(WKV_ERR_ARG, "states must be 4-byte aligned");
     const Range r_in[] = {rng("k", k, io), rng("v", v, io), rng("gy", gy, io), rng("w", w, C * 4),
-                          rng("u", u, C * 4)};
-    const size_t need = T > 0 ? wkv::backward_workspace_bytes(B, T, C) : 0;
+                          rng("u", u, C * 4),
+                          rng("states", T > 0 ? states : nullptr, saved_state_bytes(B, T, C))};
+    const size_t need = T > 0 ? wkv::backward_workspace_bytes(B, T, C, saved) : 0;
     const Range r_out[] = {rng("gk", gk, io), rng("gv", gv, io), rng("gw", gw, C * 4),
                            rng("gu", gu, C * 4), rng("workspace", T > 0 ? workspace : nullptr, int64_t(need))};
     for (int i = 0; i < 5; i++) {
@@ -500,10 +524,52 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, int dtype, const float* w, con
     pr.gv = gv;
     pr.gw = gw;
     pr.gu = gu;
+    pr.saved = saved ? states : nullptr;
     pr.vec = wkv::backward_vec(C, dtype, aligned(k, 4) && aligned(v, 4) && aligned(gy, 4) &&
                                              aligned(gk, 4) && aligned(gv, 4));
     hipError_t e = wkv::launch_backward(pr, workspace, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ok() : hip_fail(e, "backward launch");
+}
+}  // namespace
+
+extern "C" {
+
+int wkv_backward(int64_t B, int64_t T, int64_t C, int dtype, const float* w, const float* u,
+                 const void* k, const void* v, const void* gy, void* gk, void* gv, float* gw,
+                 float* gu, void* workspace, size_t workspace_bytes, void* stream) {
+    return backward_impl(B, T, C, dtype, w, u, k, v, gy, nullptr, gk, gv, gw, gu, workspace,
+                         workspace_bytes, stream);
+}
+
+size_t wkv_saved_states_bytes(int64_t B, int64_t T, int64_t C) {
+    if (B < 1 || C < 1 || T < 0) return 0;
+    int64_t n = 0;
+    if (!mul3(B, T, C, &n) || !mul3(n, 8, 1, &n)) return 0;
+    return size_t(saved_state_bytes(B, T, C));
+}
+
+int wkv_forward_save(int64_t B, int64_t T, int64_t C, int dtype, const float* w, const float* u,
+                     const void* k, const void* v, void* y, float* states, void* stream) {
+    if (T > 0 && states == nullptr) return fail(WKV_ERR_NULL, "states is required when T > 0");
+    return forward_impl(B, T, C, dtype, WKV_PATH_CHAINED, w, u, k, v, nullptr, y, nullptr, nullptr,
+                        nullptr, nullptr, nullptr, nullptr, nullptr, 0, stream, false,
+                        T > 0 ? states : nullptr);
+}
+
+size_t wkv_backward_saved_workspace_size(int64_t B, int64_t C) {
+    if (B < 1 || C < 1) return 0;
+    int64_t n = 0;
+    if (!mul3(B, C, 8, &n)) return 0;
+    return wkv::backward_workspace_bytes(B, 1, C, true);
+}
+
+int wkv_backward_saved(int64_t B, int64_t T, int64_t C, int dtype, const float* w, const float* u,
+                       const void* k, const void* v, const void* gy, const float* states, void* gk,
+                       void* gv, float* gw, float* gu, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    if (T > 0 && states == nullptr) return fail(WKV_ERR_NULL, "states is required when T > 0");
+    return backward_impl(B, T, C, dtype, w, u, k, v, gy, states, gk, gv, gw, gu, workspace,
+                         workspace_bytes, stream);
 }
 
 int wkv_token_shift(int64_t B, int64_t T, int64_t C, int dtype, const void* x, const void* x_prev,

@@ -60,60 +60,64 @@ namespace wkv {
 namespace {
 
 constexpr int kBwdTokens = 16;  // tokens per sub-chunk
-constexpr int kCkptFields = 6;  // a, b, a', b', anchor, count
+static_assert(kBwdTokens == WKV_SAVED_STATE_TOKENS, "saved states are the checkpoints");
+constexpr int kCkptFields = 4;  // a, b, anchor, count
 
 __device__ __forceinline__ int bwd_wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int bwd_lane_id() { return threadIdx.x & 63; }
 
 // Forward state in anchor form: exponent p = A - m w; a, b the history sums
-// and ap, bp the age-weighted ones, all scaled by e^{-p}.
+// scaled by e^{-p}.  The same form as the forward kernels' carry, so a
+// forward that saves its carries hands the backward its checkpoints.
 struct FState {
-    float a, b, ap, bp, A, m;
+    float a, b, A, m;
     __device__ __forceinline__ void set_empty() {
-        a = b = ap = bp = 0.0f;
+        a = b = 0.0f;
         A = kEmptyP;
         m = 0.0f;
     }
 };
 
 // X <- X (+) G, G the state of the n tokens after X from the empty history.
-// Over n tokens X's terms gain n in age: a' -> e^{-n w} (a' + n a).
 __device__ __forceinline__ void combine_forward(FState& x, const FState& g, float n, float w) {
     const float d = __builtin_fmaf(-(x.m + n - g.m), w, x.A - g.A);  // X's exponent - G's
     const float e = exp_neg_abs(d);
     const bool keep = d >= 0.0f;
     const float ax = keep ? 1.0f : e;
     const float ag = keep ? e : 1.0f;
-    const float apx = __builtin_fmaf(n, x.a, x.ap);
-    const float bpx = __builtin_fmaf(n, x.b, x.bp);
     x.a = __builtin_fmaf(ax, x.a, ag * g.a);
     x.b = __builtin_fmaf(ax, x.b, ag * g.b);
-    x.ap = __builtin_fmaf(ax, apx, ag * g.ap);
-    x.bp = __builtin_fmaf(ax, bpx, ag * g.bp);
     x.A = keep ? x.A : g.A;
     x.m = keep ? x.m + n : g.m;
 }
 
-// Reverse accumulator (P, Q) in anchor form: exponent Pi - n w.
+// Reverse accumulators in anchor form, exponent Pi - n w: P, Q the sums of
+// gy_t / D_t and gy_t y_t / D_t over the later tokens, each decayed by its
+// distance, and R, U the same weighted by that distance.
 struct RState {
-    float P, Q, Pi, n;
+    float P, Q, R, U, Pi, n;
     __device__ __forceinline__ void set_empty() {
-        P = Q = 0.0f;
+        P = Q = R = U = 0.0f;
         Pi = kEmptyP;
         n = 0.0f;
     }
 };
 
 // X <- X (+) G for the reverse scan: X holds the tokens after a span of n
-// tokens (its exponent gains -n w at the span's start), G the span's own.
+// tokens (its exponent gains -n w at the span's start, and its terms n in
+// distance: R -> e^{-n w} (R + n P)), G the span's own.
 __device__ __forceinline__ void combine_reverse(RState& x, const RState& g, float n, float w) {
     const float d = __builtin_fmaf(-(x.n + n - g.n), w, x.Pi - g.Pi);
     const float e = exp_neg_abs(d);
     const bool keep = d >= 0.0f;
     const float ax = keep ? 1.0f : e;
     const float ag = keep ? e : 1.0f;
+    const float Rx = __builtin_fmaf(n, x.P, x.R);
+    const float Ux = __builtin_fmaf(n, x.Q, x.U);
     x.P = __builtin_fmaf(ax, x.P, ag * g.P);
     x.Q = __builtin_fmaf(ax, x.Q, ag * g.Q);
+    x.R = __builtin_fmaf(ax, Rx, ag * g.R);
+    x.U = __builtin_fmaf(ax, Ux, ag * g.U);
     x.Pi = keep ? x.Pi : g.Pi;
     x.n = keep ? x.n + n : g.n;
 }
@@ -126,7 +130,7 @@ struct TokenOut {
     float ed;  // gy_t e^{u+k_t} / D_t
 };
 
-// The forward read-out of one token from state s, its gw, gu terms, then the
+// The forward read-out of one token from state s, its gu term, then the
 // fold-in.  FUSED (|u - w| <= 44, c = e^{u-w} in range): the read-out reuses
 // the fold's weights, as the forward kernels do -- relative to the folded
 // exponent p' = max(p - w, k), the history weighs al = e^{p-w-p'}, the new
@@ -135,7 +139,7 @@ struct TokenOut {
 // read-out takes its own exponential against q = max(p, u + k).
 template <bool FUSED>
 __device__ __forceinline__ TokenOut forward_detail(FState& s, float k, float v, float g, float w,
-                                                   float u, float c, float& gw, float& gu) {
+                                                   float u, float c, float& gu) {
     TokenOut o;
     const float ak = s.A - k;
     const float e = __builtin_fmaf(-(s.m + 1.0f), w, ak);  // (p - w) - k
@@ -165,11 +169,8 @@ __device__ __forceinline__ TokenOut forward_detail(FState& s, float k, float v, 
     o.gr = g * rd;
     o.ed = o.gr * bo;
     gu = __builtin_fmaf(o.ed, v - o.y, gu);
-    gw = __builtin_fmaf(-(o.gr * rh), __builtin_fmaf(-o.y, s.bp, s.ap), gw);
-    // fold-in: the history decays by e^{-w}, the age-weighted sums gain the
-    // history, the new key enters with weight e^{k}
-    s.ap = al * (s.ap + s.a);
-    s.bp = al * (s.bp + s.b);
+    // fold-in: the history decays by e^{-w}, the new key enters with weight
+    // e^{k}
     s.a = __builtin_fmaf(al, s.a, be * v);
     s.b = __builtin_fmaf(al, s.b, be);
     s.A = reset ? k : s.A;
@@ -182,8 +183,7 @@ template <typename IO, int L, int VEC, bool FUSED, typename Raw>
 __device__ __forceinline__ void forward_run(FState (&s)[VEC], const Raw (&kr)[L], const Raw (&vr)[L],
                                             const Raw (&gyr)[L], const float (&w)[VEC],
                                             const float (&u)[VEC], const float (&c)[VEC], int n,
-                                            TokenOut (&to)[L][VEC], float (&gw)[VEC],
-                                            float (&gu)[VEC]) {
+                                            TokenOut (&to)[L][VEC], float (&gu)[VEC]) {
 #pragma unroll
     for (int i = 0; i < L; i++) {
         if (i < n) {
@@ -193,19 +193,22 @@ __device__ __forceinline__ void forward_run(FState (&s)[VEC], const Raw (&kr)[L]
             IO::unpack(gyr[i], gf);
 #pragma unroll
             for (int q = 0; q < VEC; q++)
-                to[i][q] = forward_detail<FUSED>(s[q], kf[q], vf[q], gf[q], w[q], u[q], c[q], gw[q], gu[q]);
+                to[i][q] = forward_detail<FUSED>(s[q], kf[q], vf[q], gf[q], w[q], u[q], c[q], gu[q]);
         }
     }
 }
 
-// One token of the backward walk: gk, gv from the running (P, Q) of the
-// later tokens, then fold this token's term in (skipped for a sub-chunk's
-// first token, whose successor is the next sub-chunk's carry).
+// One token of the backward walk: gk, gv and the token's gw term,
+// -e^{k} (v R - U), from the running sums of the later tokens, then fold this
+// token's term in (skipped for a sub-chunk's first token, whose successor is
+// the next sub-chunk's carry).  Moving one token back, every later term gains
+// one in distance: R -> e^{-w} (R + P), with P before this token's term.
 __device__ __forceinline__ void reverse_detail(RState& r, const TokenOut& o, float k, float v, float w,
-                                               bool fold, float& gk, float& gv) {
+                                               bool fold, float& gk, float& gv, float& gw) {
     const float eh = __builtin_amdgcn_exp2f(__builtin_fmaf(-r.n, w, k + r.Pi) * kLog2e);
     gv = __builtin_fmaf(eh, r.P, o.ed);
     gk = __builtin_fmaf(eh, __builtin_fmaf(v, r.P, -r.Q), o.ed * (v - o.y));
+    gw = __builtin_fmaf(-eh, __builtin_fmaf(v, r.R, -r.U), gw);
     if (fold) {
         const float e = __builtin_fmaf(-(r.n + 1.0f), w, r.Pi + o.q);  // (pi - w) - (-q)
         const float x = exp_neg_abs(e);
@@ -213,6 +216,8 @@ __device__ __forceinline__ void reverse_detail(RState& r, const TokenOut& o, flo
         const float al = reset ? x : 1.0f;
         const float be = reset ? 1.0f : x;
         const float t = be * o.gr;
+        r.R = al * (r.R + r.P);
+        r.U = al * (r.U + r.Q);
         r.P = __builtin_fmaf(al, r.P, t);
         r.Q = __builtin_fmaf(al, r.Q, t * o.y);
         r.Pi = reset ? -o.q : r.Pi;
@@ -232,16 +237,16 @@ __device__ __forceinline__ void reverse_detail(RState& r, const TokenOut& o, flo
 // recurrence").  Token by token, with den_i = b + e_i c:
 //   D_t = e^{G - i w} den_i,   y = (a + e_i c v) / den_i,
 //   gy / D_t = e^{-(G - i w)} gr,  gr = gy / den_i,
-//   gy e^{u+k} / D_t = gr e_i c,   (A'_t - y B'_t) / D_t = (a' - y b') / den_i,
-//   a' += a, b' += b, a += e_i v, b += e_i
+//   gy e^{u+k} / D_t = gr e_i c,   a += e_i v, b += e_i
 // and for the walk backwards, with S, SQ the sums of gr, gr y over the later
-// tokens of the frame plus the later frames' carried in:
-//   e^{k_t} P_t = e_t S,   e^{k_t} Q_t = e_t SQ.
-// A frame's (S, SQ) goes on to the frame before it with the factor
+// tokens of the frame plus the later frames' carried in, and S2, SQ2 the same
+// weighted by the distance (no decay: it rides on the weights):
+//   e^{k_t} P_t = e_t S,  e^{k_t} Q_t = e_t SQ,  e^{k_t} R_t = e_t S2, ...
+// A frame's sums go on to the frame before it with the factor
 // e^{G_prev - F w - G} <= 1 (the next frame's anchor is at least the previous
 // one's, decayed over the frame), and to the sub-chunk before through the
-// carry's anchor form as (S, SQ) at exponent -G of the first frame.  No
-// exponential per token but the weight itself.
+// carry's anchor form at exponent -G of the first frame.  No exponential per
+// token but the weight itself.
 //
 // Fixed weights need the values in range for every lane that holds a channel
 // (lanes past the last channel compute on stand-in data and are not asked;
@@ -307,16 +312,16 @@ struct FrameStore<2, true> {
 };
 
 // The forward re-run of a full sub-chunk in frames from the checkpoint s0: the
-// sub-chunk's gw, gu terms (returned in gw, gu, for the caller to add once the
-// walk has succeeded too) and its own (P, Q) partial.  Returns false for the
-// whole wave when some lane's values leave the range.
+// sub-chunk's gu term (returned in gu, for the caller to add once the walk has
+// succeeded too) and its own partial of the reverse sums.  Returns false for
+// the whole wave when some lane's values leave the range.
 template <typename IO, int L, int VEC, typename Raw, typename Store>
 __device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw (&kr)[L],
                                              const Raw (&vr)[L], const Raw (&gyr)[L],
                                              const float (&w)[VEC], const float (&c)[VEC],
                                              float (&te)[L][VEC], Store& st, float (&G)[kBwdFrames][VEC],
                                              float (&rho)[kBwdFrames][VEC], RState (&rg)[VEC],
-                                             float (&gw)[VEC], float (&gu)[VEC], bool active) {
+                                             float (&gu)[VEC], bool active) {
     constexpr int F = kBwdFrame, NF = kBwdFrames;
     static_assert(L == F * NF, "whole frames");
     float M[NF][VEC];
@@ -343,18 +348,22 @@ __device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw 
                 te[i][q] = __builtin_amdgcn_exp2f((te[i][q] - M[f][q]) * kLog2e);
         }
     }
-    float a[VEC], b[VEC], ap[VEC], bp[VEC], H[VEC], gwt[VEC], gut[VEC], sg[NF][VEC], sq[NF][VEC];
+    // per frame: the sums of gr and gr y over its tokens, and the same
+    // weighted by the token's place in the sub-chunk; they enter the partial
+    // (P, Q, R, U, at the first frame's anchor) with pi, the product of the
+    // factors rho of the frames before
+    float a[VEC], b[VEC], H[VEC], gut[VEC], pi[VEC], sg[VEC], sq[VEC], sgi[VEC], sqi[VEC];
+    float P[VEC], Q[VEC], R[VEC], U[VEC];
     float grmax = 0.0f, emin = 1.0f;
     bool ok = true;
 #pragma unroll
     for (int q = 0; q < VEC; q++) {
         a[q] = s0[q].a;
         b[q] = s0[q].b;
-        ap[q] = s0[q].ap;
-        bp[q] = s0[q].bp;
         H[q] = __builtin_fmaf(-s0[q].m, w[q], s0[q].A);
-        gwt[q] = 0.0f;
         gut[q] = 0.0f;
+        pi[q] = 1.0f;
+        P[q] = Q[q] = R[q] = U[q] = 0.0f;
     }
 #pragma unroll
     for (int f = 0; f < NF; f++) {
@@ -370,10 +379,17 @@ __device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw 
             ok &= max_num(alpha * b[q], beta[q] * te[f * F][q]) >= kBwdTermMin;
             a[q] *= alpha;
             b[q] *= alpha;
-            ap[q] *= alpha;
-            bp[q] *= alpha;
-            sg[f][q] = 0.0f;
-            sq[f][q] = 0.0f;
+            sg[q] = 0.0f;
+            sq[q] = 0.0f;
+            sgi[q] = 0.0f;
+            sqi[q] = 0.0f;
+            if (f > 0) {
+                // rho[f-1]: this frame's sums carried into the one before,
+                // e^{G_{f-1} - F w - G_f} <= 1
+                rho[f - 1][q] = __builtin_amdgcn_exp2f(
+                    __builtin_fmaf(-float(F), w[q], G[f - 1][q] - G[f][q]) * kLog2e);
+                pi[q] *= rho[f - 1][q];
+            }
         }
         if (__builtin_amdgcn_ballot_w64(!ok & active) != 0) return false;
 #pragma unroll
@@ -390,14 +406,14 @@ __device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw 
                 const float rd = fast_rcp(b[q] + ec);
                 const float y = __builtin_fmaf(ec, vf[q], a[q]) * rd;
                 const float gr = gf[q] * rd;
+                const float gry = gr * y;
                 gut[q] = __builtin_fmaf(gr * ec, vf[q] - y, gut[q]);
-                gwt[q] = __builtin_fmaf(-gr, __builtin_fmaf(-y, bp[q], ap[q]), gwt[q]);
-                ap[q] += a[q];
-                bp[q] += b[q];
                 a[q] = __builtin_fmaf(et, vf[q], a[q]);
                 b[q] += et;
-                sg[f][q] += gr;
-                sq[f][q] = __builtin_fmaf(gr, y, sq[f][q]);
+                sg[q] += gr;
+                sq[q] += gry;
+                sgi[q] = __builtin_fmaf(float(i), gr, sgi[q]);
+                sqi[q] = __builtin_fmaf(float(i), gry, sqi[q]);
                 grmax = max_num(grmax, __builtin_fabsf(gr));
                 emin = min_num(emin, et);
                 te[i][q] = et;
@@ -410,11 +426,17 @@ __device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw 
             // values at once
 #pragma unroll
             for (int q = 0; q < VEC; q++)
-                asm volatile("" : "+v"(a[q]), "+v"(b[q]), "+v"(ap[q]), "+v"(bp[q]), "+v"(gwt[q]),
-                             "+v"(gut[q]), "+v"(sg[f][q]), "+v"(sq[f][q]));
+                asm volatile("" : "+v"(a[q]), "+v"(b[q]), "+v"(gut[q]), "+v"(sg[q]), "+v"(sq[q]),
+                             "+v"(sgi[q]), "+v"(sqi[q]));
         }
 #pragma unroll
-        for (int q = 0; q < VEC; q++) H[q] = __builtin_fmaf(-float(F), w[q], G[f][q]);  // next frame's
+        for (int q = 0; q < VEC; q++) {
+            P[q] = __builtin_fmaf(pi[q], sg[q], P[q]);
+            Q[q] = __builtin_fmaf(pi[q], sq[q], Q[q]);
+            R[q] = __builtin_fmaf(pi[q], sgi[q], R[q]);
+            U[q] = __builtin_fmaf(pi[q], sqi[q], U[q]);
+            H[q] = __builtin_fmaf(-float(F), w[q], G[f][q]);  // the next frame's history
+        }
     }
     // gy / den beyond 2^100 (or not finite), or a weight below fp32's
     // smallest normal, for some lane: token by token.  A token's gk, gv are
@@ -424,31 +446,22 @@ __device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw 
         return false;
 #pragma unroll
     for (int q = 0; q < VEC; q++) {
-        // rho[f]: frame f+1's sums carried into frame f, e^{G_f - F w - G_{f+1}} <= 1
-#pragma unroll
-        for (int f = 0; f + 1 < NF; f++)
-            rho[f][q] = __builtin_amdgcn_exp2f(
-                __builtin_fmaf(-float(F), w[q], G[f][q] - G[f + 1][q]) * kLog2e);
-        float P = sg[NF - 1][q], Q = sq[NF - 1][q];
-#pragma unroll
-        for (int f = NF - 2; f >= 0; f--) {
-            P = __builtin_fmaf(rho[f][q], P, sg[f][q]);
-            Q = __builtin_fmaf(rho[f][q], Q, sq[f][q]);
-        }
-        rg[q].P = P;
-        rg[q].Q = Q;
+        // the partial at the sub-chunk's start: exponent -G of the first frame
+        rg[q].P = P[q];
+        rg[q].Q = Q[q];
+        rg[q].R = R[q];
+        rg[q].U = U[q];
         rg[q].Pi = -G[0][q];
         rg[q].n = 0.0f;
-        gw[q] = gwt[q];
         gu[q] = gut[q];
     }
     return true;
 }
 
 // The walk of a frame-weight sub-chunk from the carry r after it (exponent
-// r.Pi - r.n w at the sub-chunk's last token): gk, gv of every token.  Returns
-// false, writing nothing, when the carried-in sums overflow fp32 for some
-// lane of the wave.
+// r.Pi - r.n w at the sub-chunk's last token): gk, gv of every token, and the
+// sub-chunk's gw term in gw (for the caller to add).  Returns false, writing
+// nothing, when the carried-in sums overflow fp32 for some lane of the wave.
 template <typename IO, int L, int VEC, typename Raw, typename Store>
 __device__ __forceinline__ bool frames_walk(const RState (&r)[VEC], const float (&te)[L][VEC],
                                             const Store& st,
@@ -456,9 +469,12 @@ __device__ __forceinline__ bool frames_walk(const RState (&r)[VEC], const float 
                                             const float (&rho)[kBwdFrames][VEC], const Raw (&vr)[L],
                                             const float (&w)[VEC], const float (&c)[VEC],
                                             rsrc_t gkr_, rsrc_t gvr_, const uint32_t (&toff)[L],
-                                            bool active) {
+                                            bool active, float (&gw)[VEC]) {
     constexpr int F = kBwdFrame, NF = kBwdFrames;
-    float S[VEC], SQ[VEC];
+    // S, SQ: the sums of gr, gr y over the later tokens; S2, SQ2 the same
+    // weighted by the distance past the current token (both in frame
+    // coordinates)
+    float S[VEC], SQ[VEC], S2[VEC], SQ2[VEC];
     bool ok = true;
 #pragma unroll
     for (int q = 0; q < VEC; q++) {
@@ -469,7 +485,11 @@ __device__ __forceinline__ bool frames_walk(const RState (&r)[VEC], const float 
         const float h = __builtin_amdgcn_exp2f(x * (0.5f * kLog2e));
         S[q] = (h * r[q].P) * h;
         SQ[q] = (h * r[q].Q) * h;
-        ok &= __builtin_isfinite(S[q]) & __builtin_isfinite(SQ[q]);
+        S2[q] = (h * r[q].R) * h;
+        SQ2[q] = (h * r[q].U) * h;
+        ok &= __builtin_isfinite(S[q]) & __builtin_isfinite(SQ[q]) & __builtin_isfinite(S2[q]) &
+              __builtin_isfinite(SQ2[q]);
+        gw[q] = 0.0f;
     }
     if (__builtin_amdgcn_ballot_w64(!ok & active) != 0) return false;
 #pragma unroll
@@ -479,6 +499,8 @@ __device__ __forceinline__ bool frames_walk(const RState (&r)[VEC], const float 
             for (int q = 0; q < VEC; q++) {
                 S[q] *= rho[f][q];
                 SQ[q] *= rho[f][q];
+                S2[q] *= rho[f][q];
+                SQ2[q] *= rho[f][q];
             }
         }
 #pragma unroll
@@ -493,6 +515,9 @@ __device__ __forceinline__ bool frames_walk(const RState (&r)[VEC], const float 
                 const float ed = grt[q] * (e * c[q]);
                 gvf[q] = __builtin_fmaf(e, S[q], ed);
                 gkf[q] = __builtin_fmaf(ed, vf[q] - yt[q], e * __builtin_fmaf(vf[q], S[q], -SQ[q]));
+                gw[q] = __builtin_fmaf(-e, __builtin_fmaf(vf[q], S2[q], -SQ2[q]), gw[q]);
+                S2[q] += S[q];
+                SQ2[q] += SQ[q];
                 S[q] += grt[q];
                 SQ[q] = __builtin_fmaf(grt[q], yt[q], SQ[q]);
             }
@@ -514,9 +539,10 @@ struct Lanes {
     bool active;
 };
 
-// The (P, Q) hand-off through LDS: wait for the carry after sub-chunk sc
-// (wave order j), read it into r and pass carry (+) partial on to the
-// sub-chunk before.  s_rc holds four rows (P, Q, Pi, n) of 64 VEC floats.
+// The reverse sums' hand-off through LDS: wait for the carry after
+// sub-chunk sc (wave order j), read it into r and pass carry (+) partial on
+// to the sub-chunk before.  s_rc holds six rows (P, Q, R, U, Pi, n) of 64 VEC
+// floats.
 template <int VEC>
 __device__ __forceinline__ void rev_handoff(float* s_rc, int* s_rseq, const Lanes<VEC>& ln,
                                             const RState (&rg)[VEC], RState (&r)[VEC], int64_t j,
@@ -529,8 +555,10 @@ __device__ __forceinline__ void rev_handoff(float* s_rc, int* s_rseq, const Lane
         const int x = ln.lane * VEC + q;
         r[q].P = s_rc[0 * CG + x];
         r[q].Q = s_rc[1 * CG + x];
-        r[q].Pi = s_rc[2 * CG + x];
-        r[q].n = s_rc[3 * CG + x];
+        r[q].R = s_rc[2 * CG + x];
+        r[q].U = s_rc[3 * CG + x];
+        r[q].Pi = s_rc[4 * CG + x];
+        r[q].n = s_rc[5 * CG + x];
     }
     if (sc > 0) {
 #pragma unroll
@@ -540,8 +568,10 @@ __device__ __forceinline__ void rev_handoff(float* s_rc, int* s_rseq, const Lane
             combine_reverse(nr, rg[q], float(n), ln.w[q]);
             s_rc[0 * CG + x] = nr.P;
             s_rc[1 * CG + x] = nr.Q;
-            s_rc[2 * CG + x] = nr.Pi;
-            s_rc[3 * CG + x] = nr.n;
+            s_rc[2 * CG + x] = nr.R;
+            s_rc[3 * CG + x] = nr.U;
+            s_rc[4 * CG + x] = nr.Pi;
+            s_rc[5 * CG + x] = nr.n;
         }
         if (ln.lane == 0)
             __hip_atomic_store(s_rseq, int(j + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -555,22 +585,37 @@ __device__ __forceinline__ void load_checkpoint(FState (&s)[VEC], const float* c
     for (int q = 0; q < VEC; q++) {
         s[q].a = ck[0 * C + q];
         s[q].b = ck[1 * C + q];
-        s[q].ap = ck[2 * C + q];
-        s[q].bp = ck[3 * C + q];
-        s[q].A = ck[4 * C + q];
-        s[q].m = ck[5 * C + q];
+        s[q].A = ck[2 * C + q];
+        s[q].m = ck[3 * C + q];
     }
 }
 
-// A carry taken by the hand-off, kept in LDS (four rows of 64 per channel).
+// A carry taken by the hand-off, kept in LDS (six rows of 64 per channel).
+constexpr int kKeepRows = 6;
 template <int VEC>
 __device__ __forceinline__ void keep_carry(float* slot, int lane, const RState (&r)[VEC]) {
 #pragma unroll
     for (int q = 0; q < VEC; q++) {
-        slot[(q * 4 + 0) * 64 + lane] = r[q].P;
-        slot[(q * 4 + 1) * 64 + lane] = r[q].Q;
-        slot[(q * 4 + 2) * 64 + lane] = r[q].Pi;
-        slot[(q * 4 + 3) * 64 + lane] = r[q].n;
+        float* o = slot + q * kKeepRows * 64 + lane;
+        o[0 * 64] = r[q].P;
+        o[1 * 64] = r[q].Q;
+        o[2 * 64] = r[q].R;
+        o[3 * 64] = r[q].U;
+        o[4 * 64] = r[q].Pi;
+        o[5 * 64] = r[q].n;
+    }
+}
+template <int VEC>
+__device__ __forceinline__ void take_carry(const float* slot, int lane, RState (&r)[VEC]) {
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        const float* o = slot + q * kKeepRows * 64 + lane;
+        r[q].P = o[0 * 64];
+        r[q].Q = o[1 * 64];
+        r[q].R = o[2 * 64];
+        r[q].U = o[3 * 64];
+        r[q].Pi = o[4 * 64];
+        r[q].n = o[5 * 64];
     }
 }
 
@@ -580,8 +625,9 @@ struct GradWU {
 };
 
 // One sub-chunk token by token: the forward re-run from the checkpoint, the
-// (P, Q) partial and the hand-off (unless the carry was already taken and
-// kept in `slot`), the walk backwards.  Returns the sub-chunk's gw, gu terms.
+// partial of the reverse sums and the hand-off (unless the carry was already
+// taken and kept in `slot`), the walk backwards.  Returns the sub-chunk's gw,
+// gu terms.
 template <typename IO, int L, int VEC, bool FUSED>
 __device__ __forceinline__ GradWU<VEC> token_subchunk(const char* kb, const char* vb, const char* gyb,
                                                       char* gkb, char* gvb, const float* ck, int64_t C,
@@ -608,19 +654,13 @@ __device__ __forceinline__ GradWU<VEC> token_subchunk(const char* kb, const char
 #pragma unroll
     for (int q = 0; q < VEC; q++) g.gw[q] = g.gu[q] = 0.0f;
     TokenOut to[L][VEC];
-    forward_run<IO, L, VEC, FUSED>(s, kr, vr, gyr, ln.w, ln.u, ln.c, n, to, g.gw, g.gu);
+    forward_run<IO, L, VEC, FUSED>(s, kr, vr, gyr, ln.w, ln.u, ln.c, n, to, g.gu);
     RState r[VEC];
     if (have_carry) {
-#pragma unroll
-        for (int q = 0; q < VEC; q++) {
-            r[q].P = slot[(q * 4 + 0) * 64 + ln.lane];
-            r[q].Q = slot[(q * 4 + 1) * 64 + ln.lane];
-            r[q].Pi = slot[(q * 4 + 2) * 64 + ln.lane];
-            r[q].n = slot[(q * 4 + 3) * 64 + ln.lane];
-        }
+        take_carry(slot, ln.lane, r);
     } else {
-        // the sub-chunk's (P, Q) partial, max then sum: token i's term has
-        // exponent -q_i - i w at the sub-chunk's start
+        // the sub-chunk's partial, max then sum: token i's term has exponent
+        // -q_i - i w at the sub-chunk's start and lies i past it
         RState rg[VEC];
         float mx[VEC];
 #pragma unroll
@@ -645,8 +685,11 @@ __device__ __forceinline__ GradWU<VEC> token_subchunk(const char* kb, const char
                 for (int q = 0; q < VEC; q++) {
                     const float xi = __builtin_fmaf(-float(i), ln.w[q], -to[i][q].q);
                     const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(xi, kLog2e, -mxl[q])) * to[i][q].gr;
+                    const float ty = t * to[i][q].y;
                     rg[q].P += t;
-                    rg[q].Q = __builtin_fmaf(t, to[i][q].y, rg[q].Q);
+                    rg[q].Q += ty;
+                    rg[q].R = __builtin_fmaf(float(i), t, rg[q].R);
+                    rg[q].U = __builtin_fmaf(float(i), ty, rg[q].U);
                 }
             }
         }
@@ -663,7 +706,7 @@ __device__ __forceinline__ GradWU<VEC> token_subchunk(const char* kb, const char
             IO::unpack(vr[i], vf);
 #pragma unroll
             for (int q = 0; q < VEC; q++)
-                reverse_detail(r[q], to[i][q], kf[q], vf[q], ln.w[q], i > 0, gkf[q], gvf[q]);
+                reverse_detail(r[q], to[i][q], kf[q], vf[q], ln.w[q], i > 0, gkf[q], gvf[q], g.gw[q]);
             if (ln.active) {
                 const uint32_t o = ln.voff + uint32_t(i) * ln.row_bytes;
                 Buf<Raw>::store(IO::pack(gkf), gkr_, o, 0);
@@ -685,7 +728,9 @@ __device__ __attribute__((noinline)) GradWU<VEC> token_subchunk_call(
                                              slot, have_carry);
 }
 
-template <int DT, int VEC, int NWV>
+// SAVED: the checkpoints come from the forward that produced y (pr.ckpt holds
+// them) and phase F is skipped.
+template <int DT, int VEC, int NWV, bool SAVED>
 __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProblem pr, int64_t gpr,
                                                                     int64_t nsub) {
     using IO = Io<DT, VEC>;
@@ -693,7 +738,7 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     constexpr int L = kBwdTokens;
     constexpr int CG = 64 * VEC;
     __shared__ float s_fc[kCkptFields][CG];  // forward carry before sub-chunk s_fseq
-    __shared__ float s_rc[4][CG];            // reverse carry after sub-chunk nsub-1-s_rseq
+    __shared__ float s_rc[6][CG];            // reverse carry after sub-chunk nsub-1-s_rseq
     __shared__ float s_red[2][NWV][CG];      // per-wave gw, gu
     __shared__ int s_fseq, s_rseq;
     // y, gy / den of the frame path's sub-chunk, per wave (two channels a lane)
@@ -701,7 +746,7 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     __shared__ float4 s_stash[STASH ? NWV : 1][STASH ? L * 64 : 1];
     // a carry the frame path has taken but could not use, per wave (in the
     // stash, free by then, when there is one)
-    __shared__ float s_keep[STASH ? 1 : NWV][STASH ? 1 : 4 * VEC * 64];
+    __shared__ float s_keep[STASH ? 1 : NWV][STASH ? 1 : kKeepRows * VEC * 64];
 
     const int wave = bwd_wave_id();
     const int lane = bwd_lane_id();
@@ -734,16 +779,16 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
             e.set_empty();
             s_fc[0][lane * VEC + q] = e.a;
             s_fc[1][lane * VEC + q] = e.b;
-            s_fc[2][lane * VEC + q] = e.ap;
-            s_fc[3][lane * VEC + q] = e.bp;
-            s_fc[4][lane * VEC + q] = e.A;
-            s_fc[5][lane * VEC + q] = e.m;
+            s_fc[2][lane * VEC + q] = e.A;
+            s_fc[3][lane * VEC + q] = e.m;
             RState r;
             r.set_empty();
             s_rc[0][lane * VEC + q] = r.P;
             s_rc[1][lane * VEC + q] = r.Q;
-            s_rc[2][lane * VEC + q] = r.Pi;
-            s_rc[3][lane * VEC + q] = r.n;
+            s_rc[2][lane * VEC + q] = r.R;
+            s_rc[3][lane * VEC + q] = r.U;
+            s_rc[4][lane * VEC + q] = r.Pi;
+            s_rc[5][lane * VEC + q] = r.n;
         }
         if (lane == 0) {
             s_fseq = 0;
@@ -765,7 +810,7 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     float* ckpt = pr.ckpt + bb * nsub * kCkptFields * C + (active ? c : c0);
 
     // ---------------- phase F: forward carries and checkpoints ----------------
-    for (int64_t sc = wave; sc < nsub; sc += NWV) {
+    for (int64_t sc = SAVED ? nsub : wave; sc < nsub; sc += NWV) {
         const int64_t t0 = sc * L;
         const int n = T - t0 >= L ? L : int(T - t0);
         const int64_t base = gbase + t0 * int64_t(row_bytes);
@@ -812,15 +857,11 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
                 if (i < n) {
                     float vf[VEC];
                     IO::unpack(vr[i], vf);
-                    const float age = float(n - 1 - i);
 #pragma unroll
                     for (int q = 0; q < VEC; q++) {
                         const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[i][q], kLog2e, -mxl[q]));
-                        const float ev = e * vf[q];
-                        g[q].a += ev;
+                        g[q].a = __builtin_fmaf(e, vf[q], g[q].a);
                         g[q].b += e;
-                        g[q].ap = __builtin_fmaf(age, ev, g[q].ap);
-                        g[q].bp = __builtin_fmaf(age, e, g[q].bp);
                     }
                 }
             }
@@ -832,10 +873,8 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
         for (int q = 0; q < VEC; q++) {
             x[q].a = s_fc[0][lane * VEC + q];
             x[q].b = s_fc[1][lane * VEC + q];
-            x[q].ap = s_fc[2][lane * VEC + q];
-            x[q].bp = s_fc[3][lane * VEC + q];
-            x[q].A = s_fc[4][lane * VEC + q];
-            x[q].m = s_fc[5][lane * VEC + q];
+            x[q].A = s_fc[2][lane * VEC + q];
+            x[q].m = s_fc[3][lane * VEC + q];
         }
         if (sc + 1 < nsub) {
 #pragma unroll
@@ -844,10 +883,8 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
                 combine_forward(nx, g[q], float(n), w[q]);
                 s_fc[0][lane * VEC + q] = nx.a;
                 s_fc[1][lane * VEC + q] = nx.b;
-                s_fc[2][lane * VEC + q] = nx.ap;
-                s_fc[3][lane * VEC + q] = nx.bp;
-                s_fc[4][lane * VEC + q] = nx.A;
-                s_fc[5][lane * VEC + q] = nx.m;
+                s_fc[2][lane * VEC + q] = nx.A;
+                s_fc[3][lane * VEC + q] = nx.m;
             }
             if (lane == 0)
                 __hip_atomic_store(&s_fseq, int(sc + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -858,10 +895,8 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
             for (int q = 0; q < VEC; q++) {
                 ck[0 * C + q] = x[q].a;
                 ck[1 * C + q] = x[q].b;
-                ck[2 * C + q] = x[q].ap;
-                ck[3 * C + q] = x[q].bp;
-                ck[4 * C + q] = x[q].A;
-                ck[5 * C + q] = x[q].m;
+                ck[2 * C + q] = x[q].A;
+                ck[3 * C + q] = x[q].m;
             }
         }
     }
@@ -937,12 +972,12 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
                 }
                 float G[kBwdFrames][VEC], rho[kBwdFrames][VEC], gwt[VEC], gut[VEC];
                 RState rg[VEC];
-                if (frames_rerun<IO, L, VEC>(s, kr, vr, gyr, w, cb, te, st, G, rho, rg, gwt, gut, active)) {
+                if (frames_rerun<IO, L, VEC>(s, kr, vr, gyr, w, cb, te, st, G, rho, rg, gut, active)) {
                     RState r[VEC];
                     rev_handoff(rc, &s_rseq, ln, rg, r, j, sc, n);
                     const rsrc_t gkr_ = make_rsrc(at_out(pr.gk, sc));
                     const rsrc_t gvr_ = make_rsrc(at_out(pr.gv, sc));
-                    if (frames_walk<IO, L, VEC>(r, te, st, G, rho, vr, w, cb, gkr_, gvr_, toff, active)) {
+                    if (frames_walk<IO, L, VEC>(r, te, st, G, rho, vr, w, cb, gkr_, gvr_, toff, active, gwt)) {
 #pragma unroll
                         for (int q = 0; q < VEC; q++) {
                             gw[q] += gwt[q];
@@ -1032,10 +1067,10 @@ int backward_vec(int64_t C, int dtype, bool aligned) {
     return (dtype == kBF16 && C % 2 == 0 && aligned) ? 2 : 1;
 }
 
-size_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C) {
+size_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C, bool saved) {
     const size_t nsub = size_t((T + kBwdTokens - 1) / kBwdTokens);
     const size_t cols = size_t(B) * size_t(C);
-    return up256(cols * nsub * kCkptFields * 4) + 2 * up256(cols * 4);
+    return (saved ? 0 : up256(cols * nsub * kCkptFields * 4)) + 2 * up256(cols * 4);
 }
 
 hipError_t launch_backward(BackwardProblem pr, void* workspace, hipStream_t stream) {
@@ -1046,9 +1081,11 @@ hipError_t launch_backward(BackwardProblem pr, void* workspace, hipStream_t stre
     }
     const int64_t cols = pr.B * pr.C;
     const int64_t nsub = (pr.T + kBwdTokens - 1) / kBwdTokens;
+    const bool saved = pr.saved != nullptr;
     char* ws = static_cast<char*>(workspace);
-    pr.ckpt = reinterpret_cast<float*>(ws);
-    const size_t ck = up256(size_t(cols) * size_t(nsub) * kCkptFields * 4);
+    const size_t ck = saved ? 0 : up256(size_t(cols) * size_t(nsub) * kCkptFields * 4);
+    // the kernel only reads the checkpoints when they are saved ones
+    pr.ckpt = saved ? const_cast<float*>(pr.saved) : reinterpret_cast<float*>(ws);
     pr.part_w = reinterpret_cast<float*>(ws + ck);
     pr.part_u = reinterpret_cast<float*>(ws + ck + up256(size_t(cols) * 4));
     const int64_t cg = 64 * pr.vec;
@@ -1056,12 +1093,19 @@ hipError_t launch_backward(BackwardProblem pr, void* workspace, hipStream_t stre
     const dim3 grid(unsigned(pr.B * gpr));
     constexpr int NW = 8;
     const dim3 block(NW * 64);
-    if (pr.dtype == kBF16 && pr.vec == 2)
-        hipLaunchKernelGGL((backward_chained_kernel<kBF16, 2, NW>), grid, block, 0, stream, pr, gpr, nsub);
-    else if (pr.dtype == kBF16)
-        hipLaunchKernelGGL((backward_chained_kernel<kBF16, 1, NW>), grid, block, 0, stream, pr, gpr, nsub);
+    auto go = [&](auto saved_tag) {
+        constexpr bool S = decltype(saved_tag)::value;
+        if (pr.dtype == kBF16 && pr.vec == 2)
+            hipLaunchKernelGGL((backward_chained_kernel<kBF16, 2, NW, S>), grid, block, 0, stream, pr, gpr, nsub);
+        else if (pr.dtype == kBF16)
+            hipLaunchKernelGGL((backward_chained_kernel<kBF16, 1, NW, S>), grid, block, 0, stream, pr, gpr, nsub);
+        else
+            hipLaunchKernelGGL((backward_chained_kernel<kF32, 1, NW, S>), grid, block, 0, stream, pr, gpr, nsub);
+    };
+    if (saved)
+        go(std::integral_constant<bool, true>{});
     else
-        hipLaunchKernelGGL((backward_chained_kernel<kF32, 1, NW>), grid, block, 0, stream, pr, gpr, nsub);
+        go(std::integral_constant<bool, false>{});
     hipLaunchKernelGGL(backward_reduce, dim3(unsigned((pr.C + 255) / 256)), dim3(256), 0, stream, pr);
     return hipGetLastError();
 }

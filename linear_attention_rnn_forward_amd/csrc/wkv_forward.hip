@@ -978,7 +978,24 @@ __device__ __forceinline__ void chain_handoff(Lane<VEC>& s, const Part<VEC>& gw,
     for (int q = 0; q < VEC; q++) { s.a[q] = x.a[q]; s.b[q] = x.b[q]; s.A[q] = x.A[q]; s.m[q] = x.m[q]; }
 }
 
-template <int DT, int VEC, int NWV, bool GATED>
+// The carry of sub-chunk sc (the state before it, in s) to pr.states
+// [B][nsub][a, b, A, m][C]: the backward's checkpoints.
+template <int VEC>
+__device__ __forceinline__ void save_carry(const Lane<VEC>& s, const ForwardProblem& pr, int64_t bb,
+                                           int64_t sc, int64_t nsub, int64_t c, bool active) {
+    if (!active) return;
+    float* o = pr.states + (bb * nsub + sc) * 4 * pr.C + c;
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        o[0 * pr.C + q] = s.a[q];
+        o[1 * pr.C + q] = s.b[q];
+        o[2 * pr.C + q] = s.A[q];
+        o[3 * pr.C + q] = s.m[q];
+    }
+}
+
+// SAVE: each sub-chunk's carry also goes to pr.states (save_carry).
+template <int DT, int VEC, int NWV, bool GATED, bool SAVE>
 __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProblem pr, int64_t gpr,
                                                                    int64_t nsub) {
     using IO = Io<DT, VEC>;
@@ -1045,6 +1062,7 @@ __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProble
             // chain of hand-offs that every wave of the workgroup waits on
             pin_weights(fw, gw);
             chain_handoff<VEC>(s, gw, n, sc, nsub, s_carry, &s_seq, lane, after);
+            if constexpr (SAVE) save_carry(s, pr, bb, sc, nsub, c, active);
             run_block_weights<DT, VEC, L, GATED>(s, fw, vr, gated_rr<GATED>(rr, kr), kr_, yr_, voff,
                                                  row_bytes, active);
         } else {
@@ -1064,6 +1082,7 @@ __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProble
                         rr, make_rsrc(static_cast<const char*>(pr.r) + base), voff, row_bytes, n);
             }
             chain_handoff<VEC>(s, gw, n, sc, nsub, s_carry, &s_seq, lane, after);
+            if constexpr (SAVE) save_carry(s, pr, bb, sc, nsub, c, active);
             const Raw (&rg)[L] = gated_rr<GATED>(rr, kr);
             if (n == L) {
                 if (fused)
@@ -1159,13 +1178,13 @@ int chained_waves(int64_t ngroups, int device_cus) {
 }
 
 namespace {
-template <bool GATED>
+template <bool GATED, bool SAVE>
 void launch_chained_t(const ForwardProblem& pr, int nw, dim3 grid, int64_t gpr, int64_t nsub,
                       hipStream_t stream) {
     const dim3 block(nw * 64);
 #define WKV_LAUNCH_CHAINED(DT, V, NW)                                                             \
-    hipLaunchKernelGGL((forward_chained_kernel<DT, V, NW, GATED>), grid, block, 0, stream, pr, gpr, \
-                       nsub)
+    hipLaunchKernelGGL((forward_chained_kernel<DT, V, NW, GATED, SAVE>), grid, block, 0, stream, pr, \
+                       gpr, nsub)
 #define WKV_CHAINED_NW(DT, V)                                   \
     switch (nw) {                                              \
         case 16: WKV_LAUNCH_CHAINED(DT, V, 16); break;         \
@@ -1192,10 +1211,15 @@ hipError_t launch_forward_chained(const ForwardProblem& pr, hipStream_t stream) 
     const int64_t nsub = (pr.T + kChainTokens - 1) / kChainTokens;
     const int nw = chained_waves(ngroups, device_cu_count());
     const dim3 grid(static_cast<unsigned>(ngroups));
+    // saved states are the backward's checkpoints: one per 16 tokens
+    if (pr.states != nullptr && (pr.r != nullptr || kChainTokens != WKV_SAVED_STATE_TOKENS))
+        return hipErrorInvalidValue;
     if (pr.r != nullptr)
-        launch_chained_t<true>(pr, nw, grid, gpr, nsub, stream);
+        launch_chained_t<true, false>(pr, nw, grid, gpr, nsub, stream);
+    else if (pr.states != nullptr)
+        launch_chained_t<false, true>(pr, nw, grid, gpr, nsub, stream);
     else
-        launch_chained_t<false>(pr, nw, grid, gpr, nsub, stream);
+        launch_chained_t<false, false>(pr, nw, grid, gpr, nsub, stream);
     return hipGetLastError();
 }
 

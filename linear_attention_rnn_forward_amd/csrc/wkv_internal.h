@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "wkv.h"
+
 namespace wkv {
 
 struct ForwardProblem {
@@ -18,6 +20,7 @@ struct ForwardProblem {
     const float *a_in, *b_in, *p_in;  // all null or all set
     float *a_out, *b_out, *p_out;     // all null or all set
     const void* r = nullptr;          // receptance [B,T,C]: y = sigmoid(r) * wkv when set
+    float* states = nullptr;          // [B][ceil(T/16)][4][C]: the chained path's carries, when set
 };
 
 // Geometry of the chunked path for one problem.
@@ -70,12 +73,13 @@ struct BackwardProblem {
     float *gw, *gu;                // [C]
     int vec = 1;                   // channels per lane (backward_vec)
     // workspace sections (set by launch_backward)
-    float* ckpt = nullptr;         // [B][T/16][6][C] forward state before each sub-chunk
+    const float* saved = nullptr;  // [B][ceil(T/16)][4][C] checkpoints saved by the forward, or null
+    float* ckpt = nullptr;         // [B][ceil(T/16)][4][C] forward state before each sub-chunk
     float* part_w = nullptr;       // [B,C] per-column gw
     float* part_u = nullptr;       // [B,C] per-column gu
 };
 int backward_vec(int64_t C, int dtype, bool aligned);
-size_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C);
+size_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C, bool saved);
 hipError_t launch_backward(BackwardProblem pr, void* workspace, hipStream_t stream);
 
 // Tokens per lane in the token shift: each lane reads the row before its run

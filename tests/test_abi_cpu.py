@@ -33,13 +33,15 @@ def test_header_lists_the_boundary_calls():
     for n in ("wkv_forward", "wkv_step", "wkv_token_shift", "wkv_forward_workspace_size",
               "wkv_forward_gated", "wkv_step_gated", "wkv_backward", "wkv_backward_workspace_size",
               "wkv_status_string", "wkv_last_error", "wkv_mat_forward", "wkv_mat_forward_path",
-              "wkv_mat_step", "wkv_bounded_wait_failures", "wkv_forward_auto_path"):
+              "wkv_mat_step", "wkv_bounded_wait_failures", "wkv_forward_auto_path",
+              "wkv_forward_save", "wkv_backward_saved", "wkv_saved_states_bytes",
+              "wkv_backward_saved_workspace_size"):
         assert n in names
 
 
 def test_abi_version_and_status_strings():
     L = wkv.lib()
-    assert L.wkv_abi_version() == 105
+    assert L.wkv_abi_version() == 106
     for code in range(0, -9, -1):
         assert L.wkv_status_string(code).decode()
     assert L.wkv_status_string(-100).decode() == "unknown status"
@@ -222,12 +224,12 @@ def test_session_save_checks_arguments():
 
 
 def test_backward_workspace_size():
-    """The forward state before every 16-token sub-chunk (6 fp32 per column)
+    """The forward state before every 16-token sub-chunk (4 fp32 per column)
     plus per-column gw, gu partials, each section rounded up to 256 bytes."""
     L = wkv.lib()
-    assert L.wkv_backward_workspace_size(2, 3, 64) == 3072 + 2 * 512
-    assert L.wkv_backward_workspace_size(2, 17, 64) == 2 * 3072 + 2 * 512
-    assert L.wkv_backward_workspace_size(16, 4096, 2048) == 16 * 2048 * 256 * 24 + 2 * 16 * 2048 * 4
+    assert L.wkv_backward_workspace_size(2, 3, 64) == 2048 + 2 * 512
+    assert L.wkv_backward_workspace_size(2, 17, 64) == 2 * 2048 + 2 * 512
+    assert L.wkv_backward_workspace_size(16, 4096, 2048) == 16 * 2048 * 256 * 16 + 2 * 16 * 2048 * 4
     assert L.wkv_backward_workspace_size(1, 1, 1) == 3 * 256
     assert L.wkv_backward_workspace_size(0, 8, 8) == 0
     assert L.wkv_backward_workspace_size(1 << 40, 1 << 40, 8) == 0
@@ -259,6 +261,61 @@ def test_backward_rejects_bad_arguments():
     assert call(ws=20 * G + 16) == -4              # misaligned
     assert call(ws=6 * G) == -5                    # workspace on gk
     assert call(C=1 << 26) == -2                   # sub-chunk offsets beyond 32 bits
+
+
+def test_saved_state_sizes():
+    """[B][ceil(T/16)][4][C] fp32 states; the saved backward's workspace is
+    only the per-column partials."""
+    L = wkv.lib()
+    assert L.wkv_saved_states_bytes(2, 3, 64) == 2 * 1 * 4 * 64 * 4
+    assert L.wkv_saved_states_bytes(2, 17, 64) == 2 * 2 * 4 * 64 * 4
+    assert L.wkv_saved_states_bytes(16, 4096, 2048) == 16 * 256 * 4 * 2048 * 4
+    assert L.wkv_saved_states_bytes(1, 0, 8) == 0
+    assert L.wkv_saved_states_bytes(0, 8, 8) == 0
+    assert L.wkv_backward_saved_workspace_size(2, 64) == 2 * 512
+    assert L.wkv_backward_saved_workspace_size(16, 2048) == 2 * 16 * 2048 * 4
+    assert L.wkv_backward_saved_workspace_size(0, 8) == 0
+    assert wkv.saved_states_shape(2, 17, 64) == (2, 2, 4, 64)
+
+
+def test_forward_save_rejects_bad_arguments():
+    L = wkv.lib()
+
+    def call(dtype=0, B=2, T=33, C=64, **over):
+        a = dict(w=1, u=2, k=3, v=4, y=5, states=6)
+        a.update(over)
+        ptr = {n: (P(int(x * G)) if x is not None else None) for n, x in a.items()}
+        return L.wkv_forward_save(B, T, C, dtype, ptr["w"], ptr["u"], ptr["k"], ptr["v"], ptr["y"],
+                                  ptr["states"], None)
+
+    assert call(dtype=5) == -3
+    assert call(B=0) == -2 and call(T=-1) == -2
+    assert call(states=None) == -1
+    assert call(states=3) == -5                   # states on k
+    assert b"states overlaps k" in L.wkv_last_error()
+    assert call(states=5) == -5                   # states on y
+    assert call(states=6 + 2 / G) == -8            # misaligned (2 bytes off)
+
+
+def test_backward_saved_rejects_bad_arguments():
+    L = wkv.lib()
+    B, T, C = 2, 33, 64
+    need = L.wkv_backward_saved_workspace_size(B, C)
+
+    def call(ws=20 * G, ws_bytes=need, **over):
+        a = dict(w=1, u=2, k=3, v=4, gy=5, states=10, gk=6, gv=7, gw=8, gu=9)
+        a.update(over)
+        ptr = {n: (P(int(x * G)) if x is not None else None) for n, x in a.items()}
+        return L.wkv_backward_saved(B, T, C, 0, ptr["w"], ptr["u"], ptr["k"], ptr["v"], ptr["gy"],
+                                    ptr["states"], ptr["gk"], ptr["gv"], ptr["gw"], ptr["gu"],
+                                    P(ws) if ws else None, ws_bytes, None)
+
+    assert call(states=None) == -1
+    assert call(gk=10) == -5                      # gk on the states
+    assert b"gk overlaps states" in L.wkv_last_error()
+    assert call(ws=10 * G) == -5                  # workspace on the states
+    assert call(ws_bytes=need - 1) == -4
+    assert call(states=10 + 2 / G) == -8           # misaligned
 
 
 # ---------------------------------------------------------------------------

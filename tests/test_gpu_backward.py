@@ -1,5 +1,7 @@
 """GPU parity of wkv_backward (gradients of sum(gy * wkv) from the empty
-history) against the fp64 oracle.
+history) against the fp64 oracle, and of wkv_backward_saved, which starts
+from the states wkv_forward_save kept instead of recomputing them (the
+`saved` cases).
 
 Error measure: each gradient is a sum of terms gy_t alpha[t,i] (v_i - y_t)
 (or without the last factor, or weighted by the age t-1-i), so the rounding
@@ -51,19 +53,25 @@ def bf16_exact(a):
     return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(np.asarray(a, dtype=np.float32)))
 
 
-def run_backward(k, v, w, u, g, dtype, dev):
-    """k, v, g: fp32 arrays (bf16-exact when dtype is bf16)."""
+def run_backward(k, v, w, u, g, dtype, dev, saved=False):
+    """k, v, g: fp32 arrays (bf16-exact when dtype is bf16).  saved: the
+    states from forward_save, then backward from them."""
     import linear_attention_rnn_forward_amd as wkv
     torch = _torch()
     bits = (lambda a: synth.f32_to_bf16_bits(a)) if dtype == "bf16" else (lambda a: None)
     kd, vd, gd = (to_dev(a, dev, bits(a)) for a in (k, v, g))
-    out = wkv.backward(kd, vd, to_dev(w, dev), to_dev(u, dev), gd)
+    wd, ud = to_dev(w, dev), to_dev(u, dev)
+    states = wkv.forward_save(kd, vd, wd, ud)[1] if saved else None
+    out = wkv.backward(kd, vd, wd, ud, gd, states=states)
     torch.cuda.synchronize()
     return tuple(host(t) for t in out)
 
 
-def check(k, v, w, u, g, dtype, dev, label=""):
-    got = run_backward(k, v, w, u, g, dtype, dev)
+SAVED = pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
+
+
+def check(k, v, w, u, g, dtype, dev, label="", saved=False):
+    got = run_backward(k, v, w, u, g, dtype, dev, saved)
     ref = oracle.backward(k, v, w, u, g)
     mag = oracle.backward(k, v, w, u, g, magnitude=True)
     errs = {}
@@ -91,8 +99,9 @@ def workload_inputs(wl):
     ("bf16_main", synth.BF16_MAIN.resized(B=2, T=512, C=128)),
     ("long_ctx", synth.LONG_CTX.resized(B=1, T=1500, C=40)),
 ])
-def test_workload_recipes(device, name, wl):
-    _, errs = check(*workload_inputs(wl), wl.dtype, device, name)
+@SAVED
+def test_workload_recipes(device, name, wl, saved):
+    _, errs = check(*workload_inputs(wl), wl.dtype, device, name, saved)
     print(name, {k: f"{v:.2e}" for k, v in errs.items()})
 
 
@@ -102,11 +111,12 @@ SHAPES = [(1, 1, 1), (1, 2, 3), (3, 17, 5), (1, 16, 256), (2, 33, 257), (1, 129,
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_ragged_shapes(device, shape, dtype):
+@SAVED
+def test_ragged_shapes(device, shape, dtype, saved):
     B, T, C = shape
     base = synth.BF16_MAIN if dtype == "bf16" else synth.TINY
     wl = base.resized(B=B, T=T, C=C, seed=3000 + B * T + C)
-    check(*workload_inputs(wl), dtype, device, f"{shape}")
+    check(*workload_inputs(wl), dtype, device, f"{shape}", saved)
 
 
 # ---------------------------------------------------------------------------
@@ -163,7 +173,8 @@ def _cols(B, T, C, seed):
                  rng.normal(0, 1, (B, T, C)).astype(np.float32))
 
 
-def test_monotone_keys_move_the_anchor_every_token_or_never(device):
+@SAVED
+def test_monotone_keys_move_the_anchor_every_token_or_never(device, saved):
     """Rising keys (k_t = 0.5 t) make each token the new maximum, in both
     passes' stabilisation; falling keys never do."""
     B, T, C = 2, 200, 64
@@ -172,11 +183,12 @@ def test_monotone_keys_move_the_anchor_every_token_or_never(device):
     w = np.exp(rng.uniform(-5, 1, C)).astype(np.float32)
     u = rng.normal(0, 0.5, C).astype(np.float32)
     for k in (np.broadcast_to(ramp, (B, T, C)).copy(), np.broadcast_to(-ramp, (B, T, C)).copy()):
-        check(k, v, w, u, g, "f32", device, "ramp")
+        check(k, v, w, u, g, "f32", device, "ramp", saved)
 
 
 @pytest.mark.parametrize("omega", [-8.0, 0.0, 2.0, 3.7, 4.0])
-def test_decay_extremes(device, omega):
+@SAVED
+def test_decay_extremes(device, omega, saved):
     """w from e^-8 (a window of thousands of tokens) to e^4 = 55 (only the
     current and the previous token matter; |u - w| > 44 takes the read-out
     with its own exponential)."""
@@ -185,10 +197,11 @@ def test_decay_extremes(device, omega):
     k = rng.normal(0, 2, (B, T, C)).astype(np.float32)
     w = np.full(C, np.exp(omega), dtype=np.float32)
     u = rng.normal(0, 0.5, C).astype(np.float32)
-    check(k, v, w, u, g, "f32", device, f"omega={omega}")
+    check(k, v, w, u, g, "f32", device, f"omega={omega}", saved)
 
 
-def test_mixed_read_out_forms(device):
+@SAVED
+def test_mixed_read_out_forms(device, saved):
     """Column groups whose channels all have |u - w| <= 44 reuse the fold's
     exponential for the read-out; a group with any other channel takes the
     separate read-out.  Here the first 64 channels have w = e^4 (and the
@@ -201,11 +214,12 @@ def test_mixed_read_out_forms(device):
     u = rng.normal(0, 0.5, C).astype(np.float32)
     w[:64] = np.float32(np.exp(4.0))
     u[64:128] = 50.0
-    check(k, v, w, u, g, "f32", device, "mixed f32")
-    check(bf16_exact(k), bf16_exact(v), w, u, bf16_exact(g), "bf16", device, "mixed bf16")
+    check(k, v, w, u, g, "f32", device, "mixed f32", saved)
+    check(bf16_exact(k), bf16_exact(v), w, u, bf16_exact(g), "bf16", device, "mixed bf16", saved)
 
 
-def test_keys_far_outside_exp_range(device):
+@SAVED
+def test_keys_far_outside_exp_range(device, saved):
     """k ~ N(0, 30): e^k overflows fp32 for a third of the keys; every
     exponential the kernels take has a non-positive argument."""
     B, T, C = 2, 300, 64
@@ -213,7 +227,7 @@ def test_keys_far_outside_exp_range(device):
     k = rng.normal(0, 30, (B, T, C)).astype(np.float32)
     w = np.exp(rng.uniform(-5, 1, C)).astype(np.float32)
     u = rng.normal(0, 0.5, C).astype(np.float32)
-    check(k, v, w, u, g, "f32", device, "wide keys")
+    check(k, v, w, u, g, "f32", device, "wide keys", saved)
 
 
 def test_zero_output_gradient_gives_zero(device):
@@ -258,7 +272,8 @@ def test_unaligned_tensors(device, dtype):
         assert scaled_err(host(x), r, m) <= tol
 
 
-def test_deterministic_and_graph_replay(device):
+@SAVED
+def test_deterministic_and_graph_replay(device, saved):
     """Two eager calls agree bit for bit (gw, gu are reduced over the batch
     in a fixed order), and a captured HIP graph replays the same bits."""
     import linear_attention_rnn_forward_amd as wkv
@@ -268,9 +283,12 @@ def test_deterministic_and_graph_replay(device):
     bits = synth.f32_to_bf16_bits
     kd, vd, gd = (to_dev(a, device, bits(a)) for a in (k, v, g))
     wd, ud = to_dev(w, device), to_dev(u, device)
-    ws = torch.empty(wkv.backward_workspace_size(wl.B, wl.T, wl.C), dtype=torch.uint8, device=device)
-    first = [t.clone() for t in wkv.backward(kd, vd, wd, ud, gd, workspace=ws)]
-    second = wkv.backward(kd, vd, wd, ud, gd, workspace=ws)
+    st = wkv.forward_save(kd, vd, wd, ud)[1] if saved else None
+    need = (wkv.backward_saved_workspace_size(wl.B, wl.C) if saved
+            else wkv.backward_workspace_size(wl.B, wl.T, wl.C))
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    first = [t.clone() for t in wkv.backward(kd, vd, wd, ud, gd, workspace=ws, states=st)]
+    second = wkv.backward(kd, vd, wd, ud, gd, workspace=ws, states=st)
     torch.cuda.synchronize()
     for a, b in zip(first, second):
         assert torch.equal(a, b)
@@ -280,7 +298,7 @@ def test_deterministic_and_graph_replay(device):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
         with torch.cuda.graph(graph, stream=s):
-            wkv.backward(kd, vd, wd, ud, gd, out=outs, workspace=ws)
+            wkv.backward(kd, vd, wd, ud, gd, out=outs, workspace=ws, states=st)
     torch.cuda.current_stream().wait_stream(s)
     for _ in range(3):
         for o in outs:
@@ -296,13 +314,14 @@ def test_deterministic_and_graph_replay(device):
 # the full-size workload: B=16, T=4096, C=2048 bf16, sampled columns
 # ---------------------------------------------------------------------------
 
-def test_bf16_main_full_size_sampled(device):
+@SAVED
+def test_bf16_main_full_size_sampled(device, saved):
     """The bf16 workload at its full size, in the launch bench.py times.
     gk, gv are checked on whole columns (b, c) and gw, gu on one channel
     (all 16 batch rows), each against the oracle run on those columns alone."""
     wl = synth.BF16_MAIN
     k, v, w, u, g = workload_inputs(wl)
-    gk, gv, gw, gu = run_backward(k, v, w, u, g, "bf16", device)
+    gk, gv, gw, gu = run_backward(k, v, w, u, g, "bf16", device, saved)
     c0 = 1234
     sl = (slice(None), slice(None), slice(c0, c0 + 1))
     ref = oracle.backward(k[sl], v[sl], w[c0:c0 + 1], u[c0:c0 + 1], g[sl])
