@@ -323,7 +323,7 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, int dtype,
  * wkv_forward_save: wkv_forward from the empty history (no state in or out)
  * that also writes
  *   states      [B][ceil(T/16)][4][C] fp32 device array,
- *               wkv_saved_states_bytes(B, T, C) bytes, 4-byte aligned: for
+ *               wkv_saved_states_bytes(B, T, C) bytes, 8-byte aligned: for
  *               sub-chunk s (tokens 16 s .. 16 s + 15) of row b the
  *               recurrence's state before its first token, in the anchor
  *               form (a, b, A, m): the history sums scaled by e^{-p},

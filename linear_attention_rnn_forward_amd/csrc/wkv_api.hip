@@ -141,7 +141,7 @@ int forward_impl(int64_t B, int64_t T, int64_t C, int dtype, int path, const flo
         for (const Range& ro : r_out)
             if (overlap(r_st, ro)) return fail(WKV_ERR_ALIAS, "states overlaps %s", ro.name);
         if (overlap(r_st, r_y)) return fail(WKV_ERR_ALIAS, "states overlaps y");
-        if (!aligned(states, 4)) return fail(WKV_ERR_ARG, "states must be 4-byte aligned");
+        if (!aligned(states, 8)) return fail(WKV_ERR_ARG, "states must be 8-byte aligned");
     }
 
     wkv::ForwardProblem pr;
@@ -490,7 +490,7 @@ int backward_impl(int64_t B, int64_t T, int64_t C, int dtype, const float* w, co
         return fail(WKV_ERR_SHAPE, "C too large for 32-bit offsets within a sub-chunk");
     const int64_t io = n * int64_t(esize(dtype));
     const bool saved = states != nullptr;
-    if (saved && T > 0 && !aligned(states, 4)) return fail(WKV_ERR_ARG, "states must be 4-byte aligned");
+    if (saved && T > 0 && !aligned(states, 8)) return fail(WKV_ERR_ARG, "states must be 8-byte aligned");
     const Range r_in[] = {rng("k", k, io), rng("v", v, io), rng("gy", gy, io), rng("w", w, C * 4),
                           rng("u", u, C * 4),
                           rng("states", T > 0 ? states : nullptr, saved_state_bytes(B, T, C))};

@@ -468,7 +468,7 @@ __device__ __forceinline__ bool frames_walk(const RState (&r)[VEC], const float 
                                             const float (&G)[kBwdFrames][VEC],
                                             const float (&rho)[kBwdFrames][VEC], const Raw (&vr)[L],
                                             const float (&w)[VEC], const float (&c)[VEC],
-                                            rsrc_t gkr_, rsrc_t gvr_, const uint32_t (&toff)[L],
+                                            rsrc_t gkr_, rsrc_t gvr_, uint32_t voff, uint32_t row_bytes,
                                             bool active, float (&gw)[VEC]) {
     constexpr int F = kBwdFrame, NF = kBwdFrames;
     // S, SQ: the sums of gr, gr y over the later tokens; S2, SQ2 the same
@@ -522,8 +522,8 @@ __device__ __forceinline__ bool frames_walk(const RState (&r)[VEC], const float 
                 SQ[q] = __builtin_fmaf(grt[q], yt[q], SQ[q]);
             }
             if (active) {
-                Buf<Raw>::store(IO::pack(gkf), gkr_, toff[i], 0);
-                Buf<Raw>::store(IO::pack(gvf), gvr_, toff[i], 0);
+                Buf<Raw>::store(IO::pack(gkf), gkr_, voff, uint32_t(i) * row_bytes);
+                Buf<Raw>::store(IO::pack(gvf), gvr_, voff, uint32_t(i) * row_bytes);
             }
         }
     }
@@ -800,9 +800,9 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     constexpr int64_t es = sizeof(Raw) / VEC;
     const uint32_t row_bytes = uint32_t(C * es);
     const uint32_t voff = active ? uint32_t(lane) * uint32_t(sizeof(Raw)) : 0u;
-    uint32_t toff[L];
-#pragma unroll
-    for (int i = 0; i < L; i++) toff[i] = voff + uint32_t(i) * row_bytes;
+    // token i of a sub-chunk at byte voff + i row_bytes of its base: the
+    // second part as the buffer instructions' scalar offset, so that no
+    // vector register holds a per-token offset
     const int64_t gbase = (bb * T * C + c0) * es;
     // checkpoints: [B][nsub][field][C] fp32
     // (lanes past the last channel read the group's first channel: stand-in
@@ -820,8 +820,8 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
 #pragma unroll
         for (int i = 0; i < L; i++) {
             if (i < n) {
-                kr[i] = Buf<Raw>::template load<kStreamLoad>(kr_, toff[i], 0);
-                vr[i] = Buf<Raw>::template load<kStreamLoad>(vr_, toff[i], 0);
+                kr[i] = Buf<Raw>::template load<kStreamLoad>(kr_, voff, uint32_t(i) * row_bytes);
+                vr[i] = Buf<Raw>::template load<kStreamLoad>(vr_, voff, uint32_t(i) * row_bytes);
             }
         }
         // the sub-chunk from the empty history, max then sum: token i has
@@ -952,15 +952,17 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
             const float* ck = ckpt + sc * kCkptFields * C;
             bool have_carry = false;  // the hand-off has run
             if (n == L) {
-                const rsrc_t kr_ = make_rsrc(at(pr.k, sc));
-                const rsrc_t vr_ = make_rsrc(at(pr.v, sc));
-                const rsrc_t gr_ = make_rsrc(at(pr.gy, sc));
                 Raw kr[L], vr[L], gyr[L];
+                {
+                    const rsrc_t kr_ = make_rsrc(at(pr.k, sc));
+                    const rsrc_t vr_ = make_rsrc(at(pr.v, sc));
+                    const rsrc_t gr_ = make_rsrc(at(pr.gy, sc));
 #pragma unroll
-                for (int i = 0; i < L; i++) {
-                    kr[i] = Buf<Raw>::template load<kStreamLoad>(kr_, toff[i], 0);
-                    vr[i] = Buf<Raw>::template load<kStreamLoad>(vr_, toff[i], 0);
-                    gyr[i] = Buf<Raw>::template load<kStreamLoad>(gr_, toff[i], 0);
+                    for (int i = 0; i < L; i++) {
+                        kr[i] = Buf<Raw>::template load<kStreamLoad>(kr_, voff, uint32_t(i) * row_bytes);
+                        vr[i] = Buf<Raw>::template load<kStreamLoad>(vr_, voff, uint32_t(i) * row_bytes);
+                        gyr[i] = Buf<Raw>::template load<kStreamLoad>(gr_, voff, uint32_t(i) * row_bytes);
+                    }
                 }
                 FState s[VEC];
                 load_checkpoint(s, ck, C);
@@ -977,7 +979,7 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
                     rev_handoff(rc, &s_rseq, ln, rg, r, j, sc, n);
                     const rsrc_t gkr_ = make_rsrc(at_out(pr.gk, sc));
                     const rsrc_t gvr_ = make_rsrc(at_out(pr.gv, sc));
-                    if (frames_walk<IO, L, VEC>(r, te, st, G, rho, vr, w, cb, gkr_, gvr_, toff, active, gwt)) {
+                    if (frames_walk<IO, L, VEC>(r, te, st, G, rho, vr, w, cb, gkr_, gvr_, voff, row_bytes, active, gwt)) {
 #pragma unroll
                         for (int q = 0; q < VEC; q++) {
                             gw[q] += gwt[q];

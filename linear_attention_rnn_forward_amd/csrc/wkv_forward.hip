@@ -985,12 +985,20 @@ __device__ __forceinline__ void save_carry(const Lane<VEC>& s, const ForwardProb
                                            int64_t sc, int64_t nsub, int64_t c, bool active) {
     if (!active) return;
     float* o = pr.states + (bb * nsub + sc) * 4 * pr.C + c;
+    if constexpr (VEC == 2) {
+        // one 8-byte store per field (c is even and the rows 8-byte aligned)
+        *reinterpret_cast<float2*>(o + 0 * pr.C) = make_float2(s.a[0], s.a[1]);
+        *reinterpret_cast<float2*>(o + 1 * pr.C) = make_float2(s.b[0], s.b[1]);
+        *reinterpret_cast<float2*>(o + 2 * pr.C) = make_float2(s.A[0], s.A[1]);
+        *reinterpret_cast<float2*>(o + 3 * pr.C) = make_float2(s.m[0], s.m[1]);
+    } else {
 #pragma unroll
-    for (int q = 0; q < VEC; q++) {
-        o[0 * pr.C + q] = s.a[q];
-        o[1 * pr.C + q] = s.b[q];
-        o[2 * pr.C + q] = s.A[q];
-        o[3 * pr.C + q] = s.m[q];
+        for (int q = 0; q < VEC; q++) {
+            o[0 * pr.C + q] = s.a[q];
+            o[1 * pr.C + q] = s.b[q];
+            o[2 * pr.C + q] = s.A[q];
+            o[3 * pr.C + q] = s.m[q];
+        }
     }
 }
 

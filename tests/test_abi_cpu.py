@@ -294,7 +294,7 @@ def test_forward_save_rejects_bad_arguments():
     assert call(states=3) == -5                   # states on k
     assert b"states overlaps k" in L.wkv_last_error()
     assert call(states=5) == -5                   # states on y
-    assert call(states=6 + 2 / G) == -8            # misaligned (2 bytes off)
+    assert call(states=6 + 4 / G) == -8            # misaligned (4 bytes off)
 
 
 def test_backward_saved_rejects_bad_arguments():
@@ -315,7 +315,7 @@ def test_backward_saved_rejects_bad_arguments():
     assert b"gk overlaps states" in L.wkv_last_error()
     assert call(ws=10 * G) == -5                  # workspace on the states
     assert call(ws_bytes=need - 1) == -4
-    assert call(states=10 + 2 / G) == -8           # misaligned
+    assert call(states=10 + 4 / G) == -8           # misaligned (4 bytes off)
 
 
 # ---------------------------------------------------------------------------
