@@ -14,7 +14,9 @@ CPU oracle timed on the same workload on the host cores.
 Other workloads (--workload): tiny, small_lm, long_ctx (wkv_forward),
 bf16_main_gated (the default workload through wkv_forward_gated, the
 receptance gate fused), bf16_main_backward (wkv_backward over the default
-workload's shape; a step is its three launches), decode (wkv_step over [32,256,4096] fp32),
+workload's shape; a step is its two launches), bf16_main_backward_saved
+(wkv_backward_saved from wkv_forward_save's states, made before the timed
+region; the line also reports what saving them adds to the forward), decode (wkv_step over [32,256,4096] fp32),
 token_shift (bf16, B=16 T=4096 C=2048), mat_main / mat_eagle (the
 matrix-valued-state operator of RWKV-6 Finch / RWKV-5 Eagle, wkv_mat_forward
 over B=16 T=4096 and 32 heads of 64, bf16), mat_decode (wkv_mat_step over
@@ -43,6 +45,7 @@ KERNEL_SOURCES = {
     "tiny": _FORWARD_SOURCES, "small_lm": _FORWARD_SOURCES, "bf16_main": _FORWARD_SOURCES,
     "bf16_main_gated": _FORWARD_SOURCES, "long_ctx": _FORWARD_SOURCES,
     "bf16_main_backward": ["wkv_backward.hip"] + _COMMON_SOURCES,
+    "bf16_main_backward_saved": ["wkv_backward.hip"] + _COMMON_SOURCES,
     "decode": ["wkv_step.hip"] + _COMMON_SOURCES,
     "token_shift": ["wkv_token_shift.hip"] + _COMMON_SOURCES,
     "mat_main": ["wkv_mat.hip"] + _COMMON_SOURCES, "mat_eagle": ["wkv_mat.hip"] + _COMMON_SOURCES,
@@ -172,9 +175,11 @@ class ForwardBench:
 
 class BackwardBench:
     """wkv_backward over the forward workload's shape: k, v and the output
-    gradient gy read, gk, gv written (plus gw, gu [C])."""
+    gradient gy read, gk, gv written (plus gw, gu [C]).  saved: the training
+    pair's backward, wkv_backward_saved, from the states wkv_forward_save kept
+    (made once before the timed region, as a training step's forward would)."""
 
-    def __init__(self, wl, dev):
+    def __init__(self, wl, dev, saved=False):
         import numpy as np
         import torch
 
@@ -195,18 +200,56 @@ class BackwardBench:
                     torch.empty(wl.C, device=dev), torch.empty(wl.C, device=dev))
         import linear_attention_rnn_forward_amd as wkv
         self.wkv = wkv
-        self.ws = torch.empty(wkv.backward_workspace_size(wl.B, wl.T, wl.C), dtype=torch.uint8,
-                              device=dev)
+        self.saved = saved
+        self.states = None
+        self.save_cost = None
+        if saved:
+            self.ws = torch.empty(wkv.backward_saved_workspace_size(wl.B, wl.C), dtype=torch.uint8,
+                                  device=dev)
+            self.states = wkv.forward_save(self.k, self.v, self.w, self.u)[1]
+            self.save_cost = self._save_cost(dev)
+        else:
+            self.ws = torch.empty(wkv.backward_workspace_size(wl.B, wl.T, wl.C), dtype=torch.uint8,
+                                  device=dev)
         es = 2 if wl.dtype == "bf16" else 4
         self.units = wl.B * wl.T * wl.C
         # k, v, gy read and gk, gv written once; w, u read, gw, gu written
+        # (the saved states, 1 byte per token-channel, are not counted)
         self.alg_bytes = 5 * es * self.units + 16 * wl.C
-        self.launches = 3          # forward-in-time pass, reverse pass, batch reduction
+        # the kernel (forward-in-time phase, skipped when saved, then the
+        # reverse phase) and the batch reduction
+        self.launches = 2
         self.dtype = "f32"
         self.io = "bf16" if wl.dtype == "bf16" else "f32"
 
+    def _save_cost(self, dev, n=20):
+        """What saving the states adds to the forward: wkv_forward_save
+        against the chained wkv_forward it runs, per launch, in us."""
+        import torch
+        y = torch.empty_like(self.k)
+        st = torch.empty_like(self.states)
+        stream = torch.cuda.current_stream(dev)
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / n
+        plain = timed(lambda: self.wkv.forward(self.k, self.v, self.w, self.u, out=y, path="chained"))
+        save = timed(lambda: self.wkv.forward_save(self.k, self.v, self.w, self.u, out=y, states=st))
+        return {"forward_chained_us": round(plain, 1), "forward_save_us": round(save, 1),
+                "states_bytes": st.numel() * 4}
+
     def step(self):
-        self.wkv.backward(self.k, self.v, self.w, self.u, self.g, out=self.out, workspace=self.ws)
+        self.wkv.backward(self.k, self.v, self.w, self.u, self.g, out=self.out, workspace=self.ws,
+                          states=self.states)
 
     def check_replay(self):
         """The graph's last outputs equal an eager launch's bit for bit (the
@@ -220,9 +263,14 @@ class BackwardBench:
                 raise RuntimeError("graph replay gradients differ from the eager launch")
 
     def config(self):
-        return {"workload": "wkv_backward (gradients of k, v, w, u) over " + self.wl.name,
-                "B": self.wl.B, "T": self.wl.T, "C": self.wl.C, "io_dtype": self.io,
-                "state_dtype": "f32"}
+        c = {"workload": ("wkv_backward_saved (gradients of k, v, w, u from wkv_forward_save's "
+                          "states) over " if self.saved else
+                          "wkv_backward (gradients of k, v, w, u) over ") + self.wl.name,
+             "B": self.wl.B, "T": self.wl.T, "C": self.wl.C, "io_dtype": self.io,
+             "state_dtype": "f32"}
+        if self.saved:
+            c["saved_states"] = self.save_cost
+        return c
 
     def cpu_baseline(self):
         import oracle
@@ -577,6 +625,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="bf16_main",
                     choices=["tiny", "small_lm", "bf16_main", "bf16_main_gated", "bf16_main_backward",
+                             "bf16_main_backward_saved",
                              "long_ctx", "decode", "token_shift", "hbm_copy", "mat_main",
                              "mat_eagle", "mat_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -601,6 +650,8 @@ def main():
         bench = ForwardBench(synth.BF16_MAIN, dev, gated=True)
     elif args.workload == "bf16_main_backward":
         bench = BackwardBench(synth.BF16_MAIN, dev)
+    elif args.workload == "bf16_main_backward_saved":
+        bench = BackwardBench(synth.BF16_MAIN, dev, saved=True)
     elif args.workload == "decode":
         bench = DecodeBench(dev)
     elif args.workload == "mat_main":
