@@ -1186,25 +1186,16 @@ int chained_waves(int64_t ngroups, int device_cus) {
 }
 
 namespace {
-// The gated kernel holds the receptance of a sub-chunk besides the forward's
-// registers: at 16 waves (128 registers) its bf16 form spilled 7, and 8
-// waves ran it faster (197 against 200-202 us on the bf16 workload).
 template <bool GATED, bool SAVE>
 void launch_chained_t(const ForwardProblem& pr, int nw, dim3 grid, int64_t gpr, int64_t nsub,
                       hipStream_t stream) {
-    if (GATED && nw > 8) nw = 8;
     const dim3 block(nw * 64);
 #define WKV_LAUNCH_CHAINED(DT, V, NW)                                                             \
     hipLaunchKernelGGL((forward_chained_kernel<DT, V, NW, GATED, SAVE>), grid, block, 0, stream, pr, \
                        gpr, nsub)
 #define WKV_CHAINED_NW(DT, V)                                   \
     switch (nw) {                                              \
-        case 16:                                               \
-            if constexpr (!GATED) {                            \
-                WKV_LAUNCH_CHAINED(DT, V, 16);                 \
-                break;                                         \
-            }                                                  \
-            [[fallthrough]];                                   \
+        case 16: WKV_LAUNCH_CHAINED(DT, V, 16); break;         \
         case 8: WKV_LAUNCH_CHAINED(DT, V, 8); break;           \
         case 4: WKV_LAUNCH_CHAINED(DT, V, 4); break;           \
         default: WKV_LAUNCH_CHAINED(DT, V, 2); break;          \
