@@ -795,14 +795,18 @@ __global__ __launch_bounds__(kChunkWaves * 64) void forward_chunked_kernel(Forwa
     const int64_t T = pr.T;
     const int64_t t_begin = j * TILE + int64_t(wave) * L;
     const int n = T - t_begin >= L ? L : (T - t_begin > 0 ? int(T - t_begin) : 0);
+    // lanes past the last channel take lane 0's channels: its data, parameters
+    // and state, so they compute lane 0's values bit for bit and store lane
+    // 0's bytes once more.  No store then needs a branch on the lane (one a
+    // token cost about 1% of the bf16 workload's time)
+    const int64_t cs = active ? c : c0;
 
     Lane<VEC> s;
-    load_params(s, pr, c, active);
+    load_params(s, pr, cs, true);
 
     // k, v of this wave's tokens, kept in registers until y is written
     constexpr int64_t es = sizeof(Raw) / VEC;
     const uint32_t row_bytes = uint32_t(pr.C * es);
-    // lanes past C read lane 0's words (in bounds) and never store
     const uint32_t voff = active ? uint32_t(lane) * uint32_t(sizeof(Raw)) : 0u;
     const int64_t base = ((bb * T + t_begin) * pr.C + c0) * es;
     Raw kr[L], vr[L], rr[GATED ? L : 1];
@@ -864,7 +868,7 @@ __global__ __launch_bounds__(kChunkWaves * 64) void forward_chunked_kernel(Forwa
         const bool last_tile = j == ca.tiles_per_group - 1;
         Part<VEC> x;
         if (j == 0) {
-            load_state(x.a, x.b, x.A, x.m, pr, bb * pr.C + c, active);
+            load_state(x.a, x.b, x.A, x.m, pr, bb * pr.C + cs, true);
         } else {
             if (!last_tile) publish<VEC>(ca, g, j, 0, pre, lane);
             look_back<VEC>(ca, g, j, TILE, s, x, lane);
@@ -914,14 +918,14 @@ __global__ __launch_bounds__(kChunkWaves * 64) void forward_chunked_kernel(Forwa
     const Raw (&rg)[L] = gated_rr<GATED>(rr, kr);
     if (n == L) {
         if (fused)
-            run_block<DT, VEC, L, true, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
+            run_block<DT, VEC, L, true, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, true);
         else
-            run_block<DT, VEC, L, false, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
+            run_block<DT, VEC, L, false, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, true);
     } else {
         if (fused)
-            run_block<DT, VEC, L, true, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
+            run_block<DT, VEC, L, true, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, true);
         else
-            run_block<DT, VEC, L, false, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
+            run_block<DT, VEC, L, false, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, true);
     }
     if (t_begin + n == T && active && pr.a_out != nullptr) store_state(s, pr, bb * pr.C + c);
 }
@@ -1021,12 +1025,14 @@ __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProble
     const int64_t c = c0 + int64_t(lane) * VEC;
     const bool active = c < pr.C;
     const int64_t T = pr.T;
+    // lanes past the last channel mirror lane 0, as on the chunked path
+    const int64_t cs = active ? c : c0;
 
     Lane<VEC> s;
-    load_params(s, pr, c, active);
+    load_params(s, pr, cs, true);
     if (wave == 0) {
         float a[VEC], b[VEC], A[VEC], m[VEC];
-        load_state(a, b, A, m, pr, bb * pr.C + c, active);
+        load_state(a, b, A, m, pr, bb * pr.C + cs, true);
 #pragma unroll
         for (int q = 0; q < VEC; q++) {
             s_carry[0][lane * VEC + q] = a[q];
@@ -1072,7 +1078,7 @@ __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProble
             chain_handoff<VEC>(s, gw, n, sc, nsub, s_carry, &s_seq, lane, after);
             if constexpr (SAVE) save_carry(s, pr, bb, sc, nsub, c, active);
             run_block_weights<DT, VEC, L, GATED>(s, fw, vr, gated_rr<GATED>(rr, kr), kr_, yr_, voff,
-                                                 row_bytes, active);
+                                                 row_bytes, true);
         } else {
             Raw kr[L], vr[L], rr[GATED ? L : 1];
             Part<VEC> gw;
@@ -1094,14 +1100,14 @@ __global__ __launch_bounds__(NWV * 64) void forward_chained_kernel(ForwardProble
             const Raw (&rg)[L] = gated_rr<GATED>(rr, kr);
             if (n == L) {
                 if (fused)
-                    run_block<DT, VEC, L, true, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
+                    run_block<DT, VEC, L, true, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, true);
                 else
-                    run_block<DT, VEC, L, false, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
+                    run_block<DT, VEC, L, false, true, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, true);
             } else {
                 if (fused)
-                    run_block<DT, VEC, L, true, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
+                    run_block<DT, VEC, L, true, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, true);
                 else
-                    run_block<DT, VEC, L, false, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, active);
+                    run_block<DT, VEC, L, false, false, GATED>(s, kr, vr, rg, yr_, voff, row_bytes, n, true);
             }
         }
         if (sc == nsub - 1 && active && pr.a_out != nullptr) {
