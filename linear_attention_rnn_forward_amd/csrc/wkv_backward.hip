@@ -521,10 +521,8 @@ __device__ __forceinline__ bool frames_walk(const RState (&r)[VEC], const float 
                 S[q] += grt[q];
                 SQ[q] = __builtin_fmaf(grt[q], yt[q], SQ[q]);
             }
-            if (active) {
-                Buf<Raw>::store(IO::pack(gkf), gkr_, voff, uint32_t(i) * row_bytes);
-                Buf<Raw>::store(IO::pack(gvf), gvr_, voff, uint32_t(i) * row_bytes);
-            }
+            Buf<Raw>::store(IO::pack(gkf), gkr_, voff, uint32_t(i) * row_bytes);
+            Buf<Raw>::store(IO::pack(gvf), gvr_, voff, uint32_t(i) * row_bytes);
         }
     }
     return true;
@@ -536,7 +534,6 @@ struct Lanes {
     float w[VEC], u[VEC], c[VEC];  // decay, bonus, e^{u-w}
     uint32_t voff, row_bytes;      // byte offset of this lane's channels, of one token
     int lane;
-    bool active;
 };
 
 // The reverse sums' hand-off through LDS: wait for the carry after
@@ -707,11 +704,9 @@ __device__ __forceinline__ GradWU<VEC> token_subchunk(const char* kb, const char
 #pragma unroll
             for (int q = 0; q < VEC; q++)
                 reverse_detail(r[q], to[i][q], kf[q], vf[q], ln.w[q], i > 0, gkf[q], gvf[q], g.gw[q]);
-            if (ln.active) {
-                const uint32_t o = ln.voff + uint32_t(i) * ln.row_bytes;
-                Buf<Raw>::store(IO::pack(gkf), gkr_, o, 0);
-                Buf<Raw>::store(IO::pack(gvf), gvr_, o, 0);
-            }
+            const uint32_t o = ln.voff + uint32_t(i) * ln.row_bytes;
+            Buf<Raw>::store(IO::pack(gkf), gkr_, o, 0);
+            Buf<Raw>::store(IO::pack(gvf), gvr_, o, 0);
         }
     }
     return g;
@@ -761,8 +756,12 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     bool fus = true;
 #pragma unroll
     for (int q = 0; q < VEC; q++) {
-        w[q] = active ? pr.w[c + q] : 1.0f;
-        u[q] = active ? pr.u[c + q] : 0.0f;
+        // lanes past the last channel mirror lane 0 (its channels' data,
+        // parameters and checkpoints): they compute its values bit for bit, so
+        // their gk, gv stores write lane 0's bytes once more and need no
+        // branch; the range checks still ask only lanes that hold a channel
+        w[q] = pr.w[(active ? c : c0) + q];
+        u[q] = pr.u[(active ? c : c0) + q];
         const float wmu = w[q] - u[q];
         fus = fus && __builtin_fabsf(wmu) <= kFusedMaxAbsUW;
         cb[q] = __builtin_amdgcn_exp2f(-wmu * kLog2e);  // e^{u-w}
@@ -805,8 +804,7 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     // vector register holds a per-token offset
     const int64_t gbase = (bb * T * C + c0) * es;
     // checkpoints: [B][nsub][field][C] fp32
-    // (lanes past the last channel read the group's first channel: stand-in
-    // data inside the workspace, never stored)
+    // (lanes past the last channel read the group's first channel's)
     float* ckpt = pr.ckpt + bb * nsub * kCkptFields * C + (active ? c : c0);
 
     // ---------------- phase F: forward carries and checkpoints ----------------
@@ -917,7 +915,6 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     ln.voff = voff;
     ln.row_bytes = row_bytes;
     ln.lane = lane;
-    ln.active = active;
     float* rc = &s_rc[0][0];
     // a carry the frame path has taken but could not use: in the stash (free
     // by then) when there is one
