@@ -503,23 +503,28 @@ __device__ __forceinline__ bool frames_walk(const RState (&r)[VEC], const float 
                 SQ2[q] *= rho[f][q];
             }
         }
+        // the frame's y, gy / den, read in the order they are used, all
+        // before the first is needed: read token by token, each read's LDS
+        // latency stood in the walk's way
+        float yt[F][VEC], grt[F][VEC];
+#pragma unroll
+        for (int j = F - 1; j >= 0; j--) st.get(f * F + j, yt[j], grt[j]);
 #pragma unroll
         for (int j = F - 1; j >= 0; j--) {
             const int i = f * F + j;
-            float vf[VEC], gkf[VEC], gvf[VEC], yt[VEC], grt[VEC];
+            float vf[VEC], gkf[VEC], gvf[VEC];
             IO::unpack(vr[i], vf);
-            st.get(i, yt, grt);
 #pragma unroll
             for (int q = 0; q < VEC; q++) {
                 const float e = te[i][q];
-                const float ed = grt[q] * (e * c[q]);
+                const float ed = grt[j][q] * (e * c[q]);
                 gvf[q] = __builtin_fmaf(e, S[q], ed);
-                gkf[q] = __builtin_fmaf(ed, vf[q] - yt[q], e * __builtin_fmaf(vf[q], S[q], -SQ[q]));
+                gkf[q] = __builtin_fmaf(ed, vf[q] - yt[j][q], e * __builtin_fmaf(vf[q], S[q], -SQ[q]));
                 gw[q] = __builtin_fmaf(-e, __builtin_fmaf(vf[q], S2[q], -SQ2[q]), gw[q]);
                 S2[q] += S[q];
                 SQ2[q] += SQ[q];
-                S[q] += grt[q];
-                SQ[q] = __builtin_fmaf(grt[q], yt[q], SQ[q]);
+                S[q] += grt[j][q];
+                SQ[q] = __builtin_fmaf(grt[j][q], yt[j][q], SQ[q]);
             }
             Buf<Raw>::store(IO::pack(gkf), gkr_, voff, uint32_t(i) * row_bytes);
             Buf<Raw>::store(IO::pack(gvf), gvr_, voff, uint32_t(i) * row_bytes);
