@@ -311,21 +311,23 @@ struct FrameStore<2, true> {
     }
 };
 
-// The forward re-run of a full sub-chunk in frames from the checkpoint s0: the
-// sub-chunk's gu term (returned in gu, for the caller to add once the walk has
-// succeeded too) and its own partial of the reverse sums.  Returns false for
-// the whole wave when some lane's values leave the range.
+// The forward re-run of a full sub-chunk in frames from the checkpoint s0:
+// the sub-chunk's own partial of the reverse sums.  Returns false for the
+// whole wave when some lane's values leave the range.
 template <typename IO, int L, int VEC, typename Raw, typename Store>
 __device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw (&kr)[L],
                                              const Raw (&vr)[L], const Raw (&gyr)[L],
                                              const float (&w)[VEC], const float (&c)[VEC],
                                              float (&te)[L][VEC], Store& st, float (&G)[kBwdFrames][VEC],
                                              float (&rho)[kBwdFrames][VEC], RState (&rg)[VEC],
-                                             float (&gu)[VEC], bool active) {
+                                             bool active) {
     constexpr int F = kBwdFrame, NF = kBwdFrames;
     static_assert(L == F * NF, "whole frames");
-    float M[NF][VEC];
-    // frame keys and frame maxima; then e^{x - M}
+    // frame keys x and frame maxima M; the frame anchors G, each the larger of
+    // M and the history's exponent H at the frame's start (H of the first
+    // frame from the checkpoint, of the next G - F w); then the weights
+    // e^{x - G}, all at most 1
+    float M[NF][VEC], H0[VEC];
 #pragma unroll
     for (int f = 0; f < NF; f++) {
 #pragma unroll
@@ -340,19 +342,32 @@ __device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw 
                 M[f][q] = j == 0 ? x : max_num(M[f][q], x);
             }
         }
+    }
+#pragma unroll
+    for (int q = 0; q < VEC; q++) {
+        H0[q] = __builtin_fmaf(-s0[q].m, w[q], s0[q].A);
+        float h = H0[q];
+#pragma unroll
+        for (int f = 0; f < NF; f++) {
+            G[f][q] = max_num(h, M[f][q]);
+            h = __builtin_fmaf(-float(F), w[q], G[f][q]);
+        }
+    }
+#pragma unroll
+    for (int f = 0; f < NF; f++) {
 #pragma unroll
         for (int j = 0; j < F; j++) {
             const int i = f * F + j;
 #pragma unroll
             for (int q = 0; q < VEC; q++)
-                te[i][q] = __builtin_amdgcn_exp2f((te[i][q] - M[f][q]) * kLog2e);
+                te[i][q] = __builtin_amdgcn_exp2f((te[i][q] - G[f][q]) * kLog2e);
         }
     }
     // per frame: the sums of gr and gr y over its tokens, and the same
     // weighted by the token's place in the sub-chunk; they enter the partial
     // (P, Q, R, U, at the first frame's anchor) with pi, the product of the
     // factors rho of the frames before
-    float a[VEC], b[VEC], H[VEC], gut[VEC], pi[VEC], sg[VEC], sq[VEC], sgi[VEC], sqi[VEC];
+    float a[VEC], b[VEC], pi[VEC], sg[VEC], sq[VEC], sgi[VEC], sqi[VEC];
     float P[VEC], Q[VEC], R[VEC], U[VEC];
     float grmax = 0.0f, emin = 1.0f;
     bool ok = true;
@@ -360,23 +375,20 @@ __device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw 
     for (int q = 0; q < VEC; q++) {
         a[q] = s0[q].a;
         b[q] = s0[q].b;
-        H[q] = __builtin_fmaf(-s0[q].m, w[q], s0[q].A);
-        gut[q] = 0.0f;
         pi[q] = 1.0f;
         P[q] = Q[q] = R[q] = U[q] = 0.0f;
     }
 #pragma unroll
     for (int f = 0; f < NF; f++) {
-        float beta[VEC];
 #pragma unroll
         for (int q = 0; q < VEC; q++) {
-            const float d = H[q] - M[f][q];
-            const float e = exp_neg_abs(d);
-            const bool keep = d >= 0.0f;
-            const float alpha = keep ? 1.0f : e;
-            beta[q] = keep ? e : 1.0f;
-            G[f][q] = keep ? H[q] : M[f][q];
-            ok &= max_num(alpha * b[q], beta[q] * te[f * F][q]) >= kBwdTermMin;
+            // the history's sums move to the frame's anchor: e^{H - G} <= 1.
+            // For a later frame H = G_{f-1} - F w, and the same factor
+            // carries the frame's reverse sums into the frame before (rho)
+            const float x = f == 0 ? H0[q] - G[0][q]
+                                   : __builtin_fmaf(-float(F), w[q], G[f - 1][q] - G[f][q]);
+            const float alpha = __builtin_amdgcn_exp2f(x * kLog2e);
+            ok &= max_num(alpha * b[q], te[f * F][q]) >= kBwdTermMin;
             a[q] *= alpha;
             b[q] *= alpha;
             sg[q] = 0.0f;
@@ -384,11 +396,8 @@ __device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw 
             sgi[q] = 0.0f;
             sqi[q] = 0.0f;
             if (f > 0) {
-                // rho[f-1]: this frame's sums carried into the one before,
-                // e^{G_{f-1} - F w - G_f} <= 1
-                rho[f - 1][q] = __builtin_amdgcn_exp2f(
-                    __builtin_fmaf(-float(F), w[q], G[f - 1][q] - G[f][q]) * kLog2e);
-                pi[q] *= rho[f - 1][q];
+                rho[f - 1][q] = alpha;
+                pi[q] *= alpha;
             }
         }
         if (__builtin_amdgcn_ballot_w64(!ok & active) != 0) return false;
@@ -401,13 +410,12 @@ __device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw 
             float yt[VEC], grt[VEC];
 #pragma unroll
             for (int q = 0; q < VEC; q++) {
-                const float et = te[i][q] * beta[q];
+                const float et = te[i][q];
                 const float ec = et * c[q];
                 const float rd = fast_rcp(b[q] + ec);
                 const float y = __builtin_fmaf(ec, vf[q], a[q]) * rd;
                 const float gr = gf[q] * rd;
                 const float gry = gr * y;
-                gut[q] = __builtin_fmaf(gr * ec, vf[q] - y, gut[q]);
                 a[q] = __builtin_fmaf(et, vf[q], a[q]);
                 b[q] += et;
                 sg[q] += gr;
@@ -416,7 +424,6 @@ __device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw 
                 sqi[q] = __builtin_fmaf(float(i), gry, sqi[q]);
                 grmax = max_num(grmax, __builtin_fabsf(gr));
                 emin = min_num(emin, et);
-                te[i][q] = et;
                 yt[q] = y;
                 grt[q] = gr;
             }
@@ -426,8 +433,8 @@ __device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw 
             // values at once
 #pragma unroll
             for (int q = 0; q < VEC; q++)
-                asm volatile("" : "+v"(a[q]), "+v"(b[q]), "+v"(gut[q]), "+v"(sg[q]), "+v"(sq[q]),
-                             "+v"(sgi[q]), "+v"(sqi[q]));
+                asm volatile("" : "+v"(a[q]), "+v"(b[q]), "+v"(sg[q]), "+v"(sq[q]), "+v"(sgi[q]),
+                             "+v"(sqi[q]));
         }
 #pragma unroll
         for (int q = 0; q < VEC; q++) {
@@ -435,7 +442,6 @@ __device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw 
             Q[q] = __builtin_fmaf(pi[q], sq[q], Q[q]);
             R[q] = __builtin_fmaf(pi[q], sgi[q], R[q]);
             U[q] = __builtin_fmaf(pi[q], sqi[q], U[q]);
-            H[q] = __builtin_fmaf(-float(F), w[q], G[f][q]);  // the next frame's history
         }
     }
     // gy / den beyond 2^100 (or not finite), or a weight below fp32's
@@ -453,15 +459,15 @@ __device__ __forceinline__ bool frames_rerun(const FState (&s0)[VEC], const Raw 
         rg[q].U = U[q];
         rg[q].Pi = -G[0][q];
         rg[q].n = 0.0f;
-        gu[q] = gut[q];
     }
     return true;
 }
 
 // The walk of a frame-weight sub-chunk from the carry r after it (exponent
 // r.Pi - r.n w at the sub-chunk's last token): gk, gv of every token, and the
-// sub-chunk's gw term in gw (for the caller to add).  Returns false, writing
-// nothing, when the carried-in sums overflow fp32 for some lane of the wave.
+// sub-chunk's gw and gu terms in gw, gu (for the caller to add).  Returns
+// false, writing nothing, when the carried-in sums overflow fp32 for some lane
+// of the wave.
 template <typename IO, int L, int VEC, typename Raw, typename Store>
 __device__ __forceinline__ bool frames_walk(const RState (&r)[VEC], const float (&te)[L][VEC],
                                             const Store& st,
@@ -469,7 +475,7 @@ __device__ __forceinline__ bool frames_walk(const RState (&r)[VEC], const float 
                                             const float (&rho)[kBwdFrames][VEC], const Raw (&vr)[L],
                                             const float (&w)[VEC], const float (&c)[VEC],
                                             rsrc_t gkr_, rsrc_t gvr_, uint32_t voff, uint32_t row_bytes,
-                                            bool active, float (&gw)[VEC]) {
+                                            bool active, float (&gw)[VEC], float (&gu)[VEC]) {
     constexpr int F = kBwdFrame, NF = kBwdFrames;
     // S, SQ: the sums of gr, gr y over the later tokens; S2, SQ2 the same
     // weighted by the distance past the current token (both in frame
@@ -490,6 +496,7 @@ __device__ __forceinline__ bool frames_walk(const RState (&r)[VEC], const float 
         ok &= __builtin_isfinite(S[q]) & __builtin_isfinite(SQ[q]) & __builtin_isfinite(S2[q]) &
               __builtin_isfinite(SQ2[q]);
         gw[q] = 0.0f;
+        gu[q] = 0.0f;
     }
     if (__builtin_amdgcn_ballot_w64(!ok & active) != 0) return false;
 #pragma unroll
@@ -516,10 +523,14 @@ __device__ __forceinline__ bool frames_walk(const RState (&r)[VEC], const float 
             IO::unpack(vr[i], vf);
 #pragma unroll
             for (int q = 0; q < VEC; q++) {
+                // the bonus term gr e c (v - y) is the token's own part of
+                // gk and its whole gu
                 const float e = te[i][q];
                 const float ed = grt[j][q] * (e * c[q]);
+                const float own = ed * (vf[q] - yt[j][q]);
                 gvf[q] = __builtin_fmaf(e, S[q], ed);
-                gkf[q] = __builtin_fmaf(ed, vf[q] - yt[j][q], e * __builtin_fmaf(vf[q], S[q], -SQ[q]));
+                gkf[q] = __builtin_fmaf(e, __builtin_fmaf(vf[q], S[q], -SQ[q]), own);
+                gu[q] += own;
                 gw[q] = __builtin_fmaf(-e, __builtin_fmaf(vf[q], S2[q], -SQ2[q]), gw[q]);
                 S2[q] += S[q];
                 SQ2[q] += SQ[q];
@@ -976,12 +987,13 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
                 }
                 float G[kBwdFrames][VEC], rho[kBwdFrames][VEC], gwt[VEC], gut[VEC];
                 RState rg[VEC];
-                if (frames_rerun<IO, L, VEC>(s, kr, vr, gyr, w, cb, te, st, G, rho, rg, gut, active)) {
+                if (frames_rerun<IO, L, VEC>(s, kr, vr, gyr, w, cb, te, st, G, rho, rg, active)) {
                     RState r[VEC];
                     rev_handoff(rc, &s_rseq, ln, rg, r, j, sc, n);
                     const rsrc_t gkr_ = make_rsrc(at_out(pr.gk, sc));
                     const rsrc_t gvr_ = make_rsrc(at_out(pr.gv, sc));
-                    if (frames_walk<IO, L, VEC>(r, te, st, G, rho, vr, w, cb, gkr_, gvr_, voff, row_bytes, active, gwt)) {
+                    if (frames_walk<IO, L, VEC>(r, te, st, G, rho, vr, w, cb, gkr_, gvr_, voff, row_bytes, active, gwt,
+                                                gut)) {
 #pragma unroll
                         for (int q = 0; q < VEC; q++) {
                             gw[q] += gwt[q];
