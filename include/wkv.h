@@ -299,8 +299,8 @@ int wkv_session_load(int64_t L, int64_t S, int64_t C, int dtype, int64_t seq,
  *   gw, gu      [C] fp32            outputs; zero when T = 0
  *   workspace   device memory of wkv_backward_workspace_size(B, T, C) bytes,
  *               256-byte aligned (NULL allowed when T = 0); it holds the
- *               forward state before every 16-token sub-chunk (4 fp32 per
- *               channel, 1 byte per token-channel) and per-column partial
+ *               forward state before every 16-token sub-chunk (2 fp32 per
+ *               channel, half a byte per token-channel) and per-column partial
  *               sums, and is overwritten
  * No output may overlap any input, another output or the workspace.
  * Arithmetic is fp32 with every exponential of a non-positive argument;
@@ -322,12 +322,15 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, int dtype,
  *
  * wkv_forward_save: wkv_forward from the empty history (no state in or out)
  * that also writes
- *   states      [B][ceil(T/16)][4][C] fp32 device array,
+ *   states      [B][ceil(T/16)][2][C] fp32 device array,
  *               wkv_saved_states_bytes(B, T, C) bytes, 8-byte aligned: for
  *               sub-chunk s (tokens 16 s .. 16 s + 15) of row b the
- *               recurrence's state before its first token, in the anchor
- *               form (a, b, A, m): the history sums scaled by e^{-p},
- *               p = A - m w.  No chunk of it may overlap an input or y.
+ *               recurrence's state before its first token as two numbers
+ *               per channel: r, the history's weighted mean of v (a / b),
+ *               and q, the log of its total weight (p + ln b), so that the
+ *               history sums are r e^q and e^q; the empty history (s = 0)
+ *               is r = 0, q = -1e38.  No chunk of it may overlap an input
+ *               or y.
  * It always runs the chained path (one workgroup per group of 64 or 128
  * channels of a row); k, v, y, w, u and the errors are as for wkv_forward.
  *
@@ -447,7 +450,7 @@ int wkv_abi_version(void);
  */
 int wkv_bounded_wait_failures(uint64_t *count);
 
-#define WKV_ABI_VERSION 106
+#define WKV_ABI_VERSION 107
 
 #ifdef __cplusplus
 }

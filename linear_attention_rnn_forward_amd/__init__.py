@@ -24,6 +24,7 @@ import threading
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwkv.so")
+ABI_VERSION = 107  # WKV_ABI_VERSION of include/wkv.h that this binding follows
 
 F32 = 0
 BF16 = 1
@@ -115,6 +116,12 @@ def lib() -> ctypes.CDLL:
         L.wkv_forward_auto_path.argtypes = [i64, i64, i64, i32]
         L.wkv_bounded_wait_failures.restype = i32
         L.wkv_bounded_wait_failures.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
+        got = int(L.wkv_abi_version())
+        if got != ABI_VERSION:
+            # buffer sizes and layouts (the saved states among them) differ
+            # between versions: refuse rather than pass mis-sized buffers
+            raise RuntimeError(f"{LIB_PATH} has ABI version {got}, this binding needs {ABI_VERSION}: "
+                               "rebuild it with __graft_entry__.build()")
         _lib = L
     return _lib
 
@@ -304,14 +311,15 @@ SAVED_STATE_TOKENS = 16
 
 
 def saved_states_shape(B: int, T: int, C: int):
-    """Shape of forward_save's states: [B, ceil(T/16), 4, C] float32."""
-    return (B, (T + SAVED_STATE_TOKENS - 1) // SAVED_STATE_TOKENS, 4, C)
+    """Shape of forward_save's states: [B, ceil(T/16), 2, C] float32 (r, q per
+    channel: the history sums are r e^q and e^q)."""
+    return (B, (T + SAVED_STATE_TOKENS - 1) // SAVED_STATE_TOKENS, 2, C)
 
 
 def forward_save(k, v, w, u, out=None, states=None):
     """forward(k, v, w, u) from the empty history that also saves the state
     before every 16-token sub-chunk (wkv_forward_save), for backward(...,
-    states=...).  Returns (y, states); states is [B, ceil(T/16), 4, C]
+    states=...).  Returns (y, states); states is [B, ceil(T/16), 2, C]
     float32."""
     torch = _torch()
     _need(k, "k")

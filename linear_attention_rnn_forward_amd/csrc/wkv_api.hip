@@ -85,9 +85,9 @@ int check_state_aliasing(const Range* outs, int nouts, const Range* ins, int nin
     return WKV_OK;
 }
 
-// Bytes of the saved states of a [B, T, C] problem: fp32 [B][ceil(T/16)][4][C].
+// Bytes of the saved states of a [B, T, C] problem: fp32 [B][ceil(T/16)][2][C].
 int64_t saved_state_bytes(int64_t B, int64_t T, int64_t C) {
-    return B * ((T + WKV_SAVED_STATE_TOKENS - 1) / WKV_SAVED_STATE_TOKENS) * 4 * C * 4;
+    return B * ((T + WKV_SAVED_STATE_TOKENS - 1) / WKV_SAVED_STATE_TOKENS) * 2 * C * 4;
 }
 
 // r == nullptr: plain forward; else the gated form (y = sigmoid(r) * wkv).

@@ -61,7 +61,7 @@ namespace {
 
 constexpr int kBwdTokens = 16;  // tokens per sub-chunk
 static_assert(kBwdTokens == WKV_SAVED_STATE_TOKENS, "saved states are the checkpoints");
-constexpr int kCkptFields = 4;  // a, b, anchor, count
+constexpr int kCkptFields = 2;  // r, q (to_saved)
 
 __device__ __forceinline__ int bwd_wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int bwd_lane_id() { return threadIdx.x & 63; }
@@ -591,15 +591,14 @@ __device__ __forceinline__ void rev_handoff(float* s_rc, int* s_rseq, const Lane
     }
 }
 
-// The checkpoint (state before the sub-chunk) of this lane's channels.
+// The checkpoint (state before the sub-chunk) of this lane's channels, from
+// its saved form (r, q): (a, b, A, m) = (r, 1, q, 0), or the empty history.
 template <int VEC>
 __device__ __forceinline__ void load_checkpoint(FState (&s)[VEC], const float* ck, int64_t C) {
 #pragma unroll
     for (int q = 0; q < VEC; q++) {
-        s[q].a = ck[0 * C + q];
-        s[q].b = ck[1 * C + q];
-        s[q].A = ck[2 * C + q];
-        s[q].m = ck[3 * C + q];
+        from_saved(ck[0 * C + q], ck[1 * C + q], s[q].a, s[q].b, s[q].A);
+        s[q].m = 0.0f;
     }
 }
 
@@ -748,7 +747,7 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     using Raw = typename IO::Raw;
     constexpr int L = kBwdTokens;
     constexpr int CG = 64 * VEC;
-    __shared__ float s_fc[kCkptFields][CG];  // forward carry before sub-chunk s_fseq
+    __shared__ float s_fc[4][CG];  // forward carry (a, b, A, m) before sub-chunk s_fseq
     __shared__ float s_rc[6][CG];            // reverse carry after sub-chunk nsub-1-s_rseq
     __shared__ float s_red[2][NWV][CG];      // per-wave gw, gu
     __shared__ int s_fseq, s_rseq;
@@ -819,7 +818,7 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     // second part as the buffer instructions' scalar offset, so that no
     // vector register holds a per-token offset
     const int64_t gbase = (bb * T * C + c0) * es;
-    // checkpoints: [B][nsub][field][C] fp32
+    // checkpoints: [B][nsub][r, q][C] fp32
     // (lanes past the last channel read the group's first channel's)
     float* ckpt = pr.ckpt + bb * nsub * kCkptFields * C + (active ? c : c0);
 
@@ -907,10 +906,10 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
             float* ck = ckpt + sc * kCkptFields * C;
 #pragma unroll
             for (int q = 0; q < VEC; q++) {
-                ck[0 * C + q] = x[q].a;
-                ck[1 * C + q] = x[q].b;
-                ck[2 * C + q] = x[q].A;
-                ck[3 * C + q] = x[q].m;
+                float r, qs;
+                to_saved(x[q].a, x[q].b, __builtin_fmaf(-x[q].m, w[q], x[q].A), r, qs);
+                ck[0 * C + q] = r;
+                ck[1 * C + q] = qs;
             }
         }
     }

@@ -71,6 +71,23 @@ __device__ __forceinline__ float exp_neg_abs(float d) {
 }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// A state kept between kernels in two numbers per channel: r = a / b, the
+// history's weighted mean of v, and q = p + ln b, the log of its total weight
+// (so a e^p = r e^q and b e^p = e^q: the same state, one rounding each).  The
+// empty history is (0, kEmptyP).
+constexpr float kLn2 = 0.6931471805599453f;
+__device__ __forceinline__ void to_saved(float a, float b, float p, float& r, float& q) {
+    const bool empty = !(b > 0.0f);
+    r = empty ? 0.0f : a * fast_rcp(b);
+    q = empty ? kEmptyP : __builtin_fmaf(__builtin_amdgcn_logf(b), kLn2, p);
+}
+__device__ __forceinline__ void from_saved(float r, float q, float& a, float& b, float& p) {
+    const bool empty = q <= kEmptyIn;
+    a = r;
+    b = empty ? 0.0f : 1.0f;
+    p = empty ? kEmptyP : q;
+}
+
 // 1 + e^{-r}: the receptance gate sigmoid(r) = 1 / (1 + e^{-r}) is applied as
 // a factor of the read-out's denominator.
 __device__ __forceinline__ float gate_den(float r) { return 1.0f + __builtin_amdgcn_exp2f(-r * kLog2e); }

@@ -983,25 +983,25 @@ __device__ __forceinline__ void chain_handoff(Lane<VEC>& s, const Part<VEC>& gw,
 }
 
 // The carry of sub-chunk sc (the state before it, in s) to pr.states
-// [B][nsub][a, b, A, m][C]: the backward's checkpoints.
+// [B][nsub][r, q][C] (to_saved): the backward's checkpoints.
 template <int VEC>
 __device__ __forceinline__ void save_carry(const Lane<VEC>& s, const ForwardProblem& pr, int64_t bb,
                                            int64_t sc, int64_t nsub, int64_t c, bool active) {
     if (!active) return;
-    float* o = pr.states + (bb * nsub + sc) * 4 * pr.C + c;
+    float* o = pr.states + (bb * nsub + sc) * 2 * pr.C + c;
+    float r[VEC], q[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; i++)
+        to_saved(s.a[i], s.b[i], __builtin_fmaf(-s.m[i], s.ch[i].w, s.A[i]), r[i], q[i]);
     if constexpr (VEC == 2) {
         // one 8-byte store per field (c is even and the rows 8-byte aligned)
-        *reinterpret_cast<float2*>(o + 0 * pr.C) = make_float2(s.a[0], s.a[1]);
-        *reinterpret_cast<float2*>(o + 1 * pr.C) = make_float2(s.b[0], s.b[1]);
-        *reinterpret_cast<float2*>(o + 2 * pr.C) = make_float2(s.A[0], s.A[1]);
-        *reinterpret_cast<float2*>(o + 3 * pr.C) = make_float2(s.m[0], s.m[1]);
+        *reinterpret_cast<float2*>(o + 0 * pr.C) = make_float2(r[0], r[1]);
+        *reinterpret_cast<float2*>(o + 1 * pr.C) = make_float2(q[0], q[1]);
     } else {
 #pragma unroll
-        for (int q = 0; q < VEC; q++) {
-            o[0 * pr.C + q] = s.a[q];
-            o[1 * pr.C + q] = s.b[q];
-            o[2 * pr.C + q] = s.A[q];
-            o[3 * pr.C + q] = s.m[q];
+        for (int i = 0; i < VEC; i++) {
+            o[0 * pr.C + i] = r[i];
+            o[1 * pr.C + i] = q[i];
         }
     }
 }

@@ -41,7 +41,7 @@ def test_header_lists_the_boundary_calls():
 
 def test_abi_version_and_status_strings():
     L = wkv.lib()
-    assert L.wkv_abi_version() == 106
+    assert L.wkv_abi_version() == 107
     for code in range(0, -9, -1):
         assert L.wkv_status_string(code).decode()
     assert L.wkv_status_string(-100).decode() == "unknown status"
@@ -224,12 +224,12 @@ def test_session_save_checks_arguments():
 
 
 def test_backward_workspace_size():
-    """The forward state before every 16-token sub-chunk (4 fp32 per column)
+    """The forward state before every 16-token sub-chunk (2 fp32 per column)
     plus per-column gw, gu partials, each section rounded up to 256 bytes."""
     L = wkv.lib()
-    assert L.wkv_backward_workspace_size(2, 3, 64) == 2048 + 2 * 512
-    assert L.wkv_backward_workspace_size(2, 17, 64) == 2 * 2048 + 2 * 512
-    assert L.wkv_backward_workspace_size(16, 4096, 2048) == 16 * 2048 * 256 * 16 + 2 * 16 * 2048 * 4
+    assert L.wkv_backward_workspace_size(2, 3, 64) == 1024 + 2 * 512
+    assert L.wkv_backward_workspace_size(2, 17, 64) == 2 * 1024 + 2 * 512
+    assert L.wkv_backward_workspace_size(16, 4096, 2048) == 16 * 2048 * 256 * 8 + 2 * 16 * 2048 * 4
     assert L.wkv_backward_workspace_size(1, 1, 1) == 3 * 256
     assert L.wkv_backward_workspace_size(0, 8, 8) == 0
     assert L.wkv_backward_workspace_size(1 << 40, 1 << 40, 8) == 0
@@ -264,18 +264,18 @@ def test_backward_rejects_bad_arguments():
 
 
 def test_saved_state_sizes():
-    """[B][ceil(T/16)][4][C] fp32 states; the saved backward's workspace is
+    """[B][ceil(T/16)][2][C] fp32 states; the saved backward's workspace is
     only the per-column partials."""
     L = wkv.lib()
-    assert L.wkv_saved_states_bytes(2, 3, 64) == 2 * 1 * 4 * 64 * 4
-    assert L.wkv_saved_states_bytes(2, 17, 64) == 2 * 2 * 4 * 64 * 4
-    assert L.wkv_saved_states_bytes(16, 4096, 2048) == 16 * 256 * 4 * 2048 * 4
+    assert L.wkv_saved_states_bytes(2, 3, 64) == 2 * 1 * 2 * 64 * 4
+    assert L.wkv_saved_states_bytes(2, 17, 64) == 2 * 2 * 2 * 64 * 4
+    assert L.wkv_saved_states_bytes(16, 4096, 2048) == 16 * 256 * 2 * 2048 * 4
     assert L.wkv_saved_states_bytes(1, 0, 8) == 0
     assert L.wkv_saved_states_bytes(0, 8, 8) == 0
     assert L.wkv_backward_saved_workspace_size(2, 64) == 2 * 512
     assert L.wkv_backward_saved_workspace_size(16, 2048) == 2 * 16 * 2048 * 4
     assert L.wkv_backward_saved_workspace_size(0, 8) == 0
-    assert wkv.saved_states_shape(2, 17, 64) == (2, 2, 4, 64)
+    assert wkv.saved_states_shape(2, 17, 64) == (2, 2, 2, 64)
 
 
 def test_forward_save_rejects_bad_arguments():

@@ -45,15 +45,15 @@ def test_forward_save_output_and_states(device, shape, dtype):
     y, st = wkv.forward_save(kd, vd, wd, ud)
     torch.cuda.synchronize()
     assert torch.equal(y, y_ref)
-    st = st.cpu().numpy().astype(np.float64)          # [B, nsub, 4, C]
-    assert st.shape == (B, (T + 15) // 16, 4, C)
-    w = x.w.astype(np.float64)
-    # sub-chunk 0 starts from the empty history
-    assert np.all(st[:, 0, 0] == 0) and np.all(st[:, 0, 1] == 0)
+    st = st.cpu().numpy().astype(np.float64)          # [B, nsub, 2, C]: r, q
+    assert st.shape == (B, (T + 15) // 16, 2, C)
+    # sub-chunk 0 starts from the empty history: r = 0, q at the empty exponent
+    assert np.all(st[:, 0, 0] == 0) and np.all(st[:, 0, 1] <= -1e37)
     for s in range(1, st.shape[1]):
         _, ref = oracle.forward(x.k[:, :16 * s], x.v[:, :16 * s], x.w, x.u)
-        a, b, A, m = st[:, s, 0], st[:, s, 1], st[:, s, 2], st[:, s, 3]
-        ea, eb, _ = state_mismatch((a, b, A - m * w), ref)
+        # the history sums are r e^q and e^q: the state (a, b, p) = (r, 1, q)
+        r, q = st[:, s, 0], st[:, s, 1]
+        ea, eb, _ = state_mismatch((r, np.ones_like(r), q), ref)
         assert ea <= 1e-4 and eb <= 1e-4, (s, ea, eb)
 
 
