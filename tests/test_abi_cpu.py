@@ -41,10 +41,21 @@ def test_header_lists_the_boundary_calls():
 
 def test_abi_version_and_status_strings():
     L = wkv.lib()
-    assert L.wkv_abi_version() == 107
+    assert L.wkv_abi_version() == 107 == wkv.ABI_VERSION
     for code in range(0, -9, -1):
         assert L.wkv_status_string(code).decode()
     assert L.wkv_status_string(-100).decode() == "unknown status"
+
+
+def test_binding_refuses_another_abi_version(monkeypatch):
+    """Buffer layouts (the saved states among them) change with the ABI
+    version, so the binding will not drive a library built for another."""
+    monkeypatch.setattr(wkv, "_lib", None)
+    monkeypatch.setattr(wkv, "ABI_VERSION", wkv.ABI_VERSION + 1)
+    with pytest.raises(RuntimeError, match="ABI version"):
+        wkv.lib()
+    monkeypatch.undo()
+    assert wkv.lib().wkv_abi_version() == wkv.ABI_VERSION
 
 
 P = ctypes.c_void_p
