@@ -16,6 +16,25 @@ CT = 16       # tokens per chunk
 PREFETCH = 4  # chunks in the register ring
 
 
+def paired_task(bid, n):
+    """Workgroup -> (batch row, head) task of the forward kernels: heads 2j,
+    2j + 1 on workgroups j, j + n/2 (plain order for an odd count)."""
+    if n % 2:
+        return bid
+    half = n // 2
+    return 2 * bid if bid < half else 2 * (bid - half) + 1
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 7, 8, 64, 511, 512])
+def test_paired_task_is_a_bijection(n):
+    tasks = [paired_task(b, n) for b in range(n)]
+    assert sorted(tasks) == list(range(n))
+    if n % 2 == 0:
+        # the two halves of each 256-byte row piece are half a grid apart
+        for j in range(n // 2):
+            assert (tasks[j], tasks[j + n // 2]) == (2 * j, 2 * j + 1)
+
+
 def forward_offsets(B, T, H):
     """(loads, stores, state) element offsets of mat_forward_tokens_kernel:
     512 threads per (batch row, head); waves 4..7 load (producers), waves 0..3
@@ -24,7 +43,7 @@ def forward_offsets(B, T, H):
     loads, stores, state = [], [], []
     nch = (T + CT - 1) // CT
     for blk in range(B * H):
-        bb, h = divmod(blk, H)
+        bb, h = divmod(paired_task(blk, B * H), H)
         row0 = bb * T
         for thr in range(512):
             wave, lane = divmod(thr, 64)
@@ -115,7 +134,7 @@ def ring_offsets(B, T, H, per_token_z=True, strict_size=True):
     nch = (T + CT - 1) // CT
     loads, ystores, tiles = [], [], []
     for blk in range(B * H):
-        bb, h = divmod(blk, H)
+        bb, h = divmod(paired_task(blk, B * H), H)
         row0 = bb * T
         for p in range(4):                       # producer wave p (waves 4..7)
             chunks = []
