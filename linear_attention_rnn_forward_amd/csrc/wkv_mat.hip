@@ -458,7 +458,8 @@ __global__ __launch_bounds__(512, 4) void mat_forward_tokens_kernel(MatProblem p
 // then across the four lane groups.
 // ---------------------------------------------------------------------------
 
-constexpr int kSlots = 4;                       // ring slots: one per producer wave
+constexpr int kProducers = 4;                   // producer waves (chunk q to wave q mod 4)
+constexpr int kSlots = 6;                       // ring slots (chunk q to slot q mod 6)
 constexpr uint64_t kRingSpinTicks = 20000000;   // 200 ms of the 100 MHz real-time counter
 constexpr int kProducerSleep = 4;               // producers wait for a free slot at a slower poll
 
@@ -587,8 +588,9 @@ __device__ __forceinline__ void ring_produce(const MatProblem& pr, MatRing& sh, 
     const int64_t T = pr.T;
     const int g = lane >> 4, n = lane & 15;
     const int s = int(q % kSlots);
-    // the slot is free once the consumers are done with the chunk four back;
-    // that chunk's y tile goes out first (the chunks ahead leave time for it)
+    // the slot is free once the consumers are done with its previous chunk,
+    // kSlots back; that chunk's y tile goes out first (the chunks ahead leave
+    // time for it)
     ring_wait<kProducerSleep>(sh, &sh.done[s], 4 * int(q / kSlots));
     ring_store_tile(pr, sh, s, q - kSlots, q >= kSlots, lane, row0, h);
     const int live = chunk_tokens(T, q);   // tokens of the chunk; 4g + j >= live is padding
@@ -747,18 +749,21 @@ __global__ __launch_bounds__(512, 4) void mat_forward_ring_kernel(MatProblem pr)
         // two register sets: the wave's next chunk loads while this one is prepared
         RawChunk xa, xb;
         ring_load<PER_TOKEN_Z>(xa, pr, row0, h, p, nch, voff);
-        for (int64_t q = p; q < nch; q += 2 * kSlots) {
-            ring_load<PER_TOKEN_Z>(xb, pr, row0, h, q + kSlots, nch, voff);
+        for (int64_t q = p; q < nch; q += 2 * kProducers) {
+            ring_load<PER_TOKEN_Z>(xb, pr, row0, h, q + kProducers, nch, voff);
             ring_produce<PER_TOKEN_Z>(pr, sh, xa, dc, lane, row0, h, q);
-            if (q + kSlots >= nch) break;
-            ring_load<PER_TOKEN_Z>(xa, pr, row0, h, q + 2 * kSlots, nch, voff);
-            ring_produce<PER_TOKEN_Z>(pr, sh, xb, dc, lane, row0, h, q + kSlots);
+            if (q + kProducers >= nch) break;
+            ring_load<PER_TOKEN_Z>(xa, pr, row0, h, q + 2 * kProducers, nch, voff);
+            ring_produce<PER_TOKEN_Z>(pr, sh, xb, dc, lane, row0, h, q + kProducers);
         }
-        // the wave's last chunk: its y tile once the consumers are done with it
-        if (p < nch) {
-            const int64_t last = p + (nch - 1 - p) / kSlots * kSlots;
-            ring_wait<kProducerSleep>(sh, &sh.done[p], 4 * int(last / kSlots + 1));
-            ring_store_tile(pr, sh, p, last, true, lane, row0, h);
+        // each slot's last chunk (slot s by producer s mod 4): its y tile once
+        // the consumers are done with it
+        for (int s = p; s < kSlots; s += kProducers) {
+            if (s < nch) {
+                const int64_t last = s + (nch - 1 - s) / kSlots * kSlots;
+                ring_wait<kProducerSleep>(sh, &sh.done[s], 4 * int(last / kSlots + 1));
+                ring_store_tile(pr, sh, s, last, true, lane, row0, h);
+            }
         }
     } else {
         // chunks in pairs: the two chunks' products are independent but for

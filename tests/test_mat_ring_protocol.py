@@ -1,12 +1,13 @@
 """Host model of the hand-over in mat_forward_ring_kernel (csrc/wkv_mat.hip).
 
-Four producer waves and four consumer waves share a ring of four LDS slots.
-Producer p prepares chunks p, p + 4, ...: it waits until the slot's `done`
-count reaches 4 * (q / 4) (the consumers are through the chunk four back),
-writes that chunk's y tile out of the slot (unless it ran token by token),
-writes the new operands and the chunk's form flag, and publishes `ready`.
-After its last chunk it waits for the consumers once more and writes that
-tile.  The consumer waves take the chunks in pairs, each waiting for `ready`,
+Four producer waves and four consumer waves share a ring of six LDS slots
+(chunk q in slot q mod 6).  Producer p prepares chunks p, p + 4, ...: it
+waits until the slot's `done` count reaches 4 * (q / 6) (the consumers are
+through the slot's previous chunk, six back), writes that chunk's y tile out
+of the slot (unless it ran token by token), writes the new operands and the
+chunk's form flag, and publishes `ready`.  After its chunks it waits for the
+consumers once more on each slot s = p, p + 4, ... below six and writes the
+tile of that slot's last chunk.  The consumer waves take the chunks in pairs, each waiting for `ready`,
 reading the operands, writing its quarter of the y tile (or y itself for a
 token-by-token chunk) and counting itself in `done`.
 
@@ -20,7 +21,7 @@ import random
 
 import pytest
 
-SLOTS = 4
+SLOTS = 6
 WAVES = 4
 
 
@@ -51,7 +52,6 @@ class Ring:
 def producer(ring, p):
     """Generator of the producer's steps; yields a predicate while it waits."""
     q = p
-    last = None
     while q < ring.nch:
         s = q % SLOTS
         want = WAVES * (q // SLOTS)
@@ -63,14 +63,14 @@ def producer(ring, p):
         yield None
         ring.exact[s] = 1 if ring.exact_of[q] else 0
         ring.ready[s] = q
-        last = q
         yield None
-        q += SLOTS
-    if last is not None:
-        s = last % SLOTS
-        want = WAVES * (last // SLOTS + 1)
-        yield lambda s=s, want=want: ring.done[s] == want
-        ring.store_tile(s, last)
+        q += WAVES
+    for s in range(p, SLOTS, WAVES):
+        if s < ring.nch:
+            last = s + (ring.nch - 1 - s) // SLOTS * SLOTS
+            want = WAVES * (last // SLOTS + 1)
+            yield lambda s=s, want=want: ring.done[s] == want
+            ring.store_tile(s, last)
 
 
 def consumer(ring, w):
@@ -117,7 +117,7 @@ def run(nch, exact, rng):
     assert ring.y_written == {q: 1 for q in range(nch)}, ring.y_written
 
 
-@pytest.mark.parametrize("nch", [0, 1, 2, 3, 4, 5, 7, 8, 9, 13, 16])
+@pytest.mark.parametrize("nch", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 11, 12, 13, 16, 25])
 def test_ring_hand_over_random_schedules(nch):
     rng = random.Random(1000 + nch)
     for trial in range(60):
@@ -138,7 +138,7 @@ def test_ring_model_catches_an_early_release():
             ring.exact[s] = 1
             ring.ready[s] = q
             yield None
-            q += SLOTS
+            q += WAVES
 
     rng = random.Random(7)
     caught = False
