@@ -19,19 +19,20 @@
 // channels of one batch row; the tokens cut into sub-chunks of kBwdTokens,
 // handed to the waves round-robin as on the forward's chained path):
 //
-//   phase F  forward in time.  Each wave loads k, v of its sub-chunk and
-//            sums them into a partial state (a, b, a', b') from the empty
-//            history (max of the exponents, then the sum); the carry (the state before the sub-chunk) arrives
-//            through LDS, carry (+) partial goes on to the next sub-chunk, and
-//            the carry is stored to the workspace as that sub-chunk's
-//            checkpoint.
+//   phase F  forward in time (skipped when a saving forward has stored the
+//            states).  Each wave loads k, v of its sub-chunk and sums them
+//            into a partial state (a, b) from the empty history (max of the
+//            exponents, then the sum); the carry (the state before the
+//            sub-chunk) arrives through LDS, carry (+) partial goes on to the
+//            next sub-chunk, and the carry is stored to the workspace as that
+//            sub-chunk's checkpoint (two numbers per channel).
 //   phase R  backward in time, sub-chunks from the last.  Each wave loads
 //            k, v, gy and its checkpoint, re-runs the forward recurrence over
-//            the sub-chunk (outputs y_t, 1/D_t, the gu and gw terms) and
-//            sums the sub-chunk's (P, Q) contribution into a partial; the
-//            (P, Q) carry from the later sub-chunk arrives through LDS,
-//            carry (+) partial goes on to the earlier one, and the tokens are
-//            walked backwards from the carry to write gk, gv.  Full
+//            the sub-chunk (y_t and gy_t / D_t) and sums the sub-chunk's
+//            (P, Q, R, U) contribution into a partial; the carry from the
+//            later sub-chunk arrives through LDS, carry (+) partial goes on to
+//            the earlier one, and the tokens are walked backwards from the
+//            carry to write gk, gv and sum the gw, gu terms.  Full
 //            sub-chunks of channels with c = e^{u-w} in [2^-20, 2^20] run in
 //            frames of 8 tokens with one exponential per token (below);
 //            sub-chunks whose values leave the frames' range, and ragged
@@ -67,8 +68,9 @@ __device__ __forceinline__ int bwd_wave_id() { return __builtin_amdgcn_readfirst
 __device__ __forceinline__ int bwd_lane_id() { return threadIdx.x & 63; }
 
 // Forward state in anchor form: exponent p = A - m w; a, b the history sums
-// scaled by e^{-p}.  The same form as the forward kernels' carry, so a
-// forward that saves its carries hands the backward its checkpoints.
+// scaled by e^{-p}.  The same form as the forward kernels' carry; the
+// checkpoints between the phases (and the states a saving forward hands
+// over) keep it in two numbers per channel (to_saved / from_saved).
 struct FState {
     float a, b, A, m;
     __device__ __forceinline__ void set_empty() {
