@@ -93,7 +93,9 @@ def test_forward_parity(device, dtype, per_token, path):
     print(f"y err {ey:.2e} state err {es:.2e}")
 
 
-@pytest.mark.parametrize("shape", [(1, 1, 1), (1, 16, 1), (3, 17, 3), (1, 100, 4), (2, 15, 1)])
+# T = 80, 96, 193: 5, 6 and 13 chunks, around the six-slot ring's wrap
+@pytest.mark.parametrize("shape", [(1, 1, 1), (1, 16, 1), (3, 17, 3), (1, 100, 4), (2, 15, 1),
+                                   (1, 80, 2), (1, 96, 2), (2, 193, 1)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_ragged_shapes(device, shape, dtype):
     B, T, H = shape
