@@ -169,7 +169,7 @@ __device__ __forceinline__ void run_block(Lane<VEC>& s, const typename Io<DT, VE
                                                        float(i % F + 1), keep, GATED ? gd[q] : 1.0f);
                 all_keep[q] = all_keep[q] && keep;
             }
-            if (active) Buf<Raw>::store(IO::pack(yf), yr_, voff, uint32_t(i) * row_bytes);
+            if (active) Buf<Raw>::template store<kStreamStore>(IO::pack(yf), yr_, voff, uint32_t(i) * row_bytes);
         }
     }
     // the last frame starts at token f0 of the block
@@ -669,7 +669,7 @@ __device__ __forceinline__ void run_block_weights(Lane<VEC>& s, const FrameW<VEC
                     s.a[q] = __builtin_fmaf(e, vf[q], s.a[q]);
                     s.b[q] += e;
                 }
-                if (active) Buf<Raw>::store(IO::pack(yf), yr_, voff, uint32_t(i) * row_bytes);
+                if (active) Buf<Raw>::template store<kStreamStore>(IO::pack(yf), yr_, voff, uint32_t(i) * row_bytes);
             }
 #pragma unroll
             for (int q = 0; q < VEC; q++) { s.A[q] = fw.M[f][q]; s.m[q] = float(F); }
@@ -701,7 +701,7 @@ __device__ __forceinline__ void run_block_weights(Lane<VEC>& s, const FrameW<VEC
                     s.a[q] = __builtin_fmaf(et, vf[q], s.a[q]);
                     s.b[q] += et;
                 }
-                if (active) Buf<Raw>::store(IO::pack(yf), yr_, voff, uint32_t(i) * row_bytes);
+                if (active) Buf<Raw>::template store<kStreamStore>(IO::pack(yf), yr_, voff, uint32_t(i) * row_bytes);
             }
 #pragma unroll
             for (int q = 0; q < VEC; q++) {
@@ -733,7 +733,7 @@ __device__ __forceinline__ void run_block_weights(Lane<VEC>& s, const FrameW<VEC
                                                      float(j + 1), kp, GATED ? gd[q] : 1.0f);
                     all_keep[q] = all_keep[q] && kp;
                 }
-                if (active) Buf<Raw>::store(IO::pack(yf), yr_, voff, uint32_t(i) * row_bytes);
+                if (active) Buf<Raw>::template store<kStreamStore>(IO::pack(yf), yr_, voff, uint32_t(i) * row_bytes);
             }
 #pragma unroll
             for (int q = 0; q < VEC; q++) {
