@@ -395,10 +395,12 @@ constexpr int kDefaultLoad = 0;
 
 // Cache policies of the stores: the default one, and device scope (sc1),
 // which writes through the XCD's L2 instead of leaving dirty lines there to
-// be evicted among the reads.  The forward's y streams measure faster with
-// it (the bf16 workload's chained kernel 153.7 -> 147.9 us over 500
-// launches); the backward's gk, gv stores measured slightly slower and keep
-// the default.
+// be evicted among the reads.  The streams written once measure faster with
+// it: the forward's y (the bf16 workload's chained kernel 153.7 -> 147.9 us
+// over 500 launches), the decode step's y and state, the matrix-state
+// forward's y tiles.  The backward's gk, gv stores measured
+// slightly slower and keep the default; the token shift's three outputs go
+// fastest with non-temporal stores (store_stream).
 constexpr int kStreamStore = 16;
 constexpr int kDefaultStore = 0;
 

@@ -576,7 +576,8 @@ __device__ __forceinline__ void ring_store_tile(const MatProblem& pr, MatRing& s
     for (int i = 0; i < 4; i++) yv[i] = *reinterpret_cast<const u32x2_t*>(&op.yt[4 * i + g][4 * nn]);
 #pragma unroll
     for (int i = 0; i < 4; i++)
-        __builtin_amdgcn_raw_buffer_store_b64(yv[i], yr, uint32_t(4 * i + g) * row_bytes + uint32_t(8 * nn), 0u, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(yv[i], yr, uint32_t(4 * i + g) * row_bytes + uint32_t(8 * nn), 0u,
+                                              kStreamStore);
 }
 
 // Producer: the operand tiles of chunk q from the lane's raw inputs into ring
