@@ -539,8 +539,8 @@ __device__ __forceinline__ bool frames_walk(const RState (&r)[VEC], const float 
                 S[q] += grt[j][q];
                 SQ[q] = __builtin_fmaf(grt[j][q], yt[j][q], SQ[q]);
             }
-            Buf<Raw>::store(IO::pack(gkf), gkr_, voff, uint32_t(i) * row_bytes);
-            Buf<Raw>::store(IO::pack(gvf), gvr_, voff, uint32_t(i) * row_bytes);
+            Buf<Raw>::template store<kNonTemporalStore>(IO::pack(gkf), gkr_, voff, uint32_t(i) * row_bytes);
+            Buf<Raw>::template store<kNonTemporalStore>(IO::pack(gvf), gvr_, voff, uint32_t(i) * row_bytes);
         }
     }
     return true;
@@ -642,7 +642,7 @@ struct GradWU {
 // partial of the reverse sums and the hand-off (unless the carry was already
 // taken and kept in `slot`), the walk backwards.  Returns the sub-chunk's gw,
 // gu terms.
-template <typename IO, int L, int VEC, bool FUSED>
+template <typename IO, int L, int VEC, bool FUSED, int LOAD>
 __device__ __forceinline__ GradWU<VEC> token_subchunk(const char* kb, const char* vb, const char* gyb,
                                                       char* gkb, char* gvb, const float* ck, int64_t C,
                                                       Lanes<VEC> ln, int n, int64_t j, int64_t sc,
@@ -657,9 +657,9 @@ __device__ __forceinline__ GradWU<VEC> token_subchunk(const char* kb, const char
     for (int i = 0; i < L; i++) {
         if (i < n) {
             const uint32_t o = ln.voff + uint32_t(i) * ln.row_bytes;
-            kr[i] = Buf<Raw>::template load<kStreamLoad>(kr_, o, 0);
-            vr[i] = Buf<Raw>::template load<kStreamLoad>(vr_, o, 0);
-            gyr[i] = Buf<Raw>::template load<kStreamLoad>(gr_, o, 0);
+            kr[i] = Buf<Raw>::template load<LOAD>(kr_, o, 0);
+            vr[i] = Buf<Raw>::template load<LOAD>(vr_, o, 0);
+            gyr[i] = Buf<Raw>::template load<LOAD>(gr_, o, 0);
         }
     }
     FState s[VEC];
@@ -722,8 +722,8 @@ __device__ __forceinline__ GradWU<VEC> token_subchunk(const char* kb, const char
             for (int q = 0; q < VEC; q++)
                 reverse_detail(r[q], to[i][q], kf[q], vf[q], ln.w[q], i > 0, gkf[q], gvf[q], g.gw[q]);
             const uint32_t o = ln.voff + uint32_t(i) * ln.row_bytes;
-            Buf<Raw>::store(IO::pack(gkf), gkr_, o, 0);
-            Buf<Raw>::store(IO::pack(gvf), gvr_, o, 0);
+            Buf<Raw>::template store<kNonTemporalStore>(IO::pack(gkf), gkr_, o, 0);
+            Buf<Raw>::template store<kNonTemporalStore>(IO::pack(gvf), gvr_, o, 0);
         }
     }
     return g;
@@ -731,12 +731,12 @@ __device__ __forceinline__ GradWU<VEC> token_subchunk(const char* kb, const char
 
 // The same as a call of its own, for the frame loop's fallback: inlined
 // there, its registers and the frame path's would be allocated as one.
-template <typename IO, int L, int VEC, bool FUSED>
+template <typename IO, int L, int VEC, bool FUSED, int LOAD>
 __device__ __attribute__((noinline)) GradWU<VEC> token_subchunk_call(
     const char* kb, const char* vb, const char* gyb, char* gkb, char* gvb, const float* ck, int64_t C,
     Lanes<VEC> ln, int n, int64_t j, int64_t sc, float* s_rc, int* s_rseq, const float* slot,
     bool have_carry) {
-    return token_subchunk<IO, L, VEC, FUSED>(kb, vb, gyb, gkb, gvb, ck, C, ln, n, j, sc, s_rc, s_rseq,
+    return token_subchunk<IO, L, VEC, FUSED, LOAD>(kb, vb, gyb, gkb, gvb, ck, C, ln, n, j, sc, s_rc, s_rseq,
                                              slot, have_carry);
 }
 
@@ -749,6 +749,11 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
     using Raw = typename IO::Raw;
     constexpr int L = kBwdTokens;
     constexpr int CG = 64 * VEC;
+    // cache policy of phase R's k, v, gy loads: non-temporal when they are
+    // read once (saved states); when phase F has read k and v already, the
+    // default policy, so that the second reading can hit the caches (bf16
+    // workload: 439 -> 431-433 us)
+    constexpr int kWalkLoad = SAVED ? kStreamLoad : kDefaultLoad;
     __shared__ float s_fc[4][CG];  // forward carry (a, b, A, m) before sub-chunk s_fseq
     __shared__ float s_rc[6][CG];            // reverse carry after sub-chunk nsub-1-s_rseq
     __shared__ float s_red[2][NWV][CG];      // per-wave gw, gu
@@ -835,8 +840,9 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
 #pragma unroll
         for (int i = 0; i < L; i++) {
             if (i < n) {
-                kr[i] = Buf<Raw>::template load<kStreamLoad>(kr_, voff, uint32_t(i) * row_bytes);
-                vr[i] = Buf<Raw>::template load<kStreamLoad>(vr_, voff, uint32_t(i) * row_bytes);
+                // default policy: phase R reads k and v again (kWalkLoad)
+                kr[i] = Buf<Raw>::template load<kDefaultLoad>(kr_, voff, uint32_t(i) * row_bytes);
+                vr[i] = Buf<Raw>::template load<kDefaultLoad>(vr_, voff, uint32_t(i) * row_bytes);
             }
         }
         // the sub-chunk from the empty history, max then sum: token i has
@@ -973,9 +979,9 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
                     const rsrc_t gr_ = make_rsrc(at(pr.gy, sc));
 #pragma unroll
                     for (int i = 0; i < L; i++) {
-                        kr[i] = Buf<Raw>::template load<kStreamLoad>(kr_, voff, uint32_t(i) * row_bytes);
-                        vr[i] = Buf<Raw>::template load<kStreamLoad>(vr_, voff, uint32_t(i) * row_bytes);
-                        gyr[i] = Buf<Raw>::template load<kStreamLoad>(gr_, voff, uint32_t(i) * row_bytes);
+                        kr[i] = Buf<Raw>::template load<kWalkLoad>(kr_, voff, uint32_t(i) * row_bytes);
+                        vr[i] = Buf<Raw>::template load<kWalkLoad>(vr_, voff, uint32_t(i) * row_bytes);
+                        gyr[i] = Buf<Raw>::template load<kWalkLoad>(gr_, voff, uint32_t(i) * row_bytes);
                     }
                 }
                 FState s[VEC];
@@ -1008,7 +1014,7 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
                     have_carry = true;
                 }
             }
-            add(token_subchunk_call<IO, L, VEC, true>(at(pr.k, sc), at(pr.v, sc), at(pr.gy, sc),
+            add(token_subchunk_call<IO, L, VEC, true, kWalkLoad>(at(pr.k, sc), at(pr.v, sc), at(pr.gy, sc),
                                                       at_out(pr.gk, sc), at_out(pr.gv, sc), ck, C, ln, n,
                                                       j, sc, rc, &s_rseq, slot, have_carry));
         }
@@ -1017,7 +1023,7 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
             const int64_t sc = nsub - 1 - j;
             const int64_t t0 = sc * L;
             const int n = T - t0 >= L ? L : int(T - t0);
-            add(token_subchunk<IO, L, VEC, true>(at(pr.k, sc), at(pr.v, sc), at(pr.gy, sc),
+            add(token_subchunk<IO, L, VEC, true, kWalkLoad>(at(pr.k, sc), at(pr.v, sc), at(pr.gy, sc),
                                                  at_out(pr.gk, sc), at_out(pr.gv, sc),
                                                  ckpt + sc * kCkptFields * C, C, ln, n, j, sc, rc,
                                                  &s_rseq, slot, false));
@@ -1027,7 +1033,7 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
             const int64_t sc = nsub - 1 - j;
             const int64_t t0 = sc * L;
             const int n = T - t0 >= L ? L : int(T - t0);
-            add(token_subchunk<IO, L, VEC, false>(at(pr.k, sc), at(pr.v, sc), at(pr.gy, sc),
+            add(token_subchunk<IO, L, VEC, false, kWalkLoad>(at(pr.k, sc), at(pr.v, sc), at(pr.gy, sc),
                                                   at_out(pr.gk, sc), at_out(pr.gv, sc),
                                                   ckpt + sc * kCkptFields * C, C, ln, n, j, sc, rc,
                                                   &s_rseq, slot, false));

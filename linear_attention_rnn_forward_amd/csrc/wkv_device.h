@@ -398,11 +398,13 @@ constexpr int kDefaultLoad = 0;
 // be evicted among the reads.  The streams written once measure faster with
 // it: the forward's y (the bf16 workload's chained kernel 153.7 -> 147.9 us
 // over 500 launches), the decode step's y and state, the matrix-state
-// forward's y tiles.  The backward's gk, gv stores measured
-// slightly slower and keep the default; the token shift's three outputs go
-// fastest with non-temporal stores (store_stream).
+// forward's y tiles.  The backward's gk, gv and the token shift's three
+// outputs go fastest with non-temporal stores instead.
 constexpr int kStreamStore = 16;
 constexpr int kDefaultStore = 0;
+// Non-temporal stores: the backward's gk, gv (362 -> 339 us for the
+// saved-state backward on the bf16 workload; sc1 measured 364 us there).
+constexpr int kNonTemporalStore = 2;
 
 // A non-temporal load through a plain pointer (2, 4, 8 or 16 bytes), for
 // the elementwise kernels' once-read inputs.
