@@ -911,13 +911,14 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
                 __hip_atomic_store(&s_fseq, int(sc + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         if (active) {
-            float* ck = ckpt + sc * kCkptFields * C;
+            // non-temporal stores, as the forward's saved states (read once)
+            const rsrc_t cs = make_rsrc(pr.ckpt + (bb * nsub + sc) * kCkptFields * C);
 #pragma unroll
             for (int q = 0; q < VEC; q++) {
                 float r, qs;
                 to_saved(x[q].a, x[q].b, __builtin_fmaf(-x[q].m, w[q], x[q].A), r, qs);
-                ck[0 * C + q] = r;
-                ck[1 * C + q] = qs;
+                Buf<float>::template store<kNonTemporalStore>(r, cs, uint32_t(c + q) * 4u, 0u);
+                Buf<float>::template store<kNonTemporalStore>(qs, cs, uint32_t(c + q) * 4u, uint32_t(C) * 4u);
             }
         }
     }

@@ -988,20 +988,23 @@ template <int VEC>
 __device__ __forceinline__ void save_carry(const Lane<VEC>& s, const ForwardProblem& pr, int64_t bb,
                                            int64_t sc, int64_t nsub, int64_t c, bool active) {
     if (!active) return;
-    float* o = pr.states + (bb * nsub + sc) * 2 * pr.C + c;
     float r[VEC], q[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; i++)
         to_saved(s.a[i], s.b[i], __builtin_fmaf(-s.m[i], s.ch[i].w, s.A[i]), r[i], q[i]);
+    // non-temporal stores (read once, by the backward): the saving forward
+    // 172 -> 161-167 us on the bf16 workload, against plain stores
+    const rsrc_t so = make_rsrc(pr.states + (bb * nsub + sc) * 2 * pr.C);
+    const uint32_t field = uint32_t(pr.C) * uint32_t(sizeof(float));
     if constexpr (VEC == 2) {
         // one 8-byte store per field (c is even and the rows 8-byte aligned)
-        *reinterpret_cast<float2*>(o + 0 * pr.C) = make_float2(r[0], r[1]);
-        *reinterpret_cast<float2*>(o + 1 * pr.C) = make_float2(q[0], q[1]);
+        Buf<float2>::template store<kNonTemporalStore>(make_float2(r[0], r[1]), so, uint32_t(c) * 4u, 0u);
+        Buf<float2>::template store<kNonTemporalStore>(make_float2(q[0], q[1]), so, uint32_t(c) * 4u, field);
     } else {
 #pragma unroll
         for (int i = 0; i < VEC; i++) {
-            o[0 * pr.C + i] = r[i];
-            o[1 * pr.C + i] = q[i];
+            Buf<float>::template store<kNonTemporalStore>(r[i], so, uint32_t(c + i) * 4u, 0u);
+            Buf<float>::template store<kNonTemporalStore>(q[i], so, uint32_t(c + i) * 4u, field);
         }
     }
 }
