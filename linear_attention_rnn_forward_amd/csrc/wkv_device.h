@@ -397,9 +397,9 @@ constexpr int kDefaultLoad = 0;
 // which writes through the XCD's L2 instead of leaving dirty lines there to
 // be evicted among the reads.  The streams written once measure faster with
 // it: the forward's y (the bf16 workload's chained kernel 153.7 -> 147.9 us
-// over 500 launches), the decode step's y and state, the matrix-state
-// forward's y tiles.  The backward's gk, gv and the token shift's three
-// outputs go fastest with non-temporal stores instead.
+// over 500 launches) and the matrix-state forward's y tiles.  The
+// backward's gk, gv, the token shift's three outputs and the decode steps'
+// y and state go fastest with non-temporal stores instead.
 constexpr int kStreamStore = 16;
 constexpr int kDefaultStore = 0;
 // Non-temporal stores: the backward's gk, gv (362 -> 339 us for the

@@ -61,19 +61,13 @@ __global__ __launch_bounds__(256) void step_kernel(StepProblem pr, int64_t nvec)
                                    GATED ? gate_den(rf[q]) : 1.0f);
         p[q] = export_p(p[q]);
     }
-    // the outputs at device scope (sc1), each through a descriptor at the
-    // block's first element and the thread's offset from it
-    using FT = typename FV::T;
-    const int64_t i0 = int64_t(blockIdx.x) * blockDim.x;
-    const uint32_t o = threadIdx.x;
-    Buf<Raw>::template store<kStreamStore>(IO::pack(y), make_rsrc(reinterpret_cast<Raw*>(pr.y) + i0),
-                                           o * uint32_t(sizeof(Raw)), 0u);
-    Buf<FT>::template store<kStreamStore>(FV::put(a), make_rsrc(reinterpret_cast<FT*>(pr.a_out) + i0),
-                                          o * uint32_t(sizeof(FT)), 0u);
-    Buf<FT>::template store<kStreamStore>(FV::put(b), make_rsrc(reinterpret_cast<FT*>(pr.b_out) + i0),
-                                          o * uint32_t(sizeof(FT)), 0u);
-    Buf<FT>::template store<kStreamStore>(FV::put(p), make_rsrc(reinterpret_cast<FT*>(pr.p_out) + i0),
-                                          o * uint32_t(sizeof(FT)), 0u);
+    // the outputs through plain non-temporal stores (209.4 us on the decode
+    // workload, against 220.5 with default stores and 210.0 with device-scope
+    // buffer stores)
+    store_stream(reinterpret_cast<Raw*>(pr.y) + i, IO::pack(y));
+    store_stream(reinterpret_cast<typename FV::T*>(pr.a_out) + i, FV::put(a));
+    store_stream(reinterpret_cast<typename FV::T*>(pr.b_out) + i, FV::put(b));
+    store_stream(reinterpret_cast<typename FV::T*>(pr.p_out) + i, FV::put(p));
 }
 
 }  // namespace

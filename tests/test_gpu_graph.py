@@ -191,3 +191,73 @@ def test_mat_step_graph_replay(device):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, y_eager) and torch.equal(st, st_eager)
+
+
+def test_step_graph_replay_full_size(device):
+    """The decode step at the decode workload's size ([32, 256, 4096], state
+    updated in place, 4 steps in one graph): each replay equals the eager
+    chain bit for bit.  The step stores its outputs at device scope; this
+    is the shape at which the chain's bytes far exceed the caches."""
+    import linear_attention_rnn_forward_amd as wkv
+    torch = _torch()
+    Ln, S, C = 32, 256, 4096
+    gen = torch.Generator(device="cpu").manual_seed(47)
+    w = torch.exp(torch.empty(Ln, C).uniform_(-5, 1, generator=gen)).to(device)
+    u = (torch.randn(Ln, C, generator=gen) * 0.5).to(device)
+    ks = [(torch.randn(Ln, S, C, generator=gen) * 2).to(device) for _ in range(4)]
+    vs = [torch.randn(Ln, S, C, generator=gen).to(device) for _ in range(4)]
+    st0 = (torch.rand(Ln, S, C, generator=gen).to(device), torch.rand(Ln, S, C, generator=gen).to(device) + 1,
+           torch.randn(Ln, S, C, generator=gen).to(device))
+    st = tuple(s.clone() for s in st0)
+    y = torch.empty(Ln, S, C, device=device)
+
+    def run():
+        for j in range(4):
+            wkv.step(st, ks[j], vs[j], w, u, out=y, inplace=True)
+
+    run()
+    torch.cuda.synchronize()
+    y_eager, st_eager = y.clone(), tuple(s.clone() for s in st)
+    assert torch.isfinite(y_eager).all()
+    g, _ = _capture(run)
+    for rep in range(2):
+        for s, s0 in zip(st, st0):
+            s.copy_(s0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), rep
+        assert all(torch.equal(a, b) for a, b in zip(st, st_eager)), rep
+
+
+def test_mat_step_graph_replay_full_size(device):
+    """The matrix-state step at the matrix decode workload's size (32 x 64
+    rows of 64 heads, 2.1 GB of state updated in place, 4 steps in one graph):
+    each replay equals the eager chain bit for bit."""
+    import linear_attention_rnn_forward_amd as wkv
+    torch = _torch()
+    Ln, S, H = 32, 64, 64
+    C = 64 * H
+    gen = torch.Generator(device="cpu").manual_seed(53)
+    toks = [tuple(torch.randn((Ln, S, C), generator=gen).to(device) for _ in range(4)) for _ in range(4)]
+    st0 = torch.empty((Ln, S, H, 64, 64), device=device).normal_(0.0, 0.3)
+    st = st0.clone()
+    y = torch.empty((Ln, S, C), device=device)
+
+    def run():
+        for r, k, v, z in toks:
+            wkv.mat_step(st, r, k, v, z, out=y, inplace=True)
+
+    run()
+    torch.cuda.synchronize()
+    y_eager, st_eager = y.clone(), st.clone()
+    assert torch.isfinite(y_eager).all()
+    st.copy_(st0)
+    g, _ = _capture(run)
+    for rep in range(2):
+        st.copy_(st0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), rep
+        assert torch.equal(st, st_eager), rep
