@@ -911,14 +911,17 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
                 __hip_atomic_store(&s_fseq, int(sc + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         if (active) {
-            // non-temporal stores, as the forward's saved states (read once)
-            const rsrc_t cs = make_rsrc(pr.ckpt + (bb * nsub + sc) * kCkptFields * C);
+            // non-temporal stores, as the forward's saved states (read once);
+            // through plain pointers, as phase R reads them (a store through a
+            // buffer descriptor is not ordered by the compiler against loads
+            // through plain pointers)
+            float* ck = ckpt + sc * kCkptFields * C;
 #pragma unroll
             for (int q = 0; q < VEC; q++) {
                 float r, qs;
                 to_saved(x[q].a, x[q].b, __builtin_fmaf(-x[q].m, w[q], x[q].A), r, qs);
-                Buf<float>::template store<kNonTemporalStore>(r, cs, uint32_t(c + q) * 4u, 0u);
-                Buf<float>::template store<kNonTemporalStore>(qs, cs, uint32_t(c + q) * 4u, uint32_t(C) * 4u);
+                store_stream(ck + 0 * C + q, r);
+                store_stream(ck + 1 * C + q, qs);
             }
         }
     }
