@@ -55,6 +55,7 @@ constexpr int kSerialWaves = 4;                  // waves per workgroup on the s
 constexpr int kSerialTokens = WKV_SERIAL_TOKENS; // tokens loaded per batch on the serial path
 constexpr int kChunkTokens = WKV_CHUNK_TOKENS;   // L: tokens per wave on the chunked path
 constexpr int kChunkWaves = WKV_CHUNK_WAVES;     // NW: waves per tile
+constexpr int kChunkWavesWide = 2 * kChunkWaves; // the wide tiles of plan_chunked
 constexpr int kChainTokens = WKV_CHAIN_TOKENS;   // tokens per sub-chunk on the chained path
 constexpr int kFrameTokens = WKV_FRAME_TOKENS;   // tokens per frame of the running maximum
 constexpr uint64_t kSpinTicks = 20000000;  // 200 ms at 100 MHz
@@ -768,13 +769,11 @@ __device__ __forceinline__ bool wave_all_narrow(const Lane<VEC>& s) {
     return __builtin_amdgcn_ballot_w64(!f) == 0;
 }
 
-template <int DT, int VEC, bool GATED>
-__global__ __launch_bounds__(kChunkWaves * 64) void forward_chunked_kernel(ForwardProblem pr,
-                                                                           ChunkArgs ca) {
+template <int DT, int VEC, bool GATED, int NW>
+__global__ __launch_bounds__(NW * 64) void forward_chunked_kernel(ForwardProblem pr, ChunkArgs ca) {
     using IO = Io<DT, VEC>;
     using Raw = typename IO::Raw;
     constexpr int L = kChunkTokens;
-    constexpr int NW = kChunkWaves;
     constexpr int CG = 64 * VEC;
     constexpr int TILE = NW * L;
     // per-wave partial states, then their exclusive prefixes; [NW] = tile carry
@@ -1155,13 +1154,25 @@ int pick_forward_vec(int64_t C, int dtype, bool aligned) {
     return 1;
 }
 
-ChunkPlan plan_chunked(int64_t B, int64_t T, int64_t C, int vec) {
+ChunkPlan plan_chunked(int64_t B, int64_t T, int64_t C, int vec, int waves) {
     ChunkPlan pl;
     pl.vec = vec;
     const int64_t cg = 64 * pl.vec;
     const int64_t gpr = (C + cg - 1) / cg;
     pl.ngroups = B * gpr;
-    pl.tile_tokens = kChunkTokens * kChunkWaves;
+    if (waves == 0) {
+        // tiles of 8 waves; of 16 when the 8-wave tiles would outnumber the
+        // CUs and the 16-wave ones would not (B=8 T=1024 C=768 fp32: 384 tiles
+        // of 8 waves in 21.2 us, 192 of 16 in 19.2 us; at B=1 T=65536 C=4096,
+        // 16-wave tiles ran 610 against 577 us, and 4-wave tiles or 16-token
+        // waves were slower everywhere)
+        const int64_t cus = device_cu_count();
+        const int64_t t8 = pl.ngroups * ((T + kChunkTokens * kChunkWaves - 1) / (kChunkTokens * kChunkWaves));
+        const int64_t t16 = pl.ngroups * ((T + kChunkTokens * kChunkWavesWide - 1) / (kChunkTokens * kChunkWavesWide));
+        waves = (t8 > cus && t16 <= cus) ? kChunkWavesWide : kChunkWaves;
+    }
+    pl.waves = waves;
+    pl.tile_tokens = kChunkTokens * waves;
     pl.tiles_per_group = (T + pl.tile_tokens - 1) / pl.tile_tokens;
     const size_t ntiles = size_t(pl.ngroups) * size_t(pl.tiles_per_group);
     const size_t flags = (ntiles * sizeof(uint64_t) + 255) & ~size_t(255);
@@ -1173,8 +1184,9 @@ ChunkPlan plan_chunked(int64_t B, int64_t T, int64_t C, int vec) {
 size_t forward_workspace_bytes(int64_t B, int64_t T, int64_t C, int dtype, int path) {
     if (path != 2 || T == 0) return 0;
     // the size query does not see the pointers: cover both lane widths
-    const size_t w1 = plan_chunked(B, T, C, 1).workspace_bytes;
-    const size_t w2 = plan_chunked(B, T, C, pick_forward_vec(C, dtype, true)).workspace_bytes;
+    // and both tile widths: the narrower tiles need the larger workspace
+    const size_t w1 = plan_chunked(B, T, C, 1, kChunkWaves).workspace_bytes;
+    const size_t w2 = plan_chunked(B, T, C, pick_forward_vec(C, dtype, true), kChunkWaves).workspace_bytes;
     return w1 > w2 ? w1 : w2;
 }
 
@@ -1268,16 +1280,24 @@ hipError_t launch_forward_serial(const ForwardProblem& pr, hipStream_t stream) {
 }
 
 namespace {
-template <bool GATED>
-void launch_chunked_t(const ForwardProblem& pr, const ChunkArgs& ca, int vec, dim3 grid,
-                      hipStream_t stream) {
-    const dim3 block(kChunkWaves * 64);
+template <bool GATED, int NW>
+void launch_chunked_nw(const ForwardProblem& pr, const ChunkArgs& ca, int vec, dim3 grid,
+                       hipStream_t stream) {
+    const dim3 block(NW * 64);
     if (pr.dtype == kBF16 && vec == 2)
-        hipLaunchKernelGGL((forward_chunked_kernel<kBF16, 2, GATED>), grid, block, 0, stream, pr, ca);
+        hipLaunchKernelGGL((forward_chunked_kernel<kBF16, 2, GATED, NW>), grid, block, 0, stream, pr, ca);
     else if (pr.dtype == kBF16)
-        hipLaunchKernelGGL((forward_chunked_kernel<kBF16, 1, GATED>), grid, block, 0, stream, pr, ca);
+        hipLaunchKernelGGL((forward_chunked_kernel<kBF16, 1, GATED, NW>), grid, block, 0, stream, pr, ca);
     else
-        hipLaunchKernelGGL((forward_chunked_kernel<kF32, 1, GATED>), grid, block, 0, stream, pr, ca);
+        hipLaunchKernelGGL((forward_chunked_kernel<kF32, 1, GATED, NW>), grid, block, 0, stream, pr, ca);
+}
+template <bool GATED>
+void launch_chunked_t(const ForwardProblem& pr, const ChunkArgs& ca, int vec, int waves, dim3 grid,
+                      hipStream_t stream) {
+    if (waves == kChunkWavesWide)
+        launch_chunked_nw<GATED, kChunkWavesWide>(pr, ca, vec, grid, stream);
+    else
+        launch_chunked_nw<GATED, kChunkWaves>(pr, ca, vec, grid, stream);
 }
 }  // namespace
 
@@ -1299,9 +1319,9 @@ hipError_t launch_forward_chunked(const ForwardProblem& pr, void* workspace, hip
                        stream, ca.ticket, ca.flags, int64_t(ntiles));
     const dim3 grid(static_cast<unsigned>(ntiles));
     if (pr.r != nullptr)
-        launch_chunked_t<true>(pr, ca, pl.vec, grid, stream);
+        launch_chunked_t<true>(pr, ca, pl.vec, pl.waves, grid, stream);
     else
-        launch_chunked_t<false>(pr, ca, pl.vec, grid, stream);
+        launch_chunked_t<false>(pr, ca, pl.vec, pl.waves, grid, stream);
     return hipGetLastError();
 }
 

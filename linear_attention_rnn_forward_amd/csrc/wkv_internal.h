@@ -28,13 +28,16 @@ struct ChunkPlan {
     int vec;                 // channels per lane
     int64_t ngroups;         // column groups: B * ceil(C / (64 * vec))
     int64_t tiles_per_group; // ceil(T / tile_tokens)
+    int waves;               // waves per tile (workgroup)
     int tile_tokens;         // tokens per workgroup tile
     size_t workspace_bytes;
 };
 
 // Which path wkv_forward takes for a problem (never returns WKV_PATH_AUTO).
 int choose_forward_path(const ForwardProblem& pr, int device_cus);
-ChunkPlan plan_chunked(int64_t B, int64_t T, int64_t C, int vec);
+// waves: 0 to choose from the problem and the current device, else the
+// waves per tile to plan for.
+ChunkPlan plan_chunked(int64_t B, int64_t T, int64_t C, int vec, int waves = 0);
 // Channels per lane for wkv_forward: 2 for bf16 when C is even and k, v, y
 // are 4-byte aligned, else 1.
 int pick_forward_vec(int64_t C, int dtype, bool aligned);

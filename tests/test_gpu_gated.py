@@ -127,3 +127,27 @@ def test_gated_step_matches_oracle_and_forward(device, dtype, C):
     chain = torch.stack(outs, dim=1)
     tol = 1e-5 if dtype == "f32" else 2.0 ** -7
     assert guarded_rel_err(host(chain), host(o_f), 1.0) <= tol
+
+
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("dtype,C", [("f32", 768), ("bf16", 1536)])
+def test_chunked_wide_tiles_match_oracle(device, dtype, C, gated):
+    """96 column groups over 1000 tokens: 384 tiles of 8 waves would outnumber
+    the 256 CUs while 192 tiles of 16 waves do not, so the chunked path takes
+    the 16-wave tiles (a ragged last tile included); plain and gated outputs
+    and the final state against the oracle."""
+    import linear_attention_rnn_forward_amd as wkv
+    torch = _torch()
+    wl = synth.SMALL_LM.resized(B=8, T=1000, C=C, seed=71, dtype=dtype)
+    x, r, k, v, rd, w, u = _inputs(device, wl)
+    out, st = wkv.forward(k, v, w, u, r=rd if gated else None, path="chunked", return_state=True)
+    torch.cuda.synchronize()
+    if gated:
+        ref, st_ref = oracle.forward_gated(x.k, x.v, r, x.w, x.u)
+    else:
+        ref, st_ref = oracle.forward(x.k, x.v, x.w, x.u)
+    err = guarded_rel_err(host(out), ref, rms(x.v))
+    assert np.all(np.isfinite(host(out)))
+    assert err <= TOL[dtype], f"rel err {err:.3e}"
+    ea, eb, ep = state_mismatch(tuple(host(s) for s in st), st_ref)
+    assert ea <= 1e-4 and eb <= 1e-4 and ep <= 1e-4, (ea, eb, ep)
