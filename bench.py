@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -53,15 +54,25 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and blank lines (comments do not
+    change the compiled kernels; the sources hold no comment markers inside
+    string literals)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def kernel_source_hash(workload: str) -> str:
-    """Hash of the kernel sources of `workload` (every source when unknown)."""
+    """Hash of the code (comments left out) of the kernel sources of
+    `workload` (every source when unknown)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_rnn_forward_amd", "csrc")
     names = KERNEL_SOURCES.get(workload) or sorted(os.listdir(csrc))
     for name in sorted(names):
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -911,10 +911,12 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
                 __hip_atomic_store(&s_fseq, int(sc + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         if (active) {
-            // non-temporal stores, as the forward's saved states (read once);
-            // through plain pointers, as phase R reads them (a store through a
-            // buffer descriptor is not ordered by the compiler against loads
-            // through plain pointers)
+            // non-temporal stores, as the forward's saved states (read once),
+            // through plain pointers like phase R's loads of them: the
+            // matrix-state step's in-place state, written through a buffer
+            // descriptor and read through plain pointers, came out
+            // nondeterministic (cause not found), so no value a kernel reads
+            // back is written that way
             float* ck = ckpt + sc * kCkptFields * C;
 #pragma unroll
             for (int q = 0; q < VEC; q++) {

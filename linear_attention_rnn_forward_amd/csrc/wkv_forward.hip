@@ -1184,7 +1184,8 @@ ChunkPlan plan_chunked(int64_t B, int64_t T, int64_t C, int vec, int waves) {
 size_t forward_workspace_bytes(int64_t B, int64_t T, int64_t C, int dtype, int path) {
     if (path != 2 || T == 0) return 0;
     // the size query does not see the pointers: cover both lane widths
-    // and both tile widths: the narrower tiles need the larger workspace
+    // and 8-wave tiles: the chosen width may be 16 waves, whose fewer tiles
+    // need less
     const size_t w1 = plan_chunked(B, T, C, 1, kChunkWaves).workspace_bytes;
     const size_t w2 = plan_chunked(B, T, C, pick_forward_vec(C, dtype, true), kChunkWaves).workspace_bytes;
     return w1 > w2 ? w1 : w2;

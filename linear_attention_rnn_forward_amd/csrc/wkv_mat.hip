@@ -880,9 +880,11 @@ __global__ __launch_bounds__(256) void mat_step_kernel(MatStepProblem pr) {
             y[3] = __builtin_fmaf(rr[j], s4.w, y[3]);
         }
     }
-    // non-temporal stores of the state (830 -> 808 us on the decode workload);
-    // plain pointer stores: through a buffer descriptor the 200-step graph
-    // replay did not match the eager re-run bit for bit
+    // non-temporal stores of the state (830 -> 808 us on the decode workload),
+    // through plain pointers: written through a buffer descriptor (either
+    // cache policy) the in-place state came out nondeterministic at the decode
+    // workload's size, two eager runs from one state differing in a few heads
+    // (cause not found; tests/test_gpu_graph.py checks the full size)
 #pragma unroll
     for (int m = 0; m < 16; m++) store_stream(reinterpret_cast<float4*>(pr.s_out + sb + m * 4 * kN), st[m]);
     // the four row groups hold partial sums over disjoint rows
