@@ -912,11 +912,11 @@ __global__ __launch_bounds__(NWV * 64) void backward_chained_kernel(BackwardProb
         }
         if (active) {
             // non-temporal stores, as the forward's saved states (read once),
-            // through plain pointers like phase R's loads of them: the
-            // matrix-state step's in-place state, written through a buffer
-            // descriptor and read through plain pointers, came out
-            // nondeterministic (cause not found), so no value a kernel reads
-            // back is written that way
+            // through plain pointers like phase R's loads of them: memory a
+            // kernel reads back goes through one kind of access (the
+            // matrix-state step's in-place state, read through plain pointers
+            // and written through a buffer descriptor, came out
+            // nondeterministic; both through the descriptor, it did not)
             float* ck = ckpt + sc * kCkptFields * C;
 #pragma unroll
             for (int q = 0; q < VEC; q++) {

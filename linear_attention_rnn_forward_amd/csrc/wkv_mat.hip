@@ -881,10 +881,13 @@ __global__ __launch_bounds__(256) void mat_step_kernel(MatStepProblem pr) {
         }
     }
     // non-temporal stores of the state (830 -> 808 us on the decode workload),
-    // through plain pointers: written through a buffer descriptor (either
-    // cache policy) the in-place state came out nondeterministic at the decode
-    // workload's size, two eager runs from one state differing in a few heads
-    // (cause not found; tests/test_gpu_graph.py checks the full size)
+    // through plain pointers like its loads: stored through a buffer
+    // descriptor (either cache policy) while loaded through plain pointers,
+    // the in-place state came out nondeterministic at the decode workload's
+    // size (two eager runs from one state differing in a few heads), where
+    // loads and stores both through the descriptor were deterministic; the
+    // cause inside that mix was not found (tests/test_gpu_graph.py checks the
+    // full size)
 #pragma unroll
     for (int m = 0; m < 16; m++) store_stream(reinterpret_cast<float4*>(pr.s_out + sb + m * 4 * kN), st[m]);
     // the four row groups hold partial sums over disjoint rows
