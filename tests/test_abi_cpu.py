@@ -130,6 +130,17 @@ def test_workspace_sizes():
     assert L.wkv_forward_workspace_size_path(0, 10, 10, 0, 2) == 0
 
 
+def test_chunked_workspace_covers_both_tile_widths():
+    # B=8 T=1024 C=768 fp32 takes 16-wave tiles on a 256-CU part (192 tiles);
+    # the size query plans for 8-wave tiles (384), the larger workspace:
+    # 256 bytes of counters, a 256-byte-rounded 8-byte flag per tile and two
+    # 4-field fp32 descriptors of 64 channels per tile
+    L = wkv.lib()
+    tiles = 8 * (768 // 64) * (1024 // 256)
+    flags = (tiles * 8 + 255) // 256 * 256
+    assert L.wkv_forward_workspace_size_path(8, 1024, 768, 0, 2) == 256 + flags + tiles * 2 * 4 * 64 * 4
+
+
 def test_auto_path_query():
     # without a visible device the library assumes 256 compute units (MI355X)
     assert wkv.auto_path(16, 4096, 2048, wkv.BF16) == "chained"   # 256 column groups
